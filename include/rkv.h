@@ -1,0 +1,205 @@
+/*
+ * rkv.h - C ABI of the ResidualKV cache codec for AMD MI355X (gfx950).
+ *
+ * The codec follows the ResidualKV review page ("ResidualKV: 基于参考向量与残差的
+ * KV Cache 压缩", review of arXiv 2602.08005v2):
+ *   - a sparse pool of reference tokens stored directly in FP8 (section 2.4,
+ *     section 2.6 fixed stride, section 2.7 step 4);
+ *   - every other token stored as a per-token group-quantized latent residual
+ *     z = f_c(kv) - f_c(mean of its k nearest references) (sections 2.2-2.4);
+ *   - restore of selected tokens: dequantize, z W_d + mean, split K/V, RoPE at the
+ *     token's own position (section 2.5, section 2.1 last paragraph, section 2.7).
+ *
+ * Conventions shared by every entry point
+ *   - All array pointers are DEVICE pointers owned by the caller. The library never
+ *     allocates, frees or synchronises; all work is enqueued on `stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream) and runs
+ *     asynchronously.
+ *   - Host-side argument checks run before anything is launched; a failed check
+ *     returns a negative rkv_status and launches nothing.
+ *   - Conditions only the device can see (an empty reference pool, a position or
+ *     index out of range, a full pool) set bits of cache->err_word (RKV_DEVERR_*)
+ *     when err_word is not NULL; the offending token is skipped or written with
+ *     an empty reference set as documented per call.
+ *   - A failed kernel launch returns RKV_ERR_HIP.
+ *   - No global mutable state: calls are reentrant; calls that write the same
+ *     cache must be ordered by the caller (same stream or events).
+ *
+ * Layouts (row-major, C order; B = batch of independent sequences)
+ *   joint vector width  W2  = 2 * d_k = 2 * n_kv_heads * head_dim, K heads first
+ *                         then V heads (section 2.1: kv_i is the K|V concatenation)
+ *   kv input             [B, kv_len, W2]        kv_dtype
+ *   codec weights        nn.Linear layout [out_features, in_features]:
+ *                         w_c1, w_c2 [d_ff, W2]; w_c3 [d_c, d_ff]; w_d [W2, d_c]
+ *                         (the pages write x W with W [in, out]; these are W^T)
+ *   reference pool       ref_vals  [B, cap_ref, W2]  ref_dtype
+ *                         ref_pos   [B, cap_ref] int32 token position of each slot
+ *                         ref_norm2 [B, cap_ref] fp32 squared norm of the stored row
+ *                         ref_count [B] int32 number of filled slots
+ *   per-token records    codes     [B, cap_tok, d_c*bits/8] uint8 (bits = 16: fp16 latent,
+ *                                   2*d_c bytes); INT4 low nibble = even coordinate,
+ *                                   INT2 bits [2c, 2c+1] = coordinate 4m + c
+ *                         scale, zmin [B, cap_tok, d_c/group] scale_dtype: the group's
+ *                                   step Delta and minimum (section 2.4)
+ *                         ref_idx   [B, cap_tok, top_k] int32 pool slots of the chosen
+ *                                   references, ascending, -1 padded
+ *                         self_slot [B, cap_tok] int32 pool slot of a reference token,
+ *                                   -1 for an encoded token (caller initialises to -1)
+ *   decode output        [B, m, W2] = [B, m, 2, n_kv_heads, head_dim], out_dtype
+ */
+#ifndef RKV_H
+#define RKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RKV_ABI_VERSION 1
+
+typedef enum {
+    RKV_OK = 0,
+    RKV_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shape      */
+    RKV_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype combo, head_dim..)  */
+    RKV_ERR_CAPACITY = -3,    /* n or m larger than the declared capacities          */
+    RKV_ERR_ALIGNMENT = -4,   /* a pointer not 16-byte aligned                        */
+    RKV_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed           */
+    RKV_ERR_WORKSPACE = -6    /* workspace missing or smaller than required           */
+} rkv_status;
+
+typedef enum { RKV_F32 = 0, RKV_BF16 = 1, RKV_F16 = 2, RKV_FP8_E4M3 = 3 } rkv_dtype;
+
+/* Device-side error bits written to rkv_cache.err_word (atomic OR). */
+#define RKV_DEVERR_EMPTY_POOL 1   /* a token had no reference with position < its own     */
+#define RKV_DEVERR_POS_RANGE 2    /* a position outside [0, cap_tok)                      */
+#define RKV_DEVERR_REF_CAPACITY 4 /* append past cap_ref                                  */
+#define RKV_DEVERR_IDX_RANGE 8    /* a selected index outside [0, cap_tok)                */
+#define RKV_DEVERR_ROW_RANGE 16   /* a kv row index outside [0, kv_len)                   */
+
+/* Static description of one layer's codec. Supported combinations:
+ *   "bf16": kv BF16, references FP8_E4M3 (OCP e4m3fn, no scale), weights BF16,
+ *           scale/zmin F16                                   (the deployment formats)
+ *   "f32" : kv F32, references F32, weights F32, scale/zmin F32      (exact reference runs)
+ * Shapes: head_dim in {32, 64, 128}; W2 % 128 == 0; d_k % 128 == 0; d_ff % 64 == 0;
+ * d_c % 64 == 0 and d_c <= 512; group == 32; bits in {2, 4, 16 (= quantization off,
+ * fp16 latent)}; 1 <= top_k <= 8. */
+typedef struct {
+    int32_t n_kv_heads; /* N                                             */
+    int32_t head_dim;   /* D                                             */
+    int32_t d_ff;       /* compressor hidden width (section 2.3)          */
+    int32_t d_c;        /* latent width (section 2.3)                     */
+    int32_t top_k;      /* k, references per token (section 2.2)          */
+    int32_t bits;       /* residual code width b (section 2.4)            */
+    int32_t group;      /* group size g (section 2.4)                     */
+    int32_t kv_dtype;     /* rkv_dtype */
+    int32_t ref_dtype;    /* rkv_dtype */
+    int32_t scale_dtype;  /* rkv_dtype */
+    int32_t weight_dtype; /* rkv_dtype */
+    int32_t reserved;
+    double rope_theta;  /* RoPE base theta                               */
+} rkv_config;
+
+/* Codec weights of one layer, nn.Linear layout (see above), weight_dtype. */
+typedef struct {
+    const void* w_c1;
+    const void* w_c2;
+    const void* w_c3;
+    const void* w_d;
+} rkv_weights;
+
+/* Cache state of one layer for a batch of B sequences; all arrays caller-owned. */
+typedef struct {
+    int32_t batch;
+    int32_t cap_ref;
+    int32_t cap_tok;
+    int32_t reserved;
+    void* ref_vals;
+    int32_t* ref_pos;
+    float* ref_norm2;
+    int32_t* ref_count;
+    uint8_t* codes;
+    void* scale;
+    void* zmin;
+    int32_t* ref_idx;
+    int32_t* self_slot;
+    int32_t* err_word; /* optional (may be NULL) */
+} rkv_cache;
+
+/* Version of this ABI (RKV_ABI_VERSION). */
+int32_t rkv_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* rkv_status_string(rkv_status status);
+
+/* Host-only check of a configuration (no GPU needed): RKV_OK, RKV_ERR_INVALID_ARG
+ * for nonsense values, RKV_ERR_UNSUPPORTED for valid but unimplemented ones. */
+rkv_status rkv_validate_config(const rkv_config* cfg);
+
+/* Bytes of one sequence's record arrays, written to out[0..4]:
+ * codes, scale, zmin, ref_idx, self_slot (per token), and pool row bytes in out[5].
+ * Host-only. Returns RKV_OK or the rkv_validate_config status. */
+rkv_status rkv_record_bytes(const rkv_config* cfg, size_t out[6]);
+
+/* Workspace bytes rkv_encode needs for `batch` sequences of `n` tokens with a pool
+ * capacity of cap_ref. Host-only; 0 on an invalid configuration. */
+size_t rkv_encode_workspace_bytes(const rkv_config* cfg, int32_t batch, int32_t n, int32_t cap_ref);
+
+/* Store tokens directly as references (section 2.7 step 4; FP8 storage, section 2.4).
+ *   kv   [B, kv_len, W2] kv_dtype; rows [B, n] row of kv per token; pos [B, n] positions.
+ * Token r of sequence b goes to pool slot ref_count[b] + r, stored in ref_dtype
+ * (FP8: round to nearest even, saturating at +-448, sign kept); ref_pos and
+ * ref_norm2 of the slot and self_slot[b, pos] are set, then ref_count[b] += n
+ * (clamped to cap_ref). Out-of-range rows/positions and slots >= cap_ref are skipped
+ * and flagged. Positions must be appended in increasing order for the encode's
+ * causal pool (reference position < token position) to be a prefix. */
+rkv_status rkv_append_ref(const rkv_config* cfg, rkv_cache* cache, const void* kv, int32_t kv_len,
+                          const int32_t* rows, const int32_t* pos, int32_t n, void* stream);
+
+/* Encode tokens into residual records (sections 2.2-2.4).
+ *   kv [B, kv_len, W2], rows [B, n], pos [B, n] as for rkv_append_ref.
+ * For each token: the k_i = min(top_k, #{slots with ref_pos < pos}) references with
+ * the smallest squared L2 distance to kv (ties: lower slot) over the stored
+ * reference values; their fp32 mean (ascending-slot sum, one IEEE division), rounded
+ * to kv_dtype for the encoder; z = f_c(kv) - f_c(mean) with
+ * f_c(x) = (SiLU(x W_c1) * x W_c2) W_c3; then per group of 32 coordinates:
+ * Delta = (max - min)/(2^b - 1), stored Delta and min in scale_dtype,
+ * q = clamp(rint((z - min)/Delta), 0, 2^b - 1) (q = 0 when the stored Delta is 0);
+ * bits = 16 stores fp16(z) instead. Writes codes/scale/zmin/ref_idx at [b, pos].
+ * A token with an empty pool gets ref_idx = -1, a zero mean, and the
+ * RKV_DEVERR_EMPTY_POOL bit. workspace: >= rkv_encode_workspace_bytes(cfg, B, n,
+ * cap_ref) bytes of device memory, 256-byte aligned, owned by the caller, free to
+ * reuse once the stream has passed this call. */
+rkv_status rkv_encode(const rkv_config* cfg, const rkv_weights* w, rkv_cache* cache, const void* kv,
+                      int32_t kv_len, const int32_t* rows, const int32_t* pos, int32_t n, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Number of kernels rkv_encode runs, in order: reference search, reference
+ * selection + mean, SwiGLU hidden difference, W_c3 projection + group quantizer. */
+#define RKV_ENCODE_PHASES 4
+
+/* rkv_encode with optional per-kernel timing, for profiling harnesses. `events` is
+ * NULL or points to RKV_ENCODE_PHASES + 1 hipEvent_t handles (created by the caller);
+ * events[i] is recorded on `stream` just before kernel i and events[RKV_ENCODE_PHASES]
+ * after the last one. Everything else is exactly rkv_encode. */
+rkv_status rkv_encode_ex(const rkv_config* cfg, const rkv_weights* w, rkv_cache* cache, const void* kv,
+                         int32_t kv_len, const int32_t* rows, const int32_t* pos, int32_t n, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* events);
+
+/* Restore selected tokens (section 2.5 boxed equation, section 2.7 steps 2-3).
+ *   idx [B, m] token positions (any order; sorted gives the best locality).
+ * out[b, t] = K|V of token idx[b, t]: a reference token yields its stored value;
+ * an encoded token yields z~ W_d + mean, z~ = q * Delta + min (or the fp16 latent),
+ * mean = fp32 mean of its stored references. The K half is then rotated by RoPE at
+ * position idx[b, t]: pair (j, j + D/2) of each head by angle p * theta^(-2j/D).
+ * out_dtype: RKV_F32 or RKV_BF16. Indices outside [0, cap_tok) produce zeros and
+ * the RKV_DEVERR_IDX_RANGE bit. */
+rkv_status rkv_decode_selected(const rkv_config* cfg, const rkv_weights* w, const rkv_cache* cache,
+                               const int32_t* idx, int32_t m, void* out, int32_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RKV_H */

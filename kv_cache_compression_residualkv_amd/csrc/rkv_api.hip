@@ -1,0 +1,209 @@
+// C ABI of the codec: host-side validation, then asynchronous launches on the
+// caller's stream. Nothing here allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "rkv.h"
+#include "rkv_internal.h"
+
+using namespace rkv;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dtype_size(int dt) {
+    switch (dt) {
+        case RKV_F32: return 4;
+        case RKV_BF16: return 2;
+        case RKV_F16: return 2;
+        case RKV_FP8_E4M3: return 1;
+        default: return 0;
+    }
+}
+
+rkv_status check_config(const rkv_config* cfg, Shape* out) {
+    if (!cfg) return RKV_ERR_INVALID_ARG;
+    if (cfg->n_kv_heads <= 0 || cfg->head_dim <= 0 || cfg->d_ff <= 0 || cfg->d_c <= 0 || cfg->top_k <= 0 ||
+        cfg->group <= 0 || !(cfg->rope_theta > 0.0) || (cfg->head_dim & 1))
+        return RKV_ERR_INVALID_ARG;
+    if (dtype_size(cfg->kv_dtype) == 0 || dtype_size(cfg->ref_dtype) == 0 || dtype_size(cfg->scale_dtype) == 0 ||
+        dtype_size(cfg->weight_dtype) == 0)
+        return RKV_ERR_INVALID_ARG;
+    if (cfg->bits != 2 && cfg->bits != 4 && cfg->bits != 16) return RKV_ERR_UNSUPPORTED;
+    const bool f32 = cfg->kv_dtype == RKV_F32 && cfg->ref_dtype == RKV_F32 && cfg->scale_dtype == RKV_F32 &&
+                     cfg->weight_dtype == RKV_F32;
+    const bool bf16 = cfg->kv_dtype == RKV_BF16 && cfg->ref_dtype == RKV_FP8_E4M3 && cfg->scale_dtype == RKV_F16 &&
+                      cfg->weight_dtype == RKV_BF16;
+    if (!f32 && !bf16) return RKV_ERR_UNSUPPORTED;
+    const int D = cfg->head_dim;
+    if (D != 32 && D != 64 && D != 128) return RKV_ERR_UNSUPPORTED;
+    const long dk = (long)cfg->n_kv_heads * D;
+    if (dk > (1 << 20)) return RKV_ERR_UNSUPPORTED;
+    if (dk % 128 != 0) return RKV_ERR_UNSUPPORTED;
+    if (cfg->d_ff % 64 != 0 || cfg->d_c % 64 != 0 || cfg->d_c > 512) return RKV_ERR_UNSUPPORTED;
+    if (cfg->group != 32) return RKV_ERR_UNSUPPORTED;
+    if (cfg->top_k > 8) return RKV_ERR_UNSUPPORTED;
+    if (out) {
+        out->N = cfg->n_kv_heads;
+        out->D = D;
+        out->dk = (int)dk;
+        out->W2 = (int)(2 * dk);
+        out->d_ff = cfg->d_ff;
+        out->d_c = cfg->d_c;
+        out->top_k = cfg->top_k;
+        out->bits = cfg->bits;
+        out->group = cfg->group;
+        out->G = cfg->d_c / cfg->group;
+        out->f32 = f32;
+        out->theta = cfg->rope_theta;
+    }
+    return RKV_OK;
+}
+
+size_t code_bytes_of(const Shape& s) { return (size_t)s.d_c * s.bits / 8; }
+
+rkv_status check_cache(const Shape& s, const rkv_cache* c, bool need_records, CacheView* v) {
+    if (!c) return RKV_ERR_INVALID_ARG;
+    if (c->batch <= 0 || c->cap_ref <= 0 || c->cap_tok <= 0) return RKV_ERR_INVALID_ARG;
+    if (!c->ref_vals || !c->ref_pos || !c->ref_norm2 || !c->ref_count || !c->self_slot) return RKV_ERR_INVALID_ARG;
+    if (need_records && (!c->codes || !c->ref_idx || (s.bits != 16 && (!c->scale || !c->zmin))))
+        return RKV_ERR_INVALID_ARG;
+    if (!aligned16(c->ref_vals) || (c->codes && !aligned16(c->codes))) return RKV_ERR_ALIGNMENT;
+    if ((c->scale && !aligned16(c->scale)) || (c->zmin && !aligned16(c->zmin))) return RKV_ERR_ALIGNMENT;
+    v->B = c->batch;
+    v->cap_ref = c->cap_ref;
+    v->cap_tok = c->cap_tok;
+    v->ref_vals = c->ref_vals;
+    v->ref_pos = c->ref_pos;
+    v->ref_norm2 = c->ref_norm2;
+    v->ref_count = c->ref_count;
+    v->codes = c->codes;
+    v->scale = c->scale;
+    v->zmin = c->zmin;
+    v->ref_idx = c->ref_idx;
+    v->self_slot = c->self_slot;
+    v->err = c->err_word;
+    v->code_bytes = code_bytes_of(s);
+    return RKV_OK;
+}
+
+rkv_status from_hip(hipError_t e) { return e == hipSuccess ? RKV_OK : RKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t rkv_abi_version(void) { return RKV_ABI_VERSION; }
+
+const char* rkv_status_string(rkv_status s) {
+    switch (s) {
+        case RKV_OK: return "ok";
+        case RKV_ERR_INVALID_ARG: return "invalid argument";
+        case RKV_ERR_UNSUPPORTED: return "unsupported configuration";
+        case RKV_ERR_CAPACITY: return "capacity exceeded";
+        case RKV_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+        case RKV_ERR_HIP: return "HIP runtime error";
+        case RKV_ERR_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+rkv_status rkv_validate_config(const rkv_config* cfg) { return check_config(cfg, nullptr); }
+
+rkv_status rkv_record_bytes(const rkv_config* cfg, size_t out[6]) {
+    Shape s;
+    const rkv_status st = check_config(cfg, &s);
+    if (st != RKV_OK) return st;
+    if (!out) return RKV_ERR_INVALID_ARG;
+    const size_t sc = s.bits == 16 ? 0 : dtype_size(cfg->scale_dtype);
+    out[0] = code_bytes_of(s);
+    out[1] = (size_t)s.G * sc;
+    out[2] = (size_t)s.G * sc;
+    out[3] = (size_t)s.top_k * sizeof(int32_t);
+    out[4] = sizeof(int32_t);
+    out[5] = (size_t)s.W2 * dtype_size(cfg->ref_dtype);
+    return RKV_OK;
+}
+
+size_t rkv_encode_workspace_bytes(const rkv_config* cfg, int32_t batch, int32_t n, int32_t cap_ref) {
+    Shape s;
+    if (check_config(cfg, &s) != RKV_OK || batch <= 0 || n < 0 || cap_ref <= 0) return 0;
+    return plan_encode(s, batch, n, cap_ref).total;
+}
+
+rkv_status rkv_append_ref(const rkv_config* cfg, rkv_cache* cache, const void* kv, int32_t kv_len,
+                          const int32_t* rows, const int32_t* pos, int32_t n, void* stream) {
+    Shape s;
+    rkv_status st = check_config(cfg, &s);
+    if (st != RKV_OK) return st;
+    CacheView c;
+    st = check_cache(s, cache, false, &c);
+    if (st != RKV_OK) return st;
+    if (n < 0 || kv_len < 0) return RKV_ERR_INVALID_ARG;
+    if (n == 0) return RKV_OK;
+    if (!kv || !rows || !pos) return RKV_ERR_INVALID_ARG;
+    if (!aligned16(kv)) return RKV_ERR_ALIGNMENT;
+    if (n > cache->cap_ref) return RKV_ERR_CAPACITY;
+    return from_hip(launch_append(s, c, kv, kv_len, rows, pos, n, static_cast<hipStream_t>(stream)));
+}
+
+rkv_status rkv_encode_ex(const rkv_config* cfg, const rkv_weights* w, rkv_cache* cache, const void* kv,
+                         int32_t kv_len, const int32_t* rows, const int32_t* pos, int32_t n, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* events) {
+    Shape s;
+    rkv_status st = check_config(cfg, &s);
+    if (st != RKV_OK) return st;
+    CacheView c;
+    st = check_cache(s, cache, true, &c);
+    if (st != RKV_OK) return st;
+    if (n < 0 || kv_len < 0) return RKV_ERR_INVALID_ARG;
+    if (n == 0) return RKV_OK;
+    if (!w || !w->w_c1 || !w->w_c2 || !w->w_c3 || !kv || !rows || !pos) return RKV_ERR_INVALID_ARG;
+    if (!aligned16(kv) || !aligned16(w->w_c1) || !aligned16(w->w_c2) || !aligned16(w->w_c3))
+        return RKV_ERR_ALIGNMENT;
+    if (n > cache->cap_tok) return RKV_ERR_CAPACITY;
+    const EncodePlan p = plan_encode(s, c.B, n, c.cap_ref);
+    if (!workspace || workspace_bytes < p.total) return RKV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RKV_ERR_ALIGNMENT;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) -> hipError_t {
+        return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) : hipSuccess;
+    };
+    hipError_t e = mark(0);
+    if (e == hipSuccess) e = launch_search(s, c, p, kv, kv_len, rows, pos, n, workspace, hs);
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess) e = launch_select(s, c, p, kv, kv_len, rows, pos, n, workspace, hs);
+    if (e == hipSuccess) e = mark(2);
+    if (e == hipSuccess) e = launch_swiglu(s, c, p, kv, kv_len, rows, n, w->w_c1, w->w_c2, workspace, hs);
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) e = launch_latent_quant(s, c, p, pos, n, w->w_c3, workspace, hs);
+    if (e == hipSuccess) e = mark(4);
+    return from_hip(e);
+}
+
+rkv_status rkv_encode(const rkv_config* cfg, const rkv_weights* w, rkv_cache* cache, const void* kv,
+                      int32_t kv_len, const int32_t* rows, const int32_t* pos, int32_t n, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    return rkv_encode_ex(cfg, w, cache, kv, kv_len, rows, pos, n, workspace, workspace_bytes, stream, nullptr);
+}
+
+rkv_status rkv_decode_selected(const rkv_config* cfg, const rkv_weights* w, const rkv_cache* cache,
+                               const int32_t* idx, int32_t m, void* out, int32_t out_dtype, void* stream) {
+    Shape s;
+    rkv_status st = check_config(cfg, &s);
+    if (st != RKV_OK) return st;
+    CacheView c;
+    st = check_cache(s, cache, true, &c);
+    if (st != RKV_OK) return st;
+    if (m < 0) return RKV_ERR_INVALID_ARG;
+    if (out_dtype != RKV_F32 && out_dtype != RKV_BF16) return RKV_ERR_UNSUPPORTED;
+    if (m == 0) return RKV_OK;
+    if (!w || !w->w_d || !idx || !out) return RKV_ERR_INVALID_ARG;
+    if (!aligned16(w->w_d) || !aligned16(out)) return RKV_ERR_ALIGNMENT;
+    return from_hip(launch_decode(s, c, idx, m, w->w_d, out, out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

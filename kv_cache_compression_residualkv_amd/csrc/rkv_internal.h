@@ -1,0 +1,62 @@
+// Internal launch interface between the C ABI layer (rkv_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rkv.h"
+
+namespace rkv {
+
+// Everything a launcher needs, resolved and validated on the host.
+struct Shape {
+    int N, D, dk, W2;  // heads, head dim, d_k = N*D, W2 = 2*d_k
+    int d_ff, d_c, top_k, bits, group, G;  // G = d_c / group
+    bool f32;          // true: "f32" formats, false: "bf16" formats
+    double theta;
+};
+
+struct CacheView {
+    int B, cap_ref, cap_tok;
+    void* ref_vals;
+    int* ref_pos;
+    float* ref_norm2;
+    int* ref_count;
+    uint8_t* codes;
+    void* scale;
+    void* zmin;
+    int* ref_idx;
+    int* self_slot;
+    int* err;
+    size_t code_bytes;  // per token
+};
+
+// Search split factor and workspace carve-up of rkv_encode.
+struct EncodePlan {
+    int nsplit;        // pool chunks searched independently per token tile
+    int chunk_slots;   // slots per chunk (multiple of the slot tile)
+    size_t off_part_score, off_part_slot, off_xbar, off_dh, total;
+};
+
+EncodePlan plan_encode(const Shape& s, int B, int n, int cap_ref);
+
+hipError_t launch_append(const Shape& s, const CacheView& c, const void* kv, int kv_len, const int* rows,
+                         const int* pos, int n, hipStream_t st);
+
+hipError_t launch_search(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
+                         const int* rows, const int* pos, int n, void* ws, hipStream_t st);
+
+hipError_t launch_select(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
+                         const int* rows, const int* pos, int n, void* ws, hipStream_t st);
+
+hipError_t launch_swiglu(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
+                         const int* rows, int n, const void* w1, const void* w2, void* ws, hipStream_t st);
+
+hipError_t launch_latent_quant(const Shape& s, const CacheView& c, const EncodePlan& p, const int* pos, int n,
+                               const void* w3, void* ws, hipStream_t st);
+
+hipError_t launch_decode(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
+                         int out_dtype, hipStream_t st);
+
+}  // namespace rkv

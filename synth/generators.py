@@ -159,6 +159,13 @@ class WorkloadConfig:
     def make_weights(self, layer: int = 0) -> Dict[str, np.ndarray]:
         return codec_weights(self.two_dk, self.d_ff, self.d_c, self.weight_rng(layer), self.in_dtype)
 
+    def make_selected(self, T: Optional[int] = None, seq: int = 0, step: int = 0, layer: int = 0) -> np.ndarray:
+        """Sorted random subset of floor(select_frac * T) token positions (the read set I_t)."""
+        T = self.T if T is None else T
+        if self.select_frac >= 1.0:
+            return np.arange(T, dtype=np.int32)
+        return selected_subset(T, self.select_frac, self.subset_rng(step, seq, layer))
+
     def ref_positions(self, T: Optional[int] = None) -> np.ndarray:
         T = self.T if T is None else T
         return np.arange(0, T, self.stride, dtype=np.int32)
