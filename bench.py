@@ -151,7 +151,19 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--select-frac", type=float, default=0.3, help="read fraction for the extra selected-restore rate")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+
+        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 5}))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the codec runs on one GPU, "
               "see the multi-GPU notes in DESIGN.md)", file=sys.stderr)
