@@ -6,133 +6,115 @@
 // Delta = (max - min)/(2^b - 1), q = round((z - min)/Delta).
 //
 // Since W_c3 is linear, z = (h(kv_i) - h(mean_i)) W_c3 with h(x) = Swish(x W_c1) * x W_c2.
-//   swiglu_kernel       rows of a tile alternate kv_i / mean_i of the same token, so
-//                       the epilogue holds h of both in one lane and writes
-//                       dH = h(kv_i) - h(mean_i) in fp32 (one row per token).
-//   latent_quant_kernel z = dH W_c3. dH is split into three bf16 terms
-//                       (hi + mid + lo carries 24 significant bits), each multiplied
-//                       by the bf16 W_c3 on MFMA; the epilogue reduces each group's
-//                       min/max across the 16 lanes that hold it, stores Delta and
-//                       min, and packs the codes.
+//   swiglu_kernel       GEMM [kv_i; mean_i] x [W_c1 | W_c2]^T. Rows of a tile alternate
+//                       kv_i / mean_i of one token and the B tile interleaves W_c1
+//                       and W_c2 columns, so one lane ends with a, g of both rows:
+//                       dH = h(kv_i) - h(mean_i) is formed in registers, staged in
+//                       LDS and written coalesced. In the bf16 formats dH is written
+//                       as three bf16 terms hi + mid + lo (24 significant bits), the
+//                       three "planes" of a row of width 3 d_ff.
+//   latent_quant_kernel z = dH W_c3 as one bf16 GEMM over K' = 3 d_ff (each plane times
+//                       W_c3); the epilogue reduces each group's min/max over the 16
+//                       lanes that hold it, stores Delta and min, and packs the codes
+//                       through LDS into coalesced record writes.
 #include <float.h>
 
 #include "rkv_device.h"
+#include "rkv_gemm.h"
 #include "rkv_internal.h"
 
 namespace rkv {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kKC = 64;
-
 // ---------------------------------------------------------------- GEMM 1
-// tile: 128 rows (64 tokens x {kv, mean}) x 128 columns (64 of W_c1 and the same 64 of
-// W_c2). Waves in a 2 x 2 layout: wave (wm, wn) owns rows [64 wm, +64) and W_c1/W_c2
-// columns [32 wn, +32); its 4 x 4 MFMA tiles are (row tile) x (c1, c1, c2, c2).
-constexpr int kBM1 = 128;
-constexpr int kBN1 = 128;
 
 template <typename T>
-struct Gemm1Smem {
+struct G1 {
+    // bf16: 256 rows (128 tokens) x 128 columns (64 W_c1 + 64 W_c2); fp32: half the rows
+    static constexpr int BM = std::is_same<T, float>::value ? 128 : 256;
+    static constexpr int BN = 128;
+    static constexpr int WM = BM / 2, WN = 64;
+    static constexpr int NS = std::is_same<T, float>::value ? 1 : 3;  // dH planes
     static constexpr int P = Pitch<T, kKC>::value;
-    static constexpr size_t bytes = (size_t)(kBM1 + kBN1) * P * sizeof(T);
+    static constexpr int kHP = 68;  // fp32 pitch of the dH staging tile
+    static constexpr size_t kPipe = (size_t)2 * (BM + BN) * P * sizeof(T);
+    static constexpr size_t kEpi = (size_t)(BM / 2) * kHP * sizeof(float);
+    static constexpr size_t bytes = kPipe > kEpi ? kPipe : kEpi;
 };
 
-// copy 32 elements (compute type == storage type here)
+template <typename T, int BM>
+struct G1LoadA {
+    RowTile<T, T, BM> t;
+    const T* row[BM / 128];
+    __device__ inline void load(int s) { t.load_rows(row, s * kKC); }
+    __device__ inline void store(T* lds, int P) const { t.store(lds, P); }
+};
+
 template <typename T>
-struct Copy32 {
-    static constexpr int kWords = 32 * (int)sizeof(T) / 16;
-    uint4 w[kWords];
-    __device__ inline void load(const T* p) {
-#pragma unroll
-        for (int i = 0; i < kWords; ++i) w[i] = reinterpret_cast<const uint4*>(p)[i];
-    }
-    __device__ inline void zero() {
-#pragma unroll
-        for (int i = 0; i < kWords; ++i) w[i] = make_uint4(0, 0, 0, 0);
-    }
-    __device__ inline void store(T* p) const {
-#pragma unroll
-        for (int i = 0; i < kWords; ++i) reinterpret_cast<uint4*>(p)[i] = w[i];
-    }
+struct G1LoadB {
+    RowTile<T, T, 128> t;
+    const T* row[1];
+    __device__ inline void load(int s) { t.load_rows(row, s * kKC); }
+    __device__ inline void store(T* lds, int P) const { t.store(lds, P); }
 };
 
 __device__ inline float silu(float a) { return a / (1.0f + expf(-a)); }
 
+// grid: 8 * per blocks over MT x NT logical tiles (N tiles fastest, so the NT tiles
+// that read one A row block run back to back on one XCD).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void swiglu_kernel(const T* __restrict__ kv, int kv_len,
-                                                          const int* __restrict__ rows, int n,
-                                                          const T* __restrict__ xbar, const T* __restrict__ w1,
-                                                          const T* __restrict__ w2, int W2, int d_ff,
-                                                          float* __restrict__ dh) {
-    constexpr int P = Gemm1Smem<T>::P;
+__global__ __launch_bounds__(kGemmThreads) void swiglu_kernel(const T* __restrict__ kv, int kv_len,
+                                                              const int* __restrict__ rows, int n,
+                                                              const T* __restrict__ xbar, const T* __restrict__ w1,
+                                                              const T* __restrict__ w2, int W2, int d_ff,
+                                                              T* __restrict__ dh, int MT, int NT, int per) {
+    typedef G1<T> C;
     extern __shared__ __align__(16) unsigned char smem[];
-    T* sA = reinterpret_cast<T*>(smem);
-    T* sB = sA + kBM1 * P;
+    T* lds = reinterpret_cast<T*>(smem);
+    const int tile = xcd_tile(blockIdx.x, per);
+    if (tile >= MT * NT) return;
+    const int mt = tile / NT, nt = tile - mt * NT;
+    const int b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int b = blockIdx.z;
-    const int tok0 = blockIdx.x * (kBM1 / 2);
-    const int j0 = blockIdx.y * (kBN1 / 2);
+    const int tok0 = mt * (C::BM / 2);
+    const int j0 = nt * 64;
 
-    // staging: thread -> (row, 32-column half)
-    const int st_row = tid >> 1, st_col = (tid & 1) * 32;
-    const T* a_src = nullptr;
-    {
-        const int t = tok0 + (st_row >> 1);
+    G1LoadA<T, C::BM> la;
+#pragma unroll
+    for (int u = 0; u < C::BM / 128; ++u) {
+        const int r = RowTile<T, T, C::BM>::srow(u);
+        const int t = tok0 + (r >> 1);
+        const T* p = nullptr;
         if (t < n) {
-            if (st_row & 1) {
-                a_src = xbar + ((size_t)b * n + t) * W2;
+            if (r & 1) {
+                p = xbar + ((size_t)b * n + t) * W2;
             } else {
-                const int r = rows[(size_t)b * n + t];
-                if (r >= 0 && r < kv_len) a_src = kv + ((size_t)b * kv_len + r) * W2;
+                const int kr = rows[(size_t)b * n + t];
+                if (kr >= 0 && kr < kv_len) p = kv + ((size_t)b * kv_len + kr) * W2;
             }
         }
+        la.row[u] = p;
     }
-    const T* b_src = (st_row < 64) ? w1 + (size_t)(j0 + st_row) * W2 : w2 + (size_t)(j0 + st_row - 64) * W2;
-
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
-
-    Copy32<T> ra, rb;
-    if (a_src) ra.load(a_src + st_col); else ra.zero();
-    rb.load(b_src + st_col);
-    const int nk = W2 / kKC;
-    for (int kc = 0; kc < nk; ++kc) {
-        __syncthreads();
-        ra.store(sA + st_row * P + st_col);
-        rb.store(sB + st_row * P + st_col);
-        __syncthreads();
-        if (kc + 1 < nk) {
-            const int off = (kc + 1) * kKC + st_col;
-            if (a_src) ra.load(a_src + off);
-            rb.load(b_src + off);
-        }
-#pragma unroll
-        for (int ks = 0; ks < kKC / 32; ++ks) {
-            const int kof = ks * 32 + 8 * (lane >> 4);
-            typename Mma<T>::frag fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) fa[i] = lds_frag<T>(sA + (64 * wm + 16 * i + (lane & 15)) * P + kof);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = (j < 2) ? (32 * wn + 16 * j) : (64 + 32 * wn + 16 * (j - 2));
-                fb[j] = lds_frag<T>(sB + (col + (lane & 15)) * P + kof);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::step(acc[i][j], fa[i], fb[j]);
-        }
+    G1LoadB<T> lb;
+    {
+        // B tile rows: [c1 0..31, c2 0..31, c1 32..63, c2 32..63] so that wave wn's
+        // 64 rows are contiguous: its tiles j = 0, 1 are W_c1 and j = 2, 3 are W_c2
+        const int r = RowTile<T, T, 128>::srow(0);
+        const int half = r >> 6, q = r & 63;
+        lb.row[0] = (q < 32) ? w1 + (size_t)(j0 + 32 * half + q) * W2 : w2 + (size_t)(j0 + 32 * half + q - 32) * W2;
     }
-    // epilogue: rows 4g+0/4g+1 are kv/mean of one token, 4g+2/4g+3 of the next
+
+    f32x4 acc[C::WM / 16][C::WN / 16];
+    mainloop<T, C::BM, C::BN, C::WM, C::WN>(la, lb, W2 / kKC, W2 / kKC, lds, C::WM * wm, 64 * wn, acc,
+                                            NoBlockHook{});
+
+    // epilogue: rows 4g+0/4g+1 of a tile are kv/mean of one token, 4g+2/4g+3 of the next
+    float* sH = reinterpret_cast<float*>(smem);  // [BM/2 tokens][kHP]
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int tok = tok0 + 32 * wm + 8 * i + 2 * (lane >> 4);
+    for (int i = 0; i < C::WM / 16; ++i) {
+        const int tl = (C::WM / 2) * wm + 8 * i + 2 * (lane >> 4);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const f32x4 a = acc[i][c];
@@ -141,70 +123,91 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const T* __restrict__ 
             const float h1 = silu(a[1]) * g[1];
             const float h2 = silu(a[2]) * g[2];
             const float h3 = silu(a[3]) * g[3];
-            const int j = j0 + 32 * wn + 16 * c + (lane & 15);
-            if (tok < n) dh[((size_t)b * n + tok) * d_ff + j] = h0 - h1;
-            if (tok + 1 < n) dh[((size_t)b * n + tok + 1) * d_ff + j] = h2 - h3;
+            const int cl = 32 * wn + 16 * c + (lane & 15);
+            sH[tl * C::kHP + cl] = h0 - h1;
+            sH[(tl + 1) * C::kHP + cl] = h2 - h3;
+        }
+    }
+    __syncthreads();
+    // coalesced store: each job = 8 consecutive columns of one token, split into planes
+    constexpr int kJobs = (C::BM / 2) * 8;
+    for (int jb = tid; jb < kJobs; jb += kGemmThreads) {
+        const int tl = jb >> 3, ch = jb & 7;
+        const int t = tok0 + tl;
+        if (t >= n) continue;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sH[tl * C::kHP + 8 * ch + e];
+        T* dst = dh + ((size_t)b * n + t) * C::NS * d_ff + j0 + 8 * ch;
+        if constexpr (C::NS == 1) {
+            lds_store8<T>(dst, x);
+        } else {
+            float r1[8], r2[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float hi = (float)(bf16_t)x[e];
+                r1[e] = x[e] - hi;
+                const float mi = (float)(bf16_t)r1[e];
+                r2[e] = r1[e] - mi;
+                x[e] = hi;
+                r1[e] = mi;
+            }
+            lds_store8<T>(dst, x);
+            lds_store8<T>(dst + d_ff, r1);
+            lds_store8<T>(dst + 2 * d_ff, r2);
         }
     }
 }
 
 // ---------------------------------------------------------------- GEMM 2 + quantizer
-// tile: 128 tokens x 64 latent columns (two groups). Wave w owns tokens [32 w, +32)
-// and all 64 columns: 2 x 4 MFMA tiles per split term.
-constexpr int kBM2 = 128;
-constexpr int kBN2 = 64;
 
-template <typename T, int NS>
-struct Gemm2Smem {
+template <typename T>
+struct G2 {
+    static constexpr int BM = 128;
+    static constexpr int BN = std::is_same<T, float>::value ? 64 : 128;
+    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int NS = std::is_same<T, float>::value ? 1 : 3;
     static constexpr int P = Pitch<T, kKC>::value;
-    static constexpr size_t bytes = (size_t)(NS * kBM2 + kBN2) * P * sizeof(T);
+    static constexpr size_t kPipe = (size_t)2 * (BM + BN) * P * sizeof(T);
+    // epilogue staging: codes (or fp16 latent) per token + step/min per group
+    static constexpr int kQP = BN * 2 + 16;  // bytes per staged token row (fp16 latent is the widest)
+    static constexpr size_t kEpi = (size_t)BM * kQP + (size_t)BM * (BN / 32) * 2 * sizeof(float);
+    static constexpr size_t bytes = kPipe > kEpi ? kPipe : kEpi;
 };
 
-template <typename T, int NS>
-struct Split;
+template <typename T>
+struct G2LoadA {
+    RowTile<T, T, 128> t;
+    const T* row[1];
+    __device__ inline void load(int s) { t.load_rows(row, s * kKC); }
+    __device__ inline void store(T* lds, int P) const { t.store(lds, P); }
+};
 
-template <>
-struct Split<bf16_t, 3> {
-    // x = hi + mid + lo, each bf16; the remainders are exact in fp32
-    static __device__ inline void run(const float* x, bf16_t* d0, bf16_t* d1, bf16_t* d2) {
-        bf16_t a[8], m[8], l[8];
+// B' stage s holds W_c3 columns k = (s * kKC) mod d_ff: the three planes of dH all
+// multiply the same W_c3.
+template <typename T, int BN>
+struct G2LoadB {
+    static constexpr int kUnits = BN >= 128 ? BN / 128 : 1;
+    Raw32<T> raw[kUnits];
+    const T* row[kUnits];
+    int d_ff;
+    __device__ inline void load(int s) {
+        const int k0 = (s * kKC) % d_ff;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const bf16_t hi = (bf16_t)x[i];
-            const float r1 = x[i] - (float)hi;
-            const bf16_t mi = (bf16_t)r1;
-            const float r2 = r1 - (float)mi;
-            a[i] = hi;
-            m[i] = mi;
-            l[i] = (bf16_t)r2;
+        for (int u = 0; u < kUnits; ++u) {
+            if (row[u]) raw[u].load(row[u] + k0 + (threadIdx.x & 1) * 32);
+            else raw[u].zero();
         }
-        *reinterpret_cast<uint4*>(d0) = *reinterpret_cast<uint4*>(a);
-        *reinterpret_cast<uint4*>(d1) = *reinterpret_cast<uint4*>(m);
-        *reinterpret_cast<uint4*>(d2) = *reinterpret_cast<uint4*>(l);
+    }
+    __device__ inline void store(T* lds, int P) const {
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+            const int r = (threadIdx.x >> 1) + 128 * u;
+            if (r < BN) stage32<T>(lds + r * P + (threadIdx.x & 1) * 32, raw[u]);
+        }
     }
 };
 
-template <>
-struct Split<float, 1> {
-    static __device__ inline void run(const float* x, float* d0, float*, float*) {
-        *reinterpret_cast<float4*>(d0) = make_float4(x[0], x[1], x[2], x[3]);
-        *reinterpret_cast<float4*>(d0 + 4) = make_float4(x[4], x[5], x[6], x[7]);
-    }
-};
-
-template <typename ScT>
-__device__ inline float store_scalar(ScT* p, float v);
-template <>
-__device__ inline float store_scalar<float>(float* p, float v) {
-    *p = v;
-    return v;
-}
-template <>
-__device__ inline float store_scalar<f16_t>(f16_t* p, float v) {
-    const f16_t h = (f16_t)v;
-    *p = h;
-    return (float)h;
-}
 template <typename ScT>
 __device__ inline float round_scalar(float v);
 template <>
@@ -212,139 +215,138 @@ __device__ inline float round_scalar<float>(float v) { return v; }
 template <>
 __device__ inline float round_scalar<f16_t>(float v) { return (float)(f16_t)v; }
 
-template <typename T, int NS, typename ScT>
-__global__ __launch_bounds__(kThreads) void latent_quant_kernel(const float* __restrict__ dh, int n,
-                                                                const T* __restrict__ w3, int d_ff, int d_c,
-                                                                int bits, const int* __restrict__ pos, int cap_tok,
-                                                                uint8_t* __restrict__ codes, size_t code_bytes,
-                                                                ScT* __restrict__ scale, ScT* __restrict__ zmin) {
-    constexpr int P = Gemm2Smem<T, NS>::P;
+template <typename T, typename ScT>
+__global__ __launch_bounds__(kGemmThreads) void latent_quant_kernel(const T* __restrict__ dh, int n,
+                                                                    const T* __restrict__ w3, int d_ff, int d_c,
+                                                                    int bits, const int* __restrict__ pos,
+                                                                    int cap_tok, uint8_t* __restrict__ codes,
+                                                                    size_t code_bytes, ScT* __restrict__ scale,
+                                                                    ScT* __restrict__ zmin, int MT, int NT, int per) {
+    typedef G2<T> C;
     extern __shared__ __align__(16) unsigned char smem[];
-    T* sA = reinterpret_cast<T*>(smem);  // NS planes of [kBM2][P]
-    T* sB = sA + NS * kBM2 * P;          // [kBN2][P]
+    T* lds = reinterpret_cast<T*>(smem);
+    const int tile = xcd_tile(blockIdx.x, per);
+    if (tile >= MT * NT) return;
+    const int mt = tile / NT, nt = tile - mt * NT;
+    const int b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = blockIdx.z;
-    const int t0 = blockIdx.x * kBM2;
-    const int c0 = blockIdx.y * kBN2;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int t0 = mt * C::BM;
+    const int c0 = nt * C::BN;
+    const int Kp = C::NS * d_ff;
 
-    // staging: A 128 rows x 64 fp32 -> each thread 32 values of one row;
-    // B 64 rows x 64 -> threads 0..127 each 32 values of one row
-    const int st_row = tid >> 1, st_col = (tid & 1) * 32;
-    const float* a_src = (t0 + st_row < n) ? dh + ((size_t)b * n + t0 + st_row) * d_ff : nullptr;
-    const T* b_src = (tid < 128) ? w3 + (size_t)(c0 + st_row) * d_ff : nullptr;
-
-    f32x4 acc[2][4];
+    G2LoadA<T> la;
+    {
+        const int r = RowTile<T, T, 128>::srow(0);
+        la.row[0] = (t0 + r < n) ? dh + ((size_t)b * n + t0 + r) * Kp : nullptr;
+    }
+    G2LoadB<T, C::BN> lb;
+    lb.d_ff = d_ff;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
-
-    float4 ra[8];
-    Copy32<T> rb;
-    auto load_a = [&](int off) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            ra[i] = a_src ? reinterpret_cast<const float4*>(a_src + off)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    };
-    load_a(st_col);
-    if (b_src) rb.load(b_src + st_col);
-    const int nk = d_ff / kKC;
-    for (int kc = 0; kc < nk; ++kc) {
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float* x = reinterpret_cast<const float*>(&ra[2 * q]);
-            T* d0 = sA + st_row * P + st_col + 8 * q;
-            Split<T, NS>::run(x, d0, d0 + (NS > 1 ? kBM2 * P : 0), d0 + (NS > 2 ? 2 * kBM2 * P : 0));
-        }
-        if (b_src) rb.store(sB + st_row * P + st_col);
-        __syncthreads();
-        if (kc + 1 < nk) {
-            const int off = (kc + 1) * kKC + st_col;
-            load_a(off);
-            if (b_src) rb.load(b_src + off);
-        }
-#pragma unroll
-        for (int ks = 0; ks < kKC / 32; ++ks) {
-            const int kof = ks * 32 + 8 * (lane >> 4);
-            typename Mma<T>::frag fb[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) fb[j] = lds_frag<T>(sB + (16 * j + (lane & 15)) * P + kof);
-#pragma unroll
-            for (int sp = 0; sp < NS; ++sp) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const typename Mma<T>::frag fa =
-                        lds_frag<T>(sA + sp * kBM2 * P + (32 * wave + 16 * i + (lane & 15)) * P + kof);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::step(acc[i][j], fa, fb[j]);
-                }
-            }
-        }
+    for (int u = 0; u < G2LoadB<T, C::BN>::kUnits; ++u) {
+        const int r = (tid >> 1) + 128 * u;
+        lb.row[u] = (r < C::BN && c0 + r < d_c) ? w3 + (size_t)(c0 + r) * d_ff : nullptr;
     }
 
-    // epilogue: lane holds z[token 32 w + 16 i + 4 (lane/16) + e][col 16 j + lane%16];
-    // group gr of the tile = columns j in {2 gr, 2 gr + 1}
+    f32x4 acc[C::WM / 16][C::WN / 16];
+    // A' rows are [hi | mid | lo] (K' = NS d_ff); stage s of A' pairs with W_c3 stage s mod (d_ff / kKC)
+    mainloop<T, C::BM, C::BN, C::WM, C::WN>(la, lb, Kp / kKC, Kp / kKC, lds, C::WM * wm, C::WN * wn, acc,
+                                            NoBlockHook{});
+
+    // epilogue: lane holds z[token WM wm + 16 i + 4 (lane/16) + e][col WN wn + 16 j + lane%16]
+    uint8_t* sQ = smem;                                               // [BM][kQP] bytes
+    float* sS = reinterpret_cast<float*>(smem + (size_t)C::BM * C::kQP);  // [BM][BN/32][2]
+    constexpr int GT = C::BN / 32;  // groups per tile row
     const float levels = (float)((1 << (bits == 16 ? 1 : bits)) - 1);
-    const int G = d_c / 32;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < C::WM / 16; ++i) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int t = t0 + 32 * wave + 16 * i + 4 * (lane >> 4) + e;
-            const bool tv = t < n;
-            int p = tv ? pos[(size_t)b * n + t] : -1;
-            const bool ok = tv && p >= 0 && p < cap_tok;
-            uint8_t* rec = codes + ((size_t)b * cap_tok + (ok ? p : 0)) * code_bytes;
+            const int tl = C::WM * wm + 16 * i + 4 * (lane >> 4) + e;
             if (bits == 16) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int col = c0 + 16 * j + (lane & 15);
-                    if (ok) reinterpret_cast<f16_t*>(rec)[col] = (f16_t)acc[i][j][e];
+                for (int j = 0; j < C::WN / 16; ++j) {
+                    const int cl = C::WN * wn + 16 * j + (lane & 15);
+                    reinterpret_cast<f16_t*>(sQ + (size_t)tl * C::kQP)[cl] = (f16_t)acc[i][j][e];
                 }
                 continue;
             }
 #pragma unroll
-            for (int gr = 0; gr < 2; ++gr) {
-                const float v0 = acc[i][2 * gr][e];
-                const float v1 = acc[i][2 * gr + 1][e];
+            for (int q = 0; q < C::WN / 32; ++q) {
+                const float v0 = acc[i][2 * q][e];
+                const float v1 = acc[i][2 * q + 1][e];
                 const float lo = seg16_min(fminf(v0, v1));
                 const float hi = seg16_max(fmaxf(v0, v1));
-                const float delta = (hi - lo) / levels;
+                const float delta = __fdiv_rn(hi - lo, levels);
                 const float st = round_scalar<ScT>(delta);
                 const float zm = round_scalar<ScT>(lo);
-                const int g = (c0 >> 5) + gr;
-                if (ok && (lane & 15) == 0) {
-                    store_scalar<ScT>(scale + ((size_t)b * cap_tok + p) * G + g, delta);
-                    store_scalar<ScT>(zmin + ((size_t)b * cap_tok + p) * G + g, lo);
-                }
                 float q0 = 0.f, q1 = 0.f;
                 if (st != 0.f) {
-                    q0 = fminf(fmaxf(__builtin_rintf((v0 - zm) / st), 0.f), levels);
-                    q1 = fminf(fmaxf(__builtin_rintf((v1 - zm) / st), 0.f), levels);
+                    q0 = fminf(fmaxf(__builtin_rintf(__fdiv_rn(v0 - zm, st)), 0.f), levels);
+                    q1 = fminf(fmaxf(__builtin_rintf(__fdiv_rn(v1 - zm, st)), 0.f), levels);
                 }
-                const uint32_t iq0 = (uint32_t)q0, iq1 = (uint32_t)q1;
-                // column of v0 = 32 g + lane%16, of v1 = 32 g + 16 + lane%16
-                if (bits == 4) {
-                    const uint32_t n0 = __shfl_xor((int)iq0, 1, 64);
-                    const uint32_t n1 = __shfl_xor((int)iq1, 1, 64);
-                    if (ok && (lane & 1) == 0) {
-                        rec[(32 * g + (lane & 15)) >> 1] = (uint8_t)(iq0 | (n0 << 4));
-                        rec[(32 * g + 16 + (lane & 15)) >> 1] = (uint8_t)(iq1 | (n1 << 4));
-                    }
-                } else {  // bits == 2: four consecutive coordinates per byte
-                    uint32_t b0 = iq0 << (2 * (lane & 3));
-                    uint32_t b1 = iq1 << (2 * (lane & 3));
-                    b0 |= __shfl_xor((int)b0, 1, 64);
-                    b1 |= __shfl_xor((int)b1, 1, 64);
-                    b0 |= __shfl_xor((int)b0, 2, 64);
-                    b1 |= __shfl_xor((int)b1, 2, 64);
-                    if (ok && (lane & 3) == 0) {
-                        rec[(32 * g + (lane & 15)) >> 2] = (uint8_t)b0;
-                        rec[(32 * g + 16 + (lane & 15)) >> 2] = (uint8_t)b1;
-                    }
+                const int cl = C::WN * wn + 32 * q + (lane & 15);
+                sQ[(size_t)tl * C::kQP + cl] = (uint8_t)q0;
+                sQ[(size_t)tl * C::kQP + cl + 16] = (uint8_t)q1;
+                if ((lane & 15) == 0) {
+                    const int gl = (C::WN * wn) / 32 + q;
+                    sS[(tl * GT + gl) * 2] = st;
+                    sS[(tl * GT + gl) * 2 + 1] = zm;
                 }
             }
+        }
+    }
+    __syncthreads();
+    // coalesced record writes: 16-byte chunks of this tile's part of each record
+    const int cb = bits == 16 ? C::BN * 2 : C::BN * bits / 8;  // code bytes per token in this tile
+    const int nch = cb / 16;
+    for (int jb = tid; jb < C::BM * nch; jb += kGemmThreads) {
+        const int tl = jb / nch, ch = jb - tl * nch;
+        const int t = t0 + tl;
+        if (t >= n) continue;
+        const int p = pos[(size_t)b * n + t];
+        if (p < 0 || p >= cap_tok) continue;
+        if (c0 + (ch * 16 * 8) / (bits == 16 ? 16 : bits) >= d_c) continue;
+        const uint8_t* src = sQ + (size_t)tl * C::kQP;
+        uint4 v;
+        if (bits == 16) {
+            v = *reinterpret_cast<const uint4*>(src + 16 * ch);
+        } else if (bits == 4) {
+            uint32_t w[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t x = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x |= (uint32_t)(src[32 * ch + 8 * d + e] & 0xF) << (4 * e);
+                w[d] = x;
+            }
+            v = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t x = 0;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) x |= (uint32_t)(src[64 * ch + 16 * d + e] & 0x3) << (2 * e);
+                w[d] = x;
+            }
+            v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        const size_t rec = ((size_t)b * cap_tok + p) * code_bytes;
+        const size_t off = (size_t)(bits == 16 ? c0 * 2 : c0 * bits / 8) + 16 * ch;
+        *reinterpret_cast<uint4*>(codes + rec + off) = v;
+    }
+    if (bits != 16) {
+        const int G = d_c / 32;
+        for (int jb = tid; jb < C::BM * GT; jb += kGemmThreads) {
+            const int tl = jb / GT, gl = jb - tl * GT;
+            const int t = t0 + tl;
+            const int g = c0 / 32 + gl;
+            if (t >= n || g >= G) continue;
+            const int p = pos[(size_t)b * n + t];
+            if (p < 0 || p >= cap_tok) continue;
+            scale[((size_t)b * cap_tok + p) * G + g] = (ScT)sS[(tl * GT + gl) * 2];
+            zmin[((size_t)b * cap_tok + p) * G + g] = (ScT)sS[(tl * GT + gl) * 2 + 1];
         }
     }
 }
@@ -354,16 +356,19 @@ __global__ __launch_bounds__(kThreads) void latent_quant_kernel(const float* __r
 template <typename T>
 static hipError_t swiglu_impl(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
                               const int* rows, int n, const void* w1, const void* w2, void* ws, hipStream_t st) {
-    const size_t smem = Gemm1Smem<T>::bytes;
+    typedef G1<T> C;
+    const size_t smem = C::bytes;
     auto kern = swiglu_kernel<T>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     char* w = static_cast<char*>(ws);
-    const dim3 grid((2 * n + kBM1 - 1) / kBM1, s.d_ff / (kBN1 / 2), c.B);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, st, static_cast<const T*>(kv), kv_len, rows, n,
-                       reinterpret_cast<const T*>(w + p.off_xbar), static_cast<const T*>(w1),
-                       static_cast<const T*>(w2), s.W2, s.d_ff, reinterpret_cast<float*>(w + p.off_dh));
+    const int MT = (2 * n + C::BM - 1) / C::BM;
+    const int NT = s.d_ff / 64;
+    const int per = xcd_per(MT * NT);
+    hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(kGemmThreads), smem, st, static_cast<const T*>(kv), kv_len,
+                       rows, n, reinterpret_cast<const T*>(w + p.off_xbar), static_cast<const T*>(w1),
+                       static_cast<const T*>(w2), s.W2, s.d_ff, reinterpret_cast<T*>(w + p.off_dh), MT, NT, per);
     return hipGetLastError();
 }
 
@@ -373,26 +378,30 @@ hipError_t launch_swiglu(const Shape& s, const CacheView& c, const EncodePlan& p
     return swiglu_impl<bf16_t>(s, c, p, kv, kv_len, rows, n, w1, w2, ws, st);
 }
 
-template <typename T, int NS, typename ScT>
+template <typename T, typename ScT>
 static hipError_t latent_impl(const Shape& s, const CacheView& c, const EncodePlan& p, const int* pos, int n,
                               const void* w3, void* ws, hipStream_t st) {
-    const size_t smem = Gemm2Smem<T, NS>::bytes;
-    auto kern = latent_quant_kernel<T, NS, ScT>;
+    typedef G2<T> C;
+    const size_t smem = C::bytes;
+    auto kern = latent_quant_kernel<T, ScT>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     char* w = static_cast<char*>(ws);
-    const dim3 grid((n + kBM2 - 1) / kBM2, s.d_c / kBN2, c.B);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, st, reinterpret_cast<const float*>(w + p.off_dh), n,
-                       static_cast<const T*>(w3), s.d_ff, s.d_c, s.bits, pos, c.cap_tok, c.codes, c.code_bytes,
-                       static_cast<ScT*>(c.scale), static_cast<ScT*>(c.zmin));
+    const int MT = (n + C::BM - 1) / C::BM;
+    const int NT = (s.d_c + C::BN - 1) / C::BN;
+    const int per = xcd_per(MT * NT);
+    hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(kGemmThreads), smem, st,
+                       reinterpret_cast<const T*>(w + p.off_dh), n, static_cast<const T*>(w3), s.d_ff, s.d_c, s.bits,
+                       pos, c.cap_tok, c.codes, c.code_bytes, static_cast<ScT*>(c.scale), static_cast<ScT*>(c.zmin),
+                       MT, NT, per);
     return hipGetLastError();
 }
 
 hipError_t launch_latent_quant(const Shape& s, const CacheView& c, const EncodePlan& p, const int* pos, int n,
                                const void* w3, void* ws, hipStream_t st) {
-    if (s.f32) return latent_impl<float, 1, float>(s, c, p, pos, n, w3, ws, st);
-    return latent_impl<bf16_t, 3, f16_t>(s, c, p, pos, n, w3, ws, st);
+    if (s.f32) return latent_impl<float, float>(s, c, p, pos, n, w3, ws, st);
+    return latent_impl<bf16_t, f16_t>(s, c, p, pos, n, w3, ws, st);
 }
 
 }  // namespace rkv

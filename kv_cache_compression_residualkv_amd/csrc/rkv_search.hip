@@ -5,13 +5,16 @@
 // (arg top-k_i of -||kv_i - kv_j||^2, k_i = min(k, |pool|)) and averages them.
 //
 // Two kernels:
-//   search_kernel  - one workgroup scores a tile of 128 tokens against one chunk of
-//                    the pool. Scores ||r||^2 - 2 x.r come from MFMA (x bf16, r FP8
-//                    widened exactly to bf16, fp32 accumulation) with the pool as
-//                    the A operand so that each lane owns tokens; each lane keeps a
-//                    sorted top-8 of (score, slot) per token in registers, and the
-//                    workgroup merges its lanes' lists into one top-8 per token and
-//                    chunk.
+//   search_kernel  - one workgroup scores a tile of 128 tokens against a chunk of
+//                    pool blocks (256 slots each). Scores ||r||^2 - 2 x.r come from
+//                    MFMA (x bf16, r FP8 widened exactly to bf16, fp32 accumulation)
+//                    with the pool as the A operand so that each lane owns tokens; the
+//                    K stages of consecutive pool blocks form one pipelined sequence,
+//                    and after each block every lane folds its scores into a sorted
+//                    per-token top-8 held in registers. The workgroup finally merges
+//                    its lanes' lists into one top-8 per token and chunk. Only the
+//                    pool prefix with positions below the tile's last token is read
+//                    (the pool is position-ordered).
 //   select_kernel  - one wavefront per token merges the chunks' lists, decides the
 //                    k_i references (exact fp32 distances are computed only when the
 //                    approximate scores of the boundary candidates are closer than
@@ -21,72 +24,28 @@
 #include <limits.h>
 
 #include "rkv_device.h"
+#include "rkv_gemm.h"
 #include "rkv_internal.h"
 
 namespace rkv {
 
 namespace {
 
-constexpr int kTok = 128;   // tokens per search tile
-constexpr int kSlot = 128;  // pool slots per block
-constexpr int kKC = 64;     // K elements per LDS stage
-constexpr int kTop = 8;     // candidates kept per token
 constexpr int kThreads = 256;
+constexpr int kTop = 8;  // candidates kept per token
+constexpr int kTok = 128;  // tokens per search tile
 
-// 32 consecutive elements of storage type S held as raw 16-byte words.
-template <typename S>
-struct Raw32 {
-    static constexpr int kWords = 32 * (int)sizeof(S) / 16;
-    uint4 w[kWords];
-    __device__ inline void load(const S* p) {
-#pragma unroll
-        for (int i = 0; i < kWords; ++i) w[i] = reinterpret_cast<const uint4*>(p)[i];
-    }
-    __device__ inline void zero() {
-#pragma unroll
-        for (int i = 0; i < kWords; ++i) w[i] = make_uint4(0, 0, 0, 0);
-    }
-    __device__ inline void get8(int j, float* o) const;
+template <typename T>
+struct SC {
+    static constexpr int BM = std::is_same<T, float>::value ? 128 : 256;  // pool slots per block
+    static constexpr int BN = kTok;
+    static constexpr int WM = BM / 2, WN = 64;
+    static constexpr int P = Pitch<T, kKC>::value;
+    static constexpr size_t kPipe = (size_t)2 * (BM + BN) * P * sizeof(T);
+    static constexpr size_t kMerge = (size_t)kTok * 8 * kTop * (sizeof(float) + sizeof(int));
+    static constexpr size_t kMain = kPipe > kMerge ? kPipe : kMerge;
+    static constexpr size_t bytes = kMain + 16;
 };
-
-template <>
-__device__ inline void Raw32<fp8_t>::get8(int j, float* o) const {
-    const uint4 v = w[j >> 1];
-    const uint32_t a = (j & 1) ? v.z : v.x;
-    const uint32_t b = (j & 1) ? v.w : v.y;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = fp8_to_f32((a >> (8 * i)) & 0xFFu);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[4 + i] = fp8_to_f32((b >> (8 * i)) & 0xFFu);
-}
-
-template <>
-__device__ inline void Raw32<bf16_t>::get8(int j, float* o) const {
-    const uint4 v = w[j];
-    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        o[2 * i] = __uint_as_float(x[i] << 16);
-        o[2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u);
-    }
-}
-
-template <>
-__device__ inline void Raw32<float>::get8(int j, float* o) const {
-    const uint4 a = w[2 * j], b = w[2 * j + 1];
-    o[0] = __uint_as_float(a.x); o[1] = __uint_as_float(a.y); o[2] = __uint_as_float(a.z); o[3] = __uint_as_float(a.w);
-    o[4] = __uint_as_float(b.x); o[5] = __uint_as_float(b.y); o[6] = __uint_as_float(b.z); o[7] = __uint_as_float(b.w);
-}
-
-template <typename T, typename S>
-__device__ inline void stage32(T* dst, const Raw32<S>& r) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float v[8];
-        r.get8(j, v);
-        lds_store8<T>(dst + 8 * j, v);
-    }
-}
 
 // Sorted (ascending) insertion into a per-lane top-8 list.
 __device__ inline void top_insert(float (&ls)[kTop], int (&li)[kTop], float s, int id) {
@@ -106,65 +65,86 @@ __device__ inline void top_insert(float (&ls)[kTop], int (&li)[kTop], float s, i
     }
 }
 
-template <typename T>
-struct SearchSmem {
-    static constexpr int P = Pitch<T, kKC>::value;
-    static constexpr size_t kOperands = (size_t)(kSlot + kTok) * P * sizeof(T);
-    static constexpr size_t kMerge = (size_t)kTok * 8 * kTop * (sizeof(float) + sizeof(int));
-    static constexpr size_t kMain = kOperands > kMerge ? kOperands : kMerge;
-    static constexpr size_t kMeta = kTok * sizeof(int) + kSlot * (sizeof(int) + sizeof(float));
-    static constexpr size_t bytes = kMain + kMeta;
+// A operand: rows of the pool block of the current stage (FP8 or fp32 storage).
+template <typename T, typename RefT, int BM>
+struct PoolLoader {
+    static constexpr int kUnits = BM / 128;
+    Raw32<RefT> raw[kUnits];
+    const RefT* pool;
+    int W2, nk, blk0, count;
+    __device__ inline void load(int s) {
+        const int blk = blk0 + s / nk;
+        const int k0 = (s % nk) * kKC + (threadIdx.x & 1) * 32;
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+            const int slot = blk * BM + (threadIdx.x >> 1) + 128 * u;
+            if (slot < count) raw[u].load(pool + (size_t)slot * W2 + k0);
+            else raw[u].zero();
+        }
+    }
+    __device__ inline void store(T* lds, int P) const {
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u)
+            stage32<T>(lds + ((threadIdx.x >> 1) + 128 * u) * P + (threadIdx.x & 1) * 32, raw[u]);
+    }
 };
 
-// grid: (token tiles, pool chunks, batch); 256 threads = 4 waves in a 2 x 2 layout:
-// wave (ws, wt) scores slots [64 ws, 64 ws + 64) of the block against tokens
-// [64 wt, 64 wt + 64) of the tile (4 x 4 MFMA tiles of 16 x 16).
+// B operand: the tile's token rows; the same K stage repeats for every pool block.
+template <typename T, typename KvT>
+struct TokLoader {
+    RowTile<T, KvT, kTok> t;
+    const KvT* row[1];
+    int nk;
+    __device__ inline void load(int s) { t.load_rows(row, (s % nk) * kKC); }
+    __device__ inline void store(T* lds, int P) const { t.store(lds, P); }
+};
+
+// grid: (8 * per, batch) blocks over logical tiles (token tile, chunk), chunks fastest.
 template <typename T, typename KvT, typename RefT>
 __global__ __launch_bounds__(kThreads) void search_kernel(
     const KvT* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
     const RefT* __restrict__ ref_vals, const int* __restrict__ ref_pos, const float* __restrict__ ref_norm2,
-    const int* __restrict__ ref_count, int W2, int cap_ref, int chunk_slots, int nsplit,
+    const int* __restrict__ ref_count, int W2, int cap_ref, int blocks_per_chunk, int nsplit, int ntiles, int per,
     float* __restrict__ part_score, int* __restrict__ part_slot) {
-    typedef SearchSmem<T> SM;
-    constexpr int P = SM::P;
+    typedef SC<T> C;
     extern __shared__ __align__(16) unsigned char smem[];
-    T* sA = reinterpret_cast<T*>(smem);  // pool rows   [kSlot][P]
-    T* sB = sA + kSlot * P;              // token rows  [kTok][P]
-    float* mS = reinterpret_cast<float*>(smem);              // merge scores [kTok][8][kTop]
-    int* mI = reinterpret_cast<int*>(mS + kTok * 8 * kTop);  // merge slots
-    int* s_tokpos = reinterpret_cast<int*>(smem + SM::kMain);
-    int* s_refpos = s_tokpos + kTok;
-    float* s_norm = reinterpret_cast<float*>(s_refpos + kSlot);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    T* lds = reinterpret_cast<T*>(smem);
+    int* s_vis = reinterpret_cast<int*>(smem + C::kMain);
+    const int lt = xcd_tile(blockIdx.x, per);
+    if (lt >= ntiles * nsplit) return;
+    const int tile = lt / nsplit, split = lt - tile * nsplit;
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ws = wave >> 1, wt = wave & 1;
-    const int tile = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
     const int t0 = tile * kTok;
-    const int count = min(ref_count[b], cap_ref);
-    const int s_begin = split * chunk_slots;
-    const int s_end = min(count, s_begin + chunk_slots);
+    const int count = max(0, min(ref_count[b], cap_ref));
+    const int* rp = ref_pos + (size_t)b * cap_ref;
+    const float* rn = ref_norm2 + (size_t)b * cap_ref;
 
-    if (tid < kTok) {
-        const int t = t0 + tid;
-        s_tokpos[tid] = (t < n) ? pos[(size_t)b * n + t] : INT_MIN;
+    int tokpos_l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = t0 + 64 * wt + 16 * j + (lane & 15);
+        tokpos_l[j] = (t < n) ? pos[(size_t)b * n + t] : INT_MIN;
+    }
+    if (tid == 0) {
+        // visible pool prefix: slots with position < the tile's largest position
+        int mx = INT_MIN;
+        for (int i = 0; i < kTok && t0 + i < n; ++i) mx = max(mx, pos[(size_t)b * n + t0 + i]);
+        int lo = 0, hi = count;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (rp[mid] < mx) lo = mid + 1;
+            else hi = mid;
+        }
+        s_vis[0] = lo;
     }
     __syncthreads();
-    int tile_maxpos = INT_MIN;
-    for (int i = 0; i < kTok; ++i) tile_maxpos = max(tile_maxpos, s_tokpos[i]);
-
-    // token row pointer for this thread's staging row
-    const int st_row = tid >> 1;
-    const int st_col = (tid & 1) * 32;
-    const KvT* tok_src = nullptr;
-    {
-        const int t = t0 + st_row;
-        if (t < n) {
-            const int r = rows[(size_t)b * n + t];
-            if (r >= 0 && r < kv_len) tok_src = kv + ((size_t)b * kv_len + r) * W2;
-        }
-    }
+    const int visible = s_vis[0];
+    const int nblk = (visible + C::BM - 1) / C::BM;
+    const int blk0 = split * blocks_per_chunk;
+    const int blk1 = min(nblk, blk0 + blocks_per_chunk);
+    const int nk = W2 / kKC;
 
     float ls[4][kTop];
     int li[4][kTop];
@@ -176,79 +156,48 @@ __global__ __launch_bounds__(kThreads) void search_kernel(
             li[q][j] = -1;
         }
 
-    int tokpos_l[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) tokpos_l[tt] = s_tokpos[64 * wt + 16 * tt + (lane & 15)];
-
-    const int nk = W2 / kKC;
-    for (int sb = s_begin; sb < s_end; sb += kSlot) {
-        __syncthreads();
-        if (tid < kSlot) {
-            const int m = sb + tid;
-            const bool ok = m < s_end;
-            s_refpos[tid] = ok ? ref_pos[(size_t)b * cap_ref + m] : INT_MAX;
-            s_norm[tid] = ok ? ref_norm2[(size_t)b * cap_ref + m] : 0.f;
-        }
-        __syncthreads();
-        const int live = __syncthreads_or(tid < kSlot && s_refpos[tid] < tile_maxpos);
-        if (!live) continue;
-
-        const int slot_row = sb + st_row;
-        const RefT* ref_src =
-            (slot_row < s_end) ? ref_vals + ((size_t)b * cap_ref + slot_row) * W2 : nullptr;
-
-        f32x4 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
-
-        Raw32<RefT> ra;
-        Raw32<KvT> rb;
-        if (ref_src) ra.load(ref_src + st_col); else ra.zero();
-        if (tok_src) rb.load(tok_src + st_col); else rb.zero();
-        for (int kc = 0; kc < nk; ++kc) {
-            __syncthreads();
-            stage32<T>(sA + st_row * P + st_col, ra);
-            stage32<T>(sB + st_row * P + st_col, rb);
-            __syncthreads();
-            if (kc + 1 < nk) {
-                const int off = (kc + 1) * kKC + st_col;
-                if (ref_src) ra.load(ref_src + off);
-                if (tok_src) rb.load(tok_src + off);
+    if (blk1 > blk0) {
+        PoolLoader<T, RefT, C::BM> la;
+        la.pool = ref_vals + (size_t)b * cap_ref * W2;
+        la.W2 = W2;
+        la.nk = nk;
+        la.blk0 = blk0;
+        la.count = visible;
+        TokLoader<T, KvT> lb;
+        lb.nk = nk;
+        {
+            const int t = t0 + (tid >> 1);
+            const KvT* p = nullptr;
+            if (t < n) {
+                const int r = rows[(size_t)b * n + t];
+                if (r >= 0 && r < kv_len) p = kv + ((size_t)b * kv_len + r) * W2;
             }
-#pragma unroll
-            for (int ks = 0; ks < kKC / 32; ++ks) {
-                const int kof = ks * 32 + 8 * (lane >> 4);
-                typename Mma<T>::frag fa[4], fb[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) fa[i] = lds_frag<T>(sA + (64 * ws + 16 * i + (lane & 15)) * P + kof);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) fb[j] = lds_frag<T>(sB + (64 * wt + 16 * j + (lane & 15)) * P + kof);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::step(acc[i][j], fa[i], fb[j]);
-            }
+            lb.row[0] = p;
         }
-        // epilogue: score = ||r||^2 - 2 x.r for causal slots, into the per-token lists
+        f32x4 acc[C::WM / 16][C::WN / 16];
+        auto fold = [&](int bi, f32x4(&a)[C::WM / 16][C::WN / 16]) {
+            const int base = (blk0 + bi) * C::BM + C::WM * ws + 4 * (lane >> 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < C::WM / 16; ++i) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int sl = 64 * ws + 16 * i + 4 * (lane >> 4) + e;
-                const int rp = s_refpos[sl];
-                const float nr = s_norm[sl];
+                for (int e = 0; e < 4; ++e) {
+                    const int slot = base + 16 * i + e;
+                    const bool ok = slot < visible;
+                    const int p = ok ? rp[slot] : INT_MAX;
+                    const float nr = ok ? rn[slot] : 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (rp < tokpos_l[j]) top_insert(ls[j], li[j], fmaf(-2.f, acc[i][j][e], nr), sb + sl);
+                    for (int j = 0; j < 4; ++j)
+                        if (p < tokpos_l[j]) top_insert(ls[j], li[j], fmaf(-2.f, a[i][j][e], nr), slot);
                 }
             }
-        }
+        };
+        mainloop<T, C::BM, C::BN, C::WM, C::WN>(la, lb, (blk1 - blk0) * nk, nk, lds, C::WM * ws, 64 * wt, acc, fold);
     }
 
     // merge the 8 lists of every token (4 lane groups x 2 slot halves)
     __syncthreads();
+    float* mS = reinterpret_cast<float*>(smem);
+    int* mI = reinterpret_cast<int*>(mS + kTok * 8 * kTop);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int tl = 64 * wt + 16 * j + (lane & 15);
@@ -441,15 +390,14 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 
 EncodePlan plan_encode(const Shape& s, int B, int n, int cap_ref) {
     EncodePlan p{};
-    const int tiles = (n + kTok - 1) / kTok;
-    const int nblocks = (cap_ref + kSlot - 1) / kSlot;
-    int nsplit = (1024 + tiles * B - 1) / (tiles * B > 0 ? tiles * B : 1);
-    nsplit = nsplit < 1 ? 1 : nsplit;
-    nsplit = nsplit > 8 ? 8 : nsplit;
-    nsplit = nsplit > nblocks ? (nblocks > 0 ? nblocks : 1) : nsplit;
-    const int per = (nblocks + nsplit - 1) / nsplit;
+    const int BM = s.f32 ? SC<float>::BM : SC<bf16_t>::BM;
+    const int nblocks = (cap_ref + BM - 1) / BM;
+    int bpc = (nblocks + 7) / 8;
+    if (bpc < 2) bpc = 2;
+    int nsplit = (nblocks + bpc - 1) / bpc;
+    if (nsplit < 1) nsplit = 1;
     p.nsplit = nsplit;
-    p.chunk_slots = (per > 0 ? per : 1) * kSlot;
+    p.chunk_slots = bpc;  // pool blocks per chunk
     const size_t tok = (size_t)B * n;
     auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
     size_t off = 0;
@@ -460,7 +408,8 @@ EncodePlan plan_encode(const Shape& s, int B, int n, int cap_ref) {
     p.off_xbar = off;
     off = up(off + tok * s.W2 * (s.f32 ? 4 : 2));
     p.off_dh = off;
-    off = up(off + tok * s.d_ff * sizeof(float));
+    // dH: fp32 rows (fp32 formats) or three bf16 planes per row (bf16 formats)
+    off = up(off + tok * s.d_ff * (s.f32 ? 4 : 6));
     p.total = off;
     return p;
 }
@@ -468,16 +417,17 @@ EncodePlan plan_encode(const Shape& s, int B, int n, int cap_ref) {
 template <typename T, typename KvT, typename RefT>
 static hipError_t search_impl(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
                               const int* rows, const int* pos, int n, void* ws, hipStream_t st) {
-    const size_t smem = SearchSmem<T>::bytes;
+    const size_t smem = SC<T>::bytes;
     auto kern = search_kernel<T, KvT, RefT>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     char* w = static_cast<char*>(ws);
-    const dim3 grid((n + kTok - 1) / kTok, p.nsplit, c.B);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, st, static_cast<const KvT*>(kv), kv_len, rows, pos, n,
-                       static_cast<const RefT*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count, s.W2, c.cap_ref,
-                       p.chunk_slots, p.nsplit, reinterpret_cast<float*>(w + p.off_part_score),
+    const int ntiles = (n + kTok - 1) / kTok;
+    const int per = xcd_per(ntiles * p.nsplit);
+    hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(kThreads), smem, st, static_cast<const KvT*>(kv), kv_len, rows,
+                       pos, n, static_cast<const RefT*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count, s.W2,
+                       c.cap_ref, p.chunk_slots, p.nsplit, ntiles, per, reinterpret_cast<float*>(w + p.off_part_score),
                        reinterpret_cast<int*>(w + p.off_part_slot));
     return hipGetLastError();
 }
