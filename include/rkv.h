@@ -82,8 +82,8 @@ typedef enum { RKV_F32 = 0, RKV_BF16 = 1, RKV_F16 = 2, RKV_FP8_E4M3 = 3 } rkv_dt
  *   "bf16": kv BF16, references FP8_E4M3 (OCP e4m3fn, no scale), weights BF16,
  *           scale/zmin F16                                   (the deployment formats)
  *   "f32" : kv F32, references F32, weights F32, scale/zmin F32      (exact reference runs)
- * Shapes: head_dim in {32, 64, 128}; W2 % 128 == 0; d_k % 128 == 0; d_ff % 64 == 0;
- * d_c % 64 == 0 and d_c <= 512; group == 32; bits in {2, 4, 16 (= quantization off,
+ * Shapes: head_dim in {64, 128}; d_k % 128 == 0; d_ff % 64 == 0;
+ * d_c in {64, 128, 256, 384, 512}; group == 32; bits in {2, 4, 16 (= quantization off,
  * fp16 latent)}; 1 <= top_k <= 8. */
 typedef struct {
     int32_t n_kv_heads; /* N                                             */

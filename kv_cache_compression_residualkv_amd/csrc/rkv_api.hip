@@ -39,11 +39,13 @@ rkv_status check_config(const rkv_config* cfg, Shape* out) {
                       cfg->weight_dtype == RKV_BF16;
     if (!f32 && !bf16) return RKV_ERR_UNSUPPORTED;
     const int D = cfg->head_dim;
-    if (D != 32 && D != 64 && D != 128) return RKV_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return RKV_ERR_UNSUPPORTED;
     const long dk = (long)cfg->n_kv_heads * D;
     if (dk > (1 << 20)) return RKV_ERR_UNSUPPORTED;
     if (dk % 128 != 0) return RKV_ERR_UNSUPPORTED;
-    if (cfg->d_ff % 64 != 0 || cfg->d_c % 64 != 0 || cfg->d_c > 512) return RKV_ERR_UNSUPPORTED;
+    if (cfg->d_ff % 64 != 0) return RKV_ERR_UNSUPPORTED;
+    if (cfg->d_c != 64 && cfg->d_c != 128 && cfg->d_c != 256 && cfg->d_c != 384 && cfg->d_c != 512)
+        return RKV_ERR_UNSUPPORTED;
     if (cfg->group != 32) return RKV_ERR_UNSUPPORTED;
     if (cfg->top_k > 8) return RKV_ERR_UNSUPPORTED;
     if (out) {

@@ -6,12 +6,16 @@
 // (last paragraph): the restored pre-RoPE key is rotated at the token's own position.
 //
 // A workgroup owns one 128-column slice of the K|V output (one head at D = 128) and
-// keeps that slice of W_d resident in LDS; it walks a range of selected tokens, 128
-// at a time (32 per wavefront). The MFMA computes out^T = W_d^T z~^T: the W_d slice is
-// the A operand (from LDS), the dequantized latents are the B operand, built in
-// registers straight from the packed codes. Each lane ends up with 4 consecutive
-// output columns of one token, which makes the reference-mean gather (4 bytes per
-// reference row) and the RoPE pairing (column j with j + D/2, same lane) local.
+// keeps that slice of W_d resident in LDS; each wavefront restores 32 tokens per
+// pass. The MFMA computes out^T = W_d^T z~^T (W_d slice = A operand from LDS, the
+// dequantized latents = B operand built in registers). The K order is permuted so
+// that lane group g (lane / 16) supplies the contiguous quarter
+// [g d_c / 4, (g + 1) d_c / 4) of each token's latent over the K-steps, and the LDS
+// reads of W_d use the same permutation: a token's packed codes then arrive in a few
+// 16-byte loads, issued one pass ahead. Each lane ends with 4 consecutive output
+// columns of one token, which keeps the reference-mean gather (4 bytes per reference
+// row) and the RoPE pairing (column j with j + D/2, same lane) local; bf16 output rows
+// are staged through LDS and written as whole 256-byte row segments.
 #include <math.h>
 
 #include "rkv_device.h"
@@ -22,23 +26,21 @@ namespace rkv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCols = 128;       // output columns per workgroup
-constexpr int kWaveTok = 32;     // tokens per wavefront pass
+constexpr int kCols = 128;     // output columns per workgroup
+constexpr int kWaveTok = 32;   // tokens per wavefront pass
 constexpr int kPassTok = 4 * kWaveTok;
+constexpr int kMaxK = 8;       // references per token kept in registers
 
-struct RopeFreq {
-    double rev[64];  // theta^(-2j/D) / (2 pi): revolutions per position, j < D/2
-};
-
-template <typename T>
+template <typename T, typename OutT>
 struct DecSmem {
     static __host__ __device__ inline int pitch(int d_c) { return d_c + 16 / (int)sizeof(T); }
-    static inline size_t bytes(int d_c) { return (size_t)kCols * pitch(d_c) * sizeof(T); }
+    // bf16 output: 16 tokens x 128 columns staged per wavefront (row pitch 272 B)
+    static constexpr int kStagePitch = 272;
+    static constexpr bool kStage = sizeof(OutT) == 2;
+    static inline size_t bytes(int d_c) {
+        return (size_t)kCols * pitch(d_c) * sizeof(T) + (kStage ? (size_t)4 * 16 * kStagePitch : 0);
+    }
 };
-
-// latent fragment of one token: 8 consecutive coordinates starting at k (a multiple of 8)
-template <typename T, typename ScT>
-struct Latent;
 
 template <typename ScT>
 __device__ inline float ld_scalar(const ScT* p);
@@ -47,31 +49,141 @@ __device__ inline float ld_scalar<float>(const float* p) { return *p; }
 template <>
 __device__ inline float ld_scalar<f16_t>(const f16_t* p) { return (float)*p; }
 
+// Everything a lane needs for one token of a pass.
+template <typename ScT>
+struct TokMeta {
+    int p;        // position, -1 if none
+    int enc;      // 1: encoded token with a record; 0: reference or invalid
+    int nref;     // references averaged (a reference token averages itself)
+    int ref[kMaxK];
+    int g0;       // first group the lane's quarter touches
+    uint4 q[4];   // this lane's quarter of the packed codes (bits <= 4)
+    float sc[4], zm[4];  // step and minimum of the quarter's groups
+};
+
+template <typename ScT>
+__device__ inline void load_meta(TokMeta<ScT>& M, int t, int t_end, const int* idx, int m, int b,
+                                 const int* self_slot, const int* ref_idx, const uint8_t* codes, size_t code_bytes,
+                                 const ScT* scale, const ScT* zmin, int top_k, int cap_ref, int cap_tok, int d_c,
+                                 int bits, int g, int* err, bool flag) {
+    M.p = -1;
+    M.enc = 0;
+    M.nref = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxK; ++q) M.ref[q] = 0;
+    if (t >= t_end) return;
+    const int p = idx[(size_t)b * m + t];
+    if (p < 0 || p >= cap_tok) {
+        if (flag) flag_error(err, DEVERR_IDX_RANGE);
+        return;
+    }
+    M.p = p;
+    const size_t ro = (size_t)b * cap_tok + p;
+    const int ss = self_slot[ro];
+    if (ss >= 0) {
+        M.nref = 1;
+        M.ref[0] = min(ss, cap_ref - 1);
+        return;
+    }
+    M.enc = 1;
+    // the chosen slots come first (ascending), then -1 padding
+    const int* ri = ref_idx + ro * top_k;
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxK; ++q) {
+        const int v = (q < top_k) ? ri[q] : -1;
+        M.ref[q] = v >= 0 ? min(v, cap_ref - 1) : 0;
+        cnt += v >= 0 ? 1 : 0;
+    }
+    M.nref = cnt;
+    if (bits == 16) return;  // fp16 latents are read per K-step
+    const int quarter = d_c >> 2;
+    const int nbytes = quarter * bits / 8;  // this lane's code bytes (<= 64)
+    const uint8_t* rec = codes + ro * code_bytes + (size_t)g * nbytes;
+    if ((nbytes & 15) == 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            M.q[u] = (16 * u < nbytes) ? reinterpret_cast<const uint4*>(rec)[u] : make_uint4(0, 0, 0, 0);
+    } else {
+        uint32_t wv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) wv[u] = (4 * u < nbytes) ? reinterpret_cast<const uint32_t*>(rec)[u] : 0u;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) M.q[u] = make_uint4(wv[4 * u], wv[4 * u + 1], wv[4 * u + 2], wv[4 * u + 3]);
+    }
+    const int G = d_c / 32;
+    const int g0 = (g * quarter) >> 5;
+    const int g1 = ((g + 1) * quarter - 1) >> 5;
+    M.g0 = g0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const bool ok = g0 + u <= g1;
+        M.sc[u] = ok ? ld_scalar<ScT>(scale + ro * G + g0 + u) : 0.f;
+        M.zm[u] = ok ? ld_scalar<ScT>(zmin + ro * G + g0 + u) : 0.f;
+    }
+}
+
+// 8 consecutive latent values (quarter-relative offset 8 ks) of a token as an MFMA fragment.
 template <typename T, typename ScT>
-__device__ inline typename Mma<T>::frag latent_frag(const uint8_t* rec, const ScT* sc, const ScT* zm, int k,
-                                                    int bits) {
-    float v[8];
+__device__ inline typename Mma<T>::frag latent_frag(const TokMeta<ScT>& M, int ks, int bits, const uint8_t* rec16) {
+    typename Mma<T>::frag f;
+    if (!M.enc) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (T)0.f;
+        return f;
+    }
     if (bits == 16) {
-        const uint4 w = *reinterpret_cast<const uint4*>(rec + 2 * k);
+        const uint4 w = *reinterpret_cast<const uint4*>(rec16 + 16 * ks);
         const f16_t* h = reinterpret_cast<const f16_t*>(&w);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
-    } else {
-        const int g = k >> 5;
-        const float s = ld_scalar<ScT>(sc + g);
-        const float m = ld_scalar<ScT>(zm + g);
-        uint32_t q;
-        if (bits == 4) {
-            q = *reinterpret_cast<const uint32_t*>(rec + (k >> 1));
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = fmaf((float)((q >> (4 * i)) & 0xFu), s, m);
-        } else {
-            q = *reinterpret_cast<const uint16_t*>(rec + (k >> 2));
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = fmaf((float)((q >> (2 * i)) & 0x3u), s, m);
-        }
+        for (int i = 0; i < 8; ++i) f[i] = (T)h[i];
+        return f;
     }
-    return Mma<T>::from_float(v);
+    // a quarter starts on a group boundary (d_c / 4 is 16 or a multiple of 32), so K-step
+    // ks lies in the quarter's group ks / 4: a compile-time index once ks is unrolled
+    const float s = M.sc[ks >> 2], z = M.zm[ks >> 2];
+    uint32_t w;
+    if (bits == 4) {
+        const int word = ks;  // 8 nibbles per 32-bit word
+        const uint4 v = M.q[word >> 2];
+        const int c = word & 3;
+        w = c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+    } else {
+        const int word = ks >> 1;  // 16 two-bit codes per word, 8 per K-step
+        const uint4 v = M.q[word >> 2];
+        const int c = word & 3;
+        const uint32_t ww = c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+        w = (ks & 1) ? (ww >> 16) : (ww & 0xFFFFu);
+    }
+    if constexpr (std::is_same<T, f16_t>::value) {
+        // (0x6400 | q) is the fp16 number 1024 + q: subtract 1024, then one fp16 FMA
+        const f16x2 off = {(f16_t)1024.0f, (f16_t)1024.0f};
+        const f16x2 sv = {(f16_t)s, (f16_t)s};
+        const f16x2 zv = {(f16_t)z, (f16_t)z};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t a, bq;
+            if (bits == 4) {
+                a = (w >> (8 * i)) & 0xFu;
+                bq = (w >> (8 * i + 4)) & 0xFu;
+            } else {
+                a = (w >> (4 * i)) & 0x3u;
+                bq = (w >> (4 * i + 2)) & 0x3u;
+            }
+            const uint32_t pk = 0x64006400u | a | (bq << 16);
+            f16x2 x = *reinterpret_cast<const f16x2*>(&pk);
+            x = x - off;
+            x = __builtin_elementwise_fma(x, sv, zv);
+            f[2 * i] = x[0];
+            f[2 * i + 1] = x[1];
+        }
+    } else {
+        const int sh = bits;
+        const uint32_t mask = (1u << bits) - 1u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (T)fmaf((float)((w >> (sh * i)) & mask), s, z);
+    }
+    return f;
 }
 
 template <typename OutT>
@@ -86,21 +198,127 @@ __device__ inline void store_out4<bf16_t>(bf16_t* p, float a, float b, float c, 
     *reinterpret_cast<uint2*>(p) = *reinterpret_cast<uint2*>(t);
 }
 
-// grid: (W2 / 128 column slices, token ranges, batch)
-template <typename T, typename RefT, typename ScT, typename WT, typename OutT>
+// Epilogue of 16 tokens (lane: token tbase + lane % 16, columns col0 + 16 i + 4 g + e):
+// add the reference mean, rotate the key columns, store.
+template <typename RefT, typename ScT, typename OutT, int D>
+__device__ inline void finish_tokens(const TokMeta<ScT>& M, f32x4 (&acc)[8], int tbase, int t_end, bool rope,
+                                     const RefT* pool, int W2, int col0, const double (&rev)[D / 32][4],
+                                     unsigned char* sO, OutT* out, int m, int b) {
+    typedef DecSmem<f16_t, OutT> SM;
+    constexpr int half = D / 2, pair_tiles = half / 16, tpd = D / 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, mrow = lane & 15;
+    // reference mean: fp32 sum in ascending slot order, one IEEE division
+    const float kf = (float)M.nref;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = col0 + 16 * i + 4 * g;
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int q = 0; q < kMaxK; ++q) {
+            if (q < M.nref) {
+                const float4 v = Load4<RefT>::run(pool + (size_t)M.ref[q] * W2 + c);
+                s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+            }
+        }
+        if (M.nref > 1) {
+            s.x = __fdiv_rn(s.x, kf); s.y = __fdiv_rn(s.y, kf);
+            s.z = __fdiv_rn(s.z, kf); s.w = __fdiv_rn(s.w, kf);
+        }
+        acc[i][0] += s.x;
+        acc[i][1] += s.y;
+        acc[i][2] += s.z;
+        acc[i][3] += s.w;
+    }
+    if (rope && M.p >= 0) {
+        // RoPE at the token's own position: the phase p theta^(-2j/D) in revolutions is
+        // reduced to [-1/2, 1/2] in fp64, then sin/cos in fp32
+        const double pp = (double)M.p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int jt = i % tpd;
+            if (jt >= pair_tiles) continue;
+            const int ip = i + pair_tiles;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double r = pp * rev[jt][e];
+                const float fr = (float)(r - rint(r));
+                const float sn = __builtin_amdgcn_sinf(fr);
+                const float cs = __builtin_amdgcn_cosf(fr);
+                const float x1 = acc[i][e], x2 = acc[ip][e];
+                acc[i][e] = x1 * cs - x2 * sn;
+                acc[ip][e] = x2 * cs + x1 * sn;
+            }
+        }
+    }
+    const bool valid = M.p >= 0;
+    if constexpr (SM::kStage) {
+        // stage 16 tokens x 128 columns, then write whole row segments
+        unsigned char* st = sO + (size_t)wave * 16 * SM::kStagePitch;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            OutT* d = reinterpret_cast<OutT*>(st + mrow * SM::kStagePitch) + 16 * i + 4 * g;
+            if (valid) store_out4<OutT>(d, acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+            else store_out4<OutT>(d, 0.f, 0.f, 0.f, 0.f);
+        }
+        __builtin_amdgcn_wave_barrier();
+        // each token row: 128 columns x 2 bytes = 16 chunks of 16 bytes
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ch = lane + 64 * r;
+            const int tr = ch >> 4, cc = ch & 15;
+            const int t = tbase + tr;
+            if (t < t_end) {
+                const uint4 v = *reinterpret_cast<const uint4*>(st + tr * SM::kStagePitch + 16 * cc);
+                *reinterpret_cast<uint4*>(out + ((size_t)b * m + t) * W2 + col0 + 8 * cc) = v;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    } else {
+        const int t = tbase + mrow;
+        if (t < t_end) {
+            OutT* o = out + ((size_t)b * m + t) * W2;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int c = col0 + 16 * i + 4 * g;
+                if (valid) store_out4<OutT>(o + c, acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+                else store_out4<OutT>(o + c, 0.f, 0.f, 0.f, 0.f);
+            }
+        }
+    }
+}
+
+// grid: (W2 / 128 column slices, token ranges, batch). NKS = d_c / 32 K-steps (each lane
+// group covers d_c / 4 latent coordinates, 8 per step); D = head dimension. Both are
+// compile-time so every register array is indexed statically.
+template <typename T, typename RefT, typename ScT, typename WT, typename OutT, int NKS, int D>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     const int* __restrict__ idx, int m, int tok_per_wg, const RefT* __restrict__ ref_vals,
     const int* __restrict__ self_slot, const int* __restrict__ ref_idx, const uint8_t* __restrict__ codes,
     size_t code_bytes, const ScT* __restrict__ scale, const ScT* __restrict__ zmin, const WT* __restrict__ wd,
-    int W2, int dk, int D, int d_c, int bits, int top_k, int cap_ref, int cap_tok, RopeFreq freq,
-    OutT* __restrict__ out, int* err) {
+    int W2, int dk, int bits, int top_k, int cap_ref, int cap_tok, double theta, OutT* __restrict__ out,
+    int* err) {
+    constexpr int d_c = 32 * NKS;
+    typedef DecSmem<T, OutT> SM;
     extern __shared__ __align__(16) unsigned char smem[];
     T* sW = reinterpret_cast<T*>(smem);
-    const int P = DecSmem<T>::pitch(d_c);
+    const int P = SM::pitch(d_c);
+    unsigned char* sO = smem + (size_t)kCols * P * sizeof(T);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, mrow = lane & 15;
     const int col0 = blockIdx.x * kCols;
     const int b = blockIdx.z;
-    const int G = d_c / 32;
+    constexpr int quarter = d_c / 4;
+    constexpr int half = D / 2;
+    constexpr int pair_tiles = half / 16;  // row tiles between a column and its RoPE partner
+
+    // revolutions per position of the RoPE pairs this lane rotates: j = 16 jt + 4 g + e
+    double rev[D / 32][4];
+#pragma unroll
+    for (int jt = 0; jt < pair_tiles; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            rev[jt][e] = pow(theta, -2.0 * (double)(16 * jt + 4 * g + e) / (double)D) * 0.15915494309189535;
 
     // W_d slice [128 output columns][d_c] -> LDS in the compute type
     for (int e = tid * 8; e < kCols * d_c; e += kThreads * 8) {
@@ -112,158 +330,63 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     __syncthreads();
 
     const bool rope = col0 < dk;
-    const int half = D / 2;
-    const int pair_tiles = half / 16;  // row tiles between a column and its partner
     const int t_begin = blockIdx.y * tok_per_wg;
     const int t_end = min(m, t_begin + tok_per_wg);
     const RefT* pool = ref_vals + (size_t)b * cap_ref * W2;
+    const bool flag = blockIdx.x == 0 && g == 0;
 
-    for (int tp = t_begin + wave * kWaveTok; tp < t_end; tp += kPassTok) {
-        // per-token metadata for this lane's two tokens (lane%16 of each 16-token tile)
-        int tokp[2], nref[2], rs[2][8];
-        bool is_enc[2];
-        const uint8_t* rec[2];
-        const ScT* sc[2];
-        const ScT* zm[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int t = tp + 16 * j + (lane & 15);
-            int p = -1;
-            if (t < t_end) p = idx[(size_t)b * m + t];
-            const bool ok = p >= 0 && p < cap_tok;
-            if (t < t_end && !ok && lane < 16 && blockIdx.x == 0) flag_error(err, DEVERR_IDX_RANGE);
-            tokp[j] = ok ? p : 0;
-            const int ss = ok ? self_slot[(size_t)b * cap_tok + p] : -1;
-            is_enc[j] = ok && ss < 0;
-            int cnt = 0;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) rs[j][q] = 0;
-            if (ok && ss >= 0) {
-                rs[j][0] = min(ss, cap_ref - 1);
-                cnt = 1;
-            } else if (ok) {
-                const int* ri = ref_idx + ((size_t)b * cap_tok + p) * top_k;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    if (q < top_k) {
-                        const int v = ri[q];
-                        if (v >= 0) {
-                            rs[j][cnt < 8 ? cnt : 7] = min(v, cap_ref - 1);
-                            ++cnt;
-                        }
-                    }
-                }
-            }
-            nref[j] = ok ? cnt : 0;
-            const size_t ro = (size_t)b * cap_tok + (ok ? p : 0);
-            rec[j] = codes + ro * code_bytes;
-            sc[j] = scale + ro * G;
-            zm[j] = zmin + ro * G;
-        }
+    TokMeta<ScT> cur0, cur1, nxt0, nxt1;
+    int tp = t_begin + wave * kWaveTok;
+    auto meta = [&](TokMeta<ScT>& M, int t) {
+        load_meta<ScT>(M, t, t_end, idx, m, b, self_slot, ref_idx, codes, code_bytes, scale, zmin, top_k, cap_ref,
+                       cap_tok, d_c, bits, g, err, flag);
+    };
+    meta(cur0, tp + mrow);
+    meta(cur1, tp + 16 + mrow);
+    for (; tp < t_end; tp += kPassTok) {
+        // prefetch the next pass
+        meta(nxt0, tp + kPassTok + mrow);
+        meta(nxt1, tp + kPassTok + 16 + mrow);
+        const uint8_t* rec0 =
+            codes + ((size_t)b * cap_tok + (cur0.p >= 0 ? cur0.p : 0)) * code_bytes + (size_t)g * quarter * 2;
+        const uint8_t* rec1 =
+            codes + ((size_t)b * cap_tok + (cur1.p >= 0 ? cur1.p : 0)) * code_bytes + (size_t)g * quarter * 2;
 
-        f32x4 acc[8][2];
+        f32x4 acc0[8], acc1[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            acc[i][0] = zero4();
-            acc[i][1] = zero4();
+            acc0[i] = zero4();
+            acc1[i] = zero4();
         }
-        for (int k0 = 0; k0 < d_c; k0 += 32) {
-            const int kof = k0 + 8 * (lane >> 4);
-            typename Mma<T>::frag fz[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (is_enc[j]) {
-                    fz[j] = latent_frag<T, ScT>(rec[j], sc[j], zm[j], kof, bits);
-                } else {
-                    float zz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                    fz[j] = Mma<T>::from_float(zz);
-                }
-            }
+        for (int ks = 0; ks < NKS; ++ks) {
+            const typename Mma<T>::frag f0 = latent_frag<T, ScT>(cur0, ks, bits, rec0);
+            const typename Mma<T>::frag f1 = latent_frag<T, ScT>(cur1, ks, bits, rec1);
+            const int kof = g * quarter + 8 * ks;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const typename Mma<T>::frag fw = lds_frag<T>(sW + (16 * i + (lane & 15)) * P + kof);
-                acc[i][0] = Mma<T>::step(acc[i][0], fw, fz[0]);
-                acc[i][1] = Mma<T>::step(acc[i][1], fw, fz[1]);
+                const typename Mma<T>::frag fw = lds_frag<T>(sW + (16 * i + mrow) * P + kof);
+                acc0[i] = Mma<T>::step(acc0[i], fw, f0);
+                acc1[i] = Mma<T>::step(acc1[i], fw, f1);
             }
         }
-
-        // epilogue: lane holds columns col0 + 16 i + 4 (lane/16) + e of token j
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int t = tp + 16 * j + (lane & 15);
-            // reference mean: fp32 sum in ascending slot order, one IEEE division
-            const float kf = (float)nref[j];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int c = col0 + 16 * i + 4 * (lane >> 4);
-                float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    if (q < nref[j]) {
-                        const float4 v = Load4<RefT>::run(pool + (size_t)rs[j][q] * W2 + c);
-                        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-                    }
-                }
-                if (nref[j] > 1) {
-                    s.x = __fdiv_rn(s.x, kf); s.y = __fdiv_rn(s.y, kf);
-                    s.z = __fdiv_rn(s.z, kf); s.w = __fdiv_rn(s.w, kf);
-                }
-                acc[i][j][0] += s.x;
-                acc[i][j][1] += s.y;
-                acc[i][j][2] += s.z;
-                acc[i][j][3] += s.w;
-            }
-            if (rope) {
-                // RoPE at the token's own position: angle p * theta^(-2j/D); the phase is
-                // reduced to one revolution in fp64, then sin/cos in fp32
-                const double pp = (double)tokp[j];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int cl = (16 * i) % D;  // head-local column of this row tile
-                    if (cl >= half) continue;
-                    const int ip = i + pair_tiles;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int jj = cl + 4 * (lane >> 4) + e;
-                        const double r = pp * freq.rev[jj];
-                        const float fr = (float)(r - rint(r));
-                        float sn, cs;
-                        __sincosf(6.283185307179586f * fr, &sn, &cs);
-                        const float x1 = acc[i][j][e], x2 = acc[ip][j][e];
-                        acc[i][j][e] = x1 * cs - x2 * sn;
-                        acc[ip][j][e] = x2 * cs + x1 * sn;
-                    }
-                }
-            }
-            if (t < t_end) {
-                OutT* o = out + ((size_t)b * m + t) * W2;
-                const bool ok = tokp[j] >= 0 && (is_enc[j] || nref[j] > 0);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int c = col0 + 16 * i + 4 * (lane >> 4);
-                    if (ok)
-                        store_out4<OutT>(o + c, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-                    else
-                        store_out4<OutT>(o + c, 0.f, 0.f, 0.f, 0.f);
-                }
-            }
-        }
+        finish_tokens<RefT, ScT, OutT, D>(cur0, acc0, tp, t_end, rope, pool, W2, col0, rev, sO, out, m, b);
+        finish_tokens<RefT, ScT, OutT, D>(cur1, acc1, tp + 16, t_end, rope, pool, W2, col0, rev, sO, out, m, b);
+        cur0 = nxt0;
+        cur1 = nxt1;
     }
 }
 
 }  // namespace
 
-template <typename T, typename RefT, typename ScT, typename WT, typename OutT>
+template <typename T, typename RefT, typename ScT, typename WT, typename OutT, int NKS, int D>
 static hipError_t decode_impl(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
                               hipStream_t st) {
-    const size_t smem = DecSmem<T>::bytes(s.d_c);
-    auto kern = decode_kernel<T, RefT, ScT, WT, OutT>;
+    const size_t smem = DecSmem<T, OutT>::bytes(s.d_c);
+    auto kern = decode_kernel<T, RefT, ScT, WT, OutT, NKS, D>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    RopeFreq f{};
-    for (int j = 0; j < s.D / 2 && j < 64; ++j)
-        f.rev[j] = std::pow(s.theta, -2.0 * j / (double)s.D) / 6.283185307179586;
     const int slices = s.W2 / kCols;
     // aim at about two workgroups per CU in total
     int ranges = (512 + slices * c.B - 1) / (slices * c.B);
@@ -274,19 +397,40 @@ static hipError_t decode_impl(const Shape& s, const CacheView& c, const int* idx
     const dim3 grid(slices, ranges, c.B);
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, st, idx, m, per, static_cast<const RefT*>(c.ref_vals),
                        c.self_slot, c.ref_idx, c.codes, c.code_bytes, static_cast<const ScT*>(c.scale),
-                       static_cast<const ScT*>(c.zmin), static_cast<const WT*>(wd), s.W2, s.dk, s.D, s.d_c, s.bits,
-                       s.top_k, c.cap_ref, c.cap_tok, f, static_cast<OutT*>(out), c.err);
+                       static_cast<const ScT*>(c.zmin), static_cast<const WT*>(wd), s.W2, s.dk, s.bits, s.top_k,
+                       c.cap_ref, c.cap_tok, s.theta, static_cast<OutT*>(out), c.err);
     return hipGetLastError();
+}
+
+template <typename T, typename RefT, typename ScT, typename WT, typename OutT, int D>
+static hipError_t decode_dc(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
+                            hipStream_t st) {
+    switch (s.d_c / 32) {
+        case 2: return decode_impl<T, RefT, ScT, WT, OutT, 2, D>(s, c, idx, m, wd, out, st);
+        case 4: return decode_impl<T, RefT, ScT, WT, OutT, 4, D>(s, c, idx, m, wd, out, st);
+        case 8: return decode_impl<T, RefT, ScT, WT, OutT, 8, D>(s, c, idx, m, wd, out, st);
+        case 12: return decode_impl<T, RefT, ScT, WT, OutT, 12, D>(s, c, idx, m, wd, out, st);
+        case 16: return decode_impl<T, RefT, ScT, WT, OutT, 16, D>(s, c, idx, m, wd, out, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, typename RefT, typename ScT, typename WT, typename OutT>
+static hipError_t decode_d(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
+                           hipStream_t st) {
+    if (s.D == 64) return decode_dc<T, RefT, ScT, WT, OutT, 64>(s, c, idx, m, wd, out, st);
+    if (s.D == 128) return decode_dc<T, RefT, ScT, WT, OutT, 128>(s, c, idx, m, wd, out, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
                          int out_dtype, hipStream_t st) {
     if (s.f32) {
-        if (out_dtype == RKV_F32) return decode_impl<float, float, float, float, float>(s, c, idx, m, wd, out, st);
-        return decode_impl<float, float, float, float, bf16_t>(s, c, idx, m, wd, out, st);
+        if (out_dtype == RKV_F32) return decode_d<float, float, float, float, float>(s, c, idx, m, wd, out, st);
+        return decode_d<float, float, float, float, bf16_t>(s, c, idx, m, wd, out, st);
     }
-    if (out_dtype == RKV_F32) return decode_impl<f16_t, fp8_t, f16_t, bf16_t, float>(s, c, idx, m, wd, out, st);
-    return decode_impl<f16_t, fp8_t, f16_t, bf16_t, bf16_t>(s, c, idx, m, wd, out, st);
+    if (out_dtype == RKV_F32) return decode_d<f16_t, fp8_t, f16_t, bf16_t, float>(s, c, idx, m, wd, out, st);
+    return decode_d<f16_t, fp8_t, f16_t, bf16_t, bf16_t>(s, c, idx, m, wd, out, st);
 }
 
 }  // namespace rkv

@@ -87,6 +87,27 @@ __device__ inline void stage32(T* dst, const Raw32<S>& r) {
     }
 }
 
+// FP8 -> bf16 is exact; v_cvt_scalef32_pk_bf16_fp8 (scale 1) widens two bytes per
+// call and agrees with the OCP e4m3fn definition on all 256 codes.
+template <>
+__device__ inline void stage32<bf16_t, fp8_t>(bf16_t* dst, const Raw32<fp8_t>& r) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint4 v = r.w[h];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], 1.0f, false);
+            const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], 1.0f, true);
+            o[2 * i] = *reinterpret_cast<const uint32_t*>(&lo);
+            o[2 * i + 1] = *reinterpret_cast<const uint32_t*>(&hi);
+        }
+        reinterpret_cast<uint4*>(dst)[2 * h] = make_uint4(o[0], o[1], o[2], o[3]);
+        reinterpret_cast<uint4*>(dst)[2 * h + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
 // A tile operand of R rows (R a multiple of 128): thread t stages row (t >> 1) + 128 u,
 // columns [(t & 1) * 32, +32) of the stage, for u < R / 128. The kernel fills row[u]
 // (nullptr = zero row) before each load.

@@ -62,9 +62,11 @@ def test_config_validation(lib):
         (dict(group=16), -2),
         (dict(d_c=640), -2),
         (dict(d_c=96), -2),
+        (dict(d_c=192), -2),
         (dict(d_ff=1000), -2),
         (dict(head_dim=256, n_kv_heads=4), -2),
         (dict(n_kv_heads=3, head_dim=32), -2),
+        (dict(n_kv_heads=4, head_dim=32), -2),
     ]
     for kw, want in bad:
         assert B.rkv_validate_config(B.dataclasses.replace(base, **kw)) == want, kw
