@@ -61,65 +61,102 @@ struct TokMeta {
     float sc[4], zm[4];  // step and minimum of the quarter's groups
 };
 
+// Loads everything one token needs for the next pass. All loads depend only on the
+// position p (read two passes earlier), so they issue together.
 template <typename ScT>
-__device__ inline void load_meta(TokMeta<ScT>& M, int t, int t_end, const int* idx, int m, int b,
-                                 const int* self_slot, const int* ref_idx, const uint8_t* codes, size_t code_bytes,
-                                 const ScT* scale, const ScT* zmin, int top_k, int cap_ref, int cap_tok, int d_c,
-                                 int bits, int g, int* err, bool flag) {
-    M.p = -1;
+__device__ inline void load_meta(TokMeta<ScT>& M, int p, int b, const int* self_slot, const int* ref_idx,
+                                 const uint8_t* codes, size_t code_bytes, const ScT* scale, const ScT* zmin,
+                                 int top_k, int cap_ref, int cap_tok, int d_c, int bits, int g) {
+    M.p = p;
     M.enc = 0;
     M.nref = 0;
 #pragma unroll
     for (int q = 0; q < kMaxK; ++q) M.ref[q] = 0;
-    if (t >= t_end) return;
-    const int p = idx[(size_t)b * m + t];
-    if (p < 0 || p >= cap_tok) {
-        if (flag) flag_error(err, DEVERR_IDX_RANGE);
-        return;
+    M.g0 = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        M.q[u] = make_uint4(0, 0, 0, 0);
+        M.sc[u] = 0.f;
+        M.zm[u] = 0.f;
     }
-    M.p = p;
+    if (p < 0) return;
     const size_t ro = (size_t)b * cap_tok + p;
     const int ss = self_slot[ro];
-    if (ss >= 0) {
+    // the chosen slots come first (ascending), then -1 padding
+    const int* ri = ref_idx + ro * top_k;
+    int rv[kMaxK];
+#pragma unroll
+    for (int q = 0; q < kMaxK; ++q) rv[q] = (q < top_k) ? ri[q] : -1;
+    if (bits != 16) {
+        const int quarter = d_c >> 2;
+        const int nbytes = quarter * bits / 8;  // this lane's code bytes (<= 64)
+        const uint8_t* rec = codes + ro * code_bytes + (size_t)g * nbytes;
+        if ((nbytes & 15) == 0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                M.q[u] = (16 * u < nbytes) ? reinterpret_cast<const uint4*>(rec)[u] : make_uint4(0, 0, 0, 0);
+        } else {
+            uint32_t wv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) wv[u] = (4 * u < nbytes) ? reinterpret_cast<const uint32_t*>(rec)[u] : 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) M.q[u] = make_uint4(wv[4 * u], wv[4 * u + 1], wv[4 * u + 2], wv[4 * u + 3]);
+        }
+        const int G = d_c / 32;
+        const int g0 = (g * quarter) >> 5;
+        const int g1 = ((g + 1) * quarter - 1) >> 5;
+        M.g0 = g0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool ok = g0 + u <= g1;
+            M.sc[u] = ok ? ld_scalar<ScT>(scale + ro * G + g0 + u) : 0.f;
+            M.zm[u] = ok ? ld_scalar<ScT>(zmin + ro * G + g0 + u) : 0.f;
+        }
+    }
+    if (ss >= 0) {  // a reference token restores its stored row
         M.nref = 1;
         M.ref[0] = min(ss, cap_ref - 1);
         return;
     }
     M.enc = 1;
-    // the chosen slots come first (ascending), then -1 padding
-    const int* ri = ref_idx + ro * top_k;
     int cnt = 0;
 #pragma unroll
     for (int q = 0; q < kMaxK; ++q) {
-        const int v = (q < top_k) ? ri[q] : -1;
-        M.ref[q] = v >= 0 ? min(v, cap_ref - 1) : 0;
-        cnt += v >= 0 ? 1 : 0;
+        M.ref[q] = rv[q] >= 0 ? min(rv[q], cap_ref - 1) : 0;
+        cnt += rv[q] >= 0 ? 1 : 0;
     }
     M.nref = cnt;
-    if (bits == 16) return;  // fp16 latents are read per K-step
-    const int quarter = d_c >> 2;
-    const int nbytes = quarter * bits / 8;  // this lane's code bytes (<= 64)
-    const uint8_t* rec = codes + ro * code_bytes + (size_t)g * nbytes;
-    if ((nbytes & 15) == 0) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            M.q[u] = (16 * u < nbytes) ? reinterpret_cast<const uint4*>(rec)[u] : make_uint4(0, 0, 0, 0);
-    } else {
-        uint32_t wv[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) wv[u] = (4 * u < nbytes) ? reinterpret_cast<const uint32_t*>(rec)[u] : 0u;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) M.q[u] = make_uint4(wv[4 * u], wv[4 * u + 1], wv[4 * u + 2], wv[4 * u + 3]);
+}
+
+// Position of token t of the range, -1 when outside it or invalid (flagged).
+__device__ inline int load_pos(const int* idx, int t, int t_end, int m, int b, int cap_tok, int* err, bool flag) {
+    if (t >= t_end) return -1;
+    const int p = idx[(size_t)b * m + t];
+    if (p < 0 || p >= cap_tok) {
+        if (flag) flag_error(err, DEVERR_IDX_RANGE);
+        return -1;
     }
-    const int G = d_c / 32;
-    const int g0 = (g * quarter) >> 5;
-    const int g1 = ((g + 1) * quarter - 1) >> 5;
-    M.g0 = g0;
+    return p;
+}
+
+// First references of a token gathered ahead of the epilogue: 4 consecutive FP8 values
+// of reference q at the lane's columns of row tile i.
+constexpr int kGatherRefs = 4;
+template <typename RefT>
+struct Gather {
+    uint32_t v[8][kGatherRefs];
+};
+
+template <typename RefT, typename ScT>
+__device__ inline void issue_gather(Gather<RefT>& G, const TokMeta<ScT>& M, const RefT* pool, int W2, int col0, int g) {
+    if constexpr (std::is_same<RefT, fp8_t>::value) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const bool ok = g0 + u <= g1;
-        M.sc[u] = ok ? ld_scalar<ScT>(scale + ro * G + g0 + u) : 0.f;
-        M.zm[u] = ok ? ld_scalar<ScT>(zmin + ro * G + g0 + u) : 0.f;
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int q = 0; q < kGatherRefs; ++q)
+                G.v[i][q] = (q < M.nref)
+                                ? *reinterpret_cast<const uint32_t*>(pool + (size_t)M.ref[q] * W2 + col0 + 16 * i + 4 * g)
+                                : 0u;
     }
 }
 
@@ -201,9 +238,9 @@ __device__ inline void store_out4<bf16_t>(bf16_t* p, float a, float b, float c, 
 // Epilogue of 16 tokens (lane: token tbase + lane % 16, columns col0 + 16 i + 4 g + e):
 // add the reference mean, rotate the key columns, store.
 template <typename RefT, typename ScT, typename OutT, int D>
-__device__ inline void finish_tokens(const TokMeta<ScT>& M, f32x4 (&acc)[8], int tbase, int t_end, bool rope,
-                                     const RefT* pool, int W2, int col0, const double (&rev)[D / 32][4],
-                                     unsigned char* sO, OutT* out, int m, int b) {
+__device__ inline void finish_tokens(const TokMeta<ScT>& M, const Gather<RefT>& Gt, f32x4 (&acc)[8], int tbase,
+                                     int t_end, bool rope, const RefT* pool, int W2, int col0,
+                                     const double (&rev)[D / 32][4], unsigned char* sO, OutT* out, int m, int b) {
     typedef DecSmem<f16_t, OutT> SM;
     constexpr int half = D / 2, pair_tiles = half / 16, tpd = D / 16;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -217,7 +254,13 @@ __device__ inline void finish_tokens(const TokMeta<ScT>& M, f32x4 (&acc)[8], int
 #pragma unroll
         for (int q = 0; q < kMaxK; ++q) {
             if (q < M.nref) {
-                const float4 v = Load4<RefT>::run(pool + (size_t)M.ref[q] * W2 + c);
+                float4 v;
+                if constexpr (std::is_same<RefT, fp8_t>::value) {
+                    if (q < kGatherRefs) v = fp8x4_to_f32(Gt.v[i][q]);
+                    else v = Load4<RefT>::run(pool + (size_t)M.ref[q] * W2 + c);
+                } else {
+                    v = Load4<RefT>::run(pool + (size_t)M.ref[q] * W2 + c);
+                }
                 s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
             }
         }
@@ -320,14 +363,31 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
         for (int e = 0; e < 4; ++e)
             rev[jt][e] = pow(theta, -2.0 * (double)(16 * jt + 4 * g + e) / (double)D) * 0.15915494309189535;
 
-    // W_d slice [128 output columns][d_c] -> LDS in the compute type
-    for (int e = tid * 8; e < kCols * d_c; e += kThreads * 8) {
-        const int r = e / d_c, k = e - r * d_c;
-        float v[8];
-        Load8<WT>::run(wd + (size_t)(col0 + r) * d_c + k, v);
-        lds_store8<T>(sW + r * P + k, v);
+    // W_d slice [128 output columns][d_c] -> LDS in the compute type, 8 loads in flight
+    // per thread before they are converted and stored
+    {
+        constexpr int kIters = kCols * d_c / (kThreads * 8);
+#pragma unroll
+        for (int it0 = 0; it0 < kIters; it0 += 8) {
+            float v[8][8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (it0 + u < kIters) {
+                    const int e = (it0 + u) * kThreads * 8 + tid * 8;
+                    const int r = e / d_c, k = e - r * d_c;
+                    Load8<WT>::run(wd + (size_t)(col0 + r) * d_c + k, v[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (it0 + u < kIters) {
+                    const int e = (it0 + u) * kThreads * 8 + tid * 8;
+                    const int r = e / d_c, k = e - r * d_c;
+                    lds_store8<T>(sW + r * P + k, v[u]);
+                }
+            }
+        }
     }
-    __syncthreads();
 
     const bool rope = col0 < dk;
     const int t_begin = blockIdx.y * tok_per_wg;
@@ -335,18 +395,28 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     const RefT* pool = ref_vals + (size_t)b * cap_ref * W2;
     const bool flag = blockIdx.x == 0 && g == 0;
 
-    TokMeta<ScT> cur0, cur1, nxt0, nxt1;
+    // pipeline: positions two passes ahead, records one pass ahead, reference rows of
+    // the current pass gathered before its MFMA loop
     int tp = t_begin + wave * kWaveTok;
-    auto meta = [&](TokMeta<ScT>& M, int t) {
-        load_meta<ScT>(M, t, t_end, idx, m, b, self_slot, ref_idx, codes, code_bytes, scale, zmin, top_k, cap_ref,
-                       cap_tok, d_c, bits, g, err, flag);
+    TokMeta<ScT> cur0, cur1, nxt0, nxt1;
+    auto meta = [&](TokMeta<ScT>& M, int p) {
+        load_meta<ScT>(M, p, b, self_slot, ref_idx, codes, code_bytes, scale, zmin, top_k, cap_ref, cap_tok, d_c,
+                       bits, g);
     };
-    meta(cur0, tp + mrow);
-    meta(cur1, tp + 16 + mrow);
+    meta(cur0, load_pos(idx, tp + mrow, t_end, m, b, cap_tok, err, flag));
+    meta(cur1, load_pos(idx, tp + 16 + mrow, t_end, m, b, cap_tok, err, flag));
+    int pn0 = load_pos(idx, tp + kPassTok + mrow, t_end, m, b, cap_tok, err, flag);
+    int pn1 = load_pos(idx, tp + kPassTok + 16 + mrow, t_end, m, b, cap_tok, err, flag);
+    __syncthreads();  // W_d slice in LDS
+
     for (; tp < t_end; tp += kPassTok) {
-        // prefetch the next pass
-        meta(nxt0, tp + kPassTok + mrow);
-        meta(nxt1, tp + kPassTok + 16 + mrow);
+        Gather<RefT> ga0, ga1;
+        issue_gather<RefT, ScT>(ga0, cur0, pool, W2, col0, g);
+        issue_gather<RefT, ScT>(ga1, cur1, pool, W2, col0, g);
+        meta(nxt0, pn0);
+        meta(nxt1, pn1);
+        pn0 = load_pos(idx, tp + 2 * kPassTok + mrow, t_end, m, b, cap_tok, err, flag);
+        pn1 = load_pos(idx, tp + 2 * kPassTok + 16 + mrow, t_end, m, b, cap_tok, err, flag);
         const uint8_t* rec0 =
             codes + ((size_t)b * cap_tok + (cur0.p >= 0 ? cur0.p : 0)) * code_bytes + (size_t)g * quarter * 2;
         const uint8_t* rec1 =
@@ -370,8 +440,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
                 acc1[i] = Mma<T>::step(acc1[i], fw, f1);
             }
         }
-        finish_tokens<RefT, ScT, OutT, D>(cur0, acc0, tp, t_end, rope, pool, W2, col0, rev, sO, out, m, b);
-        finish_tokens<RefT, ScT, OutT, D>(cur1, acc1, tp + 16, t_end, rope, pool, W2, col0, rev, sO, out, m, b);
+        finish_tokens<RefT, ScT, OutT, D>(cur0, ga0, acc0, tp, t_end, rope, pool, W2, col0, rev, sO, out, m, b);
+        finish_tokens<RefT, ScT, OutT, D>(cur1, ga1, acc1, tp + 16, t_end, rope, pool, W2, col0, rev, sO, out, m, b);
         cur0 = nxt0;
         cur1 = nxt1;
     }
@@ -388,8 +458,8 @@ static hipError_t decode_impl(const Shape& s, const CacheView& c, const int* idx
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     const int slices = s.W2 / kCols;
-    // aim at about two workgroups per CU in total
-    int ranges = (512 + slices * c.B - 1) / (slices * c.B);
+    // one workgroup per CU (the W_d slice fills most of LDS)
+    int ranges = (256 + slices * c.B - 1) / (slices * c.B);
     int per = (m + ranges - 1) / ranges;
     per = ((per + kPassTok - 1) / kPassTok) * kPassTok;
     if (per < kPassTok) per = kPassTok;

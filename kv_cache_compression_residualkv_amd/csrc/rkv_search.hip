@@ -110,9 +110,14 @@ __global__ __launch_bounds__(kThreads) void search_kernel(
     extern __shared__ __align__(16) unsigned char smem[];
     T* lds = reinterpret_cast<T*>(smem);
     int* s_vis = reinterpret_cast<int*>(smem + C::kMain);
-    const int lt = xcd_tile(blockIdx.x, per);
-    if (lt >= ntiles * nsplit) return;
-    const int tile = lt / nsplit, split = lt - tile * nsplit;
+    // Causal work grows with the token position, so token tiles are dealt round-robin
+    // over the 8 XCDs (block b runs on XCD b mod 8), latest (heaviest) tiles first; the
+    // pool chunks of one tile run back to back on the same XCD and share its L2.
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int tl = j / nsplit, split = j - tl * nsplit;
+    const int tiles_x = (ntiles - x + 7) / 8;  // tiles owned by XCD x: x, x + 8, ...
+    if (tl >= tiles_x) return;
+    const int tile = x + 8 * (tiles_x - 1 - tl);
     const int b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ws = wave >> 1, wt = wave & 1;
@@ -424,7 +429,7 @@ static hipError_t search_impl(const Shape& s, const CacheView& c, const EncodePl
     if (e != hipSuccess) return e;
     char* w = static_cast<char*>(ws);
     const int ntiles = (n + kTok - 1) / kTok;
-    const int per = xcd_per(ntiles * p.nsplit);
+    const int per = ((ntiles + 7) / 8) * p.nsplit;  // blocks per XCD
     hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(kThreads), smem, st, static_cast<const KvT*>(kv), kv_len, rows,
                        pos, n, static_cast<const RefT*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count, s.W2,
                        c.cap_ref, p.chunk_slots, p.nsplit, ntiles, per, reinterpret_cast<float*>(w + p.off_part_score),
