@@ -182,17 +182,43 @@ __global__ __launch_bounds__(kThreads) void search_kernel(
         f32x4 acc[C::WM / 16][C::WN / 16];
         auto fold = [&](int bi, f32x4(&a)[C::WM / 16][C::WN / 16]) {
             const int base = (blk0 + bi) * C::BM + C::WM * ws + 4 * (lane >> 4);
+            // A candidate can only matter if it beats the 8th best of every lane holding
+            // the same token (lanes l, l^16, l^32, l^48): the smallest of those four
+            // 8th-best scores bounds the token's 8th best from above. Candidates are
+            // gated four at a time against it before any insertion work.
+            float thr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float t = ls[j][kTop - 1];
+                t = fminf(t, __shfl_xor(t, 16, 64));
+                t = fminf(t, __shfl_xor(t, 32, 64));
+                thr[j] = t;
+            }
 #pragma unroll
             for (int i = 0; i < C::WM / 16; ++i) {
+                int p[4];
+                float nr[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int slot = base + 16 * i + e;
                     const bool ok = slot < visible;
-                    const int p = ok ? rp[slot] : INT_MAX;
-                    const float nr = ok ? rn[slot] : 0.f;
+                    p[e] = ok ? rp[slot] : INT_MAX;
+                    nr[e] = ok ? rn[slot] : 0.f;
+                }
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (p < tokpos_l[j]) top_insert(ls[j], li[j], fmaf(-2.f, a[i][j][e], nr), slot);
+                for (int j = 0; j < 4; ++j) {
+                    float sc[4];
+                    float mn = FLT_MAX;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        sc[e] = (p[e] < tokpos_l[j]) ? fmaf(-2.f, a[i][j][e], nr[e]) : FLT_MAX;
+                        mn = fminf(mn, sc[e]);
+                    }
+                    if (mn < fminf(thr[j], ls[j][kTop - 1])) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (sc[e] < thr[j]) top_insert(ls[j], li[j], sc[e], base + 16 * i + e);
+                    }
                 }
             }
         };
