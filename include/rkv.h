@@ -170,7 +170,8 @@ rkv_status rkv_append_ref(const rkv_config* cfg, rkv_cache* cache, const void* k
  * A token with an empty pool gets ref_idx = -1, a zero mean, and the
  * RKV_DEVERR_EMPTY_POOL bit. workspace: >= rkv_encode_workspace_bytes(cfg, B, n,
  * cap_ref) bytes of device memory, 256-byte aligned, owned by the caller, free to
- * reuse once the stream has passed this call. */
+ * reuse once the stream has passed this call. With n > 0, kv_len must be > 0
+ * (RKV_ERR_INVALID_ARG otherwise). */
 rkv_status rkv_encode(const rkv_config* cfg, const rkv_weights* w, rkv_cache* cache, const void* kv,
                       int32_t kv_len, const int32_t* rows, const int32_t* pos, int32_t n, void* workspace,
                       size_t workspace_bytes, void* stream);

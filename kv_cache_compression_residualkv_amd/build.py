@@ -30,6 +30,16 @@ HIP_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# The tiled GEMM kernels carry more accumulator and staging state than the 256
+# architectural VGPRs hold. With the default heuristics the backend keeps MFMA
+# accumulators in VGPRs and parks them in AGPRs around every MFMA (several
+# v_accvgpr moves per MFMA); the VGPR form with the AGPRs left free keeps the
+# accumulators in place. The decoder allocates better under the default.
+PER_SOURCE_FLAGS = {
+    "rkv_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "rkv_encode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
 
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -49,7 +59,7 @@ def build(verbose: bool = False, out: Optional[str] = None, jobs: int = 5) -> st
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIP_FLAGS, *PER_SOURCE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT))

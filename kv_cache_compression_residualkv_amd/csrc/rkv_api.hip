@@ -163,6 +163,7 @@ rkv_status rkv_encode_ex(const rkv_config* cfg, const rkv_weights* w, rkv_cache*
     if (st != RKV_OK) return st;
     if (n < 0 || kv_len < 0) return RKV_ERR_INVALID_ARG;
     if (n == 0) return RKV_OK;
+    if (kv_len == 0) return RKV_ERR_INVALID_ARG;  // every token reads a row of kv
     if (!w || !w->w_c1 || !w->w_c2 || !w->w_c3 || !kv || !rows || !pos) return RKV_ERR_INVALID_ARG;
     if (!aligned16(kv) || !aligned16(w->w_c1) || !aligned16(w->w_c2) || !aligned16(w->w_c3))
         return RKV_ERR_ALIGNMENT;

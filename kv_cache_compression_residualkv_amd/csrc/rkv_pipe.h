@@ -1,0 +1,253 @@
+// Multi-stage MFMA mainloop fed by direct global -> LDS loads (gfx950).
+//
+// A workgroup of 256 threads (4 wavefronts) computes a BM x BN tile of
+// A[BM x K] * B[BN x K]^T; both operands are K-contiguous rows read in stages of
+// 64 K values.
+//
+// LDS layout of one operand stage. Rows are grouped by 16 and K by 32 (64 bytes of
+// a 16-bit row): each (row group, K step) is one 1 KB block holding its 16 rows at a
+// 64-byte pitch; inside a row, the 16-byte chunk c sits at position c ^ h(r), with
+// h(r) = r_2 + 2 (r_1 ^ r_3) from the bits of the row r within the group. One direct load of a wavefront (global_load_lds_dwordx4)
+// writes 64 x 16 bytes contiguously, lane l at 16 l, so lane l fetches row l / 4,
+// chunk (l % 4) ^ h(l / 4): four consecutive lanes read one contiguous 64-byte row
+// segment (the address unit merges them). The A or B fragment of one
+// v_mfma_f32_16x16x32 (lane l: row l % 16, chunk l / 16) is then read from one block;
+// h makes every 16 lanes of the read cover all 64 LDS banks once (and every 8 lanes
+// 32 banks once).
+// FP8 rows (64 bytes per 64 K stage) use the same 1 KB block per row group with the
+// 16-byte granule m (K values 16 m .. +16) in place of the chunk; a bf16 fragment is
+// read as 8 bytes per lane and widened.
+//
+// Pipeline: NST stage slots form a ring. Stage s + NST - 1 is issued right after
+// the barrier that opens stage s, into the slot stage s - 1 used; before that
+// barrier every wavefront waits (s_waitcnt vmcnt) until its own loads of stage s
+// have landed, and the barrier then makes all of stage s visible. Only the
+// raw s_barrier is used: a workgroup fence would make the compiler wait for every
+// outstanding load, which is exactly what the ring is meant to avoid.
+#pragma once
+
+#include "rkv_device.h"
+
+namespace rkv {
+
+#define RKV_LDS __attribute__((address_space(3)))
+
+constexpr int kPipeThreads = 256;
+constexpr int kStageK = 64;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ inline void dma16(const void* g, void* lds_block) {
+    __builtin_amdgcn_global_load_lds(g, (RKV_LDS void*)lds_block, 16, 0, 0);
+}
+
+// wavefront index as a scalar (the compiler cannot prove threadIdx.x / 64 uniform)
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// position of chunk c of row r (within its group of 16) inside the row's 64 bytes
+__device__ inline int swz(int r, int c) { return c ^ (((r >> 2) & 1) | (((r >> 1) ^ (r >> 3)) & 1) << 1); }
+
+// A 16-bit operand of R rows (R a multiple of 32). Each wavefront issues R / 32 of the
+// stage's R / 8 block loads: load u of wave w fills block (w + 4 u) = 2 g + h
+// (row group g, K step h).
+template <int R>
+struct Op16 {
+    static constexpr int kLoads = R / 32;
+    static constexpr int kStageBytes = R * kStageK * 2;
+    const char* src[kLoads];  // per lane: its row's chunk in stage 0
+    // row(r) gives the byte address of row r (any row inside the matrix; rows past
+    // the valid range must still point at readable memory)
+    template <class RowFn>
+    __device__ inline void init(RowFn&& row) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int blk = wave + 4 * u;
+            const int g = blk >> 1, h = blk & 1;
+            src[u] = reinterpret_cast<const char*>(row(16 * g + (lane >> 2))) + 64 * h + 16 * swz(lane >> 2, lane & 3);
+        }
+    }
+    __device__ inline void issue(int s, char* slot) const {
+        const int wave = wave_id();
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) dma16(src[u] + (size_t)s * (kStageK * 2), slot + 1024 * (wave + 4 * u));
+    }
+    // fragment of row group g, K step ks
+    template <typename T>
+    static __device__ inline typename Mma<T>::frag frag(const char* slot, int g, int ks) {
+        const int lane = threadIdx.x & 63, r = lane & 15;
+        return *reinterpret_cast<const typename Mma<T>::frag*>(slot + 2048 * g + 1024 * ks + 64 * r +
+                                                               16 * swz(r, lane >> 4));
+    }
+};
+
+// An FP8 operand of R rows (R a multiple of 64): one 1 KB block per row group.
+template <int R>
+struct Op8 {
+    static constexpr int kLoads = R / 64;
+    static constexpr int kStageBytes = R * kStageK;
+    const char* src[kLoads];
+    template <class RowFn>
+    __device__ inline void init(RowFn&& row) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int g = wave + 4 * u;
+            src[u] = reinterpret_cast<const char*>(row(16 * g + (lane >> 2))) + 16 * swz(lane >> 2, lane & 3);
+        }
+    }
+    __device__ inline void issue(int s, char* slot) const {
+        const int wave = wave_id();
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) dma16(src[u] + (size_t)s * kStageK, slot + 1024 * (wave + 4 * u));
+    }
+    // bf16 fragment of row group g, K step ks: K values 32 ks + 8 (lane / 16) .. +8
+    static __device__ inline bf16x8 frag_bf16(const char* slot, int g, int ks) {
+        const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
+        const uint2 v = *reinterpret_cast<const uint2*>(slot + 1024 * g + 64 * r + 16 * swz(r, 2 * ks + (q >> 1)) +
+                                                        8 * (q & 1));
+        const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, false);
+        const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, true);
+        const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.y, 1.0f, false);
+        const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.y, 1.0f, true);
+        bf16x8 f;
+        f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+        f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+        return f;
+    }
+};
+
+// Wait until this wavefront's loads of the current stage are done, given that
+// `ahead` later stages (each `per_stage` loads) may still be in flight.
+template <int NST, int PER_STAGE>
+__device__ inline void wait_stage(int ahead) {
+    if constexpr (NST >= 4) {
+        if (ahead >= 3 && 3 * PER_STAGE < 64) {
+            wait_vmcnt<(3 * PER_STAGE < 64 ? 3 * PER_STAGE : 0)>();
+            return;
+        }
+        if (ahead >= 2) {
+            wait_vmcnt<2 * PER_STAGE>();
+            return;
+        }
+    }
+    if constexpr (NST >= 3) {
+        if (ahead >= 1) {
+            wait_vmcnt<PER_STAGE>();
+            return;
+        }
+    }
+    wait_vmcnt<0>();
+}
+
+// s_waitcnt lgkmcnt(0) alone
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4)); }
+
+// Ring mainloop with the LDS fragment reads of one K step overlapped with the MFMAs
+// of the other. Per stage s (K steps 0 and 1, fragments f0 and f1):
+//   read f1(s) | MFMA f0(s) | wait, barrier | issue stage s + NST | read f0(s + 1) | MFMA f1(s)
+// The barrier sits between the two halves: before it, every wavefront has its f1(s)
+// fragments in registers (lgkmcnt 0) and its loads of stage s + 1 landed, so the slot
+// of stage s can be refilled right after it. Compiler-only fences keep the LDS reads
+// on their side of the barrier.
+//   load(F&, const char* slot_a, const char* slot_b, int ks)  reads one K step
+//   mma(const F&, Acc&)                                       multiplies it
+template <int NST, class F, class LA, class LB, class Ld, class Mm, class Acc, class OnBlock>
+__device__ inline void ring_mainloop_lrp(const LA& a, const LB& b, int n_stages, int stages_per_block, char* lds,
+                                         Ld&& load, Mm&& mma, Acc& acc, OnBlock&& on_block) {
+    static_assert(NST >= 2 && NST <= 4, "2 to 4 stages");
+    constexpr int kSlot = LA::kStageBytes + LB::kStageBytes;
+    constexpr int kPer = LA::kLoads + LB::kLoads;
+    if (n_stages <= 0) return;
+#pragma unroll
+    for (int p = 0; p < NST; ++p) {
+        if (p < n_stages) {
+            a.issue(p, lds + p * kSlot);
+            b.issue(p, lds + p * kSlot + LA::kStageBytes);
+        }
+    }
+    wait_stage<NST + 1, kPer>(min(NST - 1, n_stages - 1));
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    F f0, f1;
+    load(f0, lds, lds + LA::kStageBytes, 0);
+    int kin = 0;
+    int slot = 0;
+    // every stage but the last: no data-dependent control flow between the two halves
+    for (int s = 0; s + 1 < n_stages; ++s) {
+        const char* sa = lds + slot * kSlot;
+        load(f1, sa, sa + LA::kStageBytes, 1);
+        mma(f0, acc);
+        const int next = slot + 1 == NST ? 0 : slot + 1;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_lgkm0();
+        wait_stage<NST, kPer>(min(NST - 2, n_stages - 2 - s));
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (s + NST < n_stages) {
+            a.issue(s + NST, lds + slot * kSlot);
+            b.issue(s + NST, lds + slot * kSlot + LA::kStageBytes);
+        }
+        const char* na = lds + next * kSlot;
+        load(f0, na, na + LA::kStageBytes, 0);
+        mma(f1, acc);
+        slot = next;
+        if (++kin == stages_per_block) {
+            kin = 0;
+            on_block(s / stages_per_block, acc, false);
+        }
+    }
+    {
+        const char* sa = lds + slot * kSlot;
+        load(f1, sa, sa + LA::kStageBytes, 1);
+        mma(f0, acc);
+        mma(f1, acc);
+        on_block((n_stages - 1) / stages_per_block, acc, true);
+    }
+}
+
+// The ring mainloop. `a` and `b` issue their stage loads; `mma(slot_a, slot_b, acc)`
+// multiplies one resident stage; every `stages_per_block` stages `on_block(block, acc)`
+// sees the finished accumulators, which then restart from zero (the last block's
+// accumulators stay for the caller). LDS holds NST slots of (A stage, B stage).
+template <int NST, class LA, class LB, class Mm, class Acc, class OnBlock>
+__device__ inline void ring_mainloop(const LA& a, const LB& b, int n_stages, int stages_per_block, char* lds, Mm&& mma,
+                                     Acc& acc, OnBlock&& on_block) {
+    static_assert(NST >= 2 && NST <= 4, "2 to 4 stages");
+    constexpr int kSlot = LA::kStageBytes + LB::kStageBytes;
+    constexpr int kPer = LA::kLoads + LB::kLoads;
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p) {
+        if (p < n_stages) {
+            a.issue(p, lds + p * kSlot);
+            b.issue(p, lds + p * kSlot + LA::kStageBytes);
+        }
+    }
+    int kin = 0;
+    int slot = 0;
+    for (int s = 0; s < n_stages; ++s) {
+        const int ahead = min(NST - 2, n_stages - 1 - s);
+        wait_stage<NST, kPer>(ahead);
+        __builtin_amdgcn_s_barrier();
+        if (s + NST - 1 < n_stages) {
+            const int ns = slot == 0 ? NST - 1 : slot - 1;  // (s + NST - 1) mod NST
+            a.issue(s + NST - 1, lds + ns * kSlot);
+            b.issue(s + NST - 1, lds + ns * kSlot + LA::kStageBytes);
+        }
+        mma(lds + slot * kSlot, lds + slot * kSlot + LA::kStageBytes, acc);
+        slot = slot + 1 == NST ? 0 : slot + 1;
+        if (++kin == stages_per_block) {
+            kin = 0;
+            const bool last = s + 1 == n_stages;
+            on_block(s / stages_per_block, acc, last);
+        }
+    }
+}
+
+}  // namespace rkv

@@ -5,27 +5,35 @@
 // (arg top-k_i of -||kv_i - kv_j||^2, k_i = min(k, |pool|)) and averages them.
 //
 // Two kernels:
-//   search_kernel  - one workgroup scores a tile of 128 tokens against a chunk of
+//   search kernel  - one workgroup scores a tile of 128 tokens against a chunk of
 //                    pool blocks (256 slots each). Scores ||r||^2 - 2 x.r come from
 //                    MFMA (x bf16, r FP8 widened exactly to bf16, fp32 accumulation)
-//                    with the pool as the A operand so that each lane owns tokens; the
-//                    K stages of consecutive pool blocks form one pipelined sequence,
-//                    and after each block every lane folds its scores into a sorted
-//                    per-token top-8 held in registers. The workgroup finally merges
-//                    its lanes' lists into one top-8 per token and chunk. Only the
-//                    pool prefix with positions below the tile's last token is read
-//                    (the pool is position-ordered).
+//                    with the pool as the A operand so that each lane owns tokens.
+//                    The pool and token rows stream through an LDS ring filled by
+//                    direct global->LDS loads (the K stages of consecutive pool blocks
+//                    form one pipelined sequence). After each pool block every lane
+//                    folds its scores into a sorted per-token top-8 held in registers:
+//                    the first block of a chunk through a sorting network, later
+//                    blocks through a threshold filter whose few survivors are queued
+//                    in LDS and inserted afterwards. The workgroup finally merges its
+//                    lanes' lists into one top-8 per token and chunk. Only pool blocks
+//                    whose first position lies below the tile's last token are read
+//                    (the pool is position-ordered); single slots are masked by
+//                    position.
 //   select_kernel  - one wavefront per token merges the chunks' lists, decides the
 //                    k_i references (exact fp32 distances are computed only when the
 //                    approximate scores of the boundary candidates are closer than
 //                    their rounding bound), writes them in ascending slot order and
 //                    writes the reference mean row the encoder consumes.
+// The fp32 formats (small parity configurations) use a register-staged variant of
+// the search with fp32 MFMA and per-candidate insertion.
 #include <float.h>
 #include <limits.h>
 
 #include "rkv_device.h"
 #include "rkv_gemm.h"
 #include "rkv_internal.h"
+#include "rkv_pipe.h"
 
 namespace rkv {
 
@@ -107,7 +115,8 @@ __global__ __launch_bounds__(kThreads) void search_kernel(
     const int* __restrict__ ref_count, int W2, int cap_ref, int blocks_per_chunk, int nsplit, int ntiles, int per,
     float* __restrict__ part_score, int* __restrict__ part_slot) {
     typedef SC<T> C;
-    extern __shared__ __align__(16) unsigned char smem[];
+    extern __shared__ __align__(16) unsigned char smem_u8[];
+    unsigned char* smem = smem_u8;
     T* lds = reinterpret_cast<T*>(smem);
     int* s_vis = reinterpret_cast<int*>(smem + C::kMain);
     // Causal work grows with the token position, so token tiles are dealt round-robin
@@ -254,6 +263,364 @@ __global__ __launch_bounds__(kThreads) void search_kernel(
         const int* pi = mI + (size_t)tid * 8 * kTop;
         for (int c = 0; c < 8 * kTop; ++c) {
             if (pi[c] >= 0) top_insert(bs, bi, ps[c], pi[c]);
+        }
+        const size_t o = (((size_t)b * n + t0 + tid) * nsplit + split) * kTop;
+#pragma unroll
+        for (int q = 0; q < kTop; ++q) {
+            part_score[o + q] = bs[q];
+            part_slot[o + q] = bi[q];
+        }
+    }
+}
+
+// ------------------------------------------------------------------ bf16 / FP8 search
+
+namespace s2 {
+constexpr int kThreads = 512;  // 8 wavefronts: 2 slot halves x 4 token quarters
+constexpr int BM = 256;        // pool slots per block
+constexpr int BN = kTok;       // tokens per tile
+constexpr int NST = 2;         // LDS ring stages
+constexpr int kQ = 16;         // queued candidates per lane between two drains
+constexpr int kStageA = BM * kStageK;      // FP8 pool stage bytes
+constexpr int kStageB = BN * kStageK * 2;  // bf16 token stage bytes
+constexpr int kRing = NST * (kStageA + kStageB);
+constexpr int kQueue = kThreads * kQ * 8;
+constexpr int kMeta = BM * 8;              // positions + norms of one pool block
+constexpr int kMerge = kTok * 8 * kTop * 8;
+constexpr int kOffQueue = kRing;
+constexpr int kOffMeta = kOffQueue + kQueue;
+constexpr int kOffRed = kOffMeta + kMeta;
+constexpr int kMain = kOffRed + 64;
+constexpr size_t bytes = (size_t)(kMain > kMerge ? kMain : kMerge);
+static_assert(bytes <= 160 * 1024, "LDS budget");
+}  // namespace s2
+
+// compare-exchange on (score, slot) pairs in lexicographic order
+__device__ inline void cas(float& a, int& ia, float& b, int& ib) {
+    const bool sw = (b < a) || (b == a && ib < ia);
+    const float ta = sw ? b : a, tb = sw ? a : b;
+    const int tia = sw ? ib : ia, tib = sw ? ia : ib;
+    a = ta; b = tb; ia = tia; ib = tib;
+}
+
+// 19-comparator sorting network for 8 elements
+__device__ inline void sort8(float (&s)[8], int (&id)[8]) {
+#define RKV_C(x, y) cas(s[x], id[x], s[y], id[y])
+    RKV_C(0, 2); RKV_C(1, 3); RKV_C(4, 6); RKV_C(5, 7);
+    RKV_C(0, 4); RKV_C(1, 5); RKV_C(2, 6); RKV_C(3, 7);
+    RKV_C(0, 1); RKV_C(2, 3); RKV_C(4, 5); RKV_C(6, 7);
+    RKV_C(2, 4); RKV_C(3, 5);
+    RKV_C(1, 4); RKV_C(3, 6);
+    RKV_C(1, 2); RKV_C(3, 4); RKV_C(5, 6);
+#undef RKV_C
+}
+
+// a <- the 8 smallest of two sorted lists a, b, sorted (bitonic merge)
+__device__ inline void merge8(float (&a)[8], int (&ia)[8], const float (&b)[8], const int (&ib)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float bs = b[7 - i];
+        const int bi = ib[7 - i];
+        const bool tb = (bs < a[i]) || (bs == a[i] && bi < ia[i]);
+        a[i] = tb ? bs : a[i];
+        ia[i] = tb ? bi : ia[i];
+    }
+#define RKV_C(x, y) cas(a[x], ia[x], a[y], ia[y])
+    RKV_C(0, 4); RKV_C(1, 5); RKV_C(2, 6); RKV_C(3, 7);
+    RKV_C(0, 2); RKV_C(1, 3); RKV_C(4, 6); RKV_C(5, 7);
+    RKV_C(0, 1); RKV_C(2, 3); RKV_C(4, 5); RKV_C(6, 7);
+#undef RKV_C
+}
+
+// FP8 pool operand (8 wavefronts, 2 block loads each): stage s covers pool block
+// blk0 + s / nk, K columns (s % nk) * 64. Rows past the pool's capacity are clamped
+// (their candidates are masked by position).
+struct PoolOp {
+    static constexpr int kLoads = s2::BM / 16 / 8;
+    static constexpr int kStageBytes = s2::kStageA;
+    const char* pool;  // batch's pool base
+    int W2, nk, blk0, cap;
+    __device__ inline void issue(int s, char* slot) const {
+        const int lane = threadIdx.x & 63, wave = wave_id();
+        const int blk = blk0 + s / nk, kc = s - (s / nk) * nk;
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int g = wave + 8 * u;
+            const int r = min(blk * s2::BM + 16 * g + (lane >> 2), cap - 1);
+            dma16(pool + (size_t)r * W2 + kc * kStageK + 16 * swz(lane >> 2, lane & 3), slot + 1024 * g);
+        }
+    }
+};
+
+// bf16 token operand (8 wavefronts, 2 block loads each): the same 128 rows for every
+// pool block; load u of wave w fills block (w + 8 u) = 2 g + h.
+struct TokOp {
+    static constexpr int kLoads = s2::BN / 8 / 8;
+    static constexpr int kStageBytes = s2::kStageB;
+    const char* src[kLoads];
+    int nk;
+    __device__ inline void issue(int s, char* slot) const {
+        const int wave = wave_id();
+        const int kc = s - (s / nk) * nk;
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) dma16(src[u] + (size_t)kc * (kStageK * 2), slot + 1024 * (wave + 8 * u));
+    }
+};
+
+struct SFrag {
+    bf16x8 a[8];  // the wave's 8 pool row groups
+    bf16x8 b[2];  // the wave's 2 token row groups
+};
+
+// grid: (8 * per, batch) blocks over logical tiles (token tile, chunk), chunks fastest.
+// Wave w: slot half ws = w / 4 (rows 128 ws ..), token quarter wt = w % 4 (32 wt ..).
+template <typename KvT>
+__global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
+    const KvT* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
+    const fp8_t* __restrict__ ref_vals, const int* __restrict__ ref_pos, const float* __restrict__ ref_norm2,
+    const int* __restrict__ ref_count, int W2, int cap_ref, int blocks_per_chunk, int nsplit, int ntiles, int per,
+    float* __restrict__ part_score, int* __restrict__ part_slot) {
+    extern __shared__ __align__(16) unsigned char smem_u8[];
+    char* smem = reinterpret_cast<char*>(smem_u8);
+    constexpr int NT = s2::kThreads;
+    // token tiles dealt round-robin over the 8 XCDs, latest (heaviest) first; the
+    // chunks of one tile run back to back on one XCD
+    const int x = blockIdx.x & 7, jx = blockIdx.x >> 3;
+    const int tl = jx / nsplit, split = jx - tl * nsplit;
+    const int tiles_x = (ntiles - x + 7) / 8;
+    if (tl >= tiles_x) return;
+    const int tile = x + 8 * (tiles_x - 1 - tl);
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ws = wave >> 2, wt = wave & 3;
+    const int t0 = tile * kTok;
+    const int count = max(0, min(ref_count[b], cap_ref));
+    const int* rp = ref_pos + (size_t)b * cap_ref;
+    const float* rn = ref_norm2 + (size_t)b * cap_ref;
+    int* s_red = reinterpret_cast<int*>(smem + s2::kOffRed);
+
+    int tokpos_l[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int t = t0 + 32 * wt + 16 * j + (lane & 15);
+        tokpos_l[j] = (t < n) ? pos[(size_t)b * n + t] : INT_MIN;
+    }
+    // largest position of the tile, then the pool blocks whose first slot precedes it
+    {
+        int mp = INT_MIN;
+        if (tid < kTok && t0 + tid < n) mp = pos[(size_t)b * n + t0 + tid];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mp = max(mp, __shfl_xor(mp, o, 64));
+        if (lane == 0) s_red[wave] = mp;
+        __syncthreads();
+        int mx = INT_MIN;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) mx = max(mx, s_red[w]);
+        const int nbp = (count + s2::BM - 1) / s2::BM;
+        int v = 0;
+        for (int bb = tid; bb < nbp; bb += NT) v += rp[(size_t)bb * s2::BM] < mx ? 1 : 0;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0) s_red[8 + wave] = v;
+        __syncthreads();
+    }
+    int nblk = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) nblk += s_red[8 + w];
+    const int blk0 = split * blocks_per_chunk;
+    const int blk1 = min(nblk, blk0 + blocks_per_chunk);
+    const int nk = W2 / kStageK;
+
+    float ls[2][kTop];
+    int li[2][kTop];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int j = 0; j < kTop; ++j) {
+            ls[q][j] = FLT_MAX;
+            li[q][j] = -1;
+        }
+
+    if (blk1 > blk0) {
+        PoolOp pa;
+        pa.pool = reinterpret_cast<const char*>(ref_vals + (size_t)b * cap_ref * W2);
+        pa.W2 = W2;
+        pa.nk = nk;
+        pa.blk0 = blk0;
+        pa.cap = cap_ref;
+        TokOp pb;
+        pb.nk = nk;
+#pragma unroll
+        for (int u = 0; u < TokOp::kLoads; ++u) {
+            const int blk = wave + 8 * u;
+            const int r = 16 * (blk >> 1) + (lane >> 2);
+            const int t = min(t0 + r, n - 1);
+            int kr = rows[(size_t)b * n + t];
+            kr = (kr >= 0 && kr < kv_len) ? kr : 0;
+            pb.src[u] = reinterpret_cast<const char*>(kv + ((size_t)b * kv_len + kr) * W2) + 64 * (blk & 1) +
+                        16 * swz(lane >> 2, lane & 3);
+        }
+        int* m_pos = reinterpret_cast<int*>(smem + s2::kOffMeta);
+        float* m_nrm = reinterpret_cast<float*>(smem + s2::kOffMeta + s2::BM * 4);
+        float2* queue = reinterpret_cast<float2*>(smem + s2::kOffQueue);
+        // positions and norms of a block's slots, thread t < 256 <-> slot t, one block ahead
+        int mp_next = INT_MAX;
+        float mn_next = 0.f;
+        auto fetch_meta = [&](int blk) {
+            const int sl = blk * s2::BM + tid;
+            const bool ok = tid < s2::BM && sl < count;
+            mp_next = ok ? rp[sl] : INT_MAX;
+            mn_next = ok ? rn[sl] : 0.f;
+        };
+        fetch_meta(blk0);
+        float thr[2] = {FLT_MAX, FLT_MAX};
+
+        f32x4 acc[8][2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = zero4();
+
+        auto load = [&](SFrag& f, const char* sa, const char* sb, int ks) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) f.b[j] = Op16<s2::BN>::template frag<bf16_t>(sb, 2 * wt + j, ks);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f.a[i] = Op8<s2::BM>::frag_bf16(sa, 8 * ws + i, ks);
+        };
+        auto mma = [&](const SFrag& f, f32x4(&c)[8][2]) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) c[i][j] = Mma<bf16_t>::step(c[i][j], f.a[i], f.b[j]);
+        };
+        // lane's slots in a block: 128 ws + 16 i + 4 (lane / 16) + e
+        const int lb = 128 * ws + 4 * (lane >> 4);
+        auto fold = [&](int bi, f32x4(&a)[8][2], bool last) {
+            const int blk = blk0 + bi;
+            // publish this block's slot metadata, fetch the next block's
+            if (tid < s2::BM) {
+                m_pos[tid] = mp_next;
+                m_nrm[tid] = mn_next;
+            }
+            if (blk + 1 < blk1) fetch_meta(blk + 1);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            wait_lgkm0();
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            const int base = blk * s2::BM + lb;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (bi == 0) {
+                    // first block of the chunk: sort the lane's candidates in groups of
+                    // 8 (two slot rows of 4) and merge each group into the list
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float gs[8];
+                        int gi[8];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int i = 2 * g + h;
+                            const int4 p4 = *reinterpret_cast<const int4*>(m_pos + lb + 16 * i);
+                            const float4 n4 = *reinterpret_cast<const float4*>(m_nrm + lb + 16 * i);
+                            const int pe[4] = {p4.x, p4.y, p4.z, p4.w};
+                            const float ne[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const bool ok = pe[e] < tokpos_l[j];
+                                gs[4 * h + e] = ok ? fmaf(-2.f, a[i][j][e], ne[e]) : FLT_MAX;
+                                gi[4 * h + e] = ok ? base + 16 * i + e : -1;
+                            }
+                        }
+                        sort8(gs, gi);
+                        if (g == 0) {
+#pragma unroll
+                            for (int q = 0; q < kTop; ++q) {
+                                ls[j][q] = gs[q];
+                                li[j][q] = gi[q];
+                            }
+                        } else {
+                            merge8(ls[j], li[j], gs, gi);
+                        }
+                    }
+                } else {
+                    // later blocks: queue the candidates below the token's bound, then
+                    // insert them (the wavefront loops only over the longest queue);
+                    // two rounds of 16 candidates keep the queue at 16 entries
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        int cnt = 0;
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii) {
+                            const int i = 4 * half + ii;
+                            const int4 p4 = *reinterpret_cast<const int4*>(m_pos + lb + 16 * i);
+                            const float4 n4 = *reinterpret_cast<const float4*>(m_nrm + lb + 16 * i);
+                            const int pe[4] = {p4.x, p4.y, p4.z, p4.w};
+                            const float ne[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float sc = pe[e] < tokpos_l[j] ? fmaf(-2.f, a[i][j][e], ne[e]) : FLT_MAX;
+                                if (sc < thr[j]) {
+                                    queue[cnt * NT + tid] = make_float2(sc, __int_as_float(base + 16 * i + e));
+                                    ++cnt;
+                                }
+                            }
+                        }
+                        for (int r = 0; __any(r < cnt); ++r) {
+                            if (r < cnt) {
+                                const float2 v = queue[r * NT + tid];
+                                top_insert(ls[j], li[j], v.x, __float_as_int(v.y));
+                            }
+                        }
+                    }
+                }
+                // the token's 8th best is at most the smallest 8th best of the lanes
+                // holding it (lanes l, l ^ 16, l ^ 32, l ^ 48)
+                float t = ls[j][kTop - 1];
+                t = fminf(t, __shfl_xor(t, 16, 64));
+                t = fminf(t, __shfl_xor(t, 32, 64));
+                thr[j] = t;
+            }
+            if (!last) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) a[i][jj] = zero4();
+            }
+        };
+        ring_mainloop_lrp<s2::NST, SFrag>(pa, pb, (blk1 - blk0) * nk, nk, smem, load, mma, acc, fold);
+    }
+
+    // merge the 8 sorted lists of every token (2 slot halves x 4 lane groups)
+    __syncthreads();
+    float* mS = reinterpret_cast<float*>(smem);
+    int* mI = reinterpret_cast<int*>(mS + kTok * 8 * kTop);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int tk = 32 * wt + 16 * j + (lane & 15);
+        const int src = ws * 4 + (lane >> 4);
+#pragma unroll
+        for (int q = 0; q < kTop; ++q) {
+            mS[(src * kTop + q) * kTok + tk] = ls[j][q];
+            mI[(src * kTop + q) * kTok + tk] = li[j][q];
+        }
+    }
+    __syncthreads();
+    if (tid < kTok && t0 + tid < n) {
+        float bs[kTop], cs[kTop];
+        int bi[kTop], ci[kTop];
+#pragma unroll
+        for (int q = 0; q < kTop; ++q) {
+            bs[q] = mS[q * kTok + tid];
+            bi[q] = mI[q * kTok + tid];
+        }
+#pragma unroll
+        for (int src = 1; src < 8; ++src) {
+#pragma unroll
+            for (int q = 0; q < kTop; ++q) {
+                cs[q] = mS[(src * kTop + q) * kTok + tid];
+                ci[q] = mI[(src * kTop + q) * kTok + tid];
+            }
+            merge8(bs, bi, cs, ci);
         }
         const size_t o = (((size_t)b * n + t0 + tid) * nsplit + split) * kTop;
 #pragma unroll
@@ -463,10 +830,27 @@ static hipError_t search_impl(const Shape& s, const CacheView& c, const EncodePl
     return hipGetLastError();
 }
 
+static hipError_t search_ring_impl(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv,
+                                   int kv_len, const int* rows, const int* pos, int n, void* ws, hipStream_t st) {
+    const size_t smem = s2::bytes;
+    auto kern = search_ring_kernel<bf16_t>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    char* w = static_cast<char*>(ws);
+    const int ntiles = (n + kTok - 1) / kTok;
+    const int per = ((ntiles + 7) / 8) * p.nsplit;  // blocks per XCD
+    hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(s2::kThreads), smem, st, static_cast<const bf16_t*>(kv), kv_len,
+                       rows, pos, n, static_cast<const fp8_t*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count,
+                       s.W2, c.cap_ref, p.chunk_slots, p.nsplit, ntiles, per,
+                       reinterpret_cast<float*>(w + p.off_part_score), reinterpret_cast<int*>(w + p.off_part_slot));
+    return hipGetLastError();
+}
+
 hipError_t launch_search(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
                          const int* rows, const int* pos, int n, void* ws, hipStream_t st) {
     if (s.f32) return search_impl<float, float, float>(s, c, p, kv, kv_len, rows, pos, n, ws, st);
-    return search_impl<bf16_t, bf16_t, fp8_t>(s, c, p, kv, kv_len, rows, pos, n, ws, st);
+    return search_ring_impl(s, c, p, kv, kv_len, rows, pos, n, ws, st);
 }
 
 template <typename KvT, typename RefT>
