@@ -22,6 +22,7 @@
 #include "rkv_device.h"
 #include "rkv_gemm.h"
 #include "rkv_internal.h"
+#include "rkv_pipe.h"
 
 namespace rkv {
 
@@ -159,6 +160,124 @@ __global__ __launch_bounds__(kGemmThreads) void swiglu_kernel(const T* __restric
     }
 }
 
+// bf16 formats: the same GEMM on the direct-to-LDS ring (see rkv_pipe.h).
+namespace g1r {
+constexpr int BM = 256, BN = 128, NST = 3;
+constexpr size_t kRing = (size_t)NST * (BM + BN) * kStageK * 2;
+constexpr size_t kEpi = (size_t)(BM / 2) * G1<bf16_t>::kHP * sizeof(float);
+constexpr size_t bytes = kRing > kEpi ? kRing : kEpi;
+static_assert(bytes <= 160 * 1024, "LDS budget");
+}  // namespace g1r
+
+struct G1Frag {
+    bf16x8 a[8];
+    bf16x8 b[4];
+};
+
+__global__ __launch_bounds__(kGemmThreads) void swiglu_ring_kernel(const bf16_t* __restrict__ kv, int kv_len,
+                                                                   const int* __restrict__ rows, int n,
+                                                                   const bf16_t* __restrict__ xbar,
+                                                                   const bf16_t* __restrict__ w1,
+                                                                   const bf16_t* __restrict__ w2, int W2, int d_ff,
+                                                                   bf16_t* __restrict__ dh, int MT, int NT, int per) {
+    typedef G1<bf16_t> C;
+    extern __shared__ __align__(16) unsigned char smem_u8[];
+    char* smem = reinterpret_cast<char*>(smem_u8);
+    const int tile = xcd_tile(blockIdx.x, per);
+    if (tile >= MT * NT) return;
+    const int mt = tile / NT, nt = tile - mt * NT;
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tok0 = mt * (g1r::BM / 2);
+    const int j0 = nt * 64;
+
+    // A rows alternate kv_i / mean_i of one token. Rows past n repeat the last token;
+    // a kv row index outside [0, kv_len) reads the token's mean row instead (dH = 0;
+    // the selection kernel has flagged the token).
+    Op16<g1r::BM> la;
+    la.init([&](int r) {
+        const int t = min(tok0 + (r >> 1), n - 1);
+        const bf16_t* mrow = xbar + ((size_t)b * n + t) * W2;
+        if (r & 1) return mrow;
+        const int kr = rows[(size_t)b * n + t];
+        return (kr >= 0 && kr < kv_len) ? kv + ((size_t)b * kv_len + kr) * W2 : mrow;
+    });
+    // B tile rows: [c1 0..31, c2 0..31, c1 32..63, c2 32..63] so that wave wn's 64 rows
+    // are contiguous: its tiles j = 0, 1 are W_c1 and j = 2, 3 are W_c2
+    Op16<g1r::BN> lb;
+    lb.init([&](int r) {
+        const int half = r >> 6, q = r & 63;
+        return (q < 32) ? w1 + (size_t)(j0 + 32 * half + q) * W2 : w2 + (size_t)(j0 + 32 * half + q - 32) * W2;
+    });
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+    auto load = [&](G1Frag& f, const char* sa, const char* sb, int ks) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f.b[j] = Op16<g1r::BN>::template frag<bf16_t>(sb, 4 * wn + j, ks);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f.a[i] = Op16<g1r::BM>::template frag<bf16_t>(sa, 8 * wm + i, ks);
+    };
+    auto mma = [&](const G1Frag& f, f32x4(&c)[8][4]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[i][j] = Mma<bf16_t>::step(c[i][j], f.a[i], f.b[j]);
+    };
+    const int ns = W2 / kStageK;
+    ring_mainloop_lrp<g1r::NST, G1Frag>(la, lb, ns, ns, smem, load, mma, acc,
+                                        [](int, f32x4(&)[8][4], bool) {});
+
+    // epilogue: rows 4g+0/4g+1 of a tile are kv/mean of one token, 4g+2/4g+3 of the next
+    __syncthreads();
+    float* sH = reinterpret_cast<float*>(smem);  // [BM/2 tokens][kHP]
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int tl = 64 * wm + 8 * i + 2 * (lane >> 4);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const f32x4 a = acc[i][c];
+            const f32x4 g = acc[i][c + 2];
+            const float h0 = silu(a[0]) * g[0];
+            const float h1 = silu(a[1]) * g[1];
+            const float h2 = silu(a[2]) * g[2];
+            const float h3 = silu(a[3]) * g[3];
+            const int cl = 32 * wn + 16 * c + (lane & 15);
+            sH[tl * C::kHP + cl] = h0 - h1;
+            sH[(tl + 1) * C::kHP + cl] = h2 - h3;
+        }
+    }
+    __syncthreads();
+    // coalesced store: each job = 8 consecutive columns of one token, split into the
+    // three bf16 planes hi + mid + lo
+    constexpr int kJobs = (g1r::BM / 2) * 8;
+    for (int jb = tid; jb < kJobs; jb += kGemmThreads) {
+        const int tl = jb >> 3, ch = jb & 7;
+        const int t = tok0 + tl;
+        if (t >= n) continue;
+        float x[8], r1[8], r2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sH[tl * C::kHP + 8 * ch + e];
+        bf16_t* dst = dh + ((size_t)b * n + t) * 3 * d_ff + j0 + 8 * ch;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float hi = (float)(bf16_t)x[e];
+            r1[e] = x[e] - hi;
+            const float mi = (float)(bf16_t)r1[e];
+            r2[e] = r1[e] - mi;
+            x[e] = hi;
+            r1[e] = mi;
+        }
+        lds_store8<bf16_t>(dst, x);
+        lds_store8<bf16_t>(dst + d_ff, r1);
+        lds_store8<bf16_t>(dst + 2 * d_ff, r2);
+    }
+}
+
 // ---------------------------------------------------------------- GEMM 2 + quantizer
 
 template <typename T>
@@ -215,45 +334,17 @@ __device__ inline float round_scalar<float>(float v) { return v; }
 template <>
 __device__ inline float round_scalar<f16_t>(float v) { return (float)(f16_t)v; }
 
-template <typename T, typename ScT>
-__global__ __launch_bounds__(kGemmThreads) void latent_quant_kernel(const T* __restrict__ dh, int n,
-                                                                    const T* __restrict__ w3, int d_ff, int d_c,
-                                                                    int bits, const int* __restrict__ pos,
-                                                                    int cap_tok, uint8_t* __restrict__ codes,
-                                                                    size_t code_bytes, ScT* __restrict__ scale,
-                                                                    ScT* __restrict__ zmin, int MT, int NT, int per) {
-    typedef G2<T> C;
-    extern __shared__ __align__(16) unsigned char smem[];
-    T* lds = reinterpret_cast<T*>(smem);
-    const int tile = xcd_tile(blockIdx.x, per);
-    if (tile >= MT * NT) return;
-    const int mt = tile / NT, nt = tile - mt * NT;
-    const int b = blockIdx.y;
+// Group quantizer epilogue shared by the GEMM 2 kernels. The lane holds
+// z[token WM wm + 16 i + 4 (lane/16) + e][col WN wn + 16 j + lane%16] in acc[i][j][e];
+// each group of 32 columns is reduced over the 16 lanes that hold it, and the codes
+// are packed through LDS into coalesced 16-byte record writes.
+template <class C, typename ScT>
+__device__ inline void quant_epilogue(f32x4 (&acc)[C::WM / 16][C::WN / 16], unsigned char* smem, int t0, int c0, int b,
+                                      int n, int d_c, int bits, const int* __restrict__ pos, int cap_tok,
+                                      uint8_t* __restrict__ codes, size_t code_bytes, ScT* __restrict__ scale,
+                                      ScT* __restrict__ zmin) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int t0 = mt * C::BM;
-    const int c0 = nt * C::BN;
-    const int Kp = C::NS * d_ff;
-
-    G2LoadA<T> la;
-    {
-        const int r = RowTile<T, T, 128>::srow(0);
-        la.row[0] = (t0 + r < n) ? dh + ((size_t)b * n + t0 + r) * Kp : nullptr;
-    }
-    G2LoadB<T, C::BN> lb;
-    lb.d_ff = d_ff;
-#pragma unroll
-    for (int u = 0; u < G2LoadB<T, C::BN>::kUnits; ++u) {
-        const int r = (tid >> 1) + 128 * u;
-        lb.row[u] = (r < C::BN && c0 + r < d_c) ? w3 + (size_t)(c0 + r) * d_ff : nullptr;
-    }
-
-    f32x4 acc[C::WM / 16][C::WN / 16];
-    // A' rows are [hi | mid | lo] (K' = NS d_ff); stage s of A' pairs with W_c3 stage s mod (d_ff / kKC)
-    mainloop<T, C::BM, C::BN, C::WM, C::WN>(la, lb, Kp / kKC, Kp / kKC, lds, C::WM * wm, C::WN * wn, acc,
-                                            NoBlockHook{});
-
-    // epilogue: lane holds z[token WM wm + 16 i + 4 (lane/16) + e][col WN wn + 16 j + lane%16]
     uint8_t* sQ = smem;                                               // [BM][kQP] bytes
     float* sS = reinterpret_cast<float*>(smem + (size_t)C::BM * C::kQP);  // [BM][BN/32][2]
     constexpr int GT = C::BN / 32;  // groups per tile row
@@ -351,6 +442,129 @@ __global__ __launch_bounds__(kGemmThreads) void latent_quant_kernel(const T* __r
     }
 }
 
+template <typename T, typename ScT>
+__global__ __launch_bounds__(kGemmThreads) void latent_quant_kernel(const T* __restrict__ dh, int n,
+                                                                    const T* __restrict__ w3, int d_ff, int d_c,
+                                                                    int bits, const int* __restrict__ pos,
+                                                                    int cap_tok, uint8_t* __restrict__ codes,
+                                                                    size_t code_bytes, ScT* __restrict__ scale,
+                                                                    ScT* __restrict__ zmin, int MT, int NT, int per) {
+    typedef G2<T> C;
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* lds = reinterpret_cast<T*>(smem);
+    const int tile = xcd_tile(blockIdx.x, per);
+    if (tile >= MT * NT) return;
+    const int mt = tile / NT, nt = tile - mt * NT;
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int t0 = mt * C::BM;
+    const int c0 = nt * C::BN;
+    const int Kp = C::NS * d_ff;
+
+    G2LoadA<T> la;
+    {
+        const int r = RowTile<T, T, 128>::srow(0);
+        la.row[0] = (t0 + r < n) ? dh + ((size_t)b * n + t0 + r) * Kp : nullptr;
+    }
+    G2LoadB<T, C::BN> lb;
+    lb.d_ff = d_ff;
+#pragma unroll
+    for (int u = 0; u < G2LoadB<T, C::BN>::kUnits; ++u) {
+        const int r = (tid >> 1) + 128 * u;
+        lb.row[u] = (r < C::BN && c0 + r < d_c) ? w3 + (size_t)(c0 + r) * d_ff : nullptr;
+    }
+
+    f32x4 acc[C::WM / 16][C::WN / 16];
+    // A' rows are [hi | mid | lo] (K' = NS d_ff); stage s of A' pairs with W_c3 stage s mod (d_ff / kKC)
+    mainloop<T, C::BM, C::BN, C::WM, C::WN>(la, lb, Kp / kKC, Kp / kKC, lds, C::WM * wm, C::WN * wn, acc,
+                                            NoBlockHook{});
+
+    quant_epilogue<C, ScT>(acc, smem, t0, c0, b, n, d_c, bits, pos, cap_tok, codes, code_bytes, scale, zmin);
+}
+
+// bf16 formats: W_c3 projection + quantizer on the direct-to-LDS ring.
+namespace g2r {
+constexpr int BM = 128, BN = 128, NST = 2;
+constexpr size_t kRing = (size_t)NST * (BM + BN) * kStageK * 2;
+constexpr size_t bytes = kRing > G2<bf16_t>::kEpi ? kRing : G2<bf16_t>::kEpi;
+static_assert(bytes <= 160 * 1024, "LDS budget");
+}  // namespace g2r
+
+// W_c3 rows as the B operand: stage s reads K columns ((s mod (d_ff / 64)) * 64), so
+// the three planes of dH (K' = 3 d_ff) each meet the same W_c3.
+template <int R>
+struct WrapOp16 {
+    static constexpr int kLoads = R / 32;
+    static constexpr int kStageBytes = R * kStageK * 2;
+    const char* src[kLoads];
+    int nkm;  // stages per d_ff
+    __device__ inline void issue(int s, char* slot) const {
+        const int wave = wave_id();
+        const int kc = s % nkm;
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) dma16(src[u] + (size_t)kc * (kStageK * 2), slot + 1024 * (wave + 4 * u));
+    }
+};
+
+struct G2Frag {
+    bf16x8 a[4];
+    bf16x8 b[4];
+};
+
+__global__ __launch_bounds__(kGemmThreads) void latent_quant_ring_kernel(
+    const bf16_t* __restrict__ dh, int n, const bf16_t* __restrict__ w3, int d_ff, int d_c, int bits,
+    const int* __restrict__ pos, int cap_tok, uint8_t* __restrict__ codes, size_t code_bytes, f16_t* __restrict__ scale,
+    f16_t* __restrict__ zmin, int MT, int NT, int per) {
+    typedef G2<bf16_t> C;
+    extern __shared__ __align__(16) unsigned char smem_u8[];
+    char* smem = reinterpret_cast<char*>(smem_u8);
+    const int tile = xcd_tile(blockIdx.x, per);
+    if (tile >= MT * NT) return;
+    const int mt = tile / NT, nt = tile - mt * NT;
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int t0 = mt * g2r::BM;
+    const int c0 = nt * g2r::BN;
+    const int Kp = 3 * d_ff;
+
+    // rows past n / d_c repeat the last valid row; their results are not stored
+    Op16<g2r::BM> la;
+    la.init([&](int r) { return dh + ((size_t)b * n + min(t0 + r, n - 1)) * Kp; });
+    WrapOp16<g2r::BN> lb;
+    lb.nkm = d_ff / kStageK;
+#pragma unroll
+    for (int u = 0; u < WrapOp16<g2r::BN>::kLoads; ++u) {
+        const int blk = wave + 4 * u;
+        const int r = 16 * (blk >> 1) + (lane >> 2);
+        lb.src[u] = reinterpret_cast<const char*>(w3 + (size_t)min(c0 + r, d_c - 1) * d_ff) + 64 * (blk & 1) +
+                    16 * swz(lane >> 2, lane & 3);
+    }
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+    auto load = [&](G2Frag& f, const char* sa, const char* sb, int ks) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f.b[j] = Op16<g2r::BN>::template frag<bf16_t>(sb, 4 * wn + j, ks);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f.a[i] = Op16<g2r::BM>::template frag<bf16_t>(sa, 4 * wm + i, ks);
+    };
+    auto mma = [&](const G2Frag& f, f32x4(&c)[4][4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[i][j] = Mma<bf16_t>::step(c[i][j], f.a[i], f.b[j]);
+    };
+    const int ns = Kp / kStageK;
+    ring_mainloop_lrp<g2r::NST, G2Frag>(la, lb, ns, ns, smem, load, mma, acc, [](int, f32x4(&)[4][4], bool) {});
+    __syncthreads();
+    quant_epilogue<C, f16_t>(acc, smem_u8, t0, c0, b, n, d_c, bits, pos, cap_tok, codes, code_bytes, scale, zmin);
+}
+
 }  // namespace
 
 template <typename T>
@@ -372,10 +586,29 @@ static hipError_t swiglu_impl(const Shape& s, const CacheView& c, const EncodePl
     return hipGetLastError();
 }
 
+static hipError_t swiglu_ring_impl(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv,
+                                   int kv_len, const int* rows, int n, const void* w1, const void* w2, void* ws,
+                                   hipStream_t st) {
+    const size_t smem = g1r::bytes;
+    auto kern = swiglu_ring_kernel;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    char* w = static_cast<char*>(ws);
+    const int MT = (2 * n + g1r::BM - 1) / g1r::BM;
+    const int NT = s.d_ff / 64;
+    const int per = xcd_per(MT * NT);
+    hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(kGemmThreads), smem, st, static_cast<const bf16_t*>(kv), kv_len,
+                       rows, n, reinterpret_cast<const bf16_t*>(w + p.off_xbar), static_cast<const bf16_t*>(w1),
+                       static_cast<const bf16_t*>(w2), s.W2, s.d_ff, reinterpret_cast<bf16_t*>(w + p.off_dh), MT, NT,
+                       per);
+    return hipGetLastError();
+}
+
 hipError_t launch_swiglu(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
                          const int* rows, int n, const void* w1, const void* w2, void* ws, hipStream_t st) {
     if (s.f32) return swiglu_impl<float>(s, c, p, kv, kv_len, rows, n, w1, w2, ws, st);
-    return swiglu_impl<bf16_t>(s, c, p, kv, kv_len, rows, n, w1, w2, ws, st);
+    return swiglu_ring_impl(s, c, p, kv, kv_len, rows, n, w1, w2, ws, st);
 }
 
 template <typename T, typename ScT>
@@ -398,10 +631,28 @@ static hipError_t latent_impl(const Shape& s, const CacheView& c, const EncodePl
     return hipGetLastError();
 }
 
+static hipError_t latent_ring_impl(const Shape& s, const CacheView& c, const EncodePlan& p, const int* pos, int n,
+                                   const void* w3, void* ws, hipStream_t st) {
+    const size_t smem = g2r::bytes;
+    auto kern = latent_quant_ring_kernel;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    char* w = static_cast<char*>(ws);
+    const int MT = (n + g2r::BM - 1) / g2r::BM;
+    const int NT = (s.d_c + g2r::BN - 1) / g2r::BN;
+    const int per = xcd_per(MT * NT);
+    hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(kGemmThreads), smem, st,
+                       reinterpret_cast<const bf16_t*>(w + p.off_dh), n, static_cast<const bf16_t*>(w3), s.d_ff, s.d_c,
+                       s.bits, pos, c.cap_tok, c.codes, c.code_bytes, static_cast<f16_t*>(c.scale),
+                       static_cast<f16_t*>(c.zmin), MT, NT, per);
+    return hipGetLastError();
+}
+
 hipError_t launch_latent_quant(const Shape& s, const CacheView& c, const EncodePlan& p, const int* pos, int n,
                                const void* w3, void* ws, hipStream_t st) {
     if (s.f32) return latent_impl<float, float>(s, c, p, pos, n, w3, ws, st);
-    return latent_impl<bf16_t, f16_t>(s, c, p, pos, n, w3, ws, st);
+    return latent_ring_impl(s, c, p, pos, n, w3, ws, st);
 }
 
 }  // namespace rkv
