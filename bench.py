@@ -39,10 +39,10 @@ METRIC = "tokens/s encoded and decoded at Llama-3.1-8B KV shape; % of MFMA/HBM r
 PHASES = ("append", "search", "select", "compress", "quantize", "decode")
 KERNEL_NAMES = {
     "append": "append_ref_kernel",
-    "search": "search_kernel",
+    "search": "search_ring_kernel",
     "select": "select_kernel",
-    "compress": "swiglu_kernel",
-    "quantize": "latent_quant_kernel",
+    "compress": "swiglu_ring_kernel",
+    "quantize": "latent_quant_ring_kernel",
     "decode": "decode_kernel",
 }
 
