@@ -113,9 +113,15 @@ __device__ inline void load_meta(TokMeta<ScT>& M, int p, int b, const int* self_
             M.zm[u] = ok ? ld_scalar<ScT>(zmin + ro * G + g0 + u) : 0.f;
         }
     }
-    if (ss >= 0) {  // a reference token restores its stored row
+    if (ss >= 0) {  // a reference token restores its stored row (no latent term)
         M.nref = 1;
         M.ref[0] = min(ss, cap_ref - 1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            M.q[u] = make_uint4(0, 0, 0, 0);
+            M.sc[u] = 0.f;
+            M.zm[u] = 0.f;
+        }
         return;
     }
     M.enc = 1;
@@ -161,16 +167,15 @@ __device__ inline void issue_gather(Gather<RefT>& G, const TokMeta<ScT>& M, cons
 }
 
 // 8 consecutive latent values (quarter-relative offset 8 ks) of a token as an MFMA fragment.
-template <typename T, typename ScT>
-__device__ inline typename Mma<T>::frag latent_frag(const TokMeta<ScT>& M, int ks, int bits, const uint8_t* rec16) {
+template <typename T, typename ScT, int BITS>
+__device__ inline typename Mma<T>::frag latent_frag(const TokMeta<ScT>& M, int ks, int bits_rt, const uint8_t* rec16) {
+    const int bits = BITS ? BITS : bits_rt;  // compile-time for the bf16 formats
     typename Mma<T>::frag f;
-    if (!M.enc) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = (T)0.f;
-        return f;
-    }
+    // tokens without a record (references, invalid positions) carry zero codes, step and
+    // minimum, so the quantized path yields zeros without a branch
     if (bits == 16) {
-        const uint4 w = *reinterpret_cast<const uint4*>(rec16 + 16 * ks);
+        uint4 w = *reinterpret_cast<const uint4*>(rec16 + 16 * ks);
+        if (!M.enc) w = make_uint4(0, 0, 0, 0);
         const f16_t* h = reinterpret_cast<const f16_t*>(&w);
 #pragma unroll
         for (int i = 0; i < 8; ++i) f[i] = (T)h[i];
@@ -245,8 +250,9 @@ __device__ inline void finish_tokens(const TokMeta<ScT>& M, const Gather<RefT>& 
     constexpr int half = D / 2, pair_tiles = half / 16, tpd = D / 16;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, mrow = lane & 15;
-    // reference mean: fp32 sum in ascending slot order, one IEEE division
+    // reference mean: fp32 sum in ascending slot order, one correctly rounded division
     const float kf = (float)M.nref;
+    const float rk = __fdiv_rn(1.0f, kf > 0.f ? kf : 1.0f);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int c = col0 + 16 * i + 4 * g;
@@ -265,8 +271,13 @@ __device__ inline void finish_tokens(const TokMeta<ScT>& M, const Gather<RefT>& 
             }
         }
         if (M.nref > 1) {
-            s.x = __fdiv_rn(s.x, kf); s.y = __fdiv_rn(s.y, kf);
-            s.z = __fdiv_rn(s.z, kf); s.w = __fdiv_rn(s.w, kf);
+            if constexpr (std::is_same<RefT, fp8_t>::value) {
+                s.x = div_small(s.x, kf, rk); s.y = div_small(s.y, kf, rk);
+                s.z = div_small(s.z, kf, rk); s.w = div_small(s.w, kf, rk);
+            } else {  // fp32 references: general sums, IEEE division
+                s.x = __fdiv_rn(s.x, kf); s.y = __fdiv_rn(s.y, kf);
+                s.z = __fdiv_rn(s.z, kf); s.w = __fdiv_rn(s.w, kf);
+            }
         }
         acc[i][0] += s.x;
         acc[i][1] += s.y;
@@ -334,7 +345,7 @@ __device__ inline void finish_tokens(const TokMeta<ScT>& M, const Gather<RefT>& 
 // grid: (W2 / 128 column slices, token ranges, batch). NKS = d_c / 32 K-steps (each lane
 // group covers d_c / 4 latent coordinates, 8 per step); D = head dimension. Both are
 // compile-time so every register array is indexed statically.
-template <typename T, typename RefT, typename ScT, typename WT, typename OutT, int NKS, int D>
+template <typename T, typename RefT, typename ScT, typename WT, typename OutT, int NKS, int D, int BITS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     const int* __restrict__ idx, int m, int tok_per_wg, const RefT* __restrict__ ref_vals,
     const int* __restrict__ self_slot, const int* __restrict__ ref_idx, const uint8_t* __restrict__ codes,
@@ -401,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     TokMeta<ScT> cur0, cur1, nxt0, nxt1;
     auto meta = [&](TokMeta<ScT>& M, int p) {
         load_meta<ScT>(M, p, b, self_slot, ref_idx, codes, code_bytes, scale, zmin, top_k, cap_ref, cap_tok, d_c,
-                       bits, g);
+                       BITS ? BITS : bits, g);
     };
     meta(cur0, load_pos(idx, tp + mrow, t_end, m, b, cap_tok, err, flag));
     meta(cur1, load_pos(idx, tp + 16 + mrow, t_end, m, b, cap_tok, err, flag));
@@ -430,8 +441,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            const typename Mma<T>::frag f0 = latent_frag<T, ScT>(cur0, ks, bits, rec0);
-            const typename Mma<T>::frag f1 = latent_frag<T, ScT>(cur1, ks, bits, rec1);
+            const typename Mma<T>::frag f0 = latent_frag<T, ScT, BITS>(cur0, ks, bits, rec0);
+            const typename Mma<T>::frag f1 = latent_frag<T, ScT, BITS>(cur1, ks, bits, rec1);
             const int kof = g * quarter + 8 * ks;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -449,11 +460,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 
 }  // namespace
 
-template <typename T, typename RefT, typename ScT, typename WT, typename OutT, int NKS, int D>
+template <typename T, typename RefT, typename ScT, typename WT, typename OutT, int NKS, int D, int BITS>
 static hipError_t decode_impl(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
                               hipStream_t st) {
     const size_t smem = DecSmem<T, OutT>::bytes(s.d_c);
-    auto kern = decode_kernel<T, RefT, ScT, WT, OutT, NKS, D>;
+    auto kern = decode_kernel<T, RefT, ScT, WT, OutT, NKS, D, BITS>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
@@ -472,24 +483,37 @@ static hipError_t decode_impl(const Shape& s, const CacheView& c, const int* idx
     return hipGetLastError();
 }
 
-template <typename T, typename RefT, typename ScT, typename WT, typename OutT, int D>
+template <typename T, typename RefT, typename ScT, typename WT, typename OutT, int D, int BITS>
 static hipError_t decode_dc(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
                             hipStream_t st) {
     switch (s.d_c / 32) {
-        case 2: return decode_impl<T, RefT, ScT, WT, OutT, 2, D>(s, c, idx, m, wd, out, st);
-        case 4: return decode_impl<T, RefT, ScT, WT, OutT, 4, D>(s, c, idx, m, wd, out, st);
-        case 8: return decode_impl<T, RefT, ScT, WT, OutT, 8, D>(s, c, idx, m, wd, out, st);
-        case 12: return decode_impl<T, RefT, ScT, WT, OutT, 12, D>(s, c, idx, m, wd, out, st);
-        case 16: return decode_impl<T, RefT, ScT, WT, OutT, 16, D>(s, c, idx, m, wd, out, st);
+        case 2: return decode_impl<T, RefT, ScT, WT, OutT, 2, D, BITS>(s, c, idx, m, wd, out, st);
+        case 4: return decode_impl<T, RefT, ScT, WT, OutT, 4, D, BITS>(s, c, idx, m, wd, out, st);
+        case 8: return decode_impl<T, RefT, ScT, WT, OutT, 8, D, BITS>(s, c, idx, m, wd, out, st);
+        case 12: return decode_impl<T, RefT, ScT, WT, OutT, 12, D, BITS>(s, c, idx, m, wd, out, st);
+        case 16: return decode_impl<T, RefT, ScT, WT, OutT, 16, D, BITS>(s, c, idx, m, wd, out, st);
         default: return hipErrorInvalidValue;
+    }
+}
+
+// bf16 formats: the code width is a compile-time parameter; fp32 formats read it at run time
+template <typename T, typename RefT, typename ScT, typename WT, typename OutT, int D>
+static hipError_t decode_bits(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
+                              hipStream_t st) {
+    if constexpr (std::is_same<T, float>::value) {
+        return decode_dc<T, RefT, ScT, WT, OutT, D, 0>(s, c, idx, m, wd, out, st);
+    } else {
+        if (s.bits == 4) return decode_dc<T, RefT, ScT, WT, OutT, D, 4>(s, c, idx, m, wd, out, st);
+        if (s.bits == 2) return decode_dc<T, RefT, ScT, WT, OutT, D, 2>(s, c, idx, m, wd, out, st);
+        return decode_dc<T, RefT, ScT, WT, OutT, D, 16>(s, c, idx, m, wd, out, st);
     }
 }
 
 template <typename T, typename RefT, typename ScT, typename WT, typename OutT>
 static hipError_t decode_d(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
                            hipStream_t st) {
-    if (s.D == 64) return decode_dc<T, RefT, ScT, WT, OutT, 64>(s, c, idx, m, wd, out, st);
-    if (s.D == 128) return decode_dc<T, RefT, ScT, WT, OutT, 128>(s, c, idx, m, wd, out, st);
+    if (s.D == 64) return decode_bits<T, RefT, ScT, WT, OutT, 64>(s, c, idx, m, wd, out, st);
+    if (s.D == 128) return decode_bits<T, RefT, ScT, WT, OutT, 128>(s, c, idx, m, wd, out, st);
     return hipErrorInvalidValue;
 }
 

@@ -219,6 +219,16 @@ __device__ inline float seg16_max(float v) {
     return v;
 }
 
+// s / k correctly rounded for the reference-mean sums: s is a sum of at most 8 FP8
+// e4m3fn values (a multiple of 2^-9, |s| <= 8 * 448) and k = 1..8. With rk = RN(1/k),
+// one residual correction q + (s - q k) rk gives the IEEE quotient for every such s and
+// k (checked exhaustively against the correctly rounded division, all 2^22 sums x 8 k).
+__device__ inline float div_small(float s, float k, float rk) {
+    const float q = s * rk;
+    const float e = fmaf(-q, k, s);
+    return fmaf(e, rk, q);
+}
+
 __device__ inline float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -764,9 +764,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     }
     if (k_i == 0 && lane == 0) flag_error(err, DEVERR_EMPTY_POOL);
 
-    // reference mean: fp32 sum in ascending slot order, one IEEE division, rounded to
-    // the KV dtype for the encoder
+    // reference mean: fp32 sum in ascending slot order, one correctly rounded division,
+    // rounded to the KV dtype for the encoder
     const float kf = (float)k_i;
+    const float rk = __fdiv_rn(1.0f, k_i > 0 ? kf : 1.0f);
     for (int c = 4 * lane; c < W2; c += 256) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -776,9 +777,14 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
                 acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
             }
         }
-        if (k_i > 0) {
-            acc.x = __fdiv_rn(acc.x, kf); acc.y = __fdiv_rn(acc.y, kf);
-            acc.z = __fdiv_rn(acc.z, kf); acc.w = __fdiv_rn(acc.w, kf);
+        if (k_i > 1) {
+            if constexpr (std::is_same<RefT, fp8_t>::value) {
+                acc.x = div_small(acc.x, kf, rk); acc.y = div_small(acc.y, kf, rk);
+                acc.z = div_small(acc.z, kf, rk); acc.w = div_small(acc.w, kf, rk);
+            } else {  // fp32 references: general sums, IEEE division
+                acc.x = __fdiv_rn(acc.x, kf); acc.y = __fdiv_rn(acc.y, kf);
+                acc.z = __fdiv_rn(acc.z, kf); acc.w = __fdiv_rn(acc.w, kf);
+            }
         }
         store4<KvT>(xrow + c, acc);
     }
