@@ -107,11 +107,13 @@ struct Op8 {
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) dma16(src[u] + (size_t)s * kStageK, slot + 1024 * (wave + 4 * u));
     }
-    // bf16 fragment of row group g, K step ks: K values 32 ks + 8 (lane / 16) .. +8
-    static __device__ inline bf16x8 frag_bf16(const char* slot, int g, int ks) {
+    // raw FP8 fragment of row group g, K step ks: K values 32 ks + 8 (lane / 16) .. +8
+    static __device__ inline uint2 frag_raw(const char* slot, int g, int ks) {
         const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
-        const uint2 v = *reinterpret_cast<const uint2*>(slot + 1024 * g + 64 * r + 16 * swz(r, 2 * ks + (q >> 1)) +
-                                                        8 * (q & 1));
+        return *reinterpret_cast<const uint2*>(slot + 1024 * g + 64 * r + 16 * swz(r, 2 * ks + (q >> 1)) + 8 * (q & 1));
+    }
+    // exact widening of a raw fragment to bf16
+    static __device__ inline bf16x8 widen(uint2 v) {
         const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, false);
         const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, true);
         const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.y, 1.0f, false);

@@ -12,10 +12,10 @@
 //                    The pool and token rows stream through an LDS ring filled by
 //                    direct global->LDS loads (the K stages of consecutive pool blocks
 //                    form one pipelined sequence). After each pool block every lane
-//                    folds its scores into a sorted per-token top-8 held in registers:
-//                    the first block of a chunk through a sorting network, later
-//                    blocks through a threshold filter whose few survivors are queued
-//                    in LDS and inserted afterwards. The workgroup finally merges its
+//                    folds its scores into a sorted per-token top-8 held in registers
+//                    with a sorting network and bitonic merges on 64-bit (score, slot)
+//                    keys (no divergence, no per-candidate insertion). The workgroup
+//                    finally merges its
 //                    lanes' lists into one top-8 per token and chunk. Only pool blocks
 //                    whose first position lies below the tile's last token are read
 //                    (the pool is position-ordered); single slots are masked by
@@ -280,32 +280,46 @@ constexpr int kThreads = 512;  // 8 wavefronts: 2 slot halves x 4 token quarters
 constexpr int BM = 256;        // pool slots per block
 constexpr int BN = kTok;       // tokens per tile
 constexpr int NST = 2;         // LDS ring stages
-constexpr int kQ = 16;         // queued candidates per lane between two drains
 constexpr int kStageA = BM * kStageK;      // FP8 pool stage bytes
 constexpr int kStageB = BN * kStageK * 2;  // bf16 token stage bytes
 constexpr int kRing = NST * (kStageA + kStageB);
-constexpr int kQueue = kThreads * kQ * 8;
 constexpr int kMeta = BM * 8;              // positions + norms of one pool block
-constexpr int kMerge = kTok * 8 * kTop * 8;
-constexpr int kOffQueue = kRing;
-constexpr int kOffMeta = kOffQueue + kQueue;
+constexpr int kMerge = kTok * 8 * kTop * 8;  // 8 lists of 8 keys per token
+constexpr int kOffMeta = kRing;
 constexpr int kOffRed = kOffMeta + kMeta;
 constexpr int kMain = kOffRed + 64;
 constexpr size_t bytes = (size_t)(kMain > kMerge ? kMain : kMerge);
 static_assert(bytes <= 160 * 1024, "LDS budget");
 }  // namespace s2
 
-// compare-exchange on (score, slot) pairs in lexicographic order
-__device__ inline void cas(float& a, int& ia, float& b, int& ib) {
-    const bool sw = (b < a) || (b == a && ib < ia);
-    const float ta = sw ? b : a, tb = sw ? a : b;
-    const int tia = sw ? ib : ia, tib = sw ? ia : ib;
-    a = ta; b = tb; ia = tia; ib = tib;
+// A candidate as one 64-bit key: the score's bits mapped to an order-preserving
+// unsigned integer in the high word, the slot in the low word. Unsigned order of keys
+// is the lexicographic (score, slot) order, so a compare-exchange is one 64-bit
+// compare and four selects (no scalar mask arithmetic). Masked candidates carry
+// kNoKey (score FLT_MAX, slot -1) and sort last.
+__device__ inline uint64_t score_key(float sc, int slot) {
+    uint32_t b = __float_as_uint(sc);
+    b ^= (b & 0x80000000u) ? 0xFFFFFFFFu : 0x80000000u;
+    return ((uint64_t)b << 32) | (uint32_t)slot;
+}
+__device__ inline float key_score(uint64_t k) {
+    uint32_t b = (uint32_t)(k >> 32);
+    b ^= (b & 0x80000000u) ? 0x80000000u : 0xFFFFFFFFu;
+    return __uint_as_float(b);
+}
+__device__ inline int key_slot(uint64_t k) { return (int)(uint32_t)k; }
+constexpr uint64_t kNoKey = ((uint64_t)(0x7F7FFFFFu ^ 0x80000000u) << 32) | 0xFFFFFFFFull;
+
+__device__ inline void cas(uint64_t& a, uint64_t& b) {
+    const bool sw = b < a;
+    const uint64_t ta = sw ? b : a, tb = sw ? a : b;
+    a = ta;
+    b = tb;
 }
 
 // 19-comparator sorting network for 8 elements
-__device__ inline void sort8(float (&s)[8], int (&id)[8]) {
-#define RKV_C(x, y) cas(s[x], id[x], s[y], id[y])
+__device__ inline void sort8(uint64_t (&k)[8]) {
+#define RKV_C(x, y) cas(k[x], k[y])
     RKV_C(0, 2); RKV_C(1, 3); RKV_C(4, 6); RKV_C(5, 7);
     RKV_C(0, 4); RKV_C(1, 5); RKV_C(2, 6); RKV_C(3, 7);
     RKV_C(0, 1); RKV_C(2, 3); RKV_C(4, 5); RKV_C(6, 7);
@@ -316,16 +330,10 @@ __device__ inline void sort8(float (&s)[8], int (&id)[8]) {
 }
 
 // a <- the 8 smallest of two sorted lists a, b, sorted (bitonic merge)
-__device__ inline void merge8(float (&a)[8], int (&ia)[8], const float (&b)[8], const int (&ib)[8]) {
+__device__ inline void merge8(uint64_t (&a)[8], const uint64_t (&b)[8]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float bs = b[7 - i];
-        const int bi = ib[7 - i];
-        const bool tb = (bs < a[i]) || (bs == a[i] && bi < ia[i]);
-        a[i] = tb ? bs : a[i];
-        ia[i] = tb ? bi : ia[i];
-    }
-#define RKV_C(x, y) cas(a[x], ia[x], a[y], ia[y])
+    for (int i = 0; i < 8; ++i) a[i] = b[7 - i] < a[i] ? b[7 - i] : a[i];
+#define RKV_C(x, y) cas(a[x], a[y])
     RKV_C(0, 4); RKV_C(1, 5); RKV_C(2, 6); RKV_C(3, 7);
     RKV_C(0, 2); RKV_C(1, 3); RKV_C(4, 6); RKV_C(5, 7);
     RKV_C(0, 1); RKV_C(2, 3); RKV_C(4, 5); RKV_C(6, 7);
@@ -368,7 +376,7 @@ struct TokOp {
 };
 
 struct SFrag {
-    bf16x8 a[8];  // the wave's 8 pool row groups
+    uint2 a[8];   // the wave's 8 pool row groups (raw FP8, widened at the MFMA)
     bf16x8 b[2];  // the wave's 2 token row groups
 };
 
@@ -431,15 +439,11 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
     const int blk1 = min(nblk, blk0 + blocks_per_chunk);
     const int nk = W2 / kStageK;
 
-    float ls[2][kTop];
-    int li[2][kTop];
+    uint64_t lk[2][kTop];  // per-token sorted lists of candidate keys
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int j = 0; j < kTop; ++j) {
-            ls[q][j] = FLT_MAX;
-            li[q][j] = -1;
-        }
+        for (int j = 0; j < kTop; ++j) lk[q][j] = kNoKey;
 
     if (blk1 > blk0) {
         PoolOp pa;
@@ -462,7 +466,6 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
         }
         int* m_pos = reinterpret_cast<int*>(smem + s2::kOffMeta);
         float* m_nrm = reinterpret_cast<float*>(smem + s2::kOffMeta + s2::BM * 4);
-        float2* queue = reinterpret_cast<float2*>(smem + s2::kOffQueue);
         // positions and norms of a block's slots, thread t < 256 <-> slot t, one block ahead
         int mp_next = INT_MAX;
         float mn_next = 0.f;
@@ -473,7 +476,6 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
             mn_next = ok ? rn[sl] : 0.f;
         };
         fetch_meta(blk0);
-        float thr[2] = {FLT_MAX, FLT_MAX};
 
         f32x4 acc[8][2];
 #pragma unroll
@@ -485,13 +487,15 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
 #pragma unroll
             for (int j = 0; j < 2; ++j) f.b[j] = Op16<s2::BN>::template frag<bf16_t>(sb, 2 * wt + j, ks);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) f.a[i] = Op8<s2::BM>::frag_bf16(sa, 8 * ws + i, ks);
+            for (int i = 0; i < 8; ++i) f.a[i] = Op8<s2::BM>::frag_raw(sa, 8 * ws + i, ks);
         };
         auto mma = [&](const SFrag& f, f32x4(&c)[8][2]) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 8; ++i) {
+                const bf16x8 fa = Op8<s2::BM>::widen(f.a[i]);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) c[i][j] = Mma<bf16_t>::step(c[i][j], f.a[i], f.b[j]);
+                for (int j = 0; j < 2; ++j) c[i][j] = Mma<bf16_t>::step(c[i][j], fa, f.b[j]);
+            }
         };
         // lane's slots in a block: 128 ws + 16 i + 4 (lane / 16) + e
         const int lb = 128 * ws + 4 * (lane >> 4);
@@ -510,75 +514,35 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
             const int base = blk * s2::BM + lb;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                if (bi == 0) {
-                    // first block of the chunk: sort the lane's candidates in groups of
-                    // 8 (two slot rows of 4) and merge each group into the list
+                // sort the lane's 32 candidates of this block in groups of 8 (two slot rows
+                // of 4) and merge each group into the token's list (a bitonic merge keeps
+                // the 8 smallest): a fixed network, so the wavefront never diverges
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        float gs[8];
-                        int gi[8];
+                for (int g = 0; g < 4; ++g) {
+                    uint64_t gk[8];
 #pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            const int i = 2 * g + h;
-                            const int4 p4 = *reinterpret_cast<const int4*>(m_pos + lb + 16 * i);
-                            const float4 n4 = *reinterpret_cast<const float4*>(m_nrm + lb + 16 * i);
-                            const int pe[4] = {p4.x, p4.y, p4.z, p4.w};
-                            const float ne[4] = {n4.x, n4.y, n4.z, n4.w};
+                    for (int h = 0; h < 2; ++h) {
+                        const int i = 2 * g + h;
+                        const int4 p4 = *reinterpret_cast<const int4*>(m_pos + lb + 16 * i);
+                        const float4 n4 = *reinterpret_cast<const float4*>(m_nrm + lb + 16 * i);
+                        const int pe[4] = {p4.x, p4.y, p4.z, p4.w};
+                        const float ne[4] = {n4.x, n4.y, n4.z, n4.w};
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const bool ok = pe[e] < tokpos_l[j];
-                                gs[4 * h + e] = ok ? fmaf(-2.f, a[i][j][e], ne[e]) : FLT_MAX;
-                                gi[4 * h + e] = ok ? base + 16 * i + e : -1;
-                            }
-                        }
-                        sort8(gs, gi);
-                        if (g == 0) {
-#pragma unroll
-                            for (int q = 0; q < kTop; ++q) {
-                                ls[j][q] = gs[q];
-                                li[j][q] = gi[q];
-                            }
-                        } else {
-                            merge8(ls[j], li[j], gs, gi);
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            gk[4 * h + e] = pe[e] < tokpos_l[j] ? score_key(fmaf(-2.f, a[i][j][e], ne[e]), base + 16 * i + e)
+                                                               : kNoKey;
                     }
-                } else {
-                    // later blocks: queue the candidates below the token's bound, then
-                    // insert them (the wavefront loops only over the longest queue);
-                    // two rounds of 16 candidates keep the queue at 16 entries
+                    sort8(gk);
+                    if (bi == 0 && g == 0) {
 #pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        int cnt = 0;
-#pragma unroll
-                        for (int ii = 0; ii < 4; ++ii) {
-                            const int i = 4 * half + ii;
-                            const int4 p4 = *reinterpret_cast<const int4*>(m_pos + lb + 16 * i);
-                            const float4 n4 = *reinterpret_cast<const float4*>(m_nrm + lb + 16 * i);
-                            const int pe[4] = {p4.x, p4.y, p4.z, p4.w};
-                            const float ne[4] = {n4.x, n4.y, n4.z, n4.w};
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float sc = pe[e] < tokpos_l[j] ? fmaf(-2.f, a[i][j][e], ne[e]) : FLT_MAX;
-                                if (sc < thr[j]) {
-                                    queue[cnt * NT + tid] = make_float2(sc, __int_as_float(base + 16 * i + e));
-                                    ++cnt;
-                                }
-                            }
-                        }
-                        for (int r = 0; __any(r < cnt); ++r) {
-                            if (r < cnt) {
-                                const float2 v = queue[r * NT + tid];
-                                top_insert(ls[j], li[j], v.x, __float_as_int(v.y));
-                            }
-                        }
+                        for (int q = 0; q < kTop; ++q) lk[j][q] = gk[q];
+                    } else {
+                        merge8(lk[j], gk);
                     }
+                    // keep each group's LDS reads next to their use (hoisting all of them
+                    // ahead of the networks would exhaust the registers)
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                // the token's 8th best is at most the smallest 8th best of the lanes
-                // holding it (lanes l, l ^ 16, l ^ 32, l ^ 48)
-                float t = ls[j][kTop - 1];
-                t = fminf(t, __shfl_xor(t, 16, 64));
-                t = fminf(t, __shfl_xor(t, 32, 64));
-                thr[j] = t;
             }
             if (!last) {
 #pragma unroll
@@ -592,41 +556,30 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
 
     // merge the 8 sorted lists of every token (2 slot halves x 4 lane groups)
     __syncthreads();
-    float* mS = reinterpret_cast<float*>(smem);
-    int* mI = reinterpret_cast<int*>(mS + kTok * 8 * kTop);
+    uint64_t* mK = reinterpret_cast<uint64_t*>(smem);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int tk = 32 * wt + 16 * j + (lane & 15);
         const int src = ws * 4 + (lane >> 4);
 #pragma unroll
-        for (int q = 0; q < kTop; ++q) {
-            mS[(src * kTop + q) * kTok + tk] = ls[j][q];
-            mI[(src * kTop + q) * kTok + tk] = li[j][q];
-        }
+        for (int q = 0; q < kTop; ++q) mK[(src * kTop + q) * kTok + tk] = lk[j][q];
     }
     __syncthreads();
     if (tid < kTok && t0 + tid < n) {
-        float bs[kTop], cs[kTop];
-        int bi[kTop], ci[kTop];
+        uint64_t bk[kTop], ck[kTop];
 #pragma unroll
-        for (int q = 0; q < kTop; ++q) {
-            bs[q] = mS[q * kTok + tid];
-            bi[q] = mI[q * kTok + tid];
-        }
+        for (int q = 0; q < kTop; ++q) bk[q] = mK[q * kTok + tid];
 #pragma unroll
         for (int src = 1; src < 8; ++src) {
 #pragma unroll
-            for (int q = 0; q < kTop; ++q) {
-                cs[q] = mS[(src * kTop + q) * kTok + tid];
-                ci[q] = mI[(src * kTop + q) * kTok + tid];
-            }
-            merge8(bs, bi, cs, ci);
+            for (int q = 0; q < kTop; ++q) ck[q] = mK[(src * kTop + q) * kTok + tid];
+            merge8(bk, ck);
         }
         const size_t o = (((size_t)b * n + t0 + tid) * nsplit + split) * kTop;
 #pragma unroll
         for (int q = 0; q < kTop; ++q) {
-            part_score[o + q] = bs[q];
-            part_slot[o + q] = bi[q];
+            part_score[o + q] = key_score(bk[q]);
+            part_slot[o + q] = key_slot(bk[q]);
         }
     }
 }
