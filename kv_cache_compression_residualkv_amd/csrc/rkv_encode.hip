@@ -160,11 +160,17 @@ __global__ __launch_bounds__(kGemmThreads) void swiglu_kernel(const T* __restric
     }
 }
 
-// bf16 formats: the same GEMM on the direct-to-LDS ring (see rkv_pipe.h).
+// bf16 formats: the same GEMM on the direct-to-LDS ring (see rkv_pipe.h), with 8
+// wavefronts (two per SIMD, so one wavefront's LDS reads overlap the other's MFMAs)
+// on a 256 x 256 tile: 128 tokens (kv and mean rows) x 128 hidden columns (their
+// W_c1 and W_c2 rows). Wave w: rows 128 (w / 4) .., B rows 64 (w % 4) ...
 namespace g1r {
-constexpr int BM = 256, BN = 128, NST = 3;
+constexpr int kThreads = 512;
+constexpr int BM = 256, BN = 256, NST = 2;
+constexpr int kHid = BN / 2;  // hidden columns per tile
+constexpr int kHP = kHid + 4;  // fp32 pitch of the dH staging tile
 constexpr size_t kRing = (size_t)NST * (BM + BN) * kStageK * 2;
-constexpr size_t kEpi = (size_t)(BM / 2) * G1<bf16_t>::kHP * sizeof(float);
+constexpr size_t kEpi = (size_t)(BM / 2) * kHP * sizeof(float);
 constexpr size_t bytes = kRing > kEpi ? kRing : kEpi;
 static_assert(bytes <= 160 * 1024, "LDS budget");
 }  // namespace g1r
@@ -174,13 +180,12 @@ struct G1Frag {
     bf16x8 b[4];
 };
 
-__global__ __launch_bounds__(kGemmThreads) void swiglu_ring_kernel(const bf16_t* __restrict__ kv, int kv_len,
-                                                                   const int* __restrict__ rows, int n,
-                                                                   const bf16_t* __restrict__ xbar,
-                                                                   const bf16_t* __restrict__ w1,
-                                                                   const bf16_t* __restrict__ w2, int W2, int d_ff,
-                                                                   bf16_t* __restrict__ dh, int MT, int NT, int per) {
-    typedef G1<bf16_t> C;
+__global__ __launch_bounds__(g1r::kThreads) void swiglu_ring_kernel(const bf16_t* __restrict__ kv, int kv_len,
+                                                                    const int* __restrict__ rows, int n,
+                                                                    const bf16_t* __restrict__ xbar,
+                                                                    const bf16_t* __restrict__ w1,
+                                                                    const bf16_t* __restrict__ w2, int W2, int d_ff,
+                                                                    bf16_t* __restrict__ dh, int MT, int NT, int per) {
     extern __shared__ __align__(16) unsigned char smem_u8[];
     char* smem = reinterpret_cast<char*>(smem_u8);
     const int tile = xcd_tile(blockIdx.x, per);
@@ -188,14 +193,14 @@ __global__ __launch_bounds__(kGemmThreads) void swiglu_ring_kernel(const bf16_t*
     const int mt = tile / NT, nt = tile - mt * NT;
     const int b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int tok0 = mt * (g1r::BM / 2);
-    const int j0 = nt * 64;
+    const int j0 = nt * g1r::kHid;
 
     // A rows alternate kv_i / mean_i of one token. Rows past n repeat the last token;
     // a kv row index outside [0, kv_len) reads the token's mean row instead (dH = 0;
     // the selection kernel has flagged the token).
-    Op16<g1r::BM> la;
+    Op16<g1r::BM, 8> la;
     la.init([&](int r) {
         const int t = min(tok0 + (r >> 1), n - 1);
         const bf16_t* mrow = xbar + ((size_t)b * n + t) * W2;
@@ -203,12 +208,14 @@ __global__ __launch_bounds__(kGemmThreads) void swiglu_ring_kernel(const bf16_t*
         const int kr = rows[(size_t)b * n + t];
         return (kr >= 0 && kr < kv_len) ? kv + ((size_t)b * kv_len + kr) * W2 : mrow;
     });
-    // B tile rows: [c1 0..31, c2 0..31, c1 32..63, c2 32..63] so that wave wn's 64 rows
-    // are contiguous: its tiles j = 0, 1 are W_c1 and j = 2, 3 are W_c2
-    Op16<g1r::BN> lb;
+    // B tile rows in groups of 64: [c1 32q .. +32, c2 32q .. +32] for q = 0..3, so that
+    // wave wn's 64 rows hold matching W_c1 (tiles j = 0, 1) and W_c2 (j = 2, 3) columns;
+    // columns past d_ff repeat the last one (not stored)
+    Op16<g1r::BN, 8> lb;
     lb.init([&](int r) {
-        const int half = r >> 6, q = r & 63;
-        return (q < 32) ? w1 + (size_t)(j0 + 32 * half + q) * W2 : w2 + (size_t)(j0 + 32 * half + q - 32) * W2;
+        const int q = r >> 6, e = r & 63;
+        const int col = min(j0 + 32 * q + (e & 31), d_ff - 1);
+        return (e < 32) ? w1 + (size_t)col * W2 : w2 + (size_t)col * W2;
     });
 
     f32x4 acc[8][4];
@@ -218,9 +225,9 @@ __global__ __launch_bounds__(kGemmThreads) void swiglu_ring_kernel(const bf16_t*
         for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
     auto load = [&](G1Frag& f, const char* sa, const char* sb, int ks) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) f.b[j] = Op16<g1r::BN>::template frag<bf16_t>(sb, 4 * wn + j, ks);
+        for (int j = 0; j < 4; ++j) f.b[j] = Op16<g1r::BN, 8>::template frag<bf16_t>(sb, 4 * wn + j, ks);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f.a[i] = Op16<g1r::BM>::template frag<bf16_t>(sa, 8 * wm + i, ks);
+        for (int i = 0; i < 8; ++i) f.a[i] = Op16<g1r::BM, 8>::template frag<bf16_t>(sa, 8 * wm + i, ks);
     };
     auto mma = [&](const G1Frag& f, f32x4(&c)[8][4]) {
 #pragma unroll
@@ -247,21 +254,22 @@ __global__ __launch_bounds__(kGemmThreads) void swiglu_ring_kernel(const bf16_t*
             const float h2 = silu(a[2]) * g[2];
             const float h3 = silu(a[3]) * g[3];
             const int cl = 32 * wn + 16 * c + (lane & 15);
-            sH[tl * C::kHP + cl] = h0 - h1;
-            sH[(tl + 1) * C::kHP + cl] = h2 - h3;
+            sH[tl * g1r::kHP + cl] = h0 - h1;
+            sH[(tl + 1) * g1r::kHP + cl] = h2 - h3;
         }
     }
     __syncthreads();
     // coalesced store: each job = 8 consecutive columns of one token, split into the
     // three bf16 planes hi + mid + lo
-    constexpr int kJobs = (g1r::BM / 2) * 8;
-    for (int jb = tid; jb < kJobs; jb += kGemmThreads) {
-        const int tl = jb >> 3, ch = jb & 7;
+    constexpr int kCh = g1r::kHid / 8;
+    constexpr int kJobs = (g1r::BM / 2) * kCh;
+    for (int jb = tid; jb < kJobs; jb += g1r::kThreads) {
+        const int tl = jb / kCh, ch = jb - tl * kCh;
         const int t = tok0 + tl;
-        if (t >= n) continue;
+        if (t >= n || j0 + 8 * ch >= d_ff) continue;
         float x[8], r1[8], r2[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = sH[tl * C::kHP + 8 * ch + e];
+        for (int e = 0; e < 8; ++e) x[e] = sH[tl * g1r::kHP + 8 * ch + e];
         bf16_t* dst = dh + ((size_t)b * n + t) * 3 * d_ff + j0 + 8 * ch;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -596,9 +604,9 @@ static hipError_t swiglu_ring_impl(const Shape& s, const CacheView& c, const Enc
     if (e != hipSuccess) return e;
     char* w = static_cast<char*>(ws);
     const int MT = (2 * n + g1r::BM - 1) / g1r::BM;
-    const int NT = s.d_ff / 64;
+    const int NT = (s.d_ff + g1r::kHid - 1) / g1r::kHid;
     const int per = xcd_per(MT * NT);
-    hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(kGemmThreads), smem, st, static_cast<const bf16_t*>(kv), kv_len,
+    hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(g1r::kThreads), smem, st, static_cast<const bf16_t*>(kv), kv_len,
                        rows, n, reinterpret_cast<const bf16_t*>(w + p.off_xbar), static_cast<const bf16_t*>(w1),
                        static_cast<const bf16_t*>(w2), s.W2, s.d_ff, reinterpret_cast<bf16_t*>(w + p.off_dh), MT, NT,
                        per);

@@ -53,13 +53,14 @@ __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(th
 // position of chunk c of row r (within its group of 16) inside the row's 64 bytes
 __device__ inline int swz(int r, int c) { return c ^ (((r >> 2) & 1) | (((r >> 1) ^ (r >> 3)) & 1) << 1); }
 
-// A 16-bit operand of R rows (R a multiple of 32). Each wavefront issues R / 32 of the
-// stage's R / 8 block loads: load u of wave w fills block (w + 4 u) = 2 g + h
-// (row group g, K step h).
-template <int R>
+// A 16-bit operand of R rows (R a multiple of 8 NW) loaded by NW wavefronts. Each
+// wavefront issues R / (8 NW) of the stage's R / 8 block loads: load u of wave w fills
+// block (w + NW u) = 2 g + h (row group g, K step h).
+template <int R, int NW = 4>
 struct Op16 {
-    static constexpr int kLoads = R / 32;
+    static constexpr int kLoads = R / (8 * NW);
     static constexpr int kStageBytes = R * kStageK * 2;
+    static_assert(kLoads * 8 * NW == R, "rows per wavefront");
     const char* src[kLoads];  // per lane: its row's chunk in stage 0
     // row(r) gives the byte address of row r (any row inside the matrix; rows past
     // the valid range must still point at readable memory)
@@ -68,7 +69,7 @@ struct Op16 {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
-            const int blk = wave + 4 * u;
+            const int blk = wave + NW * u;
             const int g = blk >> 1, h = blk & 1;
             src[u] = reinterpret_cast<const char*>(row(16 * g + (lane >> 2))) + 64 * h + 16 * swz(lane >> 2, lane & 3);
         }
@@ -76,7 +77,7 @@ struct Op16 {
     __device__ inline void issue(int s, char* slot) const {
         const int wave = wave_id();
 #pragma unroll
-        for (int u = 0; u < kLoads; ++u) dma16(src[u] + (size_t)s * (kStageK * 2), slot + 1024 * (wave + 4 * u));
+        for (int u = 0; u < kLoads; ++u) dma16(src[u] + (size_t)s * (kStageK * 2), slot + 1024 * (wave + NW * u));
     }
     // fragment of row group g, K step ks
     template <typename T>
