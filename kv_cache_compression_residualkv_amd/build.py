@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "librkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["rkv_api.hip", "rkv_append.hip", "rkv_search.hip", "rkv_encode.hip", "rkv_decode.hip"]
+SOURCES = ["rkv_api.hip", "rkv_append.hip", "rkv_search.hip", "rkv_encode.hip", "rkv_decode.hip",
+           "rkv_decode_tiles.hip"]
 
 # Packed fp32 vector ops are kept out of the generated code (see the design notes).
 HIP_FLAGS = [
@@ -34,10 +35,11 @@ HIP_FLAGS = [
 # architectural VGPRs hold. With the default heuristics the backend keeps MFMA
 # accumulators in VGPRs and parks them in AGPRs around every MFMA (several
 # v_accvgpr moves per MFMA); the VGPR form with the AGPRs left free keeps the
-# accumulators in place. The decoder allocates better under the default.
+# accumulators in place. The column-slice decoder allocates better under the default.
 PER_SOURCE_FLAGS = {
     "rkv_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "rkv_encode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "rkv_decode_tiles.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

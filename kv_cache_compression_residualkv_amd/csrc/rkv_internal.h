@@ -59,4 +59,9 @@ hipError_t launch_latent_quant(const Shape& s, const CacheView& c, const EncodeP
 hipError_t launch_decode(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
                          int out_dtype, hipStream_t st);
 
+// Token-tile restore (bf16 formats with INT4 / INT2 codes).
+bool decode_tiles_supported(const Shape& s);
+hipError_t launch_decode_tiles(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
+                               int out_dtype, hipStream_t st);
+
 }  // namespace rkv
