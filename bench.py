@@ -183,6 +183,8 @@ def main() -> int:
     W = wl.make_weights()
     cfg = rkv.CodecConfig.from_workload(wl)
     weights = rkv.CodecWeights.from_math(W, cfg, dev)
+    # the decoder's fp16 copy is prepared once with the weights (rkv_prepare_decoder)
+    weights.prepare_decoder(cfg)
     n_ref = (T + wl.stride - 1) // wl.stride
     cache = rkv.CodecCache(cfg, 1, n_ref, T, dev)
     kv = torch.from_numpy(kv_np).to(torch.bfloat16).to(dev)[None].contiguous()

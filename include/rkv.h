@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 1
+#define RKV_ABI_VERSION 2
 
 typedef enum {
     RKV_OK = 0,
@@ -101,12 +101,16 @@ typedef struct {
     double rope_theta;  /* RoPE base theta                               */
 } rkv_config;
 
-/* Codec weights of one layer, nn.Linear layout (see above), weight_dtype. */
+/* Codec weights of one layer, nn.Linear layout (see above), weight_dtype.
+ * w_d_f16 is optional (NULL, or a buffer filled by rkv_prepare_decoder from this w_d):
+ * with it, the "bf16" formats' restore fetches the decoder as fp16 directly instead of
+ * converting w_d in every call; both give bit-identical output. */
 typedef struct {
     const void* w_c1;
     const void* w_c2;
     const void* w_c3;
     const void* w_d;
+    const void* w_d_f16;
 } rkv_weights;
 
 /* Cache state of one layer for a batch of B sequences; all arrays caller-owned. */
@@ -187,6 +191,19 @@ rkv_status rkv_encode(const rkv_config* cfg, const rkv_weights* w, rkv_cache* ca
 rkv_status rkv_encode_ex(const rkv_config* cfg, const rkv_weights* w, rkv_cache* cache, const void* kv,
                          int32_t kv_len, const int32_t* rows, const int32_t* pos, int32_t n, void* workspace,
                          size_t workspace_bytes, void* stream, void* const* events);
+
+/* Bytes of the prepared decoder of a "bf16" configuration: 2 * (2 d_k) * d_c. Host-only;
+ * 0 on an invalid or "f32" configuration. */
+size_t rkv_prepared_decoder_bytes(const rkv_config* cfg);
+
+/* Prepare the linear decoder W_d (section 2.5, the f_d of the boxed equation) for the
+ * restore: w_d_f16 receives w->w_d ([2 d_k, d_c] bf16) as fp16, in a device layout of
+ * this library (each run of 8 latent values reordered for the restore's MFMA operand).
+ * Every bf16 in the fp16 normal range converts exactly; smaller ones round toward zero.
+ * w_d_f16: >= rkv_prepared_decoder_bytes(cfg) bytes of device memory, 16-byte aligned,
+ * caller-owned; valid for as long as w_d is unchanged. Stream-ordered on `stream`.
+ * RKV_ERR_UNSUPPORTED for "f32" configurations. */
+rkv_status rkv_prepare_decoder(const rkv_config* cfg, const rkv_weights* w, void* w_d_f16, void* stream);
 
 /* Restore selected tokens (section 2.5 boxed equation, section 2.7 steps 2-3).
  *   idx [B, m] token positions (any order; sorted gives the best locality).

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     rkv_decode_selected,
     rkv_encode,
     rkv_encode_workspace_bytes,
+    rkv_prepared_decoder_bytes,
     rkv_record_bytes,
     rkv_validate_config,
 )

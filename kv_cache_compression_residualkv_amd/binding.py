@@ -46,6 +46,8 @@ EXPORTED = (
     "rkv_encode",
     "rkv_encode_ex",
     "rkv_decode_selected",
+    "rkv_prepared_decoder_bytes",
+    "rkv_prepare_decoder",
 )
 
 
@@ -74,7 +76,8 @@ class _Config(ctypes.Structure):
 
 
 class _Weights(ctypes.Structure):
-    _fields_ = [("w_c1", ctypes.c_void_p), ("w_c2", ctypes.c_void_p), ("w_c3", ctypes.c_void_p), ("w_d", ctypes.c_void_p)]
+    _fields_ = [("w_c1", ctypes.c_void_p), ("w_c2", ctypes.c_void_p), ("w_c3", ctypes.c_void_p), ("w_d", ctypes.c_void_p),
+                ("w_d_f16", ctypes.c_void_p)]
 
 
 class _Cache(ctypes.Structure):
@@ -127,6 +130,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.rkv_encode_ex.argtypes = [cfg_p, w_p, c_p, vp, i32, vp, vp, i32, vp, sz, vp, ctypes.POINTER(vp)]
     lib.rkv_decode_selected.restype = ctypes.c_int
     lib.rkv_decode_selected.argtypes = [cfg_p, w_p, c_p, vp, i32, vp, i32, vp]
+    lib.rkv_prepared_decoder_bytes.restype = sz
+    lib.rkv_prepared_decoder_bytes.argtypes = [cfg_p]
+    lib.rkv_prepare_decoder.restype = ctypes.c_int
+    lib.rkv_prepare_decoder.argtypes = [cfg_p, w_p, vp, vp]
     if path is None:
         _LIB = lib
     return lib
@@ -217,6 +224,10 @@ def rkv_encode_workspace_bytes(cfg: CodecConfig, batch: int, n: int, cap_ref: in
     return int(load_library().rkv_encode_workspace_bytes(ctypes.byref(cfg.c_struct()), batch, n, cap_ref))
 
 
+def rkv_prepared_decoder_bytes(cfg: CodecConfig) -> int:
+    return int(load_library().rkv_prepared_decoder_bytes(ctypes.byref(cfg.c_struct())))
+
+
 # ------------------------------------------------------------------------------ weights / cache
 
 
@@ -227,7 +238,24 @@ class CodecWeights:
 
     def __init__(self, w_c1: torch.Tensor, w_c2: torch.Tensor, w_c3: torch.Tensor, w_d: torch.Tensor):
         self.w_c1, self.w_c2, self.w_c3, self.w_d = (t.contiguous() for t in (w_c1, w_c2, w_c3, w_d))
-        self._c = _Weights(_ptr(self.w_c1), _ptr(self.w_c2), _ptr(self.w_c3), _ptr(self.w_d))
+        self.w_d_f16: Optional[torch.Tensor] = None
+        self._c = _Weights(_ptr(self.w_c1), _ptr(self.w_c2), _ptr(self.w_c3), _ptr(self.w_d), None)
+
+    def prepare_decoder(self, cfg: "CodecConfig", stream=None) -> "CodecWeights":
+        """Fill the optional prepared decoder (rkv_prepare_decoder) and use it from now on."""
+        n = rkv_prepared_decoder_bytes(cfg)
+        if n == 0:
+            raise RkvError("rkv_prepare_decoder", -2)
+        buf = torch.empty((n,), dtype=torch.uint8, device=self.w_d.device)
+        _check("rkv_prepare_decoder", load_library().rkv_prepare_decoder(
+            ctypes.byref(cfg.c_struct()), ctypes.byref(self._c), _ptr(buf), _stream(stream)))
+        self.w_d_f16 = buf
+        self._c.w_d_f16 = _ptr(buf)
+        return self
+
+    def drop_prepared_decoder(self) -> None:
+        self.w_d_f16 = None
+        self._c.w_d_f16 = None
 
     @classmethod
     def from_math(cls, W: Dict, cfg: CodecConfig, device="cuda") -> "CodecWeights":

@@ -35,11 +35,11 @@ HIP_FLAGS = [
 # architectural VGPRs hold. With the default heuristics the backend keeps MFMA
 # accumulators in VGPRs and parks them in AGPRs around every MFMA (several
 # v_accvgpr moves per MFMA); the VGPR form with the AGPRs left free keeps the
-# accumulators in place. The column-slice decoder allocates better under the default.
+# accumulators in place. The decoders allocate better under the default (their
+# accumulators stay in AGPRs between the MFMAs and the VGPRs hold the operands).
 PER_SOURCE_FLAGS = {
     "rkv_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "rkv_encode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-    "rkv_decode_tiles.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -206,7 +206,26 @@ rkv_status rkv_decode_selected(const rkv_config* cfg, const rkv_weights* w, cons
     if (m == 0) return RKV_OK;
     if (!w || !w->w_d || !idx || !out) return RKV_ERR_INVALID_ARG;
     if (!aligned16(w->w_d) || !aligned16(out)) return RKV_ERR_ALIGNMENT;
-    return from_hip(launch_decode(s, c, idx, m, w->w_d, out, out_dtype, static_cast<hipStream_t>(stream)));
+    // the prepared fp16 decoder serves the "bf16" formats only
+    const void* wd16 = s.f32 ? nullptr : w->w_d_f16;
+    if (wd16 && !aligned16(wd16)) return RKV_ERR_ALIGNMENT;
+    return from_hip(launch_decode(s, c, idx, m, w->w_d, wd16, out, out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t rkv_prepared_decoder_bytes(const rkv_config* cfg) {
+    Shape s;
+    if (check_config(cfg, &s) != RKV_OK || s.f32) return 0;
+    return (size_t)2 * s.W2 * s.d_c;
+}
+
+rkv_status rkv_prepare_decoder(const rkv_config* cfg, const rkv_weights* w, void* w_d_f16, void* stream) {
+    Shape s;
+    rkv_status st = check_config(cfg, &s);
+    if (st != RKV_OK) return st;
+    if (s.f32) return RKV_ERR_UNSUPPORTED;
+    if (!w || !w->w_d || !w_d_f16) return RKV_ERR_INVALID_ARG;
+    if (!aligned16(w->w_d) || !aligned16(w_d_f16)) return RKV_ERR_ALIGNMENT;
+    return from_hip(launch_prepare_decoder(s, w->w_d, w_d_f16, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -517,9 +517,9 @@ static hipError_t decode_d(const Shape& s, const CacheView& c, const int* idx, i
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
-                         int out_dtype, hipStream_t st) {
-    if (decode_tiles_supported(s)) return launch_decode_tiles(s, c, idx, m, wd, out, out_dtype, st);
+hipError_t launch_decode(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, const void* wd16,
+                         void* out, int out_dtype, hipStream_t st) {
+    if (decode_tiles_supported(s)) return launch_decode_tiles(s, c, idx, m, wd, wd16, out, out_dtype, st);
     if (s.f32) {
         if (out_dtype == RKV_F32) return decode_d<float, float, float, float, float>(s, c, idx, m, wd, out, st);
         return decode_d<float, float, float, float, bf16_t>(s, c, idx, m, wd, out, st);

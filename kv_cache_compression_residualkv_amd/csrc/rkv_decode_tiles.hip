@@ -25,6 +25,8 @@
 // the contraction does not depend on that order.
 #include <math.h>
 
+#include <type_traits>
+
 #include "rkv_device.h"
 #include "rkv_internal.h"
 #include "rkv_pipe.h"
@@ -36,23 +38,48 @@ namespace {
 namespace dt {
 constexpr int kThreads = 256;       // 4 wavefronts
 constexpr int TT = 128;             // tokens per workgroup
-constexpr int kCols = 128;          // output columns per chunk (reference slices are fetched per chunk)
+constexpr int kCols = 128;          // output columns per chunk
 constexpr int kHalf = 64;           // output columns per pass (4 MFMA tiles of 16)
-constexpr int kRefs = 4;            // reference slots per token (k <= 4), all staged in LDS
-constexpr int kWP = kStageK + 8;    // fp16 pitch of a staged W_d row (conflict-free fragment reads)
-constexpr int kWBuf = kHalf * kWP * 2;       // one W_d stage (64 rows x 64 K fp16)
-constexpr int kRefBuf = TT * kRefs * kCols;  // FP8 reference slices of one chunk
-constexpr int kOffW = 0;
-constexpr int kOffRef = kOffW + 2 * kWBuf;
-constexpr int kOffSlot = kOffRef + kRefBuf;            // int [TT][kRefs]; -1: zero row
-constexpr int kOffKd = kOffSlot + TT * kRefs * 4;      // int [TT]: divisor of the slot sum (4, or 3)
-constexpr int kOffRev = kOffKd + TT * 4;               // double [64]
-constexpr int bytes = kOffRev + 64 * 8;
-static_assert(bytes <= 160 * 1024, "LDS budget");
+constexpr int kRefs = 4;            // reference slots per token (k <= 4)
+constexpr int kRefBuf = TT * kRefs * kHalf;  // FP8 reference slices of one pass
+constexpr int kRopeP = 66;                   // float2 (cos, sin) pitch of a token's RoPE row
 }  // namespace dt
 
-// 128 zero bytes: the source of an empty reference slot's slice
-__device__ __align__(16) uint8_t g_zero_row[dt::kCols];
+// LDS layout of form 1 (register-staged W_d)
+namespace rr {
+constexpr int kWP = kStageK + 8;                 // fp16 pitch of a staged W_d row (conflict-free reads)
+constexpr int kWBuf = dt::kHalf * kWP * 2;       // one W_d stage (64 rows x 64 K fp16)
+constexpr int kWSlots = 3;                       // W_d stages resident in LDS
+constexpr int kPieces = dt::kRefBuf / (16 * dt::kThreads);  // 16-byte slices per thread and pass
+constexpr int kOffW = 0;
+constexpr int kOffRef = kOffW + kWSlots * kWBuf;       // two pass buffers
+constexpr int kOffSlot = kOffRef + 2 * dt::kRefBuf;    // int [TT][kRefs]; -1: none
+constexpr int kOffKd = kOffSlot + dt::TT * dt::kRefs * 4;  // int [TT]: divisor of the slot sum
+constexpr int kOffRope = kOffKd + dt::TT * 4;          // float2 [TT][kRopeP]
+constexpr int bytes = kOffRope + dt::TT * dt::kRopeP * 8;
+// set-up tables that live in the reference buffers until their first fill
+constexpr int kOffRev = kOffRef;                       // double [64]
+constexpr int kOffPos = kOffRef + 64 * 8;              // int [TT]
+static_assert(bytes <= 160 * 1024, "LDS budget");
+}  // namespace rr
+
+// LDS layout of form 2 (prepared fp16 W_d by direct loads)
+namespace dl {
+constexpr int NST = 4;                           // W_d stages in flight
+constexpr int kWStage = dt::kHalf * kStageK * 2;  // 8 KB
+constexpr int kOffW = 0;
+constexpr int kOffRef = kOffW + NST * kWStage;
+constexpr int kOffSlot = kOffRef + dt::kRefBuf;
+constexpr int kOffKd = kOffSlot + dt::TT * dt::kRefs * 4;
+constexpr int kOffRope = kOffKd + dt::TT * 4;
+constexpr int bytes = kOffRope + dt::TT * dt::kRopeP * 8;
+constexpr int kOffRev = kOffRef;
+constexpr int kOffPos = kOffRef + 64 * 8;
+static_assert(bytes <= 160 * 1024, "LDS budget");
+}  // namespace dl
+
+// 64 zero bytes: the slices of an empty reference slot
+__device__ __align__(16) uint8_t g_zero_slice[64];
 
 // Workgroup barrier for LDS traffic only: a fence would also wait for every
 // outstanding global load, including the reference slices fetched for the next chunk.
@@ -74,8 +101,9 @@ __device__ inline void store_row4<float>(float* p, float a, float b, float c, fl
 }
 template <>
 __device__ inline void store_row4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
-    bf16_t t[4] = {(bf16_t)a, (bf16_t)b, (bf16_t)c, (bf16_t)d};
-    *reinterpret_cast<uint2*>(p) = *reinterpret_cast<uint2*>(t);
+    const f32x2 lo = {a, b}, hi = {c, d};
+    const bf16x2 x = __builtin_convertvector(lo, bf16x2), y = __builtin_convertvector(hi, bf16x2);
+    *reinterpret_cast<uint2*>(p) = make_uint2(*reinterpret_cast<const uint32_t*>(&x), *reinterpret_cast<const uint32_t*>(&y));
 }
 
 // fp16 fragment of 8 codes (latent order 0 4 1 5 2 6 3 7) times the group's step plus
@@ -131,68 +159,19 @@ __device__ constexpr int chunk_tile(int h, int lt) {
     return D == 128 ? 2 * h + (lt & 1) + 4 * (lt >> 1) : 4 * h + lt;
 }
 
-// grid: (token tiles, column groups, batch). Each column group is `ncg` chunks of 128
-// columns starting at column 128 ncg blockIdx.y. NKS = d_c / 32 latent K-steps (step ks
-// covers latent coordinates 32 ks .. +32, i.e. quantizer group ks); D = head dimension;
-// BITS = 4 or 2.
-template <int NKS, int D, int BITS, typename OutT>
-__global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
-    const int* __restrict__ idx, int m, int ncg, const fp8_t* __restrict__ ref_vals, const int* __restrict__ self_slot,
-    const int* __restrict__ ref_idx, const uint8_t* __restrict__ codes, size_t code_bytes,
-    const f16_t* __restrict__ scale, const f16_t* __restrict__ zmin, const bf16_t* __restrict__ wd, int W2, int dk,
-    int top_k, int cap_ref, int cap_tok, double theta, OutT* __restrict__ out, int* err) {
-    constexpr int d_c = 32 * NKS;
-    constexpr int KST = d_c / kStageK;  // W_d stages per pass
-    static_assert(KST % 2 == 0 && 2 * KST < 64, "stage shape");
-    static_assert(D == 64 || D == 128, "head dimension");
-    constexpr int half = D / 2, NJ = D / 8;  // RoPE pairs per head; cos / sin per lane and token
-    extern __shared__ __align__(16) unsigned char smem[];
-    f16_t* sW = reinterpret_cast<f16_t*>(smem + dt::kOffW);
-    unsigned char* sRef = smem + dt::kOffRef;
-    int* sSlot = reinterpret_cast<int*>(smem + dt::kOffSlot);
-    int* sKd = reinterpret_cast<int*>(smem + dt::kOffKd);
-    double* sRev = reinterpret_cast<double*>(smem + dt::kOffRev);
+// ---- set-up shared by both forms ------------------------------------------------------
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, mrow = lane & 15;
-    const int b = blockIdx.z;
-    const int tt0 = blockIdx.x * dt::TT;
-    const int n0 = blockIdx.y * ncg * dt::kCols;
-    const int nchunks = min(ncg, (W2 - n0) / dt::kCols);
-    const fp8_t* pool = ref_vals + (size_t)b * cap_ref * W2;
-
-    // ---- W_d register ring. A stage is 64 rows (the pass's output columns) x 64 latent
-    // values; thread t holds rows 32 u + t / 8 (u = 0, 1), values 8 (t % 8) .. + 8.
-    // Stage x of the run sits in register slot x % 2 and LDS buffer x % 2.
-    const int wk8 = tid & 7;
-    auto load_w = [&](uint4 (&r)[2], int c, int h, int k) {
-        c = min(c, nchunks - 1);  // past the end: any readable stage (never used)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int lr = 32 * u + (tid >> 3);
-            const int col = n0 + dt::kCols * c + 16 * chunk_tile<D>(h, lr >> 4) + (lr & 15);
-            r[u] = *reinterpret_cast<const uint4*>(wd + (size_t)col * d_c + k * kStageK + 8 * wk8);
-        }
-    };
-    auto store_w = [&](const uint4 (&r)[2], int buf) {
-        f16_t* dst = sW + buf * (dt::kWBuf / 2) + (tid >> 3) * dt::kWP + 8 * wk8;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) *reinterpret_cast<f16x8*>(dst + 32 * u * dt::kWP) = w_to_f16(r[u]);
-    };
-    // stage (c, h, k) + d of the run, as (c', h', k')
-    auto ahead = [](int k, int d, int& du) { du = (k + d) / KST; return (k + d) % KST; };
-    uint4 wa[2], wb[2];
-    load_w(wa, 0, 0, 0);
-    {
-        int du;
-        const int k1 = ahead(0, 1, du);
-        load_w(wb, du >> 1, du & 1, k1);
-    }
-
-    // ---- token table: four reference slots per token (-1: zero row) and the divisor
-    // of their sum. k_i = 1, 2 or 4 references fill the slots by repetition (slot sum / 4
-    // is their mean exactly); k_i = 3 leaves one slot empty and divides by 3. A reference
-    // token restores its own stored row (k = 1).
+// Token table (threads 0..TT-1, one token each): four reference slots per token (-1: an
+// empty slot, read as zeros) and the divisor of their sum. k_i = 1, 2 or 4 references
+// fill the slots by repetition (slot sum / 4 is their mean exactly); k_i = 3 leaves one
+// slot empty and divides by 3. A reference token restores its own stored row (k = 1).
+// Also the position of every token and, for the RoPE table, the revolutions per position
+// of the pair frequencies theta^(-2j/D) / (2 pi).
+template <int D>
+__device__ inline void token_table(int* sSlot, int* sKd, int* sPos, double* sRev, const int* __restrict__ idx, int m,
+                                   int b, int tt0, const int* __restrict__ self_slot, const int* __restrict__ ref_idx,
+                                   int top_k, int cap_ref, int cap_tok, double theta, int* err) {
+    const int tid = threadIdx.x;
     if (tid < dt::TT) {
         const int t = tt0 + tid;
         int p = -1;
@@ -235,20 +214,24 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
 #pragma unroll
         for (int q = 0; q < dt::kRefs; ++q) sSlot[tid * dt::kRefs + q] = sl[q];
         sKd[tid] = n == 3 ? 3 : 4;
+        sPos[tid] = max(p, 0);
     }
-    // revolutions per position of the RoPE pair frequencies theta^(-2j/D) / (2 pi)
-    if (tid < half) sRev[tid] = pow(theta, -2.0 * (double)tid / (double)D) * 0.15915494309189535;
+    if (tid < D / 2) sRev[tid] = pow(theta, -2.0 * (double)tid / (double)D) * 0.15915494309189535;
+}
 
-    // ---- this lane's two tokens (MFMA column groups): position, and its latent as
-    // fp16 fragments of every K-step (zero for a reference token or an invalid index)
-    int tpos[2];
-    f16x8 zf[2][NKS];
+// This lane's two tokens (MFMA column groups of wavefront `wave`): the latent as fp16
+// fragments of every K-step (zero for a reference token or an invalid index).
+template <int NKS, int BITS>
+__device__ inline void latent_frags(f16x8 (&zf)[2][NKS], const int* __restrict__ idx, int m, int b, int tt0,
+                                    const int* __restrict__ self_slot, const uint8_t* __restrict__ codes,
+                                    size_t code_bytes, const f16_t* __restrict__ scale,
+                                    const f16_t* __restrict__ zmin, int cap_tok) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, mrow = lane & 15;
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
         const int t = tt0 + 32 * wave + 16 * gr + mrow;
         int p = t < m ? idx[(size_t)b * m + t] : -1;
         if (p >= cap_tok) p = -1;
-        tpos[gr] = p;
         const size_t ro = (size_t)b * cap_tok + max(p, 0);
         const bool enc = p >= 0 && self_slot[ro] < 0;
         const uint8_t* rec = codes + ro * code_bytes;
@@ -275,74 +258,393 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
                                         *reinterpret_cast<const f16x2*>(&zvp));
         }
     }
+}
 
-    // ---- first W_d stage into LDS buffer 0, the third into the freed registers
-    store_w(wa, 0);
-    {
-        int du;
-        const int k2 = ahead(0, 2, du);
-        load_w(wa, du >> 1, du & 1, k2);
+// RoPE table: cos / sin of every token's pair angles (two threads per token). The phase
+// in revolutions is reduced to [-1/2, 1/2] in fp64, then sin / cos in fp32.
+template <int D>
+__device__ inline void rope_table(float* sRope, const int* sPos, const double* sRev) {
+    const int tid = threadIdx.x, tk = tid >> 1;
+    const double pp = (double)sPos[tk];
+    for (int j = (tid & 1) * 32; j < (tid & 1) * 32 + 32 && j < D / 2; ++j) {
+        const double r = pp * sRev[j];
+        const float fr = (float)(r - rint(r));
+        *reinterpret_cast<float2*>(sRope + 2 * (tk * dt::kRopeP + j)) =
+            make_float2(__builtin_amdgcn_cosf(fr), __builtin_amdgcn_sinf(fr));
     }
-    __syncthreads();
+}
 
-    // ---- per token: divisor of the slot sum, and cos / sin of the RoPE angles of this
-    // lane's pair columns j = 16 jt + 4 g + e of a head's first half; the phase in
-    // revolutions is reduced to [-1/2, 1/2] in fp64, then sin / cos in fp32
+// Form of this wavefront's reference mean. When every token averages its four slots the
+// 1/4 rides in the selection matrix (fused); otherwise the slot sum is divided exactly per
+// token. Selection matrix of the reference MFMA (A operand, 16 x 32 FP8): output row r
+// takes K entries (q, r) of the step's two slots q; K entry 8 (lane / 16) + j of this lane
+// is (slot q = lane / 32, column 8 ((lane / 16) % 2) + j). Weight 1/4 (e4m3 0x28) for the
+// fused mean, 1 (0x38) for the exact division.
+struct MeanForm {
     float kd[2], rkd[2];
-    float rc[2][NJ], rsn[2][NJ];
+    long sel;
+    bool fused;
+};
+__device__ inline MeanForm mean_form(const int* sKd) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, mrow = lane & 15;
+    MeanForm f;
     bool all4 = true;
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
         const int k = sKd[32 * wave + 16 * gr + mrow];
         all4 = all4 && k == 4;
-        kd[gr] = (float)k;
-        rkd[gr] = __fdiv_rn(1.0f, kd[gr]);
-        const double pp = (double)max(tpos[gr], 0);
-#pragma unroll
-        for (int jt = 0; jt < NJ / 4; ++jt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const double r = pp * sRev[16 * jt + 4 * g + e];
-                const float fr = (float)(r - rint(r));
-                rc[gr][4 * jt + e] = __builtin_amdgcn_cosf(fr);
-                rsn[gr][4 * jt + e] = __builtin_amdgcn_sinf(fr);
-            }
+        f.kd[gr] = (float)k;
+        f.rkd[gr] = __fdiv_rn(1.0f, f.kd[gr]);
     }
-    // every token of this wavefront averages its four slots: the 1/4 rides in the
-    // selection matrix; otherwise the slot sum is divided exactly per token
-    const bool fused_mean = __all(all4);
-
-    // Selection matrix of the reference MFMA (A operand, 16 x 32 FP8): output row r takes
-    // K entries (q, r) of the step's two slots q; K entry 8 (lane / 16) + j of this lane
-    // is (slot q = lane / 32, column 8 ((lane / 16) % 2) + j). Weight 1/4 (e4m3 0x28) for
-    // the fused mean, 1 (0x38) for the exact-division path.
+    f.fused = __all(all4);
     const bool on = (mrow >> 3) == (g & 1);
-    const long sel = on ? (long)((fused_mean ? 0x28ull : 0x38ull) << (8 * (mrow & 7))) : 0l;
+    f.sel = on ? (long)((f.fused ? 0x28ull : 0x38ull) << (8 * (mrow & 7))) : 0l;
+    return f;
+}
 
-    // ---- reference slices of a chunk -> LDS (row p = q * TT + token, 128 bytes; the
-    // 16-byte segment s of row p sits at position s ^ (p % 8)). Wave w fetches slot
-    // q = w of all 128 tokens, eight rows per load.
-    const uint8_t* zero_row = g_zero_row;
-    auto issue_refs = [&](int c) {
-        const int col = n0 + dt::kCols * c;
-        const int wv = wave_id();
-        int sl[16];
+// End of pass h of a chunk starting at column col0: reference mean (two FP8 MFMAs per
+// output tile against the slices in R: row r = q * TT + token, 64 bytes, tile t at 16-byte
+// position t ^ ((r / 4) % 4)), RoPE on key columns, store. An invalid index has a zero
+// latent and empty slots: its row is zero already.
+template <int D, bool kFused, typename OutT>
+__device__ inline void finish_pass(f32x4 (&acc)[2][4], const unsigned char* R, const float* sRope, int h, int col0,
+                                   bool rope, const MeanForm& mf, int tt0, int m, int b, int W2,
+                                   OutT* __restrict__ out) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, mrow = lane & 15;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) sl[u] = sSlot[(8 * u + (lane >> 3)) * dt::kRefs + wv];
+    for (int gr = 0; gr < 2; ++gr) {
+        const int tk = 32 * wave + 16 * gr + mrow;
+        f32x4 (&a)[4] = acc[gr];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int pr = 128 * wv + 8 * u + (lane >> 3);
-            const int seg = (lane & 7) ^ (pr & 7);
-            const uint8_t* src =
-                sl[u] >= 0 ? reinterpret_cast<const uint8_t*>(pool) + (size_t)sl[u] * W2 + col : zero_row;
-            dma16(src + 16 * seg, sRef + 1024 * (16 * wv + u));
+        for (int lt = 0; lt < 4; ++lt) {
+            long v[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int r = (2 * hh + (g >> 1)) * dt::TT + tk;
+                v[hh] = *reinterpret_cast<const long*>(R + r * dt::kHalf + 16 * (lt ^ ((r >> 2) & 3)) + 8 * (g & 1));
+            }
+            if constexpr (kFused) {
+                a[lt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(mf.sel, v[0], a[lt], 0, 0, 0);
+                a[lt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(mf.sel, v[1], a[lt], 0, 0, 0);
+            } else {
+                f32x4 sm = zero4();
+                sm = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(mf.sel, v[0], sm, 0, 0, 0);
+                sm = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(mf.sel, v[1], sm, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[lt][e] += div_small(sm[e], mf.kd[gr], mf.rkd[gr]);
+            }
         }
-        // the reference wait counts the loads issued after these: keep later loads after them
-        __builtin_amdgcn_sched_barrier(0);
+        if (rope) {
+#pragma unroll
+            for (int lt = 0; lt < 2; ++lt) {
+                const int jt = D == 128 ? 2 * h + lt : lt;
+                const float* rp = sRope + 2 * (tk * dt::kRopeP + 16 * jt + 4 * g);
+                const float4 q01 = *reinterpret_cast<const float4*>(rp);
+                const float4 q23 = *reinterpret_cast<const float4*>(rp + 4);
+                const float cs[4] = {q01.x, q01.z, q23.x, q23.z};
+                const float sn[4] = {q01.y, q01.w, q23.y, q23.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x1 = a[lt][e], x2 = a[lt + 2][e];
+                    a[lt][e] = x1 * cs[e] - x2 * sn[e];
+                    a[lt + 2][e] = x2 * cs[e] + x1 * sn[e];
+                }
+            }
+        }
+        const int t = tt0 + tk;
+        if (t < m) {
+            OutT* o = out + ((size_t)b * m + t) * W2 + col0 + 4 * g;
+#pragma unroll
+            for (int lt = 0; lt < 4; ++lt)
+                store_row4<OutT>(o + 16 * chunk_tile<D>(h, lt), a[lt][0], a[lt][1], a[lt][2], a[lt][3]);
+        }
+    }
+}
+
+// grid: (token tiles, column groups, batch). Each column group is `ncg` chunks of 128
+// columns starting at column 128 ncg blockIdx.y. NKS = d_c / 32 latent K-steps (step ks
+// covers latent coordinates 32 ks .. +32, i.e. quantizer group ks); D = head dimension;
+// BITS = 4 or 2.
+
+// ---- form 1: W_d as stored (bf16), converted in the workgroup ---------------------------
+template <int NKS, int D, int BITS, typename OutT>
+__global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
+    const int* __restrict__ idx, int m, int ncg, const fp8_t* __restrict__ ref_vals, const int* __restrict__ self_slot,
+    const int* __restrict__ ref_idx, const uint8_t* __restrict__ codes, size_t code_bytes,
+    const f16_t* __restrict__ scale, const f16_t* __restrict__ zmin, const bf16_t* __restrict__ wd, int W2, int dk,
+    int top_k, int cap_ref, int cap_tok, double theta, OutT* __restrict__ out, int* err) {
+    constexpr int d_c = 32 * NKS;
+    constexpr int KST = d_c / kStageK;  // W_d stages per pass
+    static_assert(KST % 2 == 0 && 2 * KST < 64, "stage shape");
+    static_assert(D == 64 || D == 128, "head dimension");
+    extern __shared__ __align__(16) unsigned char smem[];
+    f16_t* sW = reinterpret_cast<f16_t*>(smem + rr::kOffW);
+    unsigned char* sRef = smem + rr::kOffRef;
+    int* sSlot = reinterpret_cast<int*>(smem + rr::kOffSlot);
+    int* sKd = reinterpret_cast<int*>(smem + rr::kOffKd);
+    float* sRope = reinterpret_cast<float*>(smem + rr::kOffRope);
+    double* sRev = reinterpret_cast<double*>(smem + rr::kOffRev);
+    int* sPos = reinterpret_cast<int*>(smem + rr::kOffPos);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int g = lane >> 4, mrow = lane & 15;
+    const int b = blockIdx.z;
+    const int tt0 = blockIdx.x * dt::TT;
+    const int n0 = blockIdx.y * ncg * dt::kCols;
+    const int nchunks = min(ncg, (W2 - n0) / dt::kCols);
+    const fp8_t* pool = ref_vals + (size_t)b * cap_ref * W2;
+
+    // ---- W_d register ring. A stage is 64 rows (the pass's output columns) x 64 latent
+    // values; thread t holds rows 32 u + t / 8 (u = 0, 1), values 8 (t % 8) .. + 8.
+    // Stage x of the run is loaded into register slot x % 2 two stages before it is
+    // written to LDS slot x % 3, one stage before it is multiplied.
+    const int wk8 = tid & 7;
+    auto load_w = [&](uint4 (&r)[2], int c, int h, int k) {
+        c = min(c, nchunks - 1);  // past the end: any readable stage (never used)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int lr = 32 * u + (tid >> 3);
+            const int col = n0 + dt::kCols * c + 16 * chunk_tile<D>(h, lr >> 4) + (lr & 15);
+            r[u] = *reinterpret_cast<const uint4*>(wd + (size_t)col * d_c + k * kStageK + 8 * wk8);
+        }
     };
-    issue_refs(0);
+    auto store_w = [&](const uint4 (&r)[2], int slot) {
+        f16_t* dst = sW + slot * (rr::kWBuf / 2) + (tid >> 3) * rr::kWP + 8 * wk8;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) *reinterpret_cast<f16x8*>(dst + 32 * u * rr::kWP) = w_to_f16(r[u]);
+    };
+    // stage (c, h, k) + d of the run as pass offset du and stage k'
+    auto ahead = [](int k, int d, int& du) { du = (k + d) / KST; return (k + d) % KST; };
+    auto load_ahead = [&](uint4 (&r)[2], int c, int h, int k, int d) {
+        int du;
+        const int kk = ahead(k, d, du);
+        load_w(r, c + ((h + du) >> 1), (h + du) & 1, kk);
+    };
+    uint4 wa[2], wb[2];
+    load_ahead(wa, 0, 0, 0, 0);
+    load_ahead(wb, 0, 0, 0, 1);
+
+    token_table<D>(sSlot, sKd, sPos, sRev, idx, m, b, tt0, self_slot, ref_idx, top_k, cap_ref, cap_tok, theta, err);
+    f16x8 zf[2][NKS];
+    latent_frags<NKS, BITS>(zf, idx, m, b, tt0, self_slot, codes, code_bytes, scale, zmin, cap_tok);
+
+    // ---- stages 0 and 1 into LDS slots 0 and 1, stages 2 and 3 into the registers
+    store_w(wa, 0);
+    load_ahead(wa, 0, 0, 0, 2);
+    store_w(wb, 1);
+    load_ahead(wb, 0, 0, 0, 3);
+    __syncthreads();
+    if (n0 < dk) rope_table<D>(sRope, sPos, sRev);
+    const MeanForm mf = mean_form(sKd);
+
+    // ---- reference slices of a pass -> LDS buffer (pass % 2), in the layout finish_pass
+    // reads. Thread t moves slices 256 u + t (u = 0..7): row 64 u + t / 4, tile t % 4;
+    // they travel through registers two stages ahead like W_d.
+    auto load_ref = [&](int c, int h, int u) -> uint4 {
+        c = min(c, nchunks - 1);  // past the end: any readable slice (never used)
+        const int r = 64 * u + (tid >> 2), q = r >> 7, tk = r & (dt::TT - 1);
+        const int sl = sSlot[tk * dt::kRefs + q];
+        const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(pool) +
+                                                         (size_t)max(sl, 0) * W2 + dt::kCols * c + n0 +
+                                                         16 * chunk_tile<D>(h, tid & 3));
+        return sl >= 0 ? v : make_uint4(0u, 0u, 0u, 0u);
+    };
+    auto store_ref = [&](uint4 v, int buf, int u) {
+        const int r = 64 * u + (tid >> 2);
+        *reinterpret_cast<uint4*>(sRef + buf * dt::kRefBuf + r * dt::kHalf + 16 * ((tid & 3) ^ ((r >> 2) & 3))) = v;
+    };
+    // slices of the next pass fetched in stage k of a pass (all 8 spread over the stages)
+    constexpr int NP = (rr::kPieces + KST - 1) / KST;
+    auto piece_lo = [](int k) { return rr::kPieces * k / KST; };
+
+    // the set-up tables in the reference buffers are read; pass 0's slices go in directly
+    __syncthreads();
+    {
+        uint4 v[rr::kPieces];
+#pragma unroll
+        for (int u = 0; u < rr::kPieces; ++u) v[u] = load_ref(0, 0, u);
+#pragma unroll
+        for (int u = 0; u < rr::kPieces; ++u) store_ref(v[u], 0, u);
+    }
+    uint4 ra[NP], rb[NP];  // register slots of the slices fetched in even / odd stages
+
+    // W_d fragments of one stage (2 K-steps x 4 tiles), read one stage ahead
+    typedef typename Mma<f16_t>::frag Frag;
+    auto read_frags = [&](Frag (&f)[2][4], int slot) {
+        const f16_t* W = sW + slot * (rr::kWBuf / 2);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int lt = 0; lt < 4; ++lt) f[kh][lt] = lds_frag<f16_t>(W + (16 * lt + mrow) * rr::kWP + 32 * kh + 8 * g);
+    };
+    __syncthreads();
+    Frag fa[2][4], fb[2][4];
+    read_frags(fa, 0);
+    int slot = 0;  // LDS slot of the current stage
 
     f32x4 acc[2][4];
+    for (int c = 0; c < nchunks; ++c) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // pass p = 2 c + h; its slices are in buffer h, the next pass's go to 1 - h
+#pragma unroll
+            for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[gr][i] = zero4();
+#pragma unroll
+            for (int k = 0; k < KST; ++k) {
+                // stage x: fragments of stage x + 1 (resident since the last barrier); stage
+                // x + 2 registers -> LDS and stage x + 4 -> those registers; the slices
+                // fetched two stages ago -> LDS and the next ones -> those registers
+                Frag (&cur)[2][4] = (k % 2 == 0) ? fa : fb;
+                Frag (&nxt)[2][4] = (k % 2 == 0) ? fb : fa;
+                uint4 (&rg)[NP] = (k % 2 == 0) ? ra : rb;
+                const int s1 = slot == 2 ? 0 : slot + 1, s2 = slot == 0 ? 2 : slot - 1;
+                read_frags(nxt, s1);
+                if (k % 2 == 0) {
+                    store_w(wa, s2);
+                    load_ahead(wa, c, h, k, 4);
+                } else {
+                    store_w(wb, s2);
+                    load_ahead(wb, c, h, k, 4);
+                }
+                {
+                    // slices fetched in stage k - 2 (of this pass, or of the previous one)
+                    const bool prev = k < 2;
+                    const int kf = prev ? k + KST - 2 : k - 2;
+                    const bool have = !prev || c > 0 || h > 0;
+                    if (have) {
+#pragma unroll
+                        for (int u = 0; u < NP; ++u)
+                            if (piece_lo(kf) + u < piece_lo(kf + 1))
+                                store_ref(rg[u], prev ? h : 1 - h, piece_lo(kf) + u);
+                    }
+                    const int cn = c + h, hn = 1 - h;  // the next pass
+#pragma unroll
+                    for (int u = 0; u < NP; ++u)
+                        if (piece_lo(k) + u < piece_lo(k + 1)) rg[u] = load_ref(cn, hn, piece_lo(k) + u);
+                }
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    const int ks = 2 * k + kh;
+#pragma unroll
+                    for (int lt = 0; lt < 4; ++lt) {
+                        acc[0][lt] = Mma<f16_t>::step(acc[0][lt], cur[kh][lt], zf[0][ks]);
+                        acc[1][lt] = Mma<f16_t>::step(acc[1][lt], cur[kh][lt], zf[1][ks]);
+                    }
+                }
+                slot = s1;
+                lds_barrier();
+            }
+            // ---- pass (c, h) done (one branch per pass on the mean's form)
+            const int col0 = n0 + dt::kCols * c;
+            const unsigned char* R = sRef + h * dt::kRefBuf;
+            if (mf.fused) finish_pass<D, true, OutT>(acc, R, sRope, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
+            else finish_pass<D, false, OutT>(acc, R, sRope, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
+        }
+    }
+}
+
+// ---- form 2: W_d prepared as fp16 (rkv_prepare_decoder), fetched by direct loads -------
+// The prepared copy and the reference slices go global -> LDS with global_load_lds:
+// no registers are staged and no VALU converts, and every wait on those loads is
+// counted here. W_d: a ring of NST stages of 64 rows x 64 latent values, each 8 blocks of
+// 16 rows x 32 values (1 KB) in the chunk-swizzled layout of rkv_pipe.h; stage x is
+// issued NST stages ahead into the slot stage x - NST used. Reference slices: one buffer,
+// fetched at the start of each pass (after the previous pass's epilogue has read it).
+template <int NKS, int D, int BITS, typename OutT>
+__global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
+    const int* __restrict__ idx, int m, int ncg, const fp8_t* __restrict__ ref_vals, const int* __restrict__ self_slot,
+    const int* __restrict__ ref_idx, const uint8_t* __restrict__ codes, size_t code_bytes,
+    const f16_t* __restrict__ scale, const f16_t* __restrict__ zmin, const f16_t* __restrict__ w16, int W2, int dk,
+    int top_k, int cap_ref, int cap_tok, double theta, OutT* __restrict__ out, int* err) {
+    constexpr int d_c = 32 * NKS;
+    constexpr int KST = d_c / kStageK;  // W_d stages per pass
+    constexpr int NST = dl::NST;
+    static_assert(KST >= 2 && 2 * KST < 64, "stage shape");
+    static_assert(D == 64 || D == 128, "head dimension");
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char* sW = smem + dl::kOffW;
+    unsigned char* sRef = smem + dl::kOffRef;
+    int* sSlot = reinterpret_cast<int*>(smem + dl::kOffSlot);
+    int* sKd = reinterpret_cast<int*>(smem + dl::kOffKd);
+    float* sRope = reinterpret_cast<float*>(smem + dl::kOffRope);
+    double* sRev = reinterpret_cast<double*>(smem + dl::kOffRev);
+    int* sPos = reinterpret_cast<int*>(smem + dl::kOffPos);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int b = blockIdx.z;
+    const int tt0 = blockIdx.x * dt::TT;
+    const int n0 = blockIdx.y * ncg * dt::kCols;
+    const int nchunks = min(ncg, (W2 - n0) / dt::kCols);
+    const int nst = 2 * nchunks * KST;  // stages of the run
+    const fp8_t* pool = ref_vals + (size_t)b * cap_ref * W2;
+
+    // stage x -> slot x % NST. Wave w fills blocks w and w + 4 (block 2 lt + kh: row group
+    // lt = local MFMA tile, K half kh); lane l fetches row l / 4, chunk swz(l / 4, l % 4).
+    auto issue_w = [&](int x) {
+        const int xs = min(x, nst - 1);  // past the end: any readable stage (never used)
+        const int pass = xs / KST, k = xs - pass * KST, c = pass >> 1, h = pass & 1;
+        const int wv = wave_id(), r = lane >> 2;
+        unsigned char* dst = sW + (x % NST) * dl::kWStage;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int blk = wv + 4 * u, lt = blk >> 1, kh = blk & 1;
+            const int col = n0 + dt::kCols * c + 16 * chunk_tile<D>(h, lt) + r;
+            dma16(w16 + (size_t)col * d_c + k * kStageK + 32 * kh + 8 * swz(r, lane & 3), dst + 1024 * blk);
+        }
+    };
+    // slices of pass p: DMA j (wave w issues 8 w .. + 8) fills rows 16 j .. + 16; lane l
+    // fills row 16 j + l / 4 at 16-byte position l % 4 with its tile (l % 4) ^ ((row / 4) % 4)
+    const uint8_t* zero = g_zero_slice;
+    auto issue_refs = [&](int pass) {
+        const int c = pass >> 1, h = pass & 1, col = n0 + dt::kCols * c;
+        const int wv = wave_id();
+        int sl[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = 16 * (8 * wv + u) + (lane >> 2);
+            sl[u] = sSlot[(r & (dt::TT - 1)) * dt::kRefs + (r >> 7)];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = 8 * wv + u, r = 16 * j + (lane >> 2);
+            const int ts = (lane & 3) ^ ((r >> 2) & 3);
+            const uint8_t* src = sl[u] >= 0 ? reinterpret_cast<const uint8_t*>(pool) + (size_t)sl[u] * W2 + col +
+                                                  16 * chunk_tile<D>(h, ts)
+                                            : zero + 16 * ts;
+            dma16(src, sRef + 1024 * j);
+        }
+    };
+
+    // W_d stages 0 .. NST - 1 (they do not depend on the tokens)
+#pragma unroll
+    for (int x = 0; x < NST; ++x) issue_w(x);
+    token_table<D>(sSlot, sKd, sPos, sRev, idx, m, b, tt0, self_slot, ref_idx, top_k, cap_ref, cap_tok, theta, err);
+    f16x8 zf[2][NKS];
+    latent_frags<NKS, BITS>(zf, idx, m, b, tt0, self_slot, codes, code_bytes, scale, zmin, cap_tok);
+    __syncthreads();
+    if (n0 < dk) rope_table<D>(sRope, sPos, sRev);
+    const MeanForm mf = mean_form(sKd);
+    // the set-up tables in the reference buffer are read; W_d stages 0 .. NST - 1 landed
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    typedef typename Mma<f16_t>::frag Frag;
+    auto read_frags = [&](Frag (&f)[2][4], int x) {
+        const unsigned char* slotp = sW + (x % NST) * dl::kWStage;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int lt = 0; lt < 4; ++lt) f[kh][lt] = Op16<64>::frag<f16_t>(reinterpret_cast<const char*>(slotp), lt, kh);
+    };
+    Frag fa[2][4], fb[2][4];
+    read_frags(fa, 0);
+    // stage 0's fragments are in registers before its slot is refilled
+    lds_barrier();
+
+    f32x4 acc[2][4];
+    int x = 0;  // stage of the run
     for (int c = 0; c < nchunks; ++c) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -352,121 +654,67 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
                 for (int i = 0; i < 4; ++i) acc[gr][i] = zero4();
 #pragma unroll
             for (int k = 0; k < KST; ++k) {
-                // stage x: write stage x + 1 to LDS, fetch stage x + 3 into its registers
-                int du;
-                const int k3 = ahead(k, 3, du);
-                const int c3 = c + ((h + du) >> 1), h3 = (h + du) & 1;
-                if (k % 2 == 0) {
-                    store_w(wb, 1);
-                    load_w(wb, c3, h3, k3);
-                } else {
-                    store_w(wa, 0);
-                    load_w(wa, c3, h3, k3);
-                }
-                const f16_t* W = sW + (k % 2) * (dt::kWBuf / 2);
+                Frag (&cur)[2][4] = (k % 2 == 0) ? fa : fb;
+                Frag (&nxt)[2][4] = (k % 2 == 0) ? fb : fa;
+                // stage x + NST into the slot of stage x (its fragments were read in the
+                // last stage), this pass's reference slices in its first stage
+                issue_w(x + NST);
+                if (k == 0) issue_refs(2 * c + h);
+                __builtin_amdgcn_sched_barrier(0);
+                read_frags(nxt, x + 1);
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh) {
                     const int ks = 2 * k + kh;
-                    typename Mma<f16_t>::frag fw[4];
-#pragma unroll
-                    for (int lt = 0; lt < 4; ++lt)
-                        fw[lt] = lds_frag<f16_t>(W + (16 * lt + mrow) * dt::kWP + 32 * kh + 8 * g);
 #pragma unroll
                     for (int lt = 0; lt < 4; ++lt) {
-                        acc[0][lt] = Mma<f16_t>::step(acc[0][lt], fw[lt], zf[0][ks]);
-                        acc[1][lt] = Mma<f16_t>::step(acc[1][lt], fw[lt], zf[1][ks]);
+                        acc[0][lt] = Mma<f16_t>::step(acc[0][lt], cur[kh][lt], zf[0][ks]);
+                        acc[1][lt] = Mma<f16_t>::step(acc[1][lt], cur[kh][lt], zf[1][ks]);
                     }
                 }
+                // stage x + 2 must have landed (next stage reads its fragments): the loads
+                // issued after it are stages x + 3 .. x + NST and, through the pass's first
+                // NST - 1 stages, this pass's 8 reference loads
+                if (k <= NST - 2) wait_vmcnt<2 * (NST - 2) + 8>();
+                else wait_vmcnt<2 * (NST - 2)>();
                 lds_barrier();
+                ++x;
             }
-
-            // ---- pass (c, h) done: reference mean, RoPE, store
-            if (h == 0) {
-                // this wavefront's reference loads of chunk c have landed once at most the
-                // W_d loads of this pass (2 per stage) are still in flight
-                wait_vmcnt<2 * KST>();
-                lds_barrier();
-            }
+            // ---- pass (c, h) done: its reference slices have landed once at most the
+            // W_d loads issued after them (2 per later stage of the pass) are in flight
+            wait_vmcnt<2 * (KST - 1)>();
+            lds_barrier();
             const int col0 = n0 + dt::kCols * c;
-            const bool rope = col0 < dk;
-#pragma unroll
-            for (int gr = 0; gr < 2; ++gr) {
-                const int tk = 32 * wave + 16 * gr + mrow;
-                f32x4 (&a)[4] = acc[gr];
-#pragma unroll
-                for (int lt = 0; lt < 4; ++lt) {
-                    const int ct = chunk_tile<D>(h, lt);
-                    long v[2];
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int pr = (2 * hh + (g >> 1)) * dt::TT + tk;
-                        v[hh] = *reinterpret_cast<const long*>(sRef + pr * dt::kCols + 16 * (ct ^ (pr & 7)) +
-                                                               8 * (g & 1));
-                    }
-                    if (fused_mean) {
-                        a[lt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(sel, v[0], a[lt], 0, 0, 0);
-                        a[lt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(sel, v[1], a[lt], 0, 0, 0);
-                    } else {
-                        f32x4 sm = zero4();
-                        sm = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(sel, v[0], sm, 0, 0, 0);
-                        sm = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(sel, v[1], sm, 0, 0, 0);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) a[lt][e] += div_small(sm[e], kd[gr], rkd[gr]);
-                    }
-                }
-                const int p = tpos[gr];
-                if (rope) {
-#pragma unroll
-                    for (int lt = 0; lt < 2; ++lt) {
-                        const int jt = D == 128 ? 2 * h + lt : lt;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float cs = rc[gr][4 * jt + e], sn = rsn[gr][4 * jt + e];
-                            const float x1 = a[lt][e], x2 = a[lt + 2][e];
-                            a[lt][e] = x1 * cs - x2 * sn;
-                            a[lt + 2][e] = x2 * cs + x1 * sn;
-                        }
-                    }
-                }
-                const int t = tt0 + tk;
-                if (t < m) {
-                    const bool valid = p >= 0;
-                    OutT* o = out + ((size_t)b * m + t) * W2 + col0 + 4 * g;
-#pragma unroll
-                    for (int lt = 0; lt < 4; ++lt) {
-                        OutT* d = o + 16 * chunk_tile<D>(h, lt);
-                        if (valid) store_row4<OutT>(d, a[lt][0], a[lt][1], a[lt][2], a[lt][3]);
-                        else store_row4<OutT>(d, 0.f, 0.f, 0.f, 0.f);
-                    }
-                }
-            }
-            // both passes are done with this chunk's reference slices: fetch the next
-            if (h == 1 && c + 1 < nchunks) {
-                lds_barrier();
-                issue_refs(c + 1);
-            }
+            if (mf.fused) finish_pass<D, true, OutT>(acc, sRef, sRope, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
+            else finish_pass<D, false, OutT>(acc, sRef, sRope, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
+            // the slices are read: the next pass may refill the buffer
+            lds_barrier();
         }
+    }
+}
+
+// rkv_prepare_decoder: W_d bf16 -> fp16, each 8 latent values in the fragment order
+// 0 4 1 5 2 6 3 7 (the conversion form 1 applies in LDS, so both forms multiply the same
+// operands in the same order).
+__global__ void prepare_decoder_kernel(const uint4* __restrict__ wd, uint4* __restrict__ w16, size_t n8) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n8) {
+        const f16x8 h = w_to_f16(wd[i]);
+        w16[i] = *reinterpret_cast<const uint4*>(&h);
     }
 }
 
 }  // namespace
 
-template <int NKS, int D, int BITS, typename OutT>
-static hipError_t tiles_impl(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
-                             hipStream_t st) {
-    auto kern = decode_tiles_kernel<NKS, D, BITS, OutT>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, dt::bytes);
-    if (e != hipSuccess) return e;
+// Workgroup grid: (token tiles, column groups, batch), one workgroup per CU. The
+// columns are split into groups so that the rounds of workgroups times the chunks per
+// workgroup (plus about half a chunk of set-up each) is smallest.
+static dim3 tiles_grid(const Shape& s, int B, int m, int* ncg_out) {
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
         ncu = 256;
     const int chunks = s.W2 / dt::kCols;
-    const long tiles = (long)((m + dt::TT - 1) / dt::TT) * c.B;
-    // one workgroup per CU: split the columns into groups so that the rounds of
-    // workgroups times the chunks per workgroup (plus about half a chunk of set-up
-    // each) is smallest
+    const long tiles = (long)((m + dt::TT - 1) / dt::TT) * B;
     int best_ncg = chunks;
     double best = 1e30;
     for (int ncg = chunks; ncg >= 1; --ncg) {
@@ -478,50 +726,83 @@ static hipError_t tiles_impl(const Shape& s, const CacheView& c, const int* idx,
             best_ncg = ncg;
         }
     }
-    const int groups = (chunks + best_ncg - 1) / best_ncg;
-    const dim3 grid((unsigned)((m + dt::TT - 1) / dt::TT), (unsigned)groups, (unsigned)c.B);
-    hipLaunchKernelGGL(kern, grid, dim3(dt::kThreads), dt::bytes, st, idx, m, best_ncg,
-                       static_cast<const fp8_t*>(c.ref_vals), c.self_slot, c.ref_idx, c.codes, c.code_bytes,
-                       static_cast<const f16_t*>(c.scale), static_cast<const f16_t*>(c.zmin),
-                       static_cast<const bf16_t*>(wd), s.W2, s.dk, s.top_k, c.cap_ref, c.cap_tok, s.theta,
-                       static_cast<OutT*>(out), c.err);
+    *ncg_out = best_ncg;
+    return dim3((unsigned)((m + dt::TT - 1) / dt::TT), (unsigned)((chunks + best_ncg - 1) / best_ncg), (unsigned)B);
+}
+
+template <int NKS, int D, int BITS, typename OutT>
+static hipError_t tiles_impl(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd,
+                             const void* wd16, void* out, hipStream_t st) {
+    int ncg = 0;
+    const dim3 grid = tiles_grid(s, c.B, m, &ncg);
+    if (wd16) {
+        auto kern = decode_tiles_dl_kernel<NKS, D, BITS, OutT>;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, dl::bytes);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, grid, dim3(dt::kThreads), dl::bytes, st, idx, m, ncg,
+                           static_cast<const fp8_t*>(c.ref_vals), c.self_slot, c.ref_idx, c.codes, c.code_bytes,
+                           static_cast<const f16_t*>(c.scale), static_cast<const f16_t*>(c.zmin),
+                           static_cast<const f16_t*>(wd16), s.W2, s.dk, s.top_k, c.cap_ref, c.cap_tok, s.theta,
+                           static_cast<OutT*>(out), c.err);
+    } else {
+        auto kern = decode_tiles_kernel<NKS, D, BITS, OutT>;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, rr::bytes);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, grid, dim3(dt::kThreads), rr::bytes, st, idx, m, ncg,
+                           static_cast<const fp8_t*>(c.ref_vals), c.self_slot, c.ref_idx, c.codes, c.code_bytes,
+                           static_cast<const f16_t*>(c.scale), static_cast<const f16_t*>(c.zmin),
+                           static_cast<const bf16_t*>(wd), s.W2, s.dk, s.top_k, c.cap_ref, c.cap_tok, s.theta,
+                           static_cast<OutT*>(out), c.err);
+    }
     return hipGetLastError();
 }
 
 template <int D, int BITS, typename OutT>
-static hipError_t tiles_dc(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
-                           hipStream_t st) {
+static hipError_t tiles_dc(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd,
+                           const void* wd16, void* out, hipStream_t st) {
     switch (s.d_c / 32) {
-        case 4: return tiles_impl<4, D, BITS, OutT>(s, c, idx, m, wd, out, st);
-        case 8: return tiles_impl<8, D, BITS, OutT>(s, c, idx, m, wd, out, st);
-        case 12: return tiles_impl<12, D, BITS, OutT>(s, c, idx, m, wd, out, st);
-        case 16: return tiles_impl<16, D, BITS, OutT>(s, c, idx, m, wd, out, st);
+        case 4: return tiles_impl<4, D, BITS, OutT>(s, c, idx, m, wd, wd16, out, st);
+        case 8: return tiles_impl<8, D, BITS, OutT>(s, c, idx, m, wd, wd16, out, st);
+        case 12: return tiles_impl<12, D, BITS, OutT>(s, c, idx, m, wd, wd16, out, st);
+        case 16: return tiles_impl<16, D, BITS, OutT>(s, c, idx, m, wd, wd16, out, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename OutT>
-static hipError_t tiles_d(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
-                          hipStream_t st) {
+static hipError_t tiles_d(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd,
+                          const void* wd16, void* out, hipStream_t st) {
     if (s.D == 64) {
-        if (s.bits == 4) return tiles_dc<64, 4, OutT>(s, c, idx, m, wd, out, st);
-        return tiles_dc<64, 2, OutT>(s, c, idx, m, wd, out, st);
+        if (s.bits == 4) return tiles_dc<64, 4, OutT>(s, c, idx, m, wd, wd16, out, st);
+        return tiles_dc<64, 2, OutT>(s, c, idx, m, wd, wd16, out, st);
     }
-    if (s.bits == 4) return tiles_dc<128, 4, OutT>(s, c, idx, m, wd, out, st);
-    return tiles_dc<128, 2, OutT>(s, c, idx, m, wd, out, st);
+    if (s.bits == 4) return tiles_dc<128, 4, OutT>(s, c, idx, m, wd, wd16, out, st);
+    return tiles_dc<128, 2, OutT>(s, c, idx, m, wd, wd16, out, st);
 }
 
 bool decode_tiles_supported(const Shape& s) {
     return !s.f32 && (s.bits == 4 || s.bits == 2) && s.group == 32 && (s.D == 64 || s.D == 128) &&
-           s.dk % dt::kCols == 0 &&
-           s.W2 % dt::kCols == 0 && s.d_c % 128 == 0 && s.d_c <= 512 && s.top_k <= dt::kRefs;
+           s.dk % dt::kCols == 0 && s.W2 % dt::kCols == 0 && s.d_c % 128 == 0 && s.d_c <= 512 &&
+           s.top_k <= dt::kRefs;
 }
 
-hipError_t launch_decode_tiles(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
-                               int out_dtype, hipStream_t st) {
+hipError_t launch_decode_tiles(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd,
+                               const void* wd16, void* out, int out_dtype, hipStream_t st) {
     if (m <= 0) return hipSuccess;
-    if (out_dtype == RKV_F32) return tiles_d<float>(s, c, idx, m, wd, out, st);
-    return tiles_d<bf16_t>(s, c, idx, m, wd, out, st);
+    if (out_dtype == RKV_F32) return tiles_d<float>(s, c, idx, m, wd, wd16, out, st);
+    return tiles_d<bf16_t>(s, c, idx, m, wd, wd16, out, st);
+}
+
+hipError_t launch_prepare_decoder(const Shape& s, const void* wd, void* wd16, hipStream_t st) {
+    const size_t n8 = (size_t)s.W2 * s.d_c / 8;
+    if (n8 == 0) return hipSuccess;
+    const unsigned threads = 256;
+    const size_t blocks = (n8 + threads - 1) / threads;
+    hipLaunchKernelGGL(prepare_decoder_kernel, dim3((unsigned)blocks), dim3(threads), 0, st,
+                       static_cast<const uint4*>(wd), static_cast<uint4*>(wd16), n8);
+    return hipGetLastError();
 }
 
 }  // namespace rkv

@@ -56,12 +56,15 @@ hipError_t launch_swiglu(const Shape& s, const CacheView& c, const EncodePlan& p
 hipError_t launch_latent_quant(const Shape& s, const CacheView& c, const EncodePlan& p, const int* pos, int n,
                                const void* w3, void* ws, hipStream_t st);
 
-hipError_t launch_decode(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
-                         int out_dtype, hipStream_t st);
+// wd16: the prepared fp16 W_d (launch_prepare_decoder) or null
+hipError_t launch_decode(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, const void* wd16,
+                         void* out, int out_dtype, hipStream_t st);
 
 // Token-tile restore (bf16 formats with INT4 / INT2 codes).
 bool decode_tiles_supported(const Shape& s);
-hipError_t launch_decode_tiles(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd, void* out,
-                               int out_dtype, hipStream_t st);
+hipError_t launch_decode_tiles(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd,
+                               const void* wd16, void* out, int out_dtype, hipStream_t st);
+// W_d (bf16, [2 d_k][d_c]) -> the fp16 form the token-tile restore reads by direct loads
+hipError_t launch_prepare_decoder(const Shape& s, const void* wd, void* wd16, hipStream_t st);
 
 }  // namespace rkv

@@ -57,8 +57,15 @@ class GpuCodec:
         B.rkv_append_ref(self.cfg, self.cache, kv_dev, refp.repeat(Bn, 1), refp.repeat(Bn, 1))
         return B.rkv_encode(self.cfg, self.W, self.cache, kv_dev, encp.repeat(Bn, 1), encp.repeat(Bn, 1), ws)
 
-    def decode(self, idx: np.ndarray, out_dtype=torch.float32) -> np.ndarray:
+    def decode(self, idx: np.ndarray, out_dtype=torch.float32, prepared: bool = False) -> np.ndarray:
+        """Restore through the C ABI; prepared=True supplies the prepared fp16 decoder
+        (rkv_prepare_decoder) when the configuration has one."""
         idx_t = torch.from_numpy(np.asarray(idx, dtype=np.int32)).to(self.device)
+        if prepared and self.cfg.mode == "bf16":
+            if self.W.w_d_f16 is None:
+                self.W.prepare_decoder(self.cfg)
+        else:
+            self.W.drop_prepared_decoder()
         out = B.rkv_decode_selected(self.cfg, self.W, self.cache, idx_t.reshape(self.batch, -1), out_dtype=out_dtype)
         torch.cuda.synchronize()
         return out.float().cpu().numpy()

@@ -34,7 +34,16 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(B.EXPORTED)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.rkv_abi_version() == 1
+    assert lib.rkv_abi_version() == 2
+
+
+def test_prepared_decoder_bytes(lib):
+    for wid in (2, 4):
+        cfg = B.CodecConfig.from_workload(workload(wid))
+        assert B.rkv_prepared_decoder_bytes(cfg) == 2 * cfg.two_dk * cfg.d_c
+    f32 = B.CodecConfig.from_workload(workload(1))
+    assert B.rkv_prepared_decoder_bytes(f32) == 0
+    assert lib.rkv_prepare_decoder(ctypes.byref(f32.c_struct()), None, None, None) in (-1, -2)
 
 
 def test_status_strings(lib):
@@ -117,6 +126,15 @@ def test_entry_points_reject_bad_arguments_on_host(lib):
     for f in ("ref_vals", "ref_pos", "ref_norm2", "ref_count", "codes", "scale", "zmin", "ref_idx", "self_slot"):
         setattr(cache, f, fake)
     w = B._Weights(fake, fake, fake, fake)
+    # the prepared decoder ("bf16" formats only): argument checks; a misaligned prepared
+    # copy is refused by the restore
+    c2 = B.CodecConfig.from_workload(workload(2)).c_struct()
+    assert lib.rkv_prepare_decoder(ctypes.byref(c), ctypes.byref(w), fake, None) == -2
+    assert lib.rkv_prepare_decoder(ctypes.byref(c2), None, fake, None) == -1
+    assert lib.rkv_prepare_decoder(ctypes.byref(c2), ctypes.byref(w), None, None) == -1
+    assert lib.rkv_prepare_decoder(ctypes.byref(c2), ctypes.byref(w), fake + 8, None) == -4
+    wp = B._Weights(fake, fake, fake, fake, fake + 8)
+    assert lib.rkv_decode_selected(ctypes.byref(c2), ctypes.byref(wp), ctypes.byref(cache), fake, 4, fake, 1, None) == -4
     # negative sizes
     assert lib.rkv_encode(ctypes.byref(c), ctypes.byref(w), ctypes.byref(cache), fake, 4, fake, fake, -1, fake, 1 << 30, None) == -1
     assert lib.rkv_decode_selected(ctypes.byref(c), ctypes.byref(w), ctypes.byref(cache), fake, -2, fake, 0, None) == -1

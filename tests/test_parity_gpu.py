@@ -109,6 +109,9 @@ def test_pipeline_parity(case):
     sel = np.stack([wl.make_selected(T, seq=b) for b in range(wl.batch)]).astype(np.int32)
     out_all = gpu.decode(np.tile(np.arange(T, dtype=np.int32), (wl.batch, 1)))
     out_sel = gpu.decode(sel)
+    # the prepared decoder (rkv_prepare_decoder) gives the same bits
+    assert np.array_equal(gpu.decode(np.tile(np.arange(T, dtype=np.int32), (wl.batch, 1)), prepared=True), out_all)
+    assert np.array_equal(gpu.decode(sel, prepared=True), out_sel)
     for b in range(wl.batch):
         orc = codec.prefill(kvs[b], wl.stride, cap_ref=gpu.cap_ref)
         gpc = mirror_cache(codec, gpu, b)
@@ -141,10 +144,11 @@ def test_bf16_output_is_rounded_fp32_output():
     gpu = GpuCodec(wl, wl.make_weights())
     gpu.prefill(gpu.to_dev(wl.make_kv()[None]), wl.T)
     idx = np.arange(wl.T, dtype=np.int32)[None]
-    f = gpu.decode(idx, torch.float32)
-    h = gpu.decode(idx, torch.bfloat16)
-    want = torch.from_numpy(f).to(torch.bfloat16).float().numpy()
-    assert np.array_equal(h.view(np.uint32), want.view(np.uint32))
+    for prepared in (False, True):
+        f = gpu.decode(idx, torch.float32, prepared=prepared)
+        h = gpu.decode(idx, torch.bfloat16, prepared=prepared)
+        want = torch.from_numpy(f).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(h.view(np.uint32), want.view(np.uint32))
 
 
 def test_streaming_equals_bulk_and_is_deterministic():
@@ -255,5 +259,6 @@ def test_full_size_sampled(wid):
     sel = np.sort(np.concatenate([sample, rng.choice(refp, 8, replace=False)]))
     out = gpu.decode(sel[None].astype(np.int32))
     assert_kv_ok(out[0], codec.decode_selected(gpc, sel), "full-size decode on gpu records")
+    assert np.array_equal(gpu.decode(sel[None].astype(np.int32), prepared=True), out)
     ma, rr, nd = assert_end_to_end(codec, out[0], orc, gpc, sel, "full-size end to end")
     print(f"[parity] full wid={wid}: end-to-end max_abs={ma:.3g} rms_rel={rr:.3g} code-diff tokens={nd}", flush=True)
