@@ -43,7 +43,7 @@ KERNEL_NAMES = {
     "select": "select_kernel",
     "compress": "swiglu_ring_kernel",
     "quantize": "latent_quant_ring_kernel",
-    "decode": "decode_tiles_kernel",
+    "decode": "decode_tiles_dl_kernel",
 }
 
 

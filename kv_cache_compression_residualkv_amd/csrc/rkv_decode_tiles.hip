@@ -577,38 +577,42 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
     const int tt0 = blockIdx.x * dt::TT;
     const int n0 = blockIdx.y * ncg * dt::kCols;
     const int nchunks = min(ncg, (W2 - n0) / dt::kCols);
-    const int nst = 2 * nchunks * KST;  // stages of the run
     const fp8_t* pool = ref_vals + (size_t)b * cap_ref * W2;
 
-    // stage x -> slot x % NST. Wave w fills blocks w and w + 4 (block 2 lt + kh: row group
-    // lt = local MFMA tile, K half kh); lane l fetches row l / 4, chunk swz(l / 4, l % 4).
-    auto issue_w = [&](int x) {
-        const int xs = min(x, nst - 1);  // past the end: any readable stage (never used)
-        const int pass = xs / KST, k = xs - pass * KST, c = pass >> 1, h = pass & 1;
-        const int wv = wave_id(), r = lane >> 2;
-        unsigned char* dst = sW + (x % NST) * dl::kWStage;
+    // stage (c, h, k) -> slot ((2 c + h) KST + k) % NST. Wave w fills blocks w and w + 4
+    // (block 2 lt + kh: row group lt = local MFMA tile, K half kh); lane l fetches row
+    // l / 4, chunk swz(l / 4, l % 4). rowoff[h][u]: the lane's output column in pass h.
+    const int wv = wave_id(), lr = lane >> 2;
+    int rowoff[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) rowoff[h][u] = 16 * chunk_tile<D>(h, (wv + 4 * u) >> 1) + lr;
+    const f16_t* wbase = w16 + (size_t)n0 * d_c + 8 * swz(lr, lane & 3);
+    auto issue_w = [&](int c, int h, int k, int slot) {
+        c = min(c, nchunks - 1);  // past the end: any readable stage (never used)
+        unsigned char* dst = sW + slot * dl::kWStage;
+        const f16_t* src = wbase + (size_t)dt::kCols * c * d_c + k * kStageK;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int blk = wv + 4 * u, lt = blk >> 1, kh = blk & 1;
-            const int col = n0 + dt::kCols * c + 16 * chunk_tile<D>(h, lt) + r;
-            dma16(w16 + (size_t)col * d_c + k * kStageK + 32 * kh + 8 * swz(r, lane & 3), dst + 1024 * blk);
+            const int blk = wv + 4 * u;
+            dma16(src + (size_t)rowoff[h][u] * d_c + 32 * (blk & 1), dst + 1024 * blk);
         }
     };
     // slices of pass p: DMA j (wave w issues 8 w .. + 8) fills rows 16 j .. + 16; lane l
     // fills row 16 j + l / 4 at 16-byte position l % 4 with its tile (l % 4) ^ ((row / 4) % 4)
     const uint8_t* zero = g_zero_slice;
-    auto issue_refs = [&](int pass) {
-        const int c = pass >> 1, h = pass & 1, col = n0 + dt::kCols * c;
-        const int wv = wave_id();
+    auto issue_refs = [&](int c, int h) {
+        const int col = n0 + dt::kCols * c;
         int sl[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int r = 16 * (8 * wv + u) + (lane >> 2);
+            const int r = 16 * (8 * wv + u) + lr;
             sl[u] = sSlot[(r & (dt::TT - 1)) * dt::kRefs + (r >> 7)];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int j = 8 * wv + u, r = 16 * j + (lane >> 2);
+            const int j = 8 * wv + u, r = 16 * j + lr;
             const int ts = (lane & 3) ^ ((r >> 2) & 3);
             const uint8_t* src = sl[u] >= 0 ? reinterpret_cast<const uint8_t*>(pool) + (size_t)sl[u] * W2 + col +
                                                   16 * chunk_tile<D>(h, ts)
@@ -616,10 +620,21 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
             dma16(src, sRef + 1024 * j);
         }
     };
+    // stage (c, h, k) + d of the run
+    auto ahead = [](int c, int h, int k, int d, int& c2, int& h2) {
+        const int du = (k + d) / KST;
+        c2 = c + ((h + du) >> 1);
+        h2 = (h + du) & 1;
+        return (k + d) % KST;
+    };
 
     // W_d stages 0 .. NST - 1 (they do not depend on the tokens)
 #pragma unroll
-    for (int x = 0; x < NST; ++x) issue_w(x);
+    for (int d = 0; d < NST; ++d) {
+        int c2, h2;
+        const int k2 = ahead(0, 0, 0, d, c2, h2);
+        issue_w(c2, h2, k2, d);
+    }
     token_table<D>(sSlot, sKd, sPos, sRev, idx, m, b, tt0, self_slot, ref_idx, top_k, cap_ref, cap_tok, theta, err);
     f16x8 zf[2][NKS];
     latent_frags<NKS, BITS>(zf, idx, m, b, tt0, self_slot, codes, code_bytes, scale, zmin, cap_tok);
@@ -630,21 +645,32 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
     wait_vmcnt<0>();
     __syncthreads();
 
+    // one K-step of W_d fragments (4 tiles)
     typedef typename Mma<f16_t>::frag Frag;
-    auto read_frags = [&](Frag (&f)[2][4], int x) {
-        const unsigned char* slotp = sW + (x % NST) * dl::kWStage;
+    auto read_frags = [&](Frag (&f)[4], int slot, int kh) {
+        const char* sp = reinterpret_cast<const char*>(sW + slot * dl::kWStage);
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int lt = 0; lt < 4; ++lt) f[kh][lt] = Op16<64>::frag<f16_t>(reinterpret_cast<const char*>(slotp), lt, kh);
+        for (int lt = 0; lt < 4; ++lt) f[lt] = Op16<64>::frag<f16_t>(sp, lt, kh);
     };
-    Frag fa[2][4], fb[2][4];
-    read_frags(fa, 0);
-    // stage 0's fragments are in registers before its slot is refilled
-    lds_barrier();
+    auto mma = [&](f32x4 (&acc)[2][4], const Frag (&f)[4], int ks) {
+#pragma unroll
+        for (int lt = 0; lt < 4; ++lt) {
+            acc[0][lt] = Mma<f16_t>::step(acc[0][lt], f[lt], zf[0][ks]);
+            acc[1][lt] = Mma<f16_t>::step(acc[1][lt], f[lt], zf[1][ks]);
+        }
+    };
+    // Per stage x (K-steps 0 and 1, fragments f0 and f1):
+    //   read f1(x) | MFMA f0(x) | wait stage x + 1, barrier | read f0(x + 1) | MFMA f1(x) |
+    //   f0(x + 1) in registers, then refill slot x with stage x + NST (and, in a pass's
+    //   first stage, fetch its reference slices).
+    // The direct loads go out right after an explicit wait on the fragment reads: the
+    // compiler treats a pending direct load as an access to both LDS and memory and turns
+    // its next wait on LDS reads into a full one, so none of its waits may fall behind one.
+    Frag f0[4], f1[4];
+    read_frags(f0, 0, 0);
+    int slot = 0;
 
     f32x4 acc[2][4];
-    int x = 0;  // stage of the run
     for (int c = 0; c < nchunks; ++c) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -654,30 +680,32 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
                 for (int i = 0; i < 4; ++i) acc[gr][i] = zero4();
 #pragma unroll
             for (int k = 0; k < KST; ++k) {
-                Frag (&cur)[2][4] = (k % 2 == 0) ? fa : fb;
-                Frag (&nxt)[2][4] = (k % 2 == 0) ? fb : fa;
-                // stage x + NST into the slot of stage x (its fragments were read in the
-                // last stage), this pass's reference slices in its first stage
-                issue_w(x + NST);
-                if (k == 0) issue_refs(2 * c + h);
+                read_frags(f1, slot, 1);
+                mma(acc, f0, 2 * k);
+                // the four fragment reads go out before the eight MFMAs that cover them
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
                 __builtin_amdgcn_sched_barrier(0);
-                read_frags(nxt, x + 1);
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh) {
-                    const int ks = 2 * k + kh;
-#pragma unroll
-                    for (int lt = 0; lt < 4; ++lt) {
-                        acc[0][lt] = Mma<f16_t>::step(acc[0][lt], cur[kh][lt], zf[0][ks]);
-                        acc[1][lt] = Mma<f16_t>::step(acc[1][lt], cur[kh][lt], zf[1][ks]);
-                    }
-                }
-                // stage x + 2 must have landed (next stage reads its fragments): the loads
-                // issued after it are stages x + 3 .. x + NST and, through the pass's first
-                // NST - 1 stages, this pass's 8 reference loads
-                if (k <= NST - 2) wait_vmcnt<2 * (NST - 2) + 8>();
+                // stage x + 1 must have landed: the loads issued after it are stages x + 2 ..
+                // x + NST - 1 and, from the pass's second stage on, its 8 reference loads
+                if (k >= 1 && k <= NST - 1) wait_vmcnt<2 * (NST - 2) + 8>();
                 else wait_vmcnt<2 * (NST - 2)>();
                 lds_barrier();
-                ++x;
+                const int next = slot + 1 == NST ? 0 : slot + 1;
+                read_frags(f0, next, 0);
+                mma(acc, f1, 2 * k + 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_lgkm0();
+                {
+                    int c2, h2;
+                    const int k2 = ahead(c, h, k, NST, c2, h2);
+                    issue_w(c2, h2, k2, slot);
+                }
+                if (k == 0) issue_refs(c, h);
+                __builtin_amdgcn_sched_barrier(0);
+                slot = next;
             }
             // ---- pass (c, h) done: its reference slices have landed once at most the
             // W_d loads issued after them (2 per later stage of the pass) are in flight
