@@ -25,6 +25,17 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// LDS reads in kernels that also have global->LDS direct loads in flight go through
+// these native vector types: a read through HIP's struct vector types (uint2, int4,
+// float4, ...) makes the compiler wait for every outstanding direct load first.
+template <typename V>
+__device__ inline V lds_load(const void* p) {
+    return *reinterpret_cast<const V*>(p);
+}
 
 // storage tag for OCP FP8 e4m3fn bytes
 struct fp8_t {

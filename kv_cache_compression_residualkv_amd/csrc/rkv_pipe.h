@@ -111,7 +111,8 @@ struct Op8 {
     // raw FP8 fragment of row group g, K step ks: K values 32 ks + 8 (lane / 16) .. +8
     static __device__ inline uint2 frag_raw(const char* slot, int g, int ks) {
         const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
-        return *reinterpret_cast<const uint2*>(slot + 1024 * g + 64 * r + 16 * swz(r, 2 * ks + (q >> 1)) + 8 * (q & 1));
+        const u32x2 v = lds_load<u32x2>(slot + 1024 * g + 64 * r + 16 * swz(r, 2 * ks + (q >> 1)) + 8 * (q & 1));
+        return make_uint2(v.x, v.y);
     }
     // exact widening of a raw fragment to bf16
     static __device__ inline bf16x8 widen(uint2 v) {

@@ -279,7 +279,7 @@ namespace s2 {
 constexpr int kThreads = 512;  // 8 wavefronts: 2 slot halves x 4 token quarters
 constexpr int BM = 256;        // pool slots per block
 constexpr int BN = kTok;       // tokens per tile
-constexpr int NST = 2;         // LDS ring stages
+constexpr int NST = 4;         // LDS ring stages
 constexpr int kStageA = BM * kStageK;      // FP8 pool stage bytes
 constexpr int kStageB = BN * kStageK * 2;  // bf16 token stage bytes
 constexpr int kRing = NST * (kStageA + kStageB);
@@ -523,10 +523,10 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int i = 2 * g + h;
-                        const int4 p4 = *reinterpret_cast<const int4*>(m_pos + lb + 16 * i);
-                        const float4 n4 = *reinterpret_cast<const float4*>(m_nrm + lb + 16 * i);
-                        const int pe[4] = {p4.x, p4.y, p4.z, p4.w};
-                        const float ne[4] = {n4.x, n4.y, n4.z, n4.w};
+                        const i32x4 p4 = lds_load<i32x4>(m_pos + lb + 16 * i);
+                        const f32x4 n4 = lds_load<f32x4>(m_nrm + lb + 16 * i);
+                        const int pe[4] = {p4[0], p4[1], p4[2], p4[3]};
+                        const float ne[4] = {n4[0], n4[1], n4[2], n4[3]};
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             gk[4 * h + e] = pe[e] < tokpos_l[j] ? score_key(fmaf(-2.f, a[i][j][e], ne[e]), base + 16 * i + e)
