@@ -275,21 +275,31 @@ __global__ __launch_bounds__(kThreads) void search_kernel(
 
 // ------------------------------------------------------------------ bf16 / FP8 search
 
+// Workgroup of 8 wavefronts: wavefront w owns pool slots 64 (w % 4) .. +64 of each
+// block and tokens 64 (w / 4) .. +64 of the tile, as 2 x 2 output tiles of one
+// v_mfma_f32_32x32x16_bf16 each. Every lane then holds 2 tokens x 32 slots of a block,
+// and every FP8 pool value is widened by two wavefronts (not four, as with 16-row
+// tiles) at the same LDS read traffic.
 namespace s2 {
-constexpr int kThreads = 512;  // 8 wavefronts: 2 slot halves x 4 token quarters
-constexpr int BM = 256;        // pool slots per block
-constexpr int BN = kTok;       // tokens per tile
-constexpr int NST = 4;         // LDS ring stages
+constexpr int kThreads = 512;
+constexpr int BM = 256;                    // pool slots per block
+constexpr int BN = kTok;                   // tokens per tile
+constexpr int NST = 4;                     // LDS ring stages
 constexpr int kStageA = BM * kStageK;      // FP8 pool stage bytes
 constexpr int kStageB = BN * kStageK * 2;  // bf16 token stage bytes
-constexpr int kRing = NST * (kStageA + kStageB);
-constexpr int kMeta = BM * 8;              // positions + norms of one pool block
+constexpr int kSlot = kStageA + kStageB;
+constexpr int kRing = NST * kSlot;
+constexpr int kMeta = BM * 8;              // positions, then norms, of one pool block
+constexpr int kMetaBufs = 4;               // blocks whose metadata may be resident
 constexpr int kMerge = kTok * 8 * kTop * 8;  // 8 lists of 8 keys per token
 constexpr int kOffMeta = kRing;
-constexpr int kOffRed = kOffMeta + kMeta;
+constexpr int kOffRed = kOffMeta + kMetaBufs * kMeta;
 constexpr int kMain = kOffRed + 64;
 constexpr size_t bytes = (size_t)(kMain > kMerge ? kMain : kMerge);
 static_assert(bytes <= 160 * 1024, "LDS budget");
+constexpr int kLoadsA = BM / 16 / 8;       // 1 KB pool blocks per wavefront and stage
+constexpr int kLoadsB = BN / 8 / 8;        // 1 KB token blocks per wavefront and stage
+constexpr int kPer = kLoadsA + kLoadsB;    // direct loads per wavefront and stage (+1 with metadata)
 }  // namespace s2
 
 // A candidate as one 64-bit key: the score's bits mapped to an order-preserving
@@ -340,48 +350,44 @@ __device__ inline void merge8(uint64_t (&a)[8], const uint64_t (&b)[8]) {
 #undef RKV_C
 }
 
-// FP8 pool operand (8 wavefronts, 2 block loads each): stage s covers pool block
-// blk0 + s / nk, K columns (s % nk) * 64. Rows past the pool's capacity are clamped
-// (their candidates are masked by position).
-struct PoolOp {
-    static constexpr int kLoads = s2::BM / 16 / 8;
-    static constexpr int kStageBytes = s2::kStageA;
-    const char* pool;  // batch's pool base
-    int W2, nk, blk0, cap;
-    __device__ inline void issue(int s, char* slot) const {
-        const int lane = threadIdx.x & 63, wave = wave_id();
-        const int blk = blk0 + s / nk, kc = s - (s / nk) * nk;
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) {
-            const int g = wave + 8 * u;
-            const int r = min(blk * s2::BM + 16 * g + (lane >> 2), cap - 1);
-            dma16(pool + (size_t)r * W2 + kc * kStageK + 16 * swz(lane >> 2, lane & 3), slot + 1024 * g);
-        }
-    }
-};
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// bf16 token operand (8 wavefronts, 2 block loads each): the same 128 rows for every
-// pool block; load u of wave w fills block (w + 8 u) = 2 g + h.
-struct TokOp {
-    static constexpr int kLoads = s2::BN / 8 / 8;
-    static constexpr int kStageBytes = s2::kStageB;
-    const char* src[kLoads];
-    int nk;
-    __device__ inline void issue(int s, char* slot) const {
-        const int wave = wave_id();
-        const int kc = s - (s / nk) * nk;
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) dma16(src[u] + (size_t)kc * (kStageK * 2), slot + 1024 * (wave + 8 * u));
-    }
-};
+// 4-byte direct load (lane l lands at byte 4 l of the LDS destination)
+__device__ inline void dma4(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (RKV_LDS void*)lds, 4, 0, 0);
+}
 
+// Eight FP8 values (two words) widened exactly to bf16
+__device__ inline bf16x8 widen8(uint32_t x, uint32_t y) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)y, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)y, 1.0f, true);
+    bf16x8 f;
+    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+    f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+    return f;
+}
+
+// LDS layout of a ring slot: the FP8 pool stage (256 rows x 64 K bytes) as 16 blocks of
+// 16 rows at a 64-byte pitch, the 16-byte granule m of row r at position m ^ h(r); the
+// bf16 token stage (128 rows x 64 K) as 16 blocks (row group g, K half q) = 2 g + q,
+// the 8-value chunk c at position c ^ h(r). One direct load fills one block, four
+// consecutive lanes fetching one contiguous 64-byte row segment.
+//
+// Fragments. A K-half p (32 K values) of a stage is consumed by two MFMAs (sub-steps
+// e = 0, 1). Lanes 0-31 supply K values 32 p + 8 e .. +8 and lanes 32-63 supply
+// 32 p + 16 + 8 e .. +8, in both operands (one consistent assignment of K to MFMA
+// slots, so the products are unchanged). A lane therefore reads its pool row's whole
+// granule 2 p + (lane / 32) once (one 16-byte read, both sub-steps), and its token
+// row's chunk 4 p + 2 (lane / 32) + e per sub-step; every 16 lanes of a read cover all
+// 64 LDS banks once.
 struct SFrag {
-    uint2 a[8];   // the wave's 8 pool row groups (raw FP8, widened at the MFMA)
-    bf16x8 b[2];  // the wave's 2 token row groups
+    u32x4 a[2];    // the wavefront's 2 pool row tiles (raw FP8, 16 K values)
+    bf16x8 b[2][2];  // [token tile][sub-step]
 };
 
 // grid: (8 * per, batch) blocks over logical tiles (token tile, chunk), chunks fastest.
-// Wave w: slot half ws = w / 4 (rows 128 ws ..), token quarter wt = w % 4 (32 wt ..).
 template <typename KvT>
 __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
     const KvT* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
@@ -400,7 +406,7 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
     const int tile = x + 8 * (tiles_x - 1 - tl);
     const int b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int ws = wave >> 2, wt = wave & 3;
+    const int wq = wave & 3, wh = wave >> 2, hl = lane >> 5, l32 = lane & 31;
     const int t0 = tile * kTok;
     const int count = max(0, min(ref_count[b], cap_ref));
     const int* rp = ref_pos + (size_t)b * cap_ref;
@@ -409,9 +415,9 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
 
     int tokpos_l[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int t = t0 + 32 * wt + 16 * j + (lane & 15);
-        tokpos_l[j] = (t < n) ? pos[(size_t)b * n + t] : INT_MIN;
+    for (int tt = 0; tt < 2; ++tt) {
+        const int t = t0 + 64 * wh + 32 * tt + l32;
+        tokpos_l[tt] = (t < n) ? pos[(size_t)b * n + t] : INT_MIN;
     }
     // largest position of the tile, then the pool blocks whose first slot precedes it
     {
@@ -446,123 +452,220 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
         for (int j = 0; j < kTop; ++j) lk[q][j] = kNoKey;
 
     if (blk1 > blk0) {
-        PoolOp pa;
-        pa.pool = reinterpret_cast<const char*>(ref_vals + (size_t)b * cap_ref * W2);
-        pa.W2 = W2;
-        pa.nk = nk;
-        pa.blk0 = blk0;
-        pa.cap = cap_ref;
-        TokOp pb;
-        pb.nk = nk;
+        const int wv = wave_id();
+        const char* pool = reinterpret_cast<const char*>(ref_vals + (size_t)b * cap_ref * W2);
+        // pool loads: load u of wave w fills block w + 8 u (rows 16 (w + 8 u) ..), lane ->
+        // row lane / 4 of it, granule position lane % 4
+        int rowa[s2::kLoadsA];
+        int cha[s2::kLoadsA];
 #pragma unroll
-        for (int u = 0; u < TokOp::kLoads; ++u) {
-            const int blk = wave + 8 * u;
+        for (int u = 0; u < s2::kLoadsA; ++u) {
+            rowa[u] = 16 * (wv + 8 * u) + (lane >> 2);
+            cha[u] = 16 * swz(lane >> 2, lane & 3);
+        }
+        // token loads: load u of wave w fills block w + 8 u = 2 g + q
+        const char* srcb[s2::kLoadsB];
+#pragma unroll
+        for (int u = 0; u < s2::kLoadsB; ++u) {
+            const int blk = wv + 8 * u;
             const int r = 16 * (blk >> 1) + (lane >> 2);
             const int t = min(t0 + r, n - 1);
             int kr = rows[(size_t)b * n + t];
             kr = (kr >= 0 && kr < kv_len) ? kr : 0;
-            pb.src[u] = reinterpret_cast<const char*>(kv + ((size_t)b * kv_len + kr) * W2) + 64 * (blk & 1) +
-                        16 * swz(lane >> 2, lane & 3);
+            srcb[u] = reinterpret_cast<const char*>(kv + ((size_t)b * kv_len + kr) * W2) + 64 * (blk & 1) +
+                      16 * swz(lane >> 2, lane & 3);
         }
-        int* m_pos = reinterpret_cast<int*>(smem + s2::kOffMeta);
-        float* m_nrm = reinterpret_cast<float*>(smem + s2::kOffMeta + s2::BM * 4);
-        // positions and norms of a block's slots, thread t < 256 <-> slot t, one block ahead
-        int mp_next = INT_MAX;
-        float mn_next = 0.f;
-        auto fetch_meta = [&](int blk) {
-            const int sl = blk * s2::BM + tid;
-            const bool ok = tid < s2::BM && sl < count;
-            mp_next = ok ? rp[sl] : INT_MAX;
-            mn_next = ok ? rn[sl] : 0.f;
-        };
-        fetch_meta(blk0);
+        // metadata loads (stage 0 of each block): waves 0-3 positions, 4-7 norms, 64 slots each
+        const int msl = 64 * (wv & 3) + lane;
+        const char* msrc = (wv < 4) ? reinterpret_cast<const char*>(rp) : reinterpret_cast<const char*>(rn);
+        const int moff = (wv < 4 ? 0 : 1024) + 256 * (wv & 3);
 
-        f32x4 acc[8][2];
+        // issue cursor: next stage to load (block ib relative to blk0, K stage ik, ring slot is)
+        int ib = 0, ik = 0, is = 0;
+        const char* arow[s2::kLoadsA];
+        auto set_block = [&](int bi) {
+            const int base = (blk0 + bi) * s2::BM;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = zero4();
-
-        auto load = [&](SFrag& f, const char* sa, const char* sb, int ks) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) f.b[j] = Op16<s2::BN>::template frag<bf16_t>(sb, 2 * wt + j, ks);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) f.a[i] = Op8<s2::BM>::frag_raw(sa, 8 * ws + i, ks);
+            for (int u = 0; u < s2::kLoadsA; ++u)
+                arow[u] = pool + (size_t)min(base + rowa[u], cap_ref - 1) * W2 + cha[u];
         };
-        auto mma = [&](const SFrag& f, f32x4(&c)[8][2]) {
+        set_block(0);
+        auto issue = [&]() {
+            char* sl = smem + is * s2::kSlot;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const bf16x8 fa = Op8<s2::BM>::widen(f.a[i]);
+            for (int u = 0; u < s2::kLoadsA; ++u) dma16(arow[u] + ik * kStageK, sl + 1024 * (wv + 8 * u));
 #pragma unroll
-                for (int j = 0; j < 2; ++j) c[i][j] = Mma<bf16_t>::step(c[i][j], fa, f.b[j]);
+            for (int u = 0; u < s2::kLoadsB; ++u)
+                dma16(srcb[u] + (size_t)ik * (kStageK * 2), sl + s2::kStageA + 1024 * (wv + 8 * u));
+            if (ik == 0) {
+                const int sl_m = min((blk0 + ib) * s2::BM + msl, cap_ref - 1);
+                dma4(msrc + 4 * (size_t)sl_m, smem + s2::kOffMeta + (ib & (s2::kMetaBufs - 1)) * s2::kMeta + moff);
+            }
+            is = is + 1 == s2::NST ? 0 : is + 1;
+            if (++ik == nk) {
+                ik = 0;
+                ++ib;
+                set_block(ib);
             }
         };
-        // lane's slots in a block: 128 ws + 16 i + 4 (lane / 16) + e
-        const int lb = 128 * ws + 4 * (lane >> 4);
-        auto fold = [&](int bi, f32x4(&a)[8][2], bool last) {
+
+        f32x16 acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+        // fragment reads of K half p of the stage in ring slot sl
+        auto load = [&](SFrag& f, int sl, int p) {
+            const char* sa = smem + sl * s2::kSlot;
+            const char* sb = sa + s2::kStageA;
+            const int r = l32 & 15;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int g = 4 * wq + 2 * st + (l32 >> 4);
+                f.a[st] = lds_load<u32x4>(sa + 1024 * g + 64 * r + 16 * swz(r, 2 * p + hl));
+            }
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int g = 4 * wh + 2 * tt + (l32 >> 4);
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    f.b[tt][e] = lds_load<bf16x8>(sb + 1024 * (2 * g + p) + 64 * r + 16 * swz(r, 2 * hl + e));
+            }
+        };
+        auto mma = [&](const SFrag& f) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    const bf16x8 wa = widen8(f.a[st][2 * e], f.a[st][2 * e + 1]);
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+                        acc[st][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, f.b[tt][e], acc[st][tt], 0, 0, 0);
+                }
+        };
+        // lane's slots of a block: 64 wq + 32 st + 8 i + 4 hl + j (accumulator element 4 i + j)
+        auto fold = [&](int bi) {
             const int blk = blk0 + bi;
-            // publish this block's slot metadata, fetch the next block's
-            if (tid < s2::BM) {
-                m_pos[tid] = mp_next;
-                m_nrm[tid] = mn_next;
-            }
-            if (blk + 1 < blk1) fetch_meta(blk + 1);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            wait_lgkm0();
-            __builtin_amdgcn_s_barrier();
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const int base = blk * s2::BM + lb;
+            const char* mb = smem + s2::kOffMeta + (bi & (s2::kMetaBufs - 1)) * s2::kMeta;
+            const int* m_pos = reinterpret_cast<const int*>(mb);
+            const float* m_nrm = reinterpret_cast<const float*>(mb + 1024);
+            const int lim = count - blk * s2::BM;  // slots at this offset and beyond are past the pool
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                // sort the lane's 32 candidates of this block in groups of 8 (two slot rows
-                // of 4) and merge each group into the token's list (a bitonic merge keeps
-                // the 8 smallest): a fixed network, so the wavefront never diverges
+            for (int g = 0; g < 4; ++g) {
+                // group g: slot tile st = g / 2, rows i = 2 (g % 2) + {0, 1}
+                const int st = g >> 1;
+                int pe[8];
+                float ne[8];
+                uint32_t sid[8];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
+                for (int h = 0; h < 2; ++h) {
+                    const int i = 2 * (g & 1) + h;
+                    const int off = 64 * wq + 32 * st + 8 * i + 4 * hl;
+                    const i32x4 p4 = lds_load<i32x4>(m_pos + off);
+                    const f32x4 n4 = lds_load<f32x4>(m_nrm + off);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        pe[4 * h + j] = (off + j < lim) ? p4[j] : INT_MAX;
+                        ne[4 * h + j] = n4[j];
+                        sid[4 * h + j] = (uint32_t)(blk * s2::BM + off + j);
+                    }
+                }
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    // masked candidates get the score FLT_MAX (branch-free); they sort after
+                    // every real score and leave the workgroup as empty entries
                     uint64_t gk[8];
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const int i = 2 * g + h;
-                        const i32x4 p4 = lds_load<i32x4>(m_pos + lb + 16 * i);
-                        const f32x4 n4 = lds_load<f32x4>(m_nrm + lb + 16 * i);
-                        const int pe[4] = {p4[0], p4[1], p4[2], p4[3]};
-                        const float ne[4] = {n4[0], n4[1], n4[2], n4[3]};
+                        const int i = 2 * (g & 1) + h;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            gk[4 * h + e] = pe[e] < tokpos_l[j] ? score_key(fmaf(-2.f, a[i][j][e], ne[e]), base + 16 * i + e)
-                                                               : kNoKey;
+                        for (int j = 0; j < 4; ++j) {
+                            const int c = 4 * h + j;
+                            const float sc = pe[c] < tokpos_l[tt] ? fmaf(-2.f, acc[st][tt][4 * i + j], ne[c]) : FLT_MAX;
+                            uint32_t hb = __float_as_uint(sc);
+                            hb ^= (uint32_t)((int)hb >> 31) | 0x80000000u;
+                            gk[c] = ((uint64_t)hb << 32) | sid[c];
+                        }
                     }
                     sort8(gk);
                     if (bi == 0 && g == 0) {
 #pragma unroll
-                        for (int q = 0; q < kTop; ++q) lk[j][q] = gk[q];
+                        for (int q = 0; q < kTop; ++q) lk[tt][q] = gk[q];
                     } else {
-                        merge8(lk[j], gk);
+                        merge8(lk[tt], gk);
                     }
-                    // keep each group's LDS reads next to their use (hoisting all of them
-                    // ahead of the networks would exhaust the registers)
-                    __builtin_amdgcn_sched_barrier(0);
                 }
+                // keep each group's LDS reads next to their use
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (!last) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int jj = 0; jj < 2; ++jj) a[i][jj] = zero4();
-            }
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
         };
-        ring_mainloop_lrp<s2::NST, SFrag>(pa, pb, (blk1 - blk0) * nk, nk, smem, load, mma, acc, fold);
+
+        // ring: stage s + NST is issued right after the barrier that follows the wait for
+        // stage s + 1, into the slot stage s used (the LDS reads of one K half overlap the
+        // MFMAs of the other)
+        const int n_st = (blk1 - blk0) * nk;
+        for (int p = 0; p < s2::NST; ++p)
+            if (p < n_st) issue();
+        if (n_st >= s2::NST) {
+            wait_vmcnt<(s2::NST - 1) * s2::kPer>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        SFrag f0, f1;
+        load(f0, 0, 0);
+        int slot = 0, kin = 0, bi = 0;
+        for (int s = 0; s + 1 < n_st; ++s) {
+            load(f1, slot, 1);
+            mma(f0);
+            const int next = slot + 1 == s2::NST ? 0 : slot + 1;
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            wait_lgkm0();
+            const int ahead = min(s2::NST - 2, n_st - 2 - s);
+            if (ahead >= 2) {
+                wait_vmcnt<2 * s2::kPer>();
+            } else if (ahead == 1) {
+                wait_vmcnt<s2::kPer>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (s + s2::NST < n_st) issue();
+            load(f0, next, 0);
+            mma(f1);
+            slot = next;
+            if (++kin == nk) {
+                kin = 0;
+                fold(bi);
+                ++bi;
+            }
+        }
+        load(f1, slot, 1);
+        mma(f0);
+        mma(f1);
+        fold(bi);
     }
 
-    // merge the 8 sorted lists of every token (2 slot halves x 4 lane groups)
+    // merge the 8 sorted lists of every token (4 slot quarters x 2 lane halves)
     __syncthreads();
     uint64_t* mK = reinterpret_cast<uint64_t*>(smem);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int tk = 32 * wt + 16 * j + (lane & 15);
-        const int src = ws * 4 + (lane >> 4);
+    for (int tt = 0; tt < 2; ++tt) {
+        const int tk = 64 * wh + 32 * tt + l32;
+        const int src = 2 * wq + hl;
 #pragma unroll
-        for (int q = 0; q < kTop; ++q) mK[(src * kTop + q) * kTok + tk] = lk[j][q];
+        for (int q = 0; q < kTop; ++q) mK[(src * kTop + q) * kTok + tk] = lk[tt][q];
     }
     __syncthreads();
     if (tid < kTok && t0 + tid < n) {
@@ -578,8 +681,9 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
         const size_t o = (((size_t)b * n + t0 + tid) * nsplit + split) * kTop;
 #pragma unroll
         for (int q = 0; q < kTop; ++q) {
-            part_score[o + q] = key_score(bk[q]);
-            part_slot[o + q] = key_slot(bk[q]);
+            const float sc = key_score(bk[q]);
+            part_score[o + q] = sc;
+            part_slot[o + q] = sc < FLT_MAX ? key_slot(bk[q]) : -1;
         }
     }
 }
