@@ -4,9 +4,13 @@
 // references of its causal pool with the smallest squared L2 distance
 // (arg top-k_i of -||kv_i - kv_j||^2, k_i = min(k, |pool|)) and averages them.
 //
-// Two kernels:
-//   search kernel  - one workgroup scores a tile of 128 tokens against a chunk of
-//                    pool blocks (256 slots each). Scores ||r||^2 - 2 x.r come from
+// Kernels:
+//   plan + queue   - per token tile, the pool blocks it has to read (those whose first
+//                    position lies below the tile's last token; the pool is
+//                    position-ordered), cut into chunks; one work queue per XCD.
+//   search kernel  - persistent, one workgroup per CU: each item scores a tile of 128
+//                    tokens against a chunk of pool blocks (256 slots each). Scores
+//                    ||r||^2 - 2 x.r come from
 //                    MFMA (x bf16, r FP8 widened exactly to bf16, fp32 accumulation)
 //                    with the pool as the A operand so that each lane owns tokens.
 //                    The pool and token rows stream through an LDS ring filled by
@@ -15,11 +19,8 @@
 //                    folds its scores into a sorted per-token top-8 held in registers
 //                    with a sorting network and bitonic merges on 64-bit (score, slot)
 //                    keys (no divergence, no per-candidate insertion). The workgroup
-//                    finally merges its
-//                    lanes' lists into one top-8 per token and chunk. Only pool blocks
-//                    whose first position lies below the tile's last token are read
-//                    (the pool is position-ordered); single slots are masked by
-//                    position.
+//                    finally merges its lanes' lists into one top-8 per token and chunk.
+//                    Single slots are masked by position.
 //   select_kernel  - one wavefront per token merges the chunks' lists, decides the
 //                    k_i references (exact fp32 distances are computed only when the
 //                    approximate scores of the boundary candidates are closer than
@@ -29,6 +30,8 @@
 // the search with fp32 MFMA and per-candidate insertion.
 #include <float.h>
 #include <limits.h>
+
+#include <algorithm>
 
 #include "rkv_device.h"
 #include "rkv_gemm.h"
@@ -387,92 +390,148 @@ struct SFrag {
     bf16x8 b[2][2];  // [token tile][sub-step]
 };
 
-// grid: (8 * per, batch) blocks over logical tiles (token tile, chunk), chunks fastest.
+// ---- work plan of the bf16 / FP8 search -------------------------------------------------
+// Pool blocks a token tile has to read: those whose first slot's position lies below the
+// tile's largest token position (the pool is appended in position order). One
+// wavefront per (tile, sequence).
+__global__ __launch_bounds__(256) void search_plan_kernel(const int* __restrict__ pos, int n,
+                                                          const int* __restrict__ ref_pos,
+                                                          const int* __restrict__ ref_count, int cap_ref, int ntiles,
+                                                          int* __restrict__ tile_nblk) {
+    const int lane = threadIdx.x & 63;
+    const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int b = blockIdx.y;
+    if (tile >= ntiles) return;
+    const int t0 = tile * kTok;
+    int mp = INT_MIN;
+    for (int j = lane; j < kTok; j += 64)
+        if (t0 + j < n) mp = max(mp, pos[(size_t)b * n + t0 + j]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mp = max(mp, __shfl_xor(mp, o, 64));
+    const int count = max(0, min(ref_count[b], cap_ref));
+    const int nbp = (count + s2::BM - 1) / s2::BM;
+    int v = 0;
+    for (int bb = lane; bb < nbp; bb += 64) v += ref_pos[(size_t)b * cap_ref + (size_t)bb * s2::BM] < mp ? 1 : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) tile_nblk[(size_t)b * ntiles + tile] = v;
+}
+
+// Work queues: tile u (u = 0 .. B ntiles - 1; sequence u % B, tile ntiles - 1 - u / B, so the
+// latest and heaviest tiles come first) contributes one item (u, c) per chunk c of bpc pool
+// blocks it reads, to queue u % 8 (one queue per XCD: the chunks of a tile share its token
+// rows in that XCD's L2). Wavefront q builds queue q and resets its counter.
+__global__ __launch_bounds__(512) void search_queue_kernel(const int* __restrict__ tile_nblk, int B, int ntiles,
+                                                           int bpc, int cap_q, int* __restrict__ items,
+                                                           int* __restrict__ ctr) {
+    const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int U = B * ntiles;
+    int base = 0;
+    for (int k0 = 0; q + 8 * k0 < U; k0 += 64) {
+        const int u = q + 8 * (k0 + lane);
+        int nch = 0;
+        if (u < U) {
+            const int b = u % B, tile = ntiles - 1 - u / B;
+            nch = (tile_nblk[(size_t)b * ntiles + tile] + bpc - 1) / bpc;
+        }
+        int incl = nch;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += t;
+        }
+        int off = base + incl - nch;
+        for (int c = 0; c < nch; ++c) items[(size_t)q * cap_q + off + c] = u * 16 + c;
+        base += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) {
+        ctr[2 * q] = 0;
+        ctr[2 * q + 1] = base;
+    }
+}
+
+// Persistent search: one workgroup per CU takes items from its XCD's queue (blockIdx.x % 8,
+// the hardware's round-robin placement), then from the other queues; an item scores token
+// tile u against pool blocks c bpc .. + bpc and leaves one sorted top-8 per token.
 template <typename KvT>
 __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
     const KvT* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
     const fp8_t* __restrict__ ref_vals, const int* __restrict__ ref_pos, const float* __restrict__ ref_norm2,
-    const int* __restrict__ ref_count, int W2, int cap_ref, int blocks_per_chunk, int nsplit, int ntiles, int per,
+    const int* __restrict__ ref_count, int W2, int cap_ref, int bpc, int nsplit, int ntiles, int B,
+    const int* __restrict__ tile_nblk, const int* __restrict__ items, int cap_q, int* __restrict__ ctr,
     float* __restrict__ part_score, int* __restrict__ part_slot) {
     extern __shared__ __align__(16) unsigned char smem_u8[];
     char* smem = reinterpret_cast<char*>(smem_u8);
-    constexpr int NT = s2::kThreads;
-    // token tiles dealt round-robin over the 8 XCDs, latest (heaviest) first; the
-    // chunks of one tile run back to back on one XCD
-    const int x = blockIdx.x & 7, jx = blockIdx.x >> 3;
-    const int tl = jx / nsplit, split = jx - tl * nsplit;
-    const int tiles_x = (ntiles - x + 7) / 8;
-    if (tl >= tiles_x) return;
-    const int tile = x + 8 * (tiles_x - 1 - tl);
-    const int b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wq = wave & 3, wh = wave >> 2, hl = lane >> 5, l32 = lane & 31;
-    const int t0 = tile * kTok;
-    const int count = max(0, min(ref_count[b], cap_ref));
-    const int* rp = ref_pos + (size_t)b * cap_ref;
-    const float* rn = ref_norm2 + (size_t)b * cap_ref;
-    int* s_red = reinterpret_cast<int*>(smem + s2::kOffRed);
-
-    int tokpos_l[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const int t = t0 + 64 * wh + 32 * tt + l32;
-        tokpos_l[tt] = (t < n) ? pos[(size_t)b * n + t] : INT_MIN;
-    }
-    // largest position of the tile, then the pool blocks whose first slot precedes it
-    {
-        int mp = INT_MIN;
-        if (tid < kTok && t0 + tid < n) mp = pos[(size_t)b * n + t0 + tid];
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) mp = max(mp, __shfl_xor(mp, o, 64));
-        if (lane == 0) s_red[wave] = mp;
-        __syncthreads();
-        int mx = INT_MIN;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) mx = max(mx, s_red[w]);
-        const int nbp = (count + s2::BM - 1) / s2::BM;
-        int v = 0;
-        for (int bb = tid; bb < nbp; bb += NT) v += rp[(size_t)bb * s2::BM] < mx ? 1 : 0;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-        if (lane == 0) s_red[8 + wave] = v;
-        __syncthreads();
-    }
-    int nblk = 0;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) nblk += s_red[8 + w];
-    const int blk0 = split * blocks_per_chunk;
-    const int blk1 = min(nblk, blk0 + blocks_per_chunk);
+    const int wv = wave_id();
     const int nk = W2 / kStageK;
+    int* s_item = reinterpret_cast<int*>(smem + s2::kOffRed);
 
-    uint64_t lk[2][kTop];  // per-token sorted lists of candidate keys
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int j = 0; j < kTop; ++j) lk[q][j] = kNoKey;
+    // next item code from queue q onwards (thread 0 claims, the workgroup reads it after a barrier)
+    int q = blockIdx.x & 7, q_tried = 0;
+    auto claim = [&]() {
+        if (tid == 0) {
+            int code = -1;
+            while (q_tried < 8) {
+                const int it = atomicAdd(&ctr[2 * q], 1);
+                if (it < ctr[2 * q + 1]) {
+                    code = items[(size_t)q * cap_q + it];
+                    break;
+                }
+                q = (q + 1) & 7;
+                ++q_tried;
+            }
+            s_item[0] = code;
+        }
+    };
+    claim();
+    __syncthreads();
+    int code = s_item[0];
 
-    if (blk1 > blk0) {
-        const int wv = wave_id();
+    while (code >= 0) {
+        const int u = code >> 4, split = code & 15;
+        const int b = u % B, tile = ntiles - 1 - u / B;
+        const int t0 = tile * kTok;
+        const int count = max(0, min(ref_count[b], cap_ref));
+        const int* rp = ref_pos + (size_t)b * cap_ref;
+        const float* rn = ref_norm2 + (size_t)b * cap_ref;
+        const int nblk = tile_nblk[(size_t)b * ntiles + tile];
+        const int blk0 = split * bpc;
+        const int blk1 = min(nblk, blk0 + bpc);
+
+        int tokpos_l[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = t0 + 64 * wh + 32 * tt + l32;
+            tokpos_l[tt] = (t < n) ? pos[(size_t)b * n + t] : INT_MIN;
+        }
+        uint64_t lk[2][kTop];  // per-token sorted lists of candidate keys
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int j = 0; j < kTop; ++j) lk[qq][j] = kNoKey;
+
         const char* pool = reinterpret_cast<const char*>(ref_vals + (size_t)b * cap_ref * W2);
         // pool loads: load u of wave w fills block w + 8 u (rows 16 (w + 8 u) ..), lane ->
         // row lane / 4 of it, granule position lane % 4
         int rowa[s2::kLoadsA];
         int cha[s2::kLoadsA];
 #pragma unroll
-        for (int u = 0; u < s2::kLoadsA; ++u) {
-            rowa[u] = 16 * (wv + 8 * u) + (lane >> 2);
-            cha[u] = 16 * swz(lane >> 2, lane & 3);
+        for (int v = 0; v < s2::kLoadsA; ++v) {
+            rowa[v] = 16 * (wv + 8 * v) + (lane >> 2);
+            cha[v] = 16 * swz(lane >> 2, lane & 3);
         }
         // token loads: load u of wave w fills block w + 8 u = 2 g + q
         const char* srcb[s2::kLoadsB];
 #pragma unroll
-        for (int u = 0; u < s2::kLoadsB; ++u) {
-            const int blk = wv + 8 * u;
+        for (int v = 0; v < s2::kLoadsB; ++v) {
+            const int blk = wv + 8 * v;
             const int r = 16 * (blk >> 1) + (lane >> 2);
             const int t = min(t0 + r, n - 1);
             int kr = rows[(size_t)b * n + t];
             kr = (kr >= 0 && kr < kv_len) ? kr : 0;
-            srcb[u] = reinterpret_cast<const char*>(kv + ((size_t)b * kv_len + kr) * W2) + 64 * (blk & 1) +
+            srcb[v] = reinterpret_cast<const char*>(kv + ((size_t)b * kv_len + kr) * W2) + 64 * (blk & 1) +
                       16 * swz(lane >> 2, lane & 3);
         }
         // metadata loads (stage 0 of each block): waves 0-3 positions, 4-7 norms, 64 slots each
@@ -486,17 +545,17 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
         auto set_block = [&](int bi) {
             const int base = (blk0 + bi) * s2::BM;
 #pragma unroll
-            for (int u = 0; u < s2::kLoadsA; ++u)
-                arow[u] = pool + (size_t)min(base + rowa[u], cap_ref - 1) * W2 + cha[u];
+            for (int v = 0; v < s2::kLoadsA; ++v)
+                arow[v] = pool + (size_t)min(base + rowa[v], cap_ref - 1) * W2 + cha[v];
         };
         set_block(0);
         auto issue = [&]() {
             char* sl = smem + is * s2::kSlot;
 #pragma unroll
-            for (int u = 0; u < s2::kLoadsA; ++u) dma16(arow[u] + ik * kStageK, sl + 1024 * (wv + 8 * u));
+            for (int v = 0; v < s2::kLoadsA; ++v) dma16(arow[v] + ik * kStageK, sl + 1024 * (wv + 8 * v));
 #pragma unroll
-            for (int u = 0; u < s2::kLoadsB; ++u)
-                dma16(srcb[u] + (size_t)ik * (kStageK * 2), sl + s2::kStageA + 1024 * (wv + 8 * u));
+            for (int v = 0; v < s2::kLoadsB; ++v)
+                dma16(srcb[v] + (size_t)ik * (kStageK * 2), sl + s2::kStageA + 1024 * (wv + 8 * v));
             if (ik == 0) {
                 const int sl_m = min((blk0 + ib) * s2::BM + msl, cap_ref - 1);
                 dma4(msrc + 4 * (size_t)sl_m, smem + s2::kOffMeta + (ib & (s2::kMetaBufs - 1)) * s2::kMeta + moff);
@@ -593,7 +652,7 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
                     sort8(gk);
                     if (bi == 0 && g == 0) {
 #pragma unroll
-                        for (int q = 0; q < kTop; ++q) lk[tt][q] = gk[q];
+                        for (int qq = 0; qq < kTop; ++qq) lk[tt][qq] = gk[qq];
                     } else {
                         merge8(lk[tt], gk);
                     }
@@ -655,36 +714,64 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
         mma(f0);
         mma(f1);
         fold(bi);
-    }
 
-    // merge the 8 sorted lists of every token (4 slot quarters x 2 lane halves)
-    __syncthreads();
-    uint64_t* mK = reinterpret_cast<uint64_t*>(smem);
+        // the next item is claimed while the lists are merged
+        __syncthreads();
+        claim();
+        // lanes l and l ^ 32 hold the same tokens: merge their lists in registers
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const int tk = 64 * wh + 32 * tt + l32;
-        const int src = 2 * wq + hl;
+        for (int tt = 0; tt < 2; ++tt) {
+            uint64_t ok[kTop];
 #pragma unroll
-        for (int q = 0; q < kTop; ++q) mK[(src * kTop + q) * kTok + tk] = lk[tt][q];
-    }
-    __syncthreads();
-    if (tid < kTok && t0 + tid < n) {
-        uint64_t bk[kTop], ck[kTop];
-#pragma unroll
-        for (int q = 0; q < kTop; ++q) bk[q] = mK[q * kTok + tid];
-#pragma unroll
-        for (int src = 1; src < 8; ++src) {
-#pragma unroll
-            for (int q = 0; q < kTop; ++q) ck[q] = mK[(src * kTop + q) * kTok + tid];
-            merge8(bk, ck);
+            for (int qq = 0; qq < kTop; ++qq) {
+                const int lo = __shfl_xor((int)(uint32_t)lk[tt][qq], 32, 64);
+                const int hi = __shfl_xor((int)(uint32_t)(lk[tt][qq] >> 32), 32, 64);
+                ok[qq] = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+            }
+            merge8(lk[tt], ok);
         }
-        const size_t o = (((size_t)b * n + t0 + tid) * nsplit + split) * kTop;
+        // then the 4 slot quarters' lists through LDS, pairwise
+        uint64_t* mK = reinterpret_cast<uint64_t*>(smem);
+        if (hl == 0) {
 #pragma unroll
-        for (int q = 0; q < kTop; ++q) {
-            const float sc = key_score(bk[q]);
-            part_score[o + q] = sc;
-            part_slot[o + q] = sc < FLT_MAX ? key_slot(bk[q]) : -1;
+            for (int tt = 0; tt < 2; ++tt) {
+                const int tk = 64 * wh + 32 * tt + l32;
+#pragma unroll
+                for (int qq = 0; qq < kTop; ++qq) mK[(wq * kTop + qq) * kTok + tk] = lk[tt][qq];
+            }
         }
+        __syncthreads();
+        if (tid < 2 * kTok) {
+            const int tk = tid & (kTok - 1), l0 = 2 * (tid >> 7);
+            uint64_t ak[kTop], bk[kTop];
+#pragma unroll
+            for (int qq = 0; qq < kTop; ++qq) {
+                ak[qq] = mK[(l0 * kTop + qq) * kTok + tk];
+                bk[qq] = mK[((l0 + 1) * kTop + qq) * kTok + tk];
+            }
+            merge8(ak, bk);
+#pragma unroll
+            for (int qq = 0; qq < kTop; ++qq) mK[(l0 * kTop + qq) * kTok + tk] = ak[qq];
+        }
+        __syncthreads();
+        if (tid < kTok && t0 + tid < n) {
+            uint64_t ak[kTop], bk[kTop];
+#pragma unroll
+            for (int qq = 0; qq < kTop; ++qq) {
+                ak[qq] = mK[qq * kTok + tid];
+                bk[qq] = mK[(2 * kTop + qq) * kTok + tid];
+            }
+            merge8(ak, bk);
+            const size_t o = (((size_t)b * n + t0 + tid) * nsplit + split) * kTop;
+#pragma unroll
+            for (int qq = 0; qq < kTop; ++qq) {
+                const float sc = key_score(ak[qq]);
+                part_score[o + qq] = sc;
+                part_slot[o + qq] = sc < FLT_MAX ? key_slot(ak[qq]) : -1;
+            }
+        }
+        code = s_item[0];
+        __syncthreads();
     }
 }
 
@@ -707,8 +794,8 @@ template <typename KvT, typename RefT>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const KvT* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
     const RefT* __restrict__ ref_vals, const float* __restrict__ ref_norm2, const float* __restrict__ part_score,
-    const int* __restrict__ part_slot, int nsplit, int W2, int cap_ref, int cap_tok, int top_k,
-    int* __restrict__ ref_idx, KvT* __restrict__ xbar, int* err) {
+    const int* __restrict__ part_slot, int nsplit, const int* __restrict__ tile_nblk, int bpc, int W2, int cap_ref,
+    int cap_tok, int top_k, int* __restrict__ ref_idx, KvT* __restrict__ xbar, int* err) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int b = blockIdx.y;
@@ -726,8 +813,14 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     const KvT* x = kv + ((size_t)b * kv_len + row) * W2;
     const RefT* pool = ref_vals + (size_t)b * cap_ref * W2;
 
-    // gather the chunks' candidates, one per lane
-    const int ncand = nsplit * kTop;  // <= 64
+    // gather the chunks' candidates, one per lane (with a work plan, only the chunks of
+    // pool blocks the token's tile read hold lists)
+    int nch = nsplit;
+    if (tile_nblk) {
+        const int ntiles = (n + kTok - 1) / kTok;
+        nch = min(nsplit, (tile_nblk[(size_t)b * ntiles + t / kTok] + bpc - 1) / bpc);
+    }
+    const int ncand = nch * kTop;  // <= 64
     float s = FLT_MAX;
     int id = -1;
     if (lane < ncand) {
@@ -862,6 +955,15 @@ EncodePlan plan_encode(const Shape& s, int B, int n, int cap_ref) {
     const size_t tok = (size_t)B * n;
     auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
     size_t off = 0;
+    // work plan of the bf16 search: blocks per tile, 8 item queues, their counters
+    const size_t units = (size_t)B * ((n + kTok - 1) / kTok);
+    p.cap_q = (int)((units + 7) / 8) * nsplit;
+    p.off_tile_nblk = off;
+    off = up(off + units * sizeof(int));
+    p.off_items = off;
+    off = up(off + (size_t)8 * p.cap_q * sizeof(int));
+    p.off_ctr = off;
+    off = up(off + 16 * sizeof(int));
     p.off_part_score = off;
     off = up(off + tok * nsplit * kTop * sizeof(float));
     p.off_part_slot = off;
@@ -893,6 +995,19 @@ static hipError_t search_impl(const Shape& s, const CacheView& c, const EncodePl
     return hipGetLastError();
 }
 
+// compute units of the current device (cached per device)
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
 static hipError_t search_ring_impl(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv,
                                    int kv_len, const int* rows, const int* pos, int n, void* ws, hipStream_t st) {
     const size_t smem = s2::bytes;
@@ -902,10 +1017,19 @@ static hipError_t search_ring_impl(const Shape& s, const CacheView& c, const Enc
     if (e != hipSuccess) return e;
     char* w = static_cast<char*>(ws);
     const int ntiles = (n + kTok - 1) / kTok;
-    const int per = ((ntiles + 7) / 8) * p.nsplit;  // blocks per XCD
-    hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(s2::kThreads), smem, st, static_cast<const bf16_t*>(kv), kv_len,
-                       rows, pos, n, static_cast<const fp8_t*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count,
-                       s.W2, c.cap_ref, p.chunk_slots, p.nsplit, ntiles, per,
+    int* tile_nblk = reinterpret_cast<int*>(w + p.off_tile_nblk);
+    int* items = reinterpret_cast<int*>(w + p.off_items);
+    int* ctr = reinterpret_cast<int*>(w + p.off_ctr);
+    hipLaunchKernelGGL(search_plan_kernel, dim3((ntiles + 3) / 4, c.B), dim3(256), 0, st, pos, n, c.ref_pos,
+                       c.ref_count, c.cap_ref, ntiles, tile_nblk);
+    hipLaunchKernelGGL(search_queue_kernel, dim3(1), dim3(512), 0, st, tile_nblk, c.B, ntiles, p.chunk_slots, p.cap_q,
+                       items, ctr);
+    // one workgroup per CU (the LDS of one fills a CU), never more than there are items
+    const long long max_items = (long long)c.B * ntiles * p.nsplit;
+    const int grid = (int)std::min<long long>(device_cus(), max_items);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(s2::kThreads), smem, st, static_cast<const bf16_t*>(kv), kv_len, rows,
+                       pos, n, static_cast<const fp8_t*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count, s.W2,
+                       c.cap_ref, p.chunk_slots, p.nsplit, ntiles, c.B, tile_nblk, items, p.cap_q, ctr,
                        reinterpret_cast<float*>(w + p.off_part_score), reinterpret_cast<int*>(w + p.off_part_slot));
     return hipGetLastError();
 }
@@ -924,7 +1048,9 @@ static hipError_t select_impl(const Shape& s, const CacheView& c, const EncodePl
     hipLaunchKernelGGL((select_kernel<KvT, RefT>), grid, dim3(kThreads), 0, st, static_cast<const KvT*>(kv), kv_len,
                        rows, pos, n, static_cast<const RefT*>(c.ref_vals), c.ref_norm2,
                        reinterpret_cast<const float*>(w + p.off_part_score),
-                       reinterpret_cast<const int*>(w + p.off_part_slot), p.nsplit, s.W2, c.cap_ref, c.cap_tok,
+                       reinterpret_cast<const int*>(w + p.off_part_slot), p.nsplit,
+                       s.f32 ? nullptr : reinterpret_cast<const int*>(w + p.off_tile_nblk), p.chunk_slots, s.W2,
+                       c.cap_ref, c.cap_tok,
                        s.top_k, c.ref_idx, reinterpret_cast<KvT*>(w + p.off_xbar), c.err);
     return hipGetLastError();
 }
