@@ -353,6 +353,32 @@ __device__ inline void merge8(uint64_t (&a)[8], const uint64_t (&b)[8]) {
 #undef RKV_C
 }
 
+// The same networks on 32-bit keys (a compare-exchange is one min and one max)
+__device__ inline void cas32(uint32_t& a, uint32_t& b) {
+    const uint32_t lo = min(a, b), hi = max(a, b);
+    a = lo;
+    b = hi;
+}
+__device__ inline void sort8_32(uint32_t (&k)[8]) {
+#define RKV_C(x, y) cas32(k[x], k[y])
+    RKV_C(0, 2); RKV_C(1, 3); RKV_C(4, 6); RKV_C(5, 7);
+    RKV_C(0, 4); RKV_C(1, 5); RKV_C(2, 6); RKV_C(3, 7);
+    RKV_C(0, 1); RKV_C(2, 3); RKV_C(4, 5); RKV_C(6, 7);
+    RKV_C(2, 4); RKV_C(3, 5);
+    RKV_C(1, 4); RKV_C(3, 6);
+    RKV_C(1, 2); RKV_C(3, 4); RKV_C(5, 6);
+#undef RKV_C
+}
+__device__ inline void merge8_32(uint32_t (&a)[8], const uint32_t (&b)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = min(a[i], b[7 - i]);
+#define RKV_C(x, y) cas32(a[x], a[y])
+    RKV_C(0, 4); RKV_C(1, 5); RKV_C(2, 6); RKV_C(3, 7);
+    RKV_C(0, 2); RKV_C(1, 3); RKV_C(4, 6); RKV_C(5, 7);
+    RKV_C(0, 1); RKV_C(2, 3); RKV_C(4, 5); RKV_C(6, 7);
+#undef RKV_C
+}
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // 4-byte direct load (lane l lands at byte 4 l of the LDS destination)
@@ -427,22 +453,33 @@ __global__ __launch_bounds__(512) void search_queue_kernel(const int* __restrict
     const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
     const int U = B * ntiles;
     int base = 0;
-    for (int k0 = 0; q + 8 * k0 < U; k0 += 64) {
-        const int u = q + 8 * (k0 + lane);
-        int nch = 0;
-        if (u < U) {
-            const int b = u % B, tile = ntiles - 1 - u / B;
-            nch = (tile_nblk[(size_t)b * ntiles + tile] + bpc - 1) / bpc;
-        }
-        int incl = nch;
+    // pass 0: the full chunks of every tile; pass 1: the shorter last chunks (the queue ends
+    // on the smallest items, which evens out when the workgroups finish)
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int k0 = 0; q + 8 * k0 < U; k0 += 64) {
+            const int u = q + 8 * (k0 + lane);
+            int c0 = 0, nch = 0;
+            if (u < U) {
+                const int b = u % B, tile = ntiles - 1 - u / B;
+                const int nb = tile_nblk[(size_t)b * ntiles + tile];
+                const int full = nb / bpc;
+                if (pass == 0) {
+                    nch = full;
+                } else {
+                    c0 = full;
+                    nch = (nb - full * bpc) > 0 ? 1 : 0;
+                }
+            }
+            int incl = nch;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int t = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += t;
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += t;
+            }
+            const int off = base + incl - nch;
+            for (int c = 0; c < nch; ++c) items[(size_t)q * cap_q + off + c] = u * 16 + c0 + c;
+            base += __shfl(incl, 63, 64);
         }
-        int off = base + incl - nch;
-        for (int c = 0; c < nch; ++c) items[(size_t)q * cap_q + off + c] = u * 16 + c;
-        base += __shfl(incl, 63, 64);
     }
     if (lane == 0) {
         ctr[2 * q] = 0;
@@ -468,28 +505,33 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
     const int nk = W2 / kStageK;
     int* s_item = reinterpret_cast<int*>(smem + s2::kOffRed);
 
-    // next item code from queue q onwards (thread 0 claims, the workgroup reads it after a barrier)
+    // next item code from queue q onwards (thread 0 claims, the workgroup reads it after a
+    // barrier). `it` is an index already taken from queue q (the claim for the next item is
+    // issued when an item starts, so its latency hides behind the item).
     int q = blockIdx.x & 7, q_tried = 0;
-    auto claim = [&]() {
+    auto claim = [&](int it) {
         if (tid == 0) {
             int code = -1;
             while (q_tried < 8) {
-                const int it = atomicAdd(&ctr[2 * q], 1);
                 if (it < ctr[2 * q + 1]) {
                     code = items[(size_t)q * cap_q + it];
                     break;
                 }
                 q = (q + 1) & 7;
                 ++q_tried;
+                if (q_tried < 8) it = atomicAdd(&ctr[2 * q], 1);
             }
             s_item[0] = code;
         }
     };
-    claim();
+    int pend = 0;
+    if (tid == 0) pend = atomicAdd(&ctr[2 * q], 1);
+    claim(pend);
     __syncthreads();
     int code = s_item[0];
 
     while (code >= 0) {
+        if (tid == 0) pend = atomicAdd(&ctr[2 * q], 1);
         const int u = code >> 4, split = code & 15;
         const int b = u % B, tile = ntiles - 1 - u / B;
         const int t0 = tile * kTok;
@@ -606,19 +648,24 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
                 }
         };
         // lane's slots of a block: 64 wq + 32 st + 8 i + 4 hl + j (accumulator element 4 i + j)
+        // A block's 32 candidates of a token are first ranked on 32-bit keys: the score's
+        // order-preserving bits with the low 5 replaced by the candidate's index in the lane
+        // (8 g + c, unique, slot order), i.e. scores rounded down by less than 32 ulps; a
+        // masked candidate is 0xFFFFFFFF. The block's best 8 then join the token's list as
+        // 64-bit (score, slot) keys. The select step widens its rounding margin to match.
         auto fold = [&](int bi) {
             const int blk = blk0 + bi;
             const char* mb = smem + s2::kOffMeta + (bi & (s2::kMetaBufs - 1)) * s2::kMeta;
             const int* m_pos = reinterpret_cast<const int*>(mb);
             const float* m_nrm = reinterpret_cast<const float*>(mb + 1024);
             const int lim = count - blk * s2::BM;  // slots at this offset and beyond are past the pool
+            uint32_t bk[2][8];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 // group g: slot tile st = g / 2, rows i = 2 (g % 2) + {0, 1}
                 const int st = g >> 1;
                 int pe[8];
                 float ne[8];
-                uint32_t sid[8];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int i = 2 * (g & 1) + h;
@@ -629,36 +676,50 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
                     for (int j = 0; j < 4; ++j) {
                         pe[4 * h + j] = (off + j < lim) ? p4[j] : INT_MAX;
                         ne[4 * h + j] = n4[j];
-                        sid[4 * h + j] = (uint32_t)(blk * s2::BM + off + j);
                     }
                 }
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    // masked candidates get the score FLT_MAX (branch-free); they sort after
-                    // every real score and leave the workgroup as empty entries
-                    uint64_t gk[8];
+                    uint32_t gk[8];
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int i = 2 * (g & 1) + h;
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const int c = 4 * h + j;
-                            const float sc = pe[c] < tokpos_l[tt] ? fmaf(-2.f, acc[st][tt][4 * i + j], ne[c]) : FLT_MAX;
-                            uint32_t hb = __float_as_uint(sc);
+                            uint32_t hb = __float_as_uint(fmaf(-2.f, acc[st][tt][4 * i + j], ne[c]));
                             hb ^= (uint32_t)((int)hb >> 31) | 0x80000000u;
-                            gk[c] = ((uint64_t)hb << 32) | sid[c];
+                            gk[c] = pe[c] < tokpos_l[tt] ? ((hb & ~31u) | (uint32_t)(8 * g + c)) : 0xFFFFFFFFu;
                         }
                     }
-                    sort8(gk);
-                    if (bi == 0 && g == 0) {
+                    sort8_32(gk);
+                    if (g == 0) {
 #pragma unroll
-                        for (int qq = 0; qq < kTop; ++qq) lk[tt][qq] = gk[qq];
+                        for (int qq = 0; qq < 8; ++qq) bk[tt][qq] = gk[qq];
                     } else {
-                        merge8(lk[tt], gk);
+                        merge8_32(bk[tt], gk);
                     }
                 }
                 // keep each group's LDS reads next to their use
                 __builtin_amdgcn_sched_barrier(0);
+            }
+            // lane-local index x -> slot offset 64 wq + 4 (lane / 32) + 32 st + 8 i + j
+            const uint32_t sbase = (uint32_t)(blk * s2::BM + 64 * wq + 4 * hl);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                uint64_t gk[8];
+#pragma unroll
+                for (int qq = 0; qq < 8; ++qq) {
+                    const uint32_t k = bk[tt][qq], x = k & 31u;
+                    gk[qq] = k == 0xFFFFFFFFu ? kNoKey
+                                              : ((uint64_t)(k & ~31u) << 32) | (sbase + x + (x & 0x1Cu));
+                }
+                if (bi == 0) {
+#pragma unroll
+                    for (int qq = 0; qq < kTop; ++qq) lk[tt][qq] = gk[qq];
+                } else {
+                    merge8(lk[tt], gk);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -717,7 +778,7 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
 
         // the next item is claimed while the lists are merged
         __syncthreads();
-        claim();
+        claim(pend);
         // lanes l and l ^ 32 hold the same tokens: merge their lists in registers
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -840,7 +901,9 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     const int nvalid = __popcll(valid_mask);
     const int k_i = min(top_k, nvalid);
 
-    // rounding bound of an approximate score: 2^-17 (||x||^2 + ||r||^2)
+    // bound on the error of an approximate score: 2^-17 (||x||^2 + ||r||^2) for the fp32
+    // accumulation of the MFMA path, and as much again for the 32-ulp rounding of its
+    // block-level ranking keys (|score| <= 2 (||x||^2 + ||r||^2))
     float xn = 0.f;
     for (int c = 4 * lane; c < W2; c += 256) {
         const float4 v = Load4<KvT>::run(x + c);
@@ -848,7 +911,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     }
     xn = wave_sum(xn);
     const float nr = (id >= 0) ? ref_norm2[(size_t)b * cap_ref + id] : 0.f;
-    const float margin = 7.62939453125e-06f * (xn + nr);  // 2^-17
+    const float margin = 1.52587890625e-05f * (xn + nr);  // 2^-16
     const bool in_set = id >= 0 && rank < k_i;
     // highest (score + margin) inside the set vs lowest (score - margin) outside it
     float hi_in = in_set ? s + margin : -FLT_MAX;
