@@ -838,19 +838,21 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
 
 // ------------------------------------------------------------------ select + mean
 
+// 8 consecutive values stored from floats (one 16-byte store for bf16, two for fp32)
 template <typename XT>
-__device__ inline void store4(XT* p, float4 v);
+__device__ inline void gstore8(XT* p, const float* v);
 template <>
-__device__ inline void store4<float>(float* p, float4 v) {
-    *reinterpret_cast<float4*>(p) = v;
+__device__ inline void gstore8<float>(float* p, const float* v) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 template <>
-__device__ inline void store4<bf16_t>(bf16_t* p, float4 v) {
-    bf16_t t[4] = {(bf16_t)v.x, (bf16_t)v.y, (bf16_t)v.z, (bf16_t)v.w};
-    *reinterpret_cast<uint2*>(p) = *reinterpret_cast<uint2*>(t);
+__device__ inline void gstore8<bf16_t>(bf16_t* p, const float* v) {
+    *reinterpret_cast<bf16x8*>(p) = Mma<bf16_t>::from_float(v);
 }
 
-// One wavefront per token; 4 tokens per block.
+// One wavefront per token; 4 tokens per block. Row accesses take 8 columns per lane
+// (chunks of 512 columns).
 template <typename KvT, typename RefT>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const KvT* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
@@ -868,11 +870,26 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     KvT* xrow = xbar + ((size_t)b * n + t) * W2;
     if (!row_ok || !pos_ok) {
         if (lane == 0) flag_error(err, (row_ok ? 0 : DEVERR_ROW_RANGE) | (pos_ok ? 0 : DEVERR_POS_RANGE));
-        for (int c = 4 * lane; c < W2; c += 256) store4<KvT>(xrow + c, make_float4(0.f, 0.f, 0.f, 0.f));
+        const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int c = 8 * lane; c < W2; c += 512) gstore8<KvT>(xrow + c, z);
         return;
     }
     const KvT* x = kv + ((size_t)b * kv_len + row) * W2;
     const RefT* pool = ref_vals + (size_t)b * cap_ref * W2;
+    // the first chunks of the token's row are loaded before the candidates are ranked, so
+    // their latency overlaps the ranking
+    constexpr int kPre = 4;
+    float xv[kPre][8];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int c = 8 * lane + 512 * u;
+        if (c < W2) {
+            Load8<KvT>::run(x + c, xv[u]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[u][e] = 0.f;
+        }
+    }
 
     // gather the chunks' candidates, one per lane (with a work plan, only the chunks of
     // pool blocks the token's tile read hold lists)
@@ -905,9 +922,15 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     // accumulation of the MFMA path, and as much again for the 32-ulp rounding of its
     // block-level ranking keys (|score| <= 2 (||x||^2 + ||r||^2))
     float xn = 0.f;
-    for (int c = 4 * lane; c < W2; c += 256) {
-        const float4 v = Load4<KvT>::run(x + c);
-        xn = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, xn))));
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xn = fmaf(xv[u][e], xv[u][e], xn);
+    for (int c = 8 * lane + 512 * kPre; c < W2; c += 512) {
+        float v[8];
+        Load8<KvT>::run(x + c, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xn = fmaf(v[e], v[e], xn);
     }
     xn = wave_sum(xn);
     const float nr = (id >= 0) ? ref_norm2[(size_t)b * cap_ref + id] : 0.f;
@@ -981,25 +1004,29 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     // rounded to the KV dtype for the encoder
     const float kf = (float)k_i;
     const float rk = __fdiv_rn(1.0f, k_i > 0 ? kf : 1.0f);
-    for (int c = 4 * lane; c < W2; c += 256) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 2
+    for (int c = 8 * lane; c < W2; c += 512) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             if (q < k_i) {
-                const float4 v = Load4<RefT>::run(pool + (size_t)slots[q] * W2 + c);
-                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+                float v[8];
+                Load8<RefT>::run(pool + (size_t)slots[q] * W2 + c, v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += v[e];
             }
         }
         if (k_i > 1) {
-            if constexpr (std::is_same<RefT, fp8_t>::value) {
-                acc.x = div_small(acc.x, kf, rk); acc.y = div_small(acc.y, kf, rk);
-                acc.z = div_small(acc.z, kf, rk); acc.w = div_small(acc.w, kf, rk);
-            } else {  // fp32 references: general sums, IEEE division
-                acc.x = __fdiv_rn(acc.x, kf); acc.y = __fdiv_rn(acc.y, kf);
-                acc.z = __fdiv_rn(acc.z, kf); acc.w = __fdiv_rn(acc.w, kf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if constexpr (std::is_same<RefT, fp8_t>::value) {
+                    acc[e] = div_small(acc[e], kf, rk);
+                } else {  // fp32 references: general sums, IEEE division
+                    acc[e] = __fdiv_rn(acc[e], kf);
+                }
             }
         }
-        store4<KvT>(xrow + c, acc);
+        gstore8<KvT>(xrow + c, acc);
     }
 }
 
