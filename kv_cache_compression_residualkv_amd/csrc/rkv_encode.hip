@@ -300,6 +300,8 @@ struct G2 {
     static constexpr int kQP = BN * 2 + 16;  // bytes per staged token row (fp16 latent is the widest)
     static constexpr size_t kEpi = (size_t)BM * kQP + (size_t)BM * (BN / 32) * 2 * sizeof(float);
     static constexpr size_t bytes = kPipe > kEpi ? kPipe : kEpi;
+    static constexpr int kThreads = kGemmThreads;
+    static constexpr int kNWN = 2;  // wavefronts along N: wave w owns rows WM (w / kNWN), columns WN (w % kNWN)
 };
 
 template <typename T>
@@ -352,7 +354,7 @@ __device__ inline void quant_epilogue(f32x4 (&acc)[C::WM / 16][C::WN / 16], unsi
                                       uint8_t* __restrict__ codes, size_t code_bytes, ScT* __restrict__ scale,
                                       ScT* __restrict__ zmin) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::kNWN, wn = wave % C::kNWN;
     uint8_t* sQ = smem;                                               // [BM][kQP] bytes
     float* sS = reinterpret_cast<float*>(smem + (size_t)C::BM * C::kQP);  // [BM][BN/32][2]
     constexpr int GT = C::BN / 32;  // groups per tile row
@@ -399,7 +401,7 @@ __device__ inline void quant_epilogue(f32x4 (&acc)[C::WM / 16][C::WN / 16], unsi
     // coalesced record writes: 16-byte chunks of this tile's part of each record
     const int cb = bits == 16 ? C::BN * 2 : C::BN * bits / 8;  // code bytes per token in this tile
     const int nch = cb / 16;
-    for (int jb = tid; jb < C::BM * nch; jb += kGemmThreads) {
+    for (int jb = tid; jb < C::BM * nch; jb += C::kThreads) {
         const int tl = jb / nch, ch = jb - tl * nch;
         const int t = t0 + tl;
         if (t >= n) continue;
@@ -437,7 +439,7 @@ __device__ inline void quant_epilogue(f32x4 (&acc)[C::WM / 16][C::WN / 16], unsi
     }
     if (bits != 16) {
         const int G = d_c / 32;
-        for (int jb = tid; jb < C::BM * GT; jb += kGemmThreads) {
+        for (int jb = tid; jb < C::BM * GT; jb += C::kThreads) {
             const int tl = jb / GT, gl = jb - tl * GT;
             const int t = t0 + tl;
             const int g = c0 / 32 + gl;
@@ -491,19 +493,30 @@ __global__ __launch_bounds__(kGemmThreads) void latent_quant_kernel(const T* __r
     quant_epilogue<C, ScT>(acc, smem, t0, c0, b, n, d_c, bits, pos, cap_tok, codes, code_bytes, scale, zmin);
 }
 
-// bf16 formats: W_c3 projection + quantizer on the direct-to-LDS ring.
+// bf16 formats: W_c3 projection + quantizer on the direct-to-LDS ring: 256 tokens x 256
+// latent columns per workgroup of 8 wavefronts (wave w: tokens 128 (w / 4) .., columns
+// 64 (w % 4) ..), so each dH row and each W_c3 row is streamed half as often as with
+// 128-wide tiles.
 namespace g2r {
-constexpr int BM = 128, BN = 128, NST = 2;
+constexpr int kThreads = 512;
+constexpr int BM = 256, BN = 256, NST = 2;
+struct Cfg {
+    static constexpr int BM = g2r::BM, BN = g2r::BN, WM = 128, WN = 64;
+    static constexpr int kQP = BN * 2 + 16;
+    static constexpr size_t kEpi = (size_t)BM * kQP + (size_t)BM * (BN / 32) * 2 * sizeof(float);
+    static constexpr int kThreads = g2r::kThreads;
+    static constexpr int kNWN = 4;
+};
 constexpr size_t kRing = (size_t)NST * (BM + BN) * kStageK * 2;
-constexpr size_t bytes = kRing > G2<bf16_t>::kEpi ? kRing : G2<bf16_t>::kEpi;
+constexpr size_t bytes = kRing > Cfg::kEpi ? kRing : Cfg::kEpi;
 static_assert(bytes <= 160 * 1024, "LDS budget");
 }  // namespace g2r
 
 // W_c3 rows as the B operand: stage s reads K columns ((s mod (d_ff / 64)) * 64), so
 // the three planes of dH (K' = 3 d_ff) each meet the same W_c3.
-template <int R>
+template <int R, int NW>
 struct WrapOp16 {
-    static constexpr int kLoads = R / 32;
+    static constexpr int kLoads = R / (8 * NW);
     static constexpr int kStageBytes = R * kStageK * 2;
     const char* src[kLoads];
     int nkm;  // stages per d_ff
@@ -511,20 +524,20 @@ struct WrapOp16 {
         const int wave = wave_id();
         const int kc = s % nkm;
 #pragma unroll
-        for (int u = 0; u < kLoads; ++u) dma16(src[u] + (size_t)kc * (kStageK * 2), slot + 1024 * (wave + 4 * u));
+        for (int u = 0; u < kLoads; ++u) dma16(src[u] + (size_t)kc * (kStageK * 2), slot + 1024 * (wave + NW * u));
     }
 };
 
 struct G2Frag {
-    bf16x8 a[4];
+    bf16x8 a[8];
     bf16x8 b[4];
 };
 
-__global__ __launch_bounds__(kGemmThreads) void latent_quant_ring_kernel(
+__global__ __launch_bounds__(g2r::kThreads) void latent_quant_ring_kernel(
     const bf16_t* __restrict__ dh, int n, const bf16_t* __restrict__ w3, int d_ff, int d_c, int bits,
     const int* __restrict__ pos, int cap_tok, uint8_t* __restrict__ codes, size_t code_bytes, f16_t* __restrict__ scale,
     f16_t* __restrict__ zmin, int MT, int NT, int per) {
-    typedef G2<bf16_t> C;
+    typedef g2r::Cfg C;
     extern __shared__ __align__(16) unsigned char smem_u8[];
     char* smem = reinterpret_cast<char*>(smem_u8);
     const int tile = xcd_tile(blockIdx.x, per);
@@ -532,43 +545,43 @@ __global__ __launch_bounds__(kGemmThreads) void latent_quant_ring_kernel(
     const int mt = tile / NT, nt = tile - mt * NT;
     const int b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::kNWN, wn = wave % C::kNWN;
     const int t0 = mt * g2r::BM;
     const int c0 = nt * g2r::BN;
     const int Kp = 3 * d_ff;
 
     // rows past n / d_c repeat the last valid row; their results are not stored
-    Op16<g2r::BM> la;
+    Op16<g2r::BM, 8> la;
     la.init([&](int r) { return dh + ((size_t)b * n + min(t0 + r, n - 1)) * Kp; });
-    WrapOp16<g2r::BN> lb;
+    WrapOp16<g2r::BN, 8> lb;
     lb.nkm = d_ff / kStageK;
 #pragma unroll
-    for (int u = 0; u < WrapOp16<g2r::BN>::kLoads; ++u) {
-        const int blk = wave + 4 * u;
+    for (int u = 0; u < WrapOp16<g2r::BN, 8>::kLoads; ++u) {
+        const int blk = wave + 8 * u;
         const int r = 16 * (blk >> 1) + (lane >> 2);
         lb.src[u] = reinterpret_cast<const char*>(w3 + (size_t)min(c0 + r, d_c - 1) * d_ff) + 64 * (blk & 1) +
                     16 * swz(lane >> 2, lane & 3);
     }
 
-    f32x4 acc[4][4];
+    f32x4 acc[8][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
     auto load = [&](G2Frag& f, const char* sa, const char* sb, int ks) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) f.b[j] = Op16<g2r::BN>::template frag<bf16_t>(sb, 4 * wn + j, ks);
+        for (int j = 0; j < 4; ++j) f.b[j] = Op16<g2r::BN, 8>::template frag<bf16_t>(sb, 4 * wn + j, ks);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f.a[i] = Op16<g2r::BM>::template frag<bf16_t>(sa, 4 * wm + i, ks);
+        for (int i = 0; i < 8; ++i) f.a[i] = Op16<g2r::BM, 8>::template frag<bf16_t>(sa, 8 * wm + i, ks);
     };
-    auto mma = [&](const G2Frag& f, f32x4(&c)[4][4]) {
+    auto mma = [&](const G2Frag& f, f32x4(&c)[8][4]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) c[i][j] = Mma<bf16_t>::step(c[i][j], f.a[i], f.b[j]);
     };
     const int ns = Kp / kStageK;
-    ring_mainloop_lrp<g2r::NST, G2Frag>(la, lb, ns, ns, smem, load, mma, acc, [](int, f32x4(&)[4][4], bool) {});
+    ring_mainloop_lrp<g2r::NST, G2Frag>(la, lb, ns, ns, smem, load, mma, acc, [](int, f32x4(&)[8][4], bool) {});
     __syncthreads();
     quant_epilogue<C, f16_t>(acc, smem_u8, t0, c0, b, n, d_c, bits, pos, cap_tok, codes, code_bytes, scale, zmin);
 }
@@ -650,7 +663,7 @@ static hipError_t latent_ring_impl(const Shape& s, const CacheView& c, const Enc
     const int MT = (n + g2r::BM - 1) / g2r::BM;
     const int NT = (s.d_c + g2r::BN - 1) / g2r::BN;
     const int per = xcd_per(MT * NT);
-    hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(kGemmThreads), smem, st,
+    hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(g2r::kThreads), smem, st,
                        reinterpret_cast<const bf16_t*>(w + p.off_dh), n, static_cast<const bf16_t*>(w3), s.d_ff, s.d_c,
                        s.bits, pos, c.cap_tok, c.codes, c.code_bytes, static_cast<f16_t*>(c.scale),
                        static_cast<f16_t*>(c.zmin), MT, NT, per);
