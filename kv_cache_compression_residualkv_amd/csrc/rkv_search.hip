@@ -505,23 +505,43 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
     const int nk = W2 / kStageK;
     int* s_item = reinterpret_cast<int*>(smem + s2::kOffRed);
 
-    // next item code from queue q onwards (thread 0 claims, the workgroup reads it after a
-    // barrier). `it` is an index already taken from queue q (the claim for the next item is
-    // issued when an item starts, so its latency hides behind the item).
-    int q = blockIdx.x & 7, q_tried = 0;
+    // next item code from queue q onwards (wavefront 0 claims, the workgroup reads it after
+    // a barrier). `it` is an index already taken from queue q (the claim for the next item
+    // is issued when an item starts, so its latency hides behind the item). When queue q is
+    // exhausted, lanes 0-7 read all eight queues' counters at once (atomic loads: the
+    // counters move under other CUs' claims) and the claim moves to the next one that still
+    // holds items; a failed attempt only raises that queue's counter, so every workgroup
+    // leaves once all queues are exhausted.
+    int q = blockIdx.x & 7;
+    int tot_q = ctr[2 * q + 1];
     auto claim = [&](int it) {
-        if (tid == 0) {
+        if (tid < 64) {
             int code = -1;
-            while (q_tried < 8) {
-                if (it < ctr[2 * q + 1]) {
-                    code = items[(size_t)q * cap_q + it];
-                    break;
-                }
-                q = (q + 1) & 7;
-                ++q_tried;
-                if (q_tried < 8) it = atomicAdd(&ctr[2 * q], 1);
+            it = __shfl(it, 0, 64);
+            bool done = false;
+            if (it < tot_q) {
+                code = items[(size_t)q * cap_q + it];
+                done = true;
             }
-            s_item[0] = code;
+            while (!done) {
+                bool rem = false;
+                if (lane < 8)
+                    rem = __hip_atomic_load(&ctr[2 * lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                          ctr[2 * lane + 1];
+                const uint32_t m = (uint32_t)__ballot(rem) & 0xFFu;
+                if (m == 0u) break;
+                const uint32_t rot = ((m >> q) | (m << (8 - q))) & 0xFFu;
+                q = (q + __ffs(rot) - 1) & 7;
+                tot_q = ctr[2 * q + 1];
+                int it2 = 0;
+                if (lane == 0) it2 = atomicAdd(&ctr[2 * q], 1);
+                it2 = __shfl(it2, 0, 64);
+                if (it2 < tot_q) {
+                    code = items[(size_t)q * cap_q + it2];
+                    done = true;
+                }
+            }
+            if (lane == 0) s_item[0] = code;
         }
     };
     int pend = 0;
