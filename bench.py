@@ -144,6 +144,281 @@ def cpu_baseline(wl, kv, W, n_enc_sample=96, n_dec_sample=2048):
     )
 
 
+def oracle_rates(wl, kv, W, refp, n_enc_sample, n_dec_sample, seconds_cap=20.0):
+    """The oracle's per-token encode and restore times (s) on a bounded sample of one sequence."""
+    from oracle import OracleCodec
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = int(blas[0]["num_threads"]) if blas else 1
+    except Exception:
+        cores = 1
+    codec = OracleCodec.from_workload(wl, W)
+    T = kv.shape[0]
+    cache = codec.new_cache(refp.size, T)
+    codec.append_ref(cache, kv[refp], refp)
+    encp = np.setdiff1d(np.arange(T, dtype=np.int64), refp)
+    sel = encp[np.linspace(0, encp.size - 1, n_enc_sample).astype(np.int64)]
+    t0 = time.perf_counter()
+    done = 0
+    for p in sel:  # one token per call, latest last; stop at the time cap
+        codec.encode(cache, kv[[p]], np.array([p]))
+        done += 1
+        if time.perf_counter() - t0 > seconds_cap:
+            break
+    t_enc = (time.perf_counter() - t0) / done
+    dec = np.unique(np.concatenate([sel[:done], refp[:: max(1, refp.size // 64)]]))[:n_dec_sample]
+    t0 = time.perf_counter()
+    codec.decode_selected(cache, dec)
+    t_dec = (time.perf_counter() - t0) / dec.size
+    return t_enc, t_dec, cores, done, dec.size
+
+
+def timed(stream, fn, reps):
+    """Average ms of fn() over reps launches on stream (HIP events)."""
+    import torch
+
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def run_other(args) -> int:
+    """The other workload shapes: Qwen2.5-7B long context (INT2, stride 16), the Llama decode
+    side over 32 layers, and 16 independent Llama sequences (INT4 and fp16 latents)."""
+    import torch
+
+    import kv_cache_compression_residualkv_amd as rkv
+    from synth import workload
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    def setup(wl, layer=0, B=1, cap_extra=0):
+        W = wl.make_weights(layer)
+        cfg = rkv.CodecConfig.from_workload(wl)
+        weights = rkv.CodecWeights.from_math(W, cfg, dev)
+        weights.prepare_decoder(cfg)
+        T = wl.T + cap_extra
+        cache = rkv.CodecCache(cfg, B, (T + wl.stride - 1) // wl.stride, T, dev)
+        return W, cfg, weights, cache
+
+    def dec_work(wl, m):
+        rec = wl.d_c * wl.bits // 8 + (wl.d_c // wl.group) * 4 + wl.top_k * 4
+        return dict(flops=2.0 * m * wl.d_c * wl.two_dk, bytes=m * (wl.two_dk * 2 + rec) + wl.two_dk * wl.d_c * 2)
+
+    def line(name, metric, value, ms, cfgd, extra):
+        d = {"metric": metric, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+             "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+             "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": dict(workload=name, **cfgd)}
+        d.update(extra)
+        print(json.dumps(d), flush=True)
+
+    if args.workload == "qwen-long":
+        wl = workload(4)
+        T, W2 = wl.T, wl.two_dk
+        print(f"[bench] generating {wl.name}: T={T} 2dk={W2}", file=sys.stderr, flush=True)
+        kv_np = wl.make_kv()
+        W, cfg, weights, cache = setup(wl)
+        kv = torch.from_numpy(kv_np).to(torch.bfloat16).to(dev)[None].contiguous()
+        refp_np = wl.ref_positions()
+        refp = torch.from_numpy(refp_np).to(dev)[None].contiguous()
+        encp = torch.from_numpy(wl.enc_positions()).to(dev)[None].contiguous()
+        sel = torch.from_numpy(wl.make_selected(T)).to(dev)[None].contiguous()
+        out = torch.empty((1, sel.shape[1], W2), dtype=torch.bfloat16, device=dev)
+        n_ref, n = refp.shape[1], encp.shape[1]
+        ws = torch.empty((rkv.rkv_encode_workspace_bytes(cfg, 1, n, n_ref),), dtype=torch.uint8, device=dev)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for e in evs:
+            e.record(stream)
+        tot = np.zeros(5)
+
+        def step(record):
+            cache.ref_count.zero_()
+            rkv.rkv_append_ref(cfg, cache, kv, refp, refp, stream=stream)
+            rkv.rkv_encode(cfg, weights, cache, kv, encp, encp, ws, stream=stream,
+                           events=[e.cuda_event for e in evs[:5]] if record else None)
+
+        for _ in range(args.warmup):
+            step(False)
+        torch.cuda.synchronize()
+        assert cache.error_bits() == 0, cache.error_bits()
+        print(f"[bench] timing {args.steps} encodes and restores", file=sys.stderr, flush=True)
+        enc_ms = 0.0
+        for _ in range(args.steps):
+            step(True)
+            torch.cuda.synchronize()
+            ph = [evs[i].elapsed_time(evs[i + 1]) for i in range(4)]
+            tot[:4] += ph
+            enc_ms += sum(ph)
+        enc_ms /= args.steps
+        tot /= args.steps
+        dec_ms = timed(stream, lambda: rkv.rkv_decode_selected(cfg, weights, cache, sel, out=out, stream=stream),
+                       args.steps)
+        m = sel.shape[1]
+        work = algorithmic_work(wl, n)
+        per_kernel = {p: dict(ms=round(tot[i], 4), **{k: v for k, v in roofline(work[p], tot[i]).items()
+                                                      if k in ("bound", "achieved", "unit", "frac")})
+                      for i, p in enumerate(("search", "select", "compress", "quantize"))}
+        dr = roofline(dec_work(wl, m), dec_ms)
+        per_kernel["decode_selected"] = dict(ms=round(dec_ms, 4), **{k: v for k, v in dr.items()
+                                                                      if k in ("bound", "achieved", "unit", "frac")})
+        extra = {"encode_tok_s": round(n / (enc_ms * 1e-3), 1), "decode_selected_tok_s": round(m / (dec_ms * 1e-3), 1),
+                 "per_kernel": per_kernel}
+        if not args.no_cpu_baseline:
+            print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+            te, td, cores, ne, nd = oracle_rates(wl, kv_np, W, refp_np, 24, 1024)
+            extra["cpu_baseline"] = dict(value=round((n + m) / (n * te + m * td), 2), unit="tokens/s", cores=cores,
+                                         kind="oracle", encode_tok_s=round(1 / te, 2), decode_tok_s=round(1 / td, 2),
+                                         sample=f"{ne} single-token encodes (full causal pool each) and {nd} restores")
+        line(wl.name, "tokens/s encoded and restored at the Qwen2.5-7B KV shape (bulk encode + 30 % restore)",
+             (n + m) / ((enc_ms + dec_ms) * 1e-3), enc_ms + dec_ms,
+             {"T": T, "two_dk": W2, "d_ff": wl.d_ff, "d_c": wl.d_c, "bits": wl.bits, "stride": wl.stride,
+              "n_encode": n, "n_restore": m}, extra)
+        return 0
+
+    if args.workload == "llama-decode":
+        wl = workload(3)
+        T, W2, L = wl.T, wl.two_dk, wl.layers
+        steps = args.steps
+        print(f"[bench] generating {wl.name}: T={T} 2dk={W2}, {L} layers (one KV history shared by the layers, "
+              f"each layer its own weights and codes)", file=sys.stderr, flush=True)
+        kv_np = wl.make_kv(T=T + steps + args.warmup)
+        kv = torch.from_numpy(kv_np).to(torch.bfloat16).to(dev)[None].contiguous()
+        refp_np = wl.ref_positions()
+        refp = torch.from_numpy(refp_np).to(dev)[None].contiguous()
+        encp = torch.from_numpy(wl.enc_positions()).to(dev)[None].contiguous()
+        layers = []
+        ws = None
+        for layer in range(L):
+            W, cfg, weights, cache = setup(wl, layer, cap_extra=steps + args.warmup + 8)
+            if ws is None:
+                ws = torch.empty((rkv.rkv_encode_workspace_bytes(cfg, 1, encp.shape[1], cache.cap_ref),),
+                                 dtype=torch.uint8, device=dev)
+            rkv.rkv_append_ref(cfg, cache, kv, refp, refp, stream=stream)
+            rkv.rkv_encode(cfg, weights, cache, kv, encp, encp, ws, stream=stream)
+            layers.append((W, cfg, weights, cache))
+        torch.cuda.synchronize()
+        sels = [torch.from_numpy(wl.make_selected(T, step=s_, layer=l_)).to(dev)[None].contiguous()
+                for s_ in range(2) for l_ in range(L)]
+        m = sels[0].shape[1]
+        out = torch.empty((1, max(x.shape[1] for x in sels), W2), dtype=torch.bfloat16, device=dev)
+        one = [torch.full((1, 1), T + j, dtype=torch.int32, device=dev) for j in range(steps + args.warmup)]
+
+        def step(j):
+            p = one[j]
+            for l_, (W, cfg, weights, cache) in enumerate(layers):
+                rkv.rkv_decode_selected(cfg, weights, cache, sels[(j % 2) * L + l_], out=out, stream=stream)
+                if (T + j) % wl.stride == 0:
+                    rkv.rkv_append_ref(cfg, cache, kv, p, p, stream=stream)
+                else:
+                    rkv.rkv_encode(cfg, weights, cache, kv, p, p, ws, stream=stream)
+
+        for j in range(args.warmup):
+            step(j)
+        torch.cuda.synchronize()
+        print(f"[bench] timing {steps} steps of {L} layers", file=sys.stderr, flush=True)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for j in range(args.warmup, args.warmup + steps):
+            step(j)
+        b.record(stream)
+        torch.cuda.synchronize()
+        step_ms = a.elapsed_time(b) / steps
+        W, cfg, weights, cache = layers[0]
+        dec_ms = timed(stream, lambda: rkv.rkv_decode_selected(cfg, weights, cache, sels[0], out=out, stream=stream),
+                       20)
+        # one-token encode latency: the row of the last history token, stored at a fresh position
+        r_enc = torch.full((1, 1), T - 1, dtype=torch.int32, device=dev)
+        p_enc = torch.full((1, 1), T + args.warmup + steps + 1, dtype=torch.int32, device=dev)
+        enc_ms = timed(stream, lambda: rkv.rkv_encode(cfg, weights, cache, kv, r_enc, p_enc, ws, stream=stream), 20)
+        for _, _, _, c_ in layers:
+            assert c_.error_bits() == 0, c_.error_bits()
+        dr = roofline(dec_work(wl, m), dec_ms)
+        extra = {"decode_tok_s": round(L * m / (step_ms * 1e-3), 1),
+                 "per_layer": {"decode_selected_ms": round(dec_ms, 4),
+                               "decode_selected": {k: v for k, v in dr.items() if k in ("bound", "achieved", "unit", "frac")},
+                               "encode_one_token_ms": round(enc_ms, 4)}}
+        if not args.no_cpu_baseline:
+            print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+            te, td, cores, ne, nd = oracle_rates(wl, kv_np[:T], layers[0][0], refp_np, 4, 512, seconds_cap=10.0)
+            extra["cpu_baseline"] = dict(value=round(L * m / (L * (m * td + te)), 2), unit="tokens/s", cores=cores,
+                                         kind="oracle", sample=f"{ne} single-token encodes and {nd} restores of one layer; "
+                                         f"step = {L} x ({m} restores + 1 encode)")
+        line(wl.name, "tokens/s restored at the Llama-3.1-8B KV shape, 32 layers, 30 % of a 131072-token history "
+             "(plus one appended token per layer and step)", L * m / (step_ms * 1e-3), step_ms,
+             {"T": T, "two_dk": W2, "layers": L, "restored_per_layer": m}, extra)
+        return 0
+
+    # batch16: 16 independent sequences; INT4 g32 and fp16 latents
+    res = {}
+    wl0 = workload(5)
+    steps = args.steps
+    print(f"[bench] generating {wl0.name}: {wl0.batch} x T={wl0.T}", file=sys.stderr, flush=True)
+    kv = torch.empty((wl0.batch, wl0.T + steps + args.warmup, wl0.two_dk), dtype=torch.bfloat16, device=dev)
+    for b_ in range(wl0.batch):
+        kv[b_] = torch.from_numpy(wl0.make_kv(T=wl0.T + steps + args.warmup, seq=b_)).to(torch.bfloat16).to(dev)
+    for bits in (4, 16):
+        wl = workload(5, bits=bits)
+        T, W2, B = wl.T, wl.two_dk, wl.batch
+        W, cfg, weights, cache = setup(wl, B=B, cap_extra=steps + args.warmup + 8)
+        refp = torch.from_numpy(np.tile(wl.ref_positions(), (B, 1))).to(dev).contiguous()
+        encp = torch.from_numpy(np.tile(wl.enc_positions(), (B, 1))).to(dev).contiguous()
+        ws = torch.empty((rkv.rkv_encode_workspace_bytes(cfg, B, encp.shape[1], cache.cap_ref),),
+                         dtype=torch.uint8, device=dev)
+        rkv.rkv_append_ref(cfg, cache, kv, refp, refp, stream=stream)
+        rkv.rkv_encode(cfg, weights, cache, kv, encp, encp, ws, stream=stream)
+        torch.cuda.synchronize()
+        sels = [torch.from_numpy(np.stack([wl.make_selected(T, seq=b_, step=s_) for b_ in range(B)])).to(dev).contiguous()
+                for s_ in range(2)]
+        m = sels[0].shape[1]
+        out = torch.empty((B, m, W2), dtype=torch.bfloat16, device=dev)
+        ones = [torch.full((B, 1), T + j, dtype=torch.int32, device=dev) for j in range(steps + args.warmup)]
+
+        def step(j):
+            rkv.rkv_decode_selected(cfg, weights, cache, sels[j % 2], out=out, stream=stream)
+            p = ones[j]
+            if (T + j) % wl.stride == 0:
+                rkv.rkv_append_ref(cfg, cache, kv, p, p, stream=stream)
+            else:
+                rkv.rkv_encode(cfg, weights, cache, kv, p, p, ws, stream=stream)
+
+        for j in range(args.warmup):
+            step(j)
+        torch.cuda.synchronize()
+        print(f"[bench] timing {steps} steps", file=sys.stderr, flush=True)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for j in range(args.warmup, args.warmup + steps):
+            step(j)
+        b.record(stream)
+        torch.cuda.synchronize()
+        step_ms = a.elapsed_time(b) / steps
+        dec_ms = timed(stream, lambda: rkv.rkv_decode_selected(cfg, weights, cache, sels[0], out=out, stream=stream), 20)
+        assert cache.error_bits() == 0, cache.error_bits()
+        dr = roofline(dec_work(wl, B * m), dec_ms)
+        res[f"bits{bits}"] = {"step_ms": round(step_ms, 4), "tokens_per_s": round(B * (m + 1) / (step_ms * 1e-3), 1),
+                              "decode_selected_ms": round(dec_ms, 4),
+                              "decode_selected": {k: v for k, v in dr.items() if k in ("bound", "achieved", "unit", "frac")}}
+        del cache, ws, out
+        torch.cuda.empty_cache()
+    r4 = res["bits4"]
+    line("llama3.1-8b-kv-batch16", "tokens/s restored and encoded, 16 Llama-3.1-8B sequences of 32768 "
+         "(30 % restore + one encode per sequence and step)", r4["tokens_per_s"], r4["step_ms"],
+         {"batch": 16, "T": 32768, "two_dk": 2048}, {"by_latent": res})
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +428,10 @@ def main() -> int:
     ap.add_argument("--select-frac", type=float, default=0.3, help="read fraction for the extra selected-restore rate")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (HBM counter calibration)")
+    ap.add_argument("--workload", default="llama-prefill",
+                    choices=("llama-prefill", "qwen-long", "llama-decode", "batch16"),
+                    help="llama-prefill (default, the headline step); the others measure the remaining "
+                         "workload shapes and print their own JSON line")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
@@ -168,6 +447,9 @@ def main() -> int:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the codec runs on one GPU, "
               "see the multi-GPU notes in DESIGN.md)", file=sys.stderr)
         return 2
+
+    if args.workload != "llama-prefill":
+        return run_other(args)
 
     import torch
 
