@@ -36,6 +36,8 @@ struct CacheView {
 struct EncodePlan {
     int nsplit;        // pool chunks searched independently per token tile
     int chunk_slots;   // slots per chunk (multiple of the slot tile)
+    bool small;        // few tokens per sequence: pool scan instead of the tiled search
+    size_t off_scores; // scan scores [B][n][cap_ref] (small only)
     int cap_q;         // items per queue of the bf16 search's work plan
     size_t off_tile_nblk, off_items, off_ctr;  // work plan: blocks per tile, item queues, counters
     size_t off_part_score, off_part_slot, off_xbar, off_dh, total;

@@ -487,6 +487,146 @@ __global__ __launch_bounds__(512) void search_queue_kernel(const int* __restrict
     }
 }
 
+// ---- few tokens per sequence (decode-time appends) --------------------------------------
+// A token against its whole pool on the MFMA tiles leaves most of a 128-token tile empty and
+// reads the pool through eight workgroups; with at most 4 tokens per sequence the pool is
+// scanned instead by one wavefront per 16 slots, scores in fp32 FMAs (bf16 x FP8 products
+// are exact in fp32, as in the MFMA path), then one workgroup per token keeps its 8 best.
+// Row columns: chunk c (1024 columns), lane l holds columns 1024 c + 16 l .. +16.
+template <int NC>
+__global__ __launch_bounds__(256) void search_scan_kernel(const bf16_t* __restrict__ kv, int kv_len,
+                                                          const int* __restrict__ rows, const int* __restrict__ pos,
+                                                          int n, const fp8_t* __restrict__ ref_vals,
+                                                          const int* __restrict__ ref_pos,
+                                                          const float* __restrict__ ref_norm2,
+                                                          const int* __restrict__ ref_count, int cap_ref,
+                                                          float* __restrict__ scores) {
+    constexpr int W2 = 1024 * NC;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int b = blockIdx.y;
+    const int count = max(0, min(ref_count[b], cap_ref));
+    const int s0 = 64 * blockIdx.x + 16 * wave;
+    if (s0 >= count) return;
+    float x[4][NC][16];
+    int tp[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        tp[t] = INT_MIN;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[t][c][e] = 0.f;
+        if (t < n) {
+            tp[t] = pos[(size_t)b * n + t];
+            int kr = rows[(size_t)b * n + t];
+            kr = (kr >= 0 && kr < kv_len) ? kr : 0;
+            const bf16_t* xr = kv + ((size_t)b * kv_len + kr) * W2;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                Load8<bf16_t>::run(xr + 1024 * c + 16 * lane, &x[t][c][0]);
+                Load8<bf16_t>::run(xr + 1024 * c + 16 * lane + 8, &x[t][c][8]);
+            }
+        }
+    }
+    const fp8_t* pool = ref_vals + (size_t)b * cap_ref * W2;
+    float res[4] = {0.f, 0.f, 0.f, 0.f};  // lane r: dots of slot s0 + r
+#pragma unroll 4
+    for (int r = 0; r < 16; ++r) {
+        const int sl = min(s0 + r, count - 1);
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(pool + (size_t)sl * W2 + 1024 * c + 16 * lane);
+            float v[16];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float4 f = fp8x4_to_f32(raw[w]);
+                v[4 * w] = f.x; v[4 * w + 1] = f.y; v[4 * w + 2] = f.z; v[4 * w + 3] = f.w;
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) part[t] = fmaf(x[t][c][e], v[e], part[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t < n) {
+                const float d = wave_sum(part[t]);
+                if (lane == r) res[t] = d;
+            }
+        }
+    }
+    const int sl = s0 + lane;
+    if (lane < 16 && sl < count) {
+        const int rpos = ref_pos[(size_t)b * cap_ref + sl];
+        const float nr = ref_norm2[(size_t)b * cap_ref + sl];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (t < n) scores[((size_t)b * n + t) * cap_ref + sl] = rpos < tp[t] ? fmaf(-2.f, res[t], nr) : FLT_MAX;
+    }
+}
+
+// The 8 best (score, slot) keys of one token over its scanned pool (one workgroup per token):
+// each thread ranks its strided candidates in groups of 8, the lists merge across the lanes of
+// a wavefront, then across the four wavefronts. Masked slots (FLT_MAX) leave as empty entries.
+__global__ __launch_bounds__(256) void search_small_topk_kernel(const float* __restrict__ scores, int n,
+                                                                const int* __restrict__ ref_count, int cap_ref,
+                                                                int nsplit, float* __restrict__ part_score,
+                                                                int* __restrict__ part_slot) {
+    __shared__ uint64_t s_l[4][kTop];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = blockIdx.x, b = blockIdx.y;
+    const int count = max(0, min(ref_count[b], cap_ref));
+    const float* sc = scores + ((size_t)b * n + t) * cap_ref;
+    uint64_t lk[kTop];
+#pragma unroll
+    for (int q = 0; q < kTop; ++q) lk[q] = kNoKey;
+    for (int g0 = 0; g0 < count; g0 += 8 * 256) {
+        uint64_t gk[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int sl = g0 + 256 * e + tid;
+            gk[e] = sl < count ? score_key(sc[sl], sl) : kNoKey;
+        }
+        sort8(gk);
+        merge8(lk, gk);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        uint64_t ok[kTop];
+#pragma unroll
+        for (int q = 0; q < kTop; ++q) {
+            const int lo = __shfl_xor((int)(uint32_t)lk[q], o, 64);
+            const int hi = __shfl_xor((int)(uint32_t)(lk[q] >> 32), o, 64);
+            ok[q] = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+        }
+        merge8(lk, ok);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int q = 0; q < kTop; ++q) s_l[wave][q] = lk[q];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        uint64_t ak[kTop], bk[kTop];
+#pragma unroll
+        for (int q = 0; q < kTop; ++q) ak[q] = s_l[0][q];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+#pragma unroll
+            for (int q = 0; q < kTop; ++q) bk[q] = s_l[w][q];
+            merge8(ak, bk);
+        }
+        const size_t o = ((size_t)b * n + t) * nsplit * kTop;
+#pragma unroll
+        for (int q = 0; q < kTop; ++q) {
+            const float v = key_score(ak[q]);
+            part_score[o + q] = v;
+            part_slot[o + q] = v < FLT_MAX ? key_slot(ak[q]) : -1;
+        }
+    }
+}
+
 // Persistent search: one workgroup per CU takes items from its XCD's queue (blockIdx.x % 8,
 // the hardware's round-robin placement), then from the other queues; an item scores token
 // tile u against pool blocks c bpc .. + bpc and leaves one sorted top-8 per token.
@@ -877,8 +1017,8 @@ template <typename KvT, typename RefT>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const KvT* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
     const RefT* __restrict__ ref_vals, const float* __restrict__ ref_norm2, const float* __restrict__ part_score,
-    const int* __restrict__ part_slot, int nsplit, const int* __restrict__ tile_nblk, int bpc, int W2, int cap_ref,
-    int cap_tok, int top_k, int* __restrict__ ref_idx, KvT* __restrict__ xbar, int* err) {
+    const int* __restrict__ part_slot, int nsplit, int nch_fixed, const int* __restrict__ tile_nblk, int bpc, int W2,
+    int cap_ref, int cap_tok, int top_k, int* __restrict__ ref_idx, KvT* __restrict__ xbar, int* err) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int b = blockIdx.y;
@@ -913,7 +1053,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 
     // gather the chunks' candidates, one per lane (with a work plan, only the chunks of
     // pool blocks the token's tile read hold lists)
-    int nch = nsplit;
+    int nch = nch_fixed;
     if (tile_nblk) {
         const int ntiles = (n + kTok - 1) / kTok;
         nch = min(nsplit, (tile_nblk[(size_t)b * ntiles + t / kTok] + bpc - 1) / bpc);
@@ -1074,6 +1214,10 @@ EncodePlan plan_encode(const Shape& s, int B, int n, int cap_ref) {
     off = up(off + (size_t)8 * p.cap_q * sizeof(int));
     p.off_ctr = off;
     off = up(off + 16 * sizeof(int));
+    // few tokens per sequence: the pool is scanned (scores [B][n][cap_ref] fp32)
+    p.small = !s.f32 && n <= 4 && (s.W2 == 1024 || s.W2 == 2048);
+    p.off_scores = off;
+    if (p.small) off = up(off + (size_t)B * n * cap_ref * sizeof(float));
     p.off_part_score = off;
     off = up(off + tok * nsplit * kTop * sizeof(float));
     p.off_part_slot = off;
@@ -1144,9 +1288,30 @@ static hipError_t search_ring_impl(const Shape& s, const CacheView& c, const Enc
     return hipGetLastError();
 }
 
+static hipError_t search_small_impl(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv,
+                                    int kv_len, const int* rows, const int* pos, int n, void* ws, hipStream_t st) {
+    char* w = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(w + p.off_scores);
+    const dim3 grid((c.cap_ref + 63) / 64, c.B);
+    if (s.W2 == 2048) {
+        hipLaunchKernelGGL(search_scan_kernel<2>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(kv), kv_len, rows,
+                           pos, n, static_cast<const fp8_t*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count,
+                           c.cap_ref, scores);
+    } else {
+        hipLaunchKernelGGL(search_scan_kernel<1>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(kv), kv_len, rows,
+                           pos, n, static_cast<const fp8_t*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count,
+                           c.cap_ref, scores);
+    }
+    hipLaunchKernelGGL(search_small_topk_kernel, dim3(n, c.B), dim3(256), 0, st, scores, n, c.ref_count, c.cap_ref,
+                       p.nsplit, reinterpret_cast<float*>(w + p.off_part_score),
+                       reinterpret_cast<int*>(w + p.off_part_slot));
+    return hipGetLastError();
+}
+
 hipError_t launch_search(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
                          const int* rows, const int* pos, int n, void* ws, hipStream_t st) {
     if (s.f32) return search_impl<float, float, float>(s, c, p, kv, kv_len, rows, pos, n, ws, st);
+    if (p.small) return search_small_impl(s, c, p, kv, kv_len, rows, pos, n, ws, st);
     return search_ring_impl(s, c, p, kv, kv_len, rows, pos, n, ws, st);
 }
 
@@ -1158,8 +1323,9 @@ static hipError_t select_impl(const Shape& s, const CacheView& c, const EncodePl
     hipLaunchKernelGGL((select_kernel<KvT, RefT>), grid, dim3(kThreads), 0, st, static_cast<const KvT*>(kv), kv_len,
                        rows, pos, n, static_cast<const RefT*>(c.ref_vals), c.ref_norm2,
                        reinterpret_cast<const float*>(w + p.off_part_score),
-                       reinterpret_cast<const int*>(w + p.off_part_slot), p.nsplit,
-                       s.f32 ? nullptr : reinterpret_cast<const int*>(w + p.off_tile_nblk), p.chunk_slots, s.W2,
+                       reinterpret_cast<const int*>(w + p.off_part_slot), p.nsplit, p.small ? 1 : p.nsplit,
+                       (s.f32 || p.small) ? nullptr : reinterpret_cast<const int*>(w + p.off_tile_nblk), p.chunk_slots,
+                       s.W2,
                        c.cap_ref, c.cap_tok,
                        s.top_k, c.ref_idx, reinterpret_cast<KvT*>(w + p.off_xbar), c.err);
     return hipGetLastError();
