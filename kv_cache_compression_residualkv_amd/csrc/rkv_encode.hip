@@ -586,6 +586,195 @@ __global__ __launch_bounds__(g2r::kThreads) void latent_quant_ring_kernel(
     quant_epilogue<C, f16_t>(acc, smem_u8, t0, c0, b, n, d_c, bits, pos, cap_tok, codes, code_bytes, scale, zmin);
 }
 
+// ---- few tokens per sequence: one-wavefront tiles on deep rings --------------------------
+// Every output element goes through the same MFMA sequence as in the tiled kernels above
+// (v_mfma_f32_16x16x32_bf16 steps over K in order, starting from zero, the same fragment
+// layout) and the same epilogue arithmetic, so a token's hidden values and codes do not
+// depend on how many tokens a call carries. A workgroup is one wavefront that keeps up to
+// NST small stages in flight.
+
+// s_waitcnt vmcnt(min(ahead, A) * PER) with a compile-time count
+template <int PER, int A>
+__device__ inline void wait_ahead(int ahead) {
+    if constexpr (A == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= A) {
+            wait_vmcnt<A * PER>();
+            return;
+        }
+        wait_ahead<PER, A - 1>(ahead);
+    }
+}
+
+// single-wavefront ring: stage s is multiplied once its own loads have landed (at most NST - 1
+// later stages in flight); its slot is refilled with stage s + NST after its reads complete
+template <int NST, class F, class LA, class LB, class Ld, class Mm>
+__device__ inline void skinny_ring(const LA& a, const LB& b, int ns, char* lds, Ld&& load, Mm&& mma) {
+    constexpr int kSlot = LA::kStageBytes + LB::kStageBytes;
+    constexpr int kPer = LA::kLoads + LB::kLoads;
+    static_assert((NST - 1) * kPer < 64, "vmcnt range");
+#pragma unroll
+    for (int p = 0; p < NST; ++p) {
+        if (p < ns) {
+            a.issue(p, lds + p * kSlot);
+            b.issue(p, lds + p * kSlot + LA::kStageBytes);
+        }
+    }
+    int slot = 0;
+    for (int s = 0; s < ns; ++s) {
+        wait_ahead<kPer, NST - 1>(min(NST - 1, ns - 1 - s));
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const char* sa = lds + slot * kSlot;
+        F f;
+        load(f, sa, sa + LA::kStageBytes, 0);
+        mma(f);
+        load(f, sa, sa + LA::kStageBytes, 1);
+        mma(f);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_lgkm0();
+        if (s + NST < ns) {
+            a.issue(s + NST, lds + slot * kSlot);
+            b.issue(s + NST, lds + slot * kSlot + LA::kStageBytes);
+        }
+        slot = slot + 1 == NST ? 0 : slot + 1;
+    }
+}
+
+namespace sk {
+constexpr int NST1 = 8;  // SwiGLU: 32 A rows + 32 B rows per stage (8 KB)
+constexpr int NST2 = 6;  // W_c3: 16 A rows + 64 B rows per stage (10 KB)
+constexpr size_t bytes1 = (size_t)NST1 * (32 + 32) * kStageK * 2;
+constexpr size_t bytes2 = (size_t)NST2 * (16 + 64) * kStageK * 2;
+struct Q2 {  // quantizer epilogue layout of the W_c3 tile
+    static constexpr int BM = 16, BN = 64, WM = 16, WN = 64;
+    static constexpr int kQP = BN * 2 + 16;
+    static constexpr int kThreads = 64;
+    static constexpr int kNWN = 1;
+};
+static_assert((size_t)Q2::BM * Q2::kQP + (size_t)Q2::BM * (Q2::BN / 32) * 2 * sizeof(float) <= bytes2, "epilogue");
+}  // namespace sk
+
+struct SkFrag1 {
+    bf16x8 a[2];
+    bf16x8 b[2];
+};
+
+// SwiGLU for up to 16 tokens of one sequence: grid (d_ff / 16, batch); the wavefront's B rows
+// are W_c1 (rows 0-15) and W_c2 (rows 16-31) of hidden columns j0 .. j0 + 16.
+__global__ __launch_bounds__(64) void swiglu_skinny_kernel(const bf16_t* __restrict__ kv, int kv_len,
+                                                           const int* __restrict__ rows, int n,
+                                                           const bf16_t* __restrict__ xbar,
+                                                           const bf16_t* __restrict__ w1,
+                                                           const bf16_t* __restrict__ w2, int W2, int d_ff,
+                                                           bf16_t* __restrict__ dh) {
+    extern __shared__ __align__(16) unsigned char smem_u8[];
+    char* smem = reinterpret_cast<char*>(smem_u8);
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int j0 = 16 * blockIdx.x;
+    Op16<32, 1> la;
+    la.init([&](int r) {
+        const int t = min(r >> 1, n - 1);
+        const bf16_t* mrow = xbar + ((size_t)b * n + t) * W2;
+        if (r & 1) return mrow;
+        const int kr = rows[(size_t)b * n + t];
+        return (kr >= 0 && kr < kv_len) ? kv + ((size_t)b * kv_len + kr) * W2 : mrow;
+    });
+    Op16<32, 1> lb;
+    lb.init([&](int r) {
+        const int col = min(j0 + (r & 15), d_ff - 1);
+        return (r < 16) ? w1 + (size_t)col * W2 : w2 + (size_t)col * W2;
+    });
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = zero4();
+    auto load = [&](SkFrag1& f, const char* sa, const char* sb, int ks) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) f.b[j] = Op16<32, 1>::template frag<bf16_t>(sb, j, ks);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) f.a[i] = Op16<32, 1>::template frag<bf16_t>(sa, i, ks);
+    };
+    auto mma = [&](const SkFrag1& f) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = Mma<bf16_t>::step(acc[i][j], f.a[i], f.b[j]);
+    };
+    skinny_ring<sk::NST1, SkFrag1>(la, lb, W2 / kStageK, smem, load, mma);
+    // A rows 2 t, 2 t + 1 are kv and mean of token t; lane: hidden column j0 + lane % 16
+    const int col = j0 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const f32x4 a = acc[i][0];
+        const f32x4 g = acc[i][1];
+        const float h0 = silu(a[0]) * g[0];
+        const float h1 = silu(a[1]) * g[1];
+        const float h2 = silu(a[2]) * g[2];
+        const float h3 = silu(a[3]) * g[3];
+        const int tl = 8 * i + 2 * (lane >> 4);
+        const float d[2] = {h0 - h1, h2 - h3};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = tl + u;
+            if (t >= n || col >= d_ff) continue;
+            const float x = d[u];
+            const float hi = (float)(bf16_t)x;
+            const float r1 = x - hi;
+            const float mi = (float)(bf16_t)r1;
+            const float r2 = r1 - mi;
+            bf16_t* dst = dh + ((size_t)b * n + t) * 3 * d_ff + col;
+            dst[0] = (bf16_t)hi;
+            dst[d_ff] = (bf16_t)mi;
+            dst[2 * d_ff] = (bf16_t)r2;
+        }
+    }
+}
+
+struct SkFrag2 {
+    bf16x8 a;
+    bf16x8 b[4];
+};
+
+// W_c3 projection + quantizer for up to 16 tokens of one sequence: grid (d_c / 64, batch)
+__global__ __launch_bounds__(64) void latent_quant_skinny_kernel(
+    const bf16_t* __restrict__ dh, int n, const bf16_t* __restrict__ w3, int d_ff, int d_c, int bits,
+    const int* __restrict__ pos, int cap_tok, uint8_t* __restrict__ codes, size_t code_bytes, f16_t* __restrict__ scale,
+    f16_t* __restrict__ zmin) {
+    extern __shared__ __align__(16) unsigned char smem_u8[];
+    char* smem = reinterpret_cast<char*>(smem_u8);
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int c0 = 64 * blockIdx.x;
+    const int Kp = 3 * d_ff;
+    Op16<16, 1> la;
+    la.init([&](int r) { return dh + ((size_t)b * n + min(r, n - 1)) * Kp; });
+    WrapOp16<64, 1> lb;
+    lb.nkm = d_ff / kStageK;
+#pragma unroll
+    for (int u = 0; u < WrapOp16<64, 1>::kLoads; ++u) {
+        const int r = 16 * (u >> 1) + (lane >> 2);
+        lb.src[u] = reinterpret_cast<const char*>(w3 + (size_t)min(c0 + r, d_c - 1) * d_ff) + 64 * (u & 1) +
+                    16 * swz(lane >> 2, lane & 3);
+    }
+    f32x4 acc[1][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[0][j] = zero4();
+    auto load = [&](SkFrag2& f, const char* sa, const char* sb, int ks) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f.b[j] = Op16<64, 1>::template frag<bf16_t>(sb, j, ks);
+        f.a = Op16<16, 1>::template frag<bf16_t>(sa, 0, ks);
+    };
+    auto mma = [&](const SkFrag2& f) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[0][j] = Mma<bf16_t>::step(acc[0][j], f.a, f.b[j]);
+    };
+    skinny_ring<sk::NST2, SkFrag2>(la, lb, Kp / kStageK, smem, load, mma);
+    quant_epilogue<sk::Q2, f16_t>(acc, smem_u8, 0, c0, b, n, d_c, bits, pos, cap_tok, codes, code_bytes, scale, zmin);
+}
+
 }  // namespace
 
 template <typename T>
@@ -626,9 +815,24 @@ static hipError_t swiglu_ring_impl(const Shape& s, const CacheView& c, const Enc
     return hipGetLastError();
 }
 
+// at most this many tokens per sequence take the one-wavefront kernels
+constexpr int kSkinnyTokens = 16;
+
+static bool skinny(const Shape& s, int n) {
+    return !s.f32 && n <= kSkinnyTokens && s.d_ff % 64 == 0 && s.d_c % 64 == 0;
+}
+
 hipError_t launch_swiglu(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
                          const int* rows, int n, const void* w1, const void* w2, void* ws, hipStream_t st) {
     if (s.f32) return swiglu_impl<float>(s, c, p, kv, kv_len, rows, n, w1, w2, ws, st);
+    if (skinny(s, n)) {
+        char* w = static_cast<char*>(ws);
+        hipLaunchKernelGGL(swiglu_skinny_kernel, dim3(s.d_ff / 16, c.B), dim3(64), sk::bytes1, st,
+                           static_cast<const bf16_t*>(kv), kv_len, rows, n,
+                           reinterpret_cast<const bf16_t*>(w + p.off_xbar), static_cast<const bf16_t*>(w1),
+                           static_cast<const bf16_t*>(w2), s.W2, s.d_ff, reinterpret_cast<bf16_t*>(w + p.off_dh));
+        return hipGetLastError();
+    }
     return swiglu_ring_impl(s, c, p, kv, kv_len, rows, n, w1, w2, ws, st);
 }
 
@@ -672,6 +876,14 @@ static hipError_t latent_ring_impl(const Shape& s, const CacheView& c, const Enc
 
 hipError_t launch_latent_quant(const Shape& s, const CacheView& c, const EncodePlan& p, const int* pos, int n,
                                const void* w3, void* ws, hipStream_t st) {
+    if (skinny(s, n)) {
+        char* w = static_cast<char*>(ws);
+        hipLaunchKernelGGL(latent_quant_skinny_kernel, dim3(s.d_c / 64, c.B), dim3(64), sk::bytes2, st,
+                           reinterpret_cast<const bf16_t*>(w + p.off_dh), n, static_cast<const bf16_t*>(w3), s.d_ff,
+                           s.d_c, s.bits, pos, c.cap_tok, c.codes, c.code_bytes, static_cast<f16_t*>(c.scale),
+                           static_cast<f16_t*>(c.zmin));
+        return hipGetLastError();
+    }
     if (s.f32) return latent_impl<float, float>(s, c, p, pos, n, w3, ws, st);
     return latent_ring_impl(s, c, p, pos, n, w3, ws, st);
 }

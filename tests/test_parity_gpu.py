@@ -178,6 +178,30 @@ def test_streaming_equals_bulk_and_is_deterministic():
 # ------------------------------------------------------------------ edge cases
 
 
+def test_few_token_calls_equal_bulk_batched():
+    """Calls with at most 4 tokens per sequence (pool scan, one-wavefront GEMMs) write the
+    same records as one bulk call (tiled search and GEMMs), batch of 3, INT4 and INT2."""
+    for wid, T, bits in ((5, 300, 4), (4, 400, 2)):
+        wl = workload(wid, T=T, batch=3, bits=bits)
+        W = wl.make_weights()
+        _banner(f"few-token calls vs bulk: wid={wid} T={T} B=3 bits={bits}")
+        kvs = np.stack([wl.make_kv(seq=b) for b in range(3)])
+        bulk = GpuCodec(wl, W)
+        kv_dev = bulk.to_dev(kvs)
+        bulk.prefill(kv_dev, T)
+        small = GpuCodec(wl, W)
+        refp = torch.from_numpy(np.tile(wl.ref_positions(), (3, 1))).cuda().contiguous()
+        B.rkv_append_ref(small.cfg, small.cache, kv_dev, refp, refp)
+        encp = wl.enc_positions()
+        for k in range(0, encp.size, 4):
+            p = torch.from_numpy(np.tile(encp[k:k + 4], (3, 1)).astype(np.int32)).cuda().contiguous()
+            B.rkv_encode(small.cfg, small.W, small.cache, kv_dev, p, p)
+        torch.cuda.synchronize()
+        assert small.cache.error_bits() == 0
+        for name in ("codes", "scale", "zmin", "ref_idx"):
+            assert torch.equal(getattr(bulk.cache, name), getattr(small.cache, name)), name
+
+
 def test_empty_pool_and_range_errors():
     wl = workload(2, T=64)
     W = wl.make_weights()
