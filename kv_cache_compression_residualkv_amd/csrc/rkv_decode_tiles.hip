@@ -235,6 +235,19 @@ __device__ inline void latent_frags(f16x8 (&zf)[2][NKS], const int* __restrict__
         const size_t ro = (size_t)b * cap_tok + max(p, 0);
         const bool enc = p >= 0 && self_slot[ro] < 0;
         const uint8_t* rec = codes + ro * code_bytes;
+        if constexpr (BITS == 16) {
+            // unquantized record: d_c fp16 values in latent order; 8 of them per lane
+            // and K-step, reordered 0 4 1 5 2 6 3 7 to match the decoder's fragments
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                u32x4 w = *reinterpret_cast<const u32x4*>(rec + 64 * ks + 16 * g);
+                if (!enc) w = u32x4{0u, 0u, 0u, 0u};
+                const u32x4 o = {(w[0] & 0xFFFFu) | (w[2] << 16), (w[0] >> 16) | (w[2] & 0xFFFF0000u),
+                                 (w[1] & 0xFFFFu) | (w[3] << 16), (w[1] >> 16) | (w[3] & 0xFFFF0000u)};
+                zf[gr][ks] = *reinterpret_cast<const f16x8*>(&o);
+            }
+            continue;
+        }
         uint32_t cw[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -364,7 +377,7 @@ __device__ inline void finish_pass(f32x4 (&acc)[2][4], const unsigned char* R, c
 // grid: (token tiles, column groups, batch). Each column group is `ncg` chunks of 128
 // columns starting at column 128 ncg blockIdx.y. NKS = d_c / 32 latent K-steps (step ks
 // covers latent coordinates 32 ks .. +32, i.e. quantizer group ks); D = head dimension;
-// BITS = 4 or 2.
+// BITS = 4 or 2 (quantized records) or 16 (fp16 latents).
 
 // ---- form 1: W_d as stored (bf16), converted in the workgroup ---------------------------
 template <int NKS, int D, int BITS, typename OutT>
@@ -804,14 +817,16 @@ static hipError_t tiles_d(const Shape& s, const CacheView& c, const int* idx, in
                           const void* wd16, void* out, hipStream_t st) {
     if (s.D == 64) {
         if (s.bits == 4) return tiles_dc<64, 4, OutT>(s, c, idx, m, wd, wd16, out, st);
+        if (s.bits == 16) return tiles_dc<64, 16, OutT>(s, c, idx, m, wd, wd16, out, st);
         return tiles_dc<64, 2, OutT>(s, c, idx, m, wd, wd16, out, st);
     }
     if (s.bits == 4) return tiles_dc<128, 4, OutT>(s, c, idx, m, wd, wd16, out, st);
+    if (s.bits == 16) return tiles_dc<128, 16, OutT>(s, c, idx, m, wd, wd16, out, st);
     return tiles_dc<128, 2, OutT>(s, c, idx, m, wd, wd16, out, st);
 }
 
 bool decode_tiles_supported(const Shape& s) {
-    return !s.f32 && (s.bits == 4 || s.bits == 2) && s.group == 32 && (s.D == 64 || s.D == 128) &&
+    return !s.f32 && (s.bits == 4 || s.bits == 2 || s.bits == 16) && s.group == 32 && (s.D == 64 || s.D == 128) &&
            s.dk % dt::kCols == 0 && s.W2 % dt::kCols == 0 && s.d_c % 128 == 0 && s.d_c <= 512 &&
            s.top_k <= dt::kRefs;
 }
