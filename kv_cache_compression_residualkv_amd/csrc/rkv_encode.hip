@@ -253,7 +253,7 @@ __global__ __launch_bounds__(g1r::kThreads) void swiglu_ring_kernel(const bf16_t
             for (int j = 0; j < 4; ++j) c[i][j] = Mma<bf16_t>::step(c[i][j], f.a[i], f.b[j]);
     };
     const int ns = W2 / kStageK;
-    ring_mainloop_lrp<g1r::NST, G1Frag>(la, lb, ns, ns, smem, load, mma, acc,
+    ring_mainloop_lrp<g1r::NST, G1Frag, 12, 32>(la, lb, ns, ns, smem, load, mma, acc,
                                         [](int, f32x4(&)[8][4], bool) {});
 
     // epilogue: rows 4g+0/4g+1 of a tile are kv/mean of one token, 4g+2/4g+3 of the next
@@ -598,7 +598,7 @@ __global__ __launch_bounds__(g2r::kThreads) void latent_quant_ring_kernel(
             for (int j = 0; j < 4; ++j) c[i][j] = Mma<bf16_t>::step(c[i][j], f.a[i], f.b[j]);
     };
     const int ns = Kp / kStageK;
-    ring_mainloop_lrp<g2r::NST, G2Frag>(la, lb, ns, ns, smem, load, mma, acc, [](int, f32x4(&)[8][4], bool) {});
+    ring_mainloop_lrp<g2r::NST, G2Frag, 12, 32>(la, lb, ns, ns, smem, load, mma, acc, [](int, f32x4(&)[8][4], bool) {});
     __syncthreads();
     quant_epilogue<C, f16_t>(acc, smem_u8, t0, c0, b, n, d_c, bits, pos, cap_tok, codes, code_bytes, scale, zmin);
 }

@@ -153,6 +153,21 @@ __device__ inline void wait_stage(int ahead) {
 // s_waitcnt lgkmcnt(0) alone
 __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4)); }
 
+// Scheduling hint for one half stage: R fragment reads spread over M MFMAs, two MFMAs
+// then one read, R times, the remaining MFMAs after. With the reads clustered ahead of
+// the MFMAs (the scheduler's own choice) the matrix pipe idles while they issue.
+template <int R, int M>
+__device__ inline void interleave_reads() {
+    static_assert(2 * R <= M, "two MFMAs per read");
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, M - 2 * R, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Ring mainloop with the LDS fragment reads of one K step overlapped with the MFMAs
 // of the other. Per stage s (K steps 0 and 1, fragments f0 and f1):
 //   read f1(s) | MFMA f0(s) | wait, barrier | issue stage s + NST | read f0(s + 1) | MFMA f1(s)
@@ -162,7 +177,10 @@ __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((0xF) | (0x3 <<
 // on their side of the barrier.
 //   load(F&, const char* slot_a, const char* slot_b, int ks)  reads one K step
 //   mma(const F&, Acc&)                                       multiplies it
-template <int NST, class F, class LA, class LB, class Ld, class Mm, class Acc, class OnBlock>
+// IL_R / IL_M (when nonzero): fragment reads and MFMAs of one K step, interleaved by
+// interleave_reads.
+template <int NST, class F, int IL_R = 0, int IL_M = 0, class LA, class LB, class Ld, class Mm, class Acc,
+          class OnBlock>
 __device__ inline void ring_mainloop_lrp(const LA& a, const LB& b, int n_stages, int stages_per_block, char* lds,
                                          Ld&& load, Mm&& mma, Acc& acc, OnBlock&& on_block) {
     static_assert(NST >= 2 && NST <= 4, "2 to 4 stages");
@@ -188,6 +206,7 @@ __device__ inline void ring_mainloop_lrp(const LA& a, const LB& b, int n_stages,
         const char* sa = lds + slot * kSlot;
         load(f1, sa, sa + LA::kStageBytes, 1);
         mma(f0, acc);
+        if constexpr (IL_R > 0) interleave_reads<IL_R, IL_M>();
         const int next = slot + 1 == NST ? 0 : slot + 1;
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         wait_lgkm0();
@@ -201,6 +220,7 @@ __device__ inline void ring_mainloop_lrp(const LA& a, const LB& b, int n_stages,
         const char* na = lds + next * kSlot;
         load(f0, na, na + LA::kStageBytes, 0);
         mma(f1, acc);
+        if constexpr (IL_R > 0) interleave_reads<IL_R, IL_M>();
         slot = next;
         if (++kin == stages_per_block) {
             kin = 0;
