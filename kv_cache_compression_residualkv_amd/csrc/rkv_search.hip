@@ -1106,13 +1106,20 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     }
     bool chosen = in_set;
     if (k_i > 0 && lo_out <= hi_in) {
-        // ambiguous boundary: exact fp32 squared distances of the best 8 candidates
-        const bool cand = id >= 0 && rank < kTop;
+        // ambiguous boundary. A candidate of the set whose score plus margin lies below
+        // every outside candidate's score minus margin is closer than all of them in
+        // exact arithmetic too, so it stays; one outside whose score minus margin lies
+        // above every set member's score plus margin stays out. Only the rest (of the
+        // best 8) get exact fp32 squared distances; the free places of the set go to
+        // the best of them by (exact distance, slot). This equals ranking all 8 exactly.
+        const bool sure_in = in_set && s + margin < lo_out;
+        const bool sure_out = !in_set && s - margin > hi_in;
+        const bool amb = id >= 0 && rank < kTop && !sure_in && !sure_out;
+        const unsigned long long am = __ballot(amb);
         float dist = FLT_MAX;
-        for (int q = 0; q < kTop; ++q) {
-            const unsigned long long mq = __ballot(rank == q && id >= 0);
-            if (mq == 0ull) break;
-            const int sq = __shfl(id, __ffsll((long long)mq) - 1, 64);
+        for (unsigned long long mq = am; mq; mq &= mq - 1) {
+            const int src = __ffsll((long long)mq) - 1;
+            const int sq = __shfl(id, src, 64);
             float acc = 0.f;
             const RefT* r = pool + (size_t)sq * W2;
             for (int c = 4 * lane; c < W2; c += 256) {
@@ -1122,18 +1129,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
                 acc += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
             }
             acc = wave_sum(acc);
-            if (cand && rank == q) dist = acc;
+            if (lane == src) dist = acc;
         }
-        // rank the candidates by (exact distance, slot)
-        int erank = 0;
-        for (int j = 0; j < kTop; ++j) {
-            const int src_lane = __ffsll((long long)__ballot(rank == j && id >= 0)) - 1;
-            if (src_lane < 0) break;
-            const float dj = __shfl(dist, src_lane, 64);
-            const int ij = __shfl(key_id, src_lane, 64);
-            erank += (dj < dist || (dj == dist && ij < key_id)) ? 1 : 0;
+        int arank = 0;
+        for (unsigned long long mq = am; mq; mq &= mq - 1) {
+            const int src = __ffsll((long long)mq) - 1;
+            const float dj = __shfl(dist, src, 64);
+            const int ij = __shfl(key_id, src, 64);
+            arank += (dj < dist || (dj == dist && ij < key_id)) ? 1 : 0;
         }
-        chosen = cand && erank < k_i;
+        const int nsure = __popcll(__ballot(sure_in));
+        chosen = sure_in || (amb && arank < k_i - nsure);
     }
     // chosen slots in ascending slot order
     int srank = 0;
