@@ -660,17 +660,41 @@ __device__ inline void skinny_ring(const LA& a, const LB& b, int ns, char* lds, 
 
 namespace sk {
 constexpr int NST1 = 8;  // SwiGLU: 32 A rows + 32 B rows per stage (8 KB)
-constexpr int NST2 = 6;  // W_c3: 16 A rows + 64 B rows per stage (10 KB)
+constexpr int NST2 = 8;  // W_c3, per wavefront: 16 A rows + 32 B rows per stage (6 KB)
 constexpr size_t bytes1 = (size_t)NST1 * (32 + 32) * kStageK * 2;
-constexpr size_t bytes2 = (size_t)NST2 * (16 + 64) * kStageK * 2;
-struct Q2 {  // quantizer epilogue layout of the W_c3 tile
-    static constexpr int BM = 16, BN = 64, WM = 16, WN = 64;
+constexpr size_t ring2 = (size_t)NST2 * (16 + 32) * kStageK * 2;  // one wavefront's ring
+constexpr size_t bytes2 = 2 * ring2;
+struct Q2 {  // quantizer epilogue layout of the W_c3 tile: two wavefronts of 32 columns
+    static constexpr int BM = 16, BN = 64, WM = 16, WN = 32;
     static constexpr int kQP = BN * 2 + 16;
-    static constexpr int kThreads = 64;
-    static constexpr int kNWN = 1;
+    static constexpr int kThreads = 128;
+    static constexpr int kNWN = 2;
 };
 static_assert((size_t)Q2::BM * Q2::kQP + (size_t)Q2::BM * (Q2::BN / 32) * 2 * sizeof(float) <= bytes2, "epilogue");
 }  // namespace sk
+
+// A 16-bit operand loaded by one wavefront into a ring of its own (every block of a stage);
+// with nkm > 0 the K stage index wraps at nkm (W_c3 against the dH planes)
+template <int R>
+struct SoloOp16 {
+    static constexpr int kLoads = R / 8;
+    static constexpr int kStageBytes = R * kStageK * 2;
+    const char* src[kLoads];
+    int nkm = 0;
+    template <class RowFn>
+    __device__ inline void init(RowFn&& row) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u)
+            src[u] = reinterpret_cast<const char*>(row(16 * (u >> 1) + (lane >> 2))) + 64 * (u & 1) +
+                     16 * swz(lane >> 2, lane & 3);
+    }
+    __device__ inline void issue(int s, char* slot) const {
+        const int kc = nkm > 0 ? s % nkm : s;
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) dma16(src[u] + (size_t)kc * (kStageK * 2), slot + 1024 * u);
+    }
+};
 
 struct SkFrag1 {
     bf16x8 a[2];
@@ -752,43 +776,42 @@ __global__ __launch_bounds__(64) void swiglu_skinny_kernel(const bf16_t* __restr
 
 struct SkFrag2 {
     bf16x8 a;
-    bf16x8 b[4];
+    bf16x8 b[2];
 };
 
-// W_c3 projection + quantizer for up to 16 tokens of one sequence: grid (d_c / 64, batch)
-__global__ __launch_bounds__(64) void latent_quant_skinny_kernel(
+// W_c3 projection + quantizer for up to 16 tokens of one sequence: grid (d_c / 64, batch), two
+// wavefronts per workgroup, each with its own ring over the 32 W_c3 rows of one quantizer group
+// (every output element sees the same MFMA sequence as in the tiled kernel)
+__global__ __launch_bounds__(128) void latent_quant_skinny_kernel(
     const bf16_t* __restrict__ dh, int n, const bf16_t* __restrict__ w3, int d_ff, int d_c, int bits,
     const int* __restrict__ pos, int cap_tok, uint8_t* __restrict__ codes, size_t code_bytes, f16_t* __restrict__ scale,
     f16_t* __restrict__ zmin) {
     extern __shared__ __align__(16) unsigned char smem_u8[];
-    char* smem = reinterpret_cast<char*>(smem_u8);
     const int b = blockIdx.y;
-    const int lane = threadIdx.x & 63;
-    const int c0 = 64 * blockIdx.x;
+    const int wave = threadIdx.x >> 6;
+    char* ring = reinterpret_cast<char*>(smem_u8) + wave * sk::ring2;
+    const int c0 = 64 * blockIdx.x;       // the workgroup's 64 latent columns
+    const int cw = c0 + 32 * wave;        // this wavefront's 32 (one quantizer group)
     const int Kp = 3 * d_ff;
-    Op16<16, 1> la;
+    SoloOp16<16> la;
     la.init([&](int r) { return dh + ((size_t)b * n + min(r, n - 1)) * Kp; });
-    WrapOp16<64, 1> lb;
+    SoloOp16<32> lb;
     lb.nkm = d_ff / kStageK;
+    lb.init([&](int r) { return w3 + (size_t)min(cw + r, d_c - 1) * d_ff; });
+    f32x4 acc[1][2];
 #pragma unroll
-    for (int u = 0; u < WrapOp16<64, 1>::kLoads; ++u) {
-        const int r = 16 * (u >> 1) + (lane >> 2);
-        lb.src[u] = reinterpret_cast<const char*>(w3 + (size_t)min(c0 + r, d_c - 1) * d_ff) + 64 * (u & 1) +
-                    16 * swz(lane >> 2, lane & 3);
-    }
-    f32x4 acc[1][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[0][j] = zero4();
+    for (int j = 0; j < 2; ++j) acc[0][j] = zero4();
     auto load = [&](SkFrag2& f, const char* sa, const char* sb, int ks) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) f.b[j] = Op16<64, 1>::template frag<bf16_t>(sb, j, ks);
+        for (int j = 0; j < 2; ++j) f.b[j] = Op16<32, 1>::template frag<bf16_t>(sb, j, ks);
         f.a = Op16<16, 1>::template frag<bf16_t>(sa, 0, ks);
     };
     auto mma = [&](const SkFrag2& f) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[0][j] = Mma<bf16_t>::step(acc[0][j], f.a, f.b[j]);
+        for (int j = 0; j < 2; ++j) acc[0][j] = Mma<bf16_t>::step(acc[0][j], f.a, f.b[j]);
     };
-    skinny_ring<sk::NST2, SkFrag2>(la, lb, Kp / kStageK, smem, load, mma);
+    skinny_ring<sk::NST2, SkFrag2>(la, lb, Kp / kStageK, ring, load, mma);
+    __syncthreads();  // the epilogue's staging overlays the rings of both wavefronts
     quant_epilogue<sk::Q2, f16_t>(acc, smem_u8, 0, c0, b, n, d_c, bits, pos, cap_tok, codes, code_bytes, scale, zmin);
 }
 
@@ -894,8 +917,11 @@ static hipError_t latent_ring_impl(const Shape& s, const CacheView& c, const Enc
 hipError_t launch_latent_quant(const Shape& s, const CacheView& c, const EncodePlan& p, const int* pos, int n,
                                const void* w3, void* ws, hipStream_t st) {
     if (skinny(s, n)) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(latent_quant_skinny_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sk::bytes2);
+        if (e != hipSuccess) return e;
         char* w = static_cast<char*>(ws);
-        hipLaunchKernelGGL(latent_quant_skinny_kernel, dim3(s.d_c / 64, c.B), dim3(64), sk::bytes2, st,
+        hipLaunchKernelGGL(latent_quant_skinny_kernel, dim3(s.d_c / 64, c.B), dim3(128), sk::bytes2, st,
                            reinterpret_cast<const bf16_t*>(w + p.off_dh), n, static_cast<const bf16_t*>(w3), s.d_ff,
                            s.d_c, s.bits, pos, c.cap_tok, c.codes, c.code_bytes, static_cast<f16_t*>(c.scale),
                            static_cast<f16_t*>(c.zmin));

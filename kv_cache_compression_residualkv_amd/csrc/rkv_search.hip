@@ -493,6 +493,9 @@ __global__ __launch_bounds__(512) void search_queue_kernel(const int* __restrict
 // scanned instead by one wavefront per 16 slots, scores in fp32 FMAs (bf16 x FP8 products
 // are exact in fp32, as in the MFMA path), then one workgroup per token keeps its 8 best.
 // Row columns: chunk c (1024 columns), lane l holds columns 1024 c + 16 l .. +16.
+// slots scored per wavefront by the pool scan (all their loads in flight at once)
+constexpr int kScanSlots = 8;
+
 template <int NC>
 __global__ __launch_bounds__(256) void search_scan_kernel(const bf16_t* __restrict__ kv, int kv_len,
                                                           const int* __restrict__ rows, const int* __restrict__ pos,
@@ -505,7 +508,7 @@ __global__ __launch_bounds__(256) void search_scan_kernel(const bf16_t* __restri
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b = blockIdx.y;
     const int count = max(0, min(ref_count[b], cap_ref));
-    const int s0 = 64 * blockIdx.x + 16 * wave;
+    const int s0 = kScanSlots * (4 * blockIdx.x + wave);
     if (s0 >= count) return;
     float x[4][NC][16];
     int tp[4];
@@ -530,8 +533,8 @@ __global__ __launch_bounds__(256) void search_scan_kernel(const bf16_t* __restri
     }
     const fp8_t* pool = ref_vals + (size_t)b * cap_ref * W2;
     float res[4] = {0.f, 0.f, 0.f, 0.f};  // lane r: dots of slot s0 + r
-#pragma unroll 4
-    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+    for (int r = 0; r < kScanSlots; ++r) {
         const int sl = min(s0 + r, count - 1);
         float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -557,7 +560,7 @@ __global__ __launch_bounds__(256) void search_scan_kernel(const bf16_t* __restri
         }
     }
     const int sl = s0 + lane;
-    if (lane < 16 && sl < count) {
+    if (lane < kScanSlots && sl < count) {
         const int rpos = ref_pos[(size_t)b * cap_ref + sl];
         const float nr = ref_norm2[(size_t)b * cap_ref + sl];
 #pragma unroll
@@ -566,27 +569,31 @@ __global__ __launch_bounds__(256) void search_scan_kernel(const bf16_t* __restri
     }
 }
 
-// The 8 best (score, slot) keys of one token over its scanned pool (one workgroup per token):
-// each thread ranks its strided candidates in groups of 8, the lists merge across the lanes of
-// a wavefront, then across the four wavefronts. Masked slots (FLT_MAX) leave as empty entries.
+// The 8 best (score, slot) keys of one token over chunk blockIdx.x of its scanned pool (one
+// workgroup per token and chunk; the pool is cut into gridDim.x equal chunks and each chunk's
+// list goes to its own split, as the tiled search leaves them): each thread ranks its strided
+// candidates in groups of 8, the lists merge across the lanes of a wavefront, then across the
+// four wavefronts. Masked slots (FLT_MAX) leave as empty entries.
 __global__ __launch_bounds__(256) void search_small_topk_kernel(const float* __restrict__ scores, int n,
                                                                 const int* __restrict__ ref_count, int cap_ref,
                                                                 int nsplit, float* __restrict__ part_score,
                                                                 int* __restrict__ part_slot) {
     __shared__ uint64_t s_l[4][kTop];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int t = blockIdx.x, b = blockIdx.y;
+    const int ck = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
     const int count = max(0, min(ref_count[b], cap_ref));
+    const int cs = (count + gridDim.x - 1) / gridDim.x;
+    const int c0 = ck * cs, c1 = min(count, c0 + cs);
     const float* sc = scores + ((size_t)b * n + t) * cap_ref;
     uint64_t lk[kTop];
 #pragma unroll
     for (int q = 0; q < kTop; ++q) lk[q] = kNoKey;
-    for (int g0 = 0; g0 < count; g0 += 8 * 256) {
+    for (int g0 = c0; g0 < c1; g0 += 8 * 256) {
         uint64_t gk[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int sl = g0 + 256 * e + tid;
-            gk[e] = sl < count ? score_key(sc[sl], sl) : kNoKey;
+            gk[e] = sl < c1 ? score_key(sc[sl], sl) : kNoKey;
         }
         sort8(gk);
         merge8(lk, gk);
@@ -617,7 +624,7 @@ __global__ __launch_bounds__(256) void search_small_topk_kernel(const float* __r
             for (int q = 0; q < kTop; ++q) bk[q] = s_l[w][q];
             merge8(ak, bk);
         }
-        const size_t o = ((size_t)b * n + t) * nsplit * kTop;
+        const size_t o = (((size_t)b * n + t) * nsplit + ck) * kTop;
 #pragma unroll
         for (int q = 0; q < kTop; ++q) {
             const float v = key_score(ak[q]);
@@ -1294,11 +1301,15 @@ static hipError_t search_ring_impl(const Shape& s, const CacheView& c, const Enc
     return hipGetLastError();
 }
 
+// pool chunks of the few-token top-k: as many as the candidate splits allow, at most 8
+// (the select step merges at most 64 candidates)
+static int small_chunks(const EncodePlan& p) { return max(1, min(8, p.nsplit)); }
+
 static hipError_t search_small_impl(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv,
                                     int kv_len, const int* rows, const int* pos, int n, void* ws, hipStream_t st) {
     char* w = static_cast<char*>(ws);
     float* scores = reinterpret_cast<float*>(w + p.off_scores);
-    const dim3 grid((c.cap_ref + 63) / 64, c.B);
+    const dim3 grid((c.cap_ref + 4 * kScanSlots - 1) / (4 * kScanSlots), c.B);
     if (s.W2 == 2048) {
         hipLaunchKernelGGL(search_scan_kernel<2>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(kv), kv_len, rows,
                            pos, n, static_cast<const fp8_t*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count,
@@ -1308,7 +1319,8 @@ static hipError_t search_small_impl(const Shape& s, const CacheView& c, const En
                            pos, n, static_cast<const fp8_t*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count,
                            c.cap_ref, scores);
     }
-    hipLaunchKernelGGL(search_small_topk_kernel, dim3(n, c.B), dim3(256), 0, st, scores, n, c.ref_count, c.cap_ref,
+    hipLaunchKernelGGL(search_small_topk_kernel, dim3(small_chunks(p), n, c.B), dim3(256), 0, st, scores, n,
+                       c.ref_count, c.cap_ref,
                        p.nsplit, reinterpret_cast<float*>(w + p.off_part_score),
                        reinterpret_cast<int*>(w + p.off_part_slot));
     return hipGetLastError();
@@ -1329,7 +1341,7 @@ static hipError_t select_impl(const Shape& s, const CacheView& c, const EncodePl
     hipLaunchKernelGGL((select_kernel<KvT, RefT>), grid, dim3(kThreads), 0, st, static_cast<const KvT*>(kv), kv_len,
                        rows, pos, n, static_cast<const RefT*>(c.ref_vals), c.ref_norm2,
                        reinterpret_cast<const float*>(w + p.off_part_score),
-                       reinterpret_cast<const int*>(w + p.off_part_slot), p.nsplit, p.small ? 1 : p.nsplit,
+                       reinterpret_cast<const int*>(w + p.off_part_slot), p.nsplit, p.small ? small_chunks(p) : p.nsplit,
                        (s.f32 || p.small) ? nullptr : reinterpret_cast<const int*>(w + p.off_tile_nblk), p.chunk_slots,
                        s.W2,
                        c.cap_ref, c.cap_tok,
