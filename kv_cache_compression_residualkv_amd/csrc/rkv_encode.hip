@@ -625,7 +625,8 @@ __device__ inline void wait_ahead(int ahead) {
 }
 
 // single-wavefront ring: stage s is multiplied once its own loads have landed (at most NST - 1
-// later stages in flight); its slot is refilled with stage s + NST after its reads complete
+// later stages in flight); its slot is refilled with stage s + NST as soon as its fragments
+// are in registers, before its MFMAs
 template <int NST, class F, class LA, class LB, class Ld, class Mm>
 __device__ inline void skinny_ring(const LA& a, const LB& b, int ns, char* lds, Ld&& load, Mm&& mma) {
     constexpr int kSlot = LA::kStageBytes + LB::kStageBytes;
@@ -643,25 +644,29 @@ __device__ inline void skinny_ring(const LA& a, const LB& b, int ns, char* lds, 
         wait_ahead<kPer, NST - 1>(min(NST - 1, ns - 1 - s));
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         const char* sa = lds + slot * kSlot;
-        F f;
-        load(f, sa, sa + LA::kStageBytes, 0);
-        mma(f);
-        load(f, sa, sa + LA::kStageBytes, 1);
-        mma(f);
+        // both K steps' fragments at once (one LDS latency per stage), the slot refilled as
+        // soon as they are in registers, then the MFMAs (K step 0 before K step 1)
+        F f0, f1;
+        load(f0, sa, sa + LA::kStageBytes, 0);
+        load(f1, sa, sa + LA::kStageBytes, 1);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         wait_lgkm0();
         if (s + NST < ns) {
             a.issue(s + NST, lds + slot * kSlot);
             b.issue(s + NST, lds + slot * kSlot + LA::kStageBytes);
         }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        mma(f0);
+        mma(f1);
         slot = slot + 1 == NST ? 0 : slot + 1;
     }
 }
 
 namespace sk {
-constexpr int NST1 = 8;  // SwiGLU: 32 A rows + 32 B rows per stage (8 KB)
-constexpr int NST2 = 8;  // W_c3, per wavefront: 16 A rows + 32 B rows per stage (6 KB)
-constexpr size_t bytes1 = (size_t)NST1 * (32 + 32) * kStageK * 2;
+constexpr int NST1 = 10;  // SwiGLU, per wavefront: 32 A rows + 16 B rows per stage (6 KB)
+constexpr int NST2 = 11;  // W_c3, per wavefront: 16 A rows + 32 B rows per stage (6 KB); 10 in flight
+constexpr size_t ring1 = (size_t)NST1 * (32 + 16) * kStageK * 2;  // one wavefront's ring
+constexpr size_t bytes1 = 2 * ring1;
 constexpr size_t ring2 = (size_t)NST2 * (16 + 32) * kStageK * 2;  // one wavefront's ring
 constexpr size_t bytes2 = 2 * ring2;
 struct Q2 {  // quantizer epilogue layout of the W_c3 tile: two wavefronts of 32 columns
@@ -698,23 +703,26 @@ struct SoloOp16 {
 
 struct SkFrag1 {
     bf16x8 a[2];
-    bf16x8 b[2];
+    bf16x8 b;
 };
 
-// SwiGLU for up to 16 tokens of one sequence: grid (d_ff / 16, batch); the wavefront's B rows
-// are W_c1 (rows 0-15) and W_c2 (rows 16-31) of hidden columns j0 .. j0 + 16.
-__global__ __launch_bounds__(64) void swiglu_skinny_kernel(const bf16_t* __restrict__ kv, int kv_len,
-                                                           const int* __restrict__ rows, int n,
-                                                           const bf16_t* __restrict__ xbar,
-                                                           const bf16_t* __restrict__ w1,
-                                                           const bf16_t* __restrict__ w2, int W2, int d_ff,
-                                                           bf16_t* __restrict__ dh) {
+// SwiGLU for up to 16 tokens of one sequence: grid (d_ff / 16, batch), two wavefronts per
+// workgroup, each with its own ring: wavefront 0 multiplies the A rows (kv and mean rows of the
+// tokens) by W_c1 rows j0 .. j0 + 16, wavefront 1 by the matching W_c2 rows, and hands its
+// accumulators to wavefront 0 through LDS for the epilogue (every output element sees the same
+// MFMA sequence as in the tiled kernel).
+__global__ __launch_bounds__(128) void swiglu_skinny_kernel(const bf16_t* __restrict__ kv, int kv_len,
+                                                            const int* __restrict__ rows, int n,
+                                                            const bf16_t* __restrict__ xbar,
+                                                            const bf16_t* __restrict__ w1,
+                                                            const bf16_t* __restrict__ w2, int W2, int d_ff,
+                                                            bf16_t* __restrict__ dh) {
     extern __shared__ __align__(16) unsigned char smem_u8[];
-    char* smem = reinterpret_cast<char*>(smem_u8);
     const int b = blockIdx.y;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    char* ring = reinterpret_cast<char*>(smem_u8) + wave * sk::ring1;
     const int j0 = 16 * blockIdx.x;
-    Op16<32, 1> la;
+    SoloOp16<32> la;
     la.init([&](int r) {
         const int t = min(r >> 1, n - 1);
         const bf16_t* mrow = xbar + ((size_t)b * n + t) * W2;
@@ -722,35 +730,36 @@ __global__ __launch_bounds__(64) void swiglu_skinny_kernel(const bf16_t* __restr
         const int kr = rows[(size_t)b * n + t];
         return (kr >= 0 && kr < kv_len) ? kv + ((size_t)b * kv_len + kr) * W2 : mrow;
     });
-    Op16<32, 1> lb;
-    lb.init([&](int r) {
-        const int col = min(j0 + (r & 15), d_ff - 1);
-        return (r < 16) ? w1 + (size_t)col * W2 : w2 + (size_t)col * W2;
-    });
-    f32x4 acc[2][2];
+    SoloOp16<16> lb;
+    const bf16_t* wsel = wave == 0 ? w1 : w2;
+    lb.init([&](int r) { return wsel + (size_t)min(j0 + r, d_ff - 1) * W2; });
+    f32x4 acc[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = zero4();
+    for (int i = 0; i < 2; ++i) acc[i] = zero4();
     auto load = [&](SkFrag1& f, const char* sa, const char* sb, int ks) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) f.b[j] = Op16<32, 1>::template frag<bf16_t>(sb, j, ks);
+        f.b = Op16<16, 1>::template frag<bf16_t>(sb, 0, ks);
 #pragma unroll
         for (int i = 0; i < 2; ++i) f.a[i] = Op16<32, 1>::template frag<bf16_t>(sa, i, ks);
     };
     auto mma = [&](const SkFrag1& f) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = Mma<bf16_t>::step(acc[i][j], f.a[i], f.b[j]);
+        for (int i = 0; i < 2; ++i) acc[i] = Mma<bf16_t>::step(acc[i], f.a[i], f.b);
     };
-    skinny_ring<sk::NST1, SkFrag1>(la, lb, W2 / kStageK, smem, load, mma);
+    skinny_ring<sk::NST1, SkFrag1>(la, lb, W2 / kStageK, ring, load, mma);
+    // wavefront 1's W_c2 accumulators -> LDS (its own ring, which it has finished reading)
+    f32x4* xg = reinterpret_cast<f32x4*>(reinterpret_cast<char*>(smem_u8) + sk::ring1);
+    if (wave == 1) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) xg[64 * i + lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave != 0) return;
     // A rows 2 t, 2 t + 1 are kv and mean of token t; lane: hidden column j0 + lane % 16
     const int col = j0 + (lane & 15);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const f32x4 a = acc[i][0];
-        const f32x4 g = acc[i][1];
+        const f32x4 a = acc[i];
+        const f32x4 g = xg[64 * i + lane];
         const float h0 = silu(a[0]) * g[0];
         const float h1 = silu(a[1]) * g[1];
         const float h2 = silu(a[2]) * g[2];
@@ -867,7 +876,10 @@ hipError_t launch_swiglu(const Shape& s, const CacheView& c, const EncodePlan& p
     if (s.f32) return swiglu_impl<float>(s, c, p, kv, kv_len, rows, n, w1, w2, ws, st);
     if (skinny(s, n)) {
         char* w = static_cast<char*>(ws);
-        hipLaunchKernelGGL(swiglu_skinny_kernel, dim3(s.d_ff / 16, c.B), dim3(64), sk::bytes1, st,
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(swiglu_skinny_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sk::bytes1);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(swiglu_skinny_kernel, dim3(s.d_ff / 16, c.B), dim3(128), sk::bytes1, st,
                            static_cast<const bf16_t*>(kv), kv_len, rows, n,
                            reinterpret_cast<const bf16_t*>(w + p.off_xbar), static_cast<const bf16_t*>(w1),
                            static_cast<const bf16_t*>(w2), s.W2, s.d_ff, reinterpret_cast<bf16_t*>(w + p.off_dh));

@@ -1077,8 +1077,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     const int key_id = id >= 0 ? id : INT_MAX;
     int rank = 0;
     for (int j = 0; j < ncand; ++j) {
-        const float sj = __shfl(s, j, 64);
-        const int ij = __shfl(key_id, j, 64);
+        const float sj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), j));
+        const int ij = __builtin_amdgcn_readlane(key_id, j);
         rank += (sj < s || (sj == s && ij < key_id)) ? 1 : 0;
     }
     const unsigned long long valid_mask = __ballot(id >= 0);
