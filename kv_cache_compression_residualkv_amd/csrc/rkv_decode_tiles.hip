@@ -169,8 +169,9 @@ __device__ constexpr int chunk_tile(int h, int lt) {
 // of the pair frequencies theta^(-2j/D) / (2 pi).
 template <int D>
 __device__ inline void token_table(int* sSlot, int* sKd, int* sPos, double* sRev, const int* __restrict__ idx, int m,
-                                   int b, int tt0, const int* __restrict__ self_slot, const int* __restrict__ ref_idx,
-                                   int top_k, int cap_ref, int cap_tok, double theta, int* err) {
+                                   int b, int tt0, bool flag, const int* __restrict__ self_slot,
+                                   const int* __restrict__ ref_idx, int top_k, int cap_ref, int cap_tok, double theta,
+                                   int* err) {
     const int tid = threadIdx.x;
     if (tid < dt::TT) {
         const int t = tt0 + tid;
@@ -178,7 +179,7 @@ __device__ inline void token_table(int* sSlot, int* sKd, int* sPos, double* sRev
         if (t < m) {
             p = idx[(size_t)b * m + t];
             if (p < 0 || p >= cap_tok) {
-                if (blockIdx.y == 0) flag_error(err, DEVERR_IDX_RANGE);
+                if (flag) flag_error(err, DEVERR_IDX_RANGE);
                 p = -1;
             }
         }
@@ -374,15 +375,49 @@ __device__ inline void finish_pass(f32x4 (&acc)[2][4], const unsigned char* R, c
     }
 }
 
-// grid: (token tiles, column groups, batch). Each column group is `ncg` chunks of 128
-// columns starting at column 128 ncg blockIdx.y. NKS = d_c / 32 latent K-steps (step ks
+// Work of workgroup blockIdx.x: a token tile (of any sequence) and a run of 128-column chunks.
+// The first T1 G1 workgroups cover tiles 0 .. T1 - 1 in runs of ncg1 chunks (G1 runs per tile),
+// the rest cover the R remaining tiles in runs of ncg2 chunks (G2 runs per tile); within each
+// part the run index varies slowest, so workgroups that run together stream the same W_d
+// columns. Tile t is tile t % tpb of sequence t / tpb.
+struct TileMapArgs {
+    int T1, ncg1, R, ncg2, tpb;
+};
+struct TileMap {
+    int b, tt0, n0, nchunks, grp;
+};
+__device__ inline TileMap tile_map(const TileMapArgs& a, int W2) {
+    const int chunks = W2 / dt::kCols;
+    const int G1 = (chunks + a.ncg1 - 1) / a.ncg1;
+    const int bid = blockIdx.x;
+    int t, grp, ncg;
+    if (bid < a.T1 * G1) {
+        grp = bid / a.T1;
+        t = bid - grp * a.T1;
+        ncg = a.ncg1;
+    } else {
+        const int r = bid - a.T1 * G1;
+        grp = r / a.R;
+        t = a.T1 + (r - grp * a.R);
+        ncg = a.ncg2;
+    }
+    TileMap m;
+    m.b = t / a.tpb;
+    m.tt0 = (t - m.b * a.tpb) * dt::TT;
+    m.n0 = grp * ncg * dt::kCols;
+    m.nchunks = min(ncg, (W2 - m.n0) / dt::kCols);
+    m.grp = grp;
+    return m;
+}
+
+// One workgroup per tile_map entry. NKS = d_c / 32 latent K-steps (step ks
 // covers latent coordinates 32 ks .. +32, i.e. quantizer group ks); D = head dimension;
 // BITS = 4 or 2 (quantized records) or 16 (fp16 latents).
 
 // ---- form 1: W_d as stored (bf16), converted in the workgroup ---------------------------
 template <int NKS, int D, int BITS, typename OutT>
 __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
-    const int* __restrict__ idx, int m, int ncg, const fp8_t* __restrict__ ref_vals, const int* __restrict__ self_slot,
+    const int* __restrict__ idx, int m, TileMapArgs ta, const fp8_t* __restrict__ ref_vals, const int* __restrict__ self_slot,
     const int* __restrict__ ref_idx, const uint8_t* __restrict__ codes, size_t code_bytes,
     const f16_t* __restrict__ scale, const f16_t* __restrict__ zmin, const bf16_t* __restrict__ wd, int W2, int dk,
     int top_k, int cap_ref, int cap_tok, double theta, OutT* __restrict__ out, int* err) {
@@ -401,10 +436,11 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int g = lane >> 4, mrow = lane & 15;
-    const int b = blockIdx.z;
-    const int tt0 = blockIdx.x * dt::TT;
-    const int n0 = blockIdx.y * ncg * dt::kCols;
-    const int nchunks = min(ncg, (W2 - n0) / dt::kCols);
+    const TileMap tm = tile_map(ta, W2);
+    const int b = tm.b;
+    const int tt0 = tm.tt0;
+    const int n0 = tm.n0;
+    const int nchunks = tm.nchunks;
     const fp8_t* pool = ref_vals + (size_t)b * cap_ref * W2;
 
     // ---- W_d register ring. A stage is 64 rows (the pass's output columns) x 64 latent
@@ -437,7 +473,8 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
     load_ahead(wa, 0, 0, 0, 0);
     load_ahead(wb, 0, 0, 0, 1);
 
-    token_table<D>(sSlot, sKd, sPos, sRev, idx, m, b, tt0, self_slot, ref_idx, top_k, cap_ref, cap_tok, theta, err);
+    token_table<D>(sSlot, sKd, sPos, sRev, idx, m, b, tt0, tm.grp == 0, self_slot, ref_idx, top_k, cap_ref, cap_tok,
+                   theta, err);
     f16x8 zf[2][NKS];
     latent_frags<NKS, BITS>(zf, idx, m, b, tt0, self_slot, codes, code_bytes, scale, zmin, cap_tok);
 
@@ -567,7 +604,7 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
 // fetched at the start of each pass (after the previous pass's epilogue has read it).
 template <int NKS, int D, int BITS, typename OutT>
 __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
-    const int* __restrict__ idx, int m, int ncg, const fp8_t* __restrict__ ref_vals, const int* __restrict__ self_slot,
+    const int* __restrict__ idx, int m, TileMapArgs ta, const fp8_t* __restrict__ ref_vals, const int* __restrict__ self_slot,
     const int* __restrict__ ref_idx, const uint8_t* __restrict__ codes, size_t code_bytes,
     const f16_t* __restrict__ scale, const f16_t* __restrict__ zmin, const f16_t* __restrict__ w16, int W2, int dk,
     int top_k, int cap_ref, int cap_tok, double theta, OutT* __restrict__ out, int* err) {
@@ -586,10 +623,11 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
     int* sPos = reinterpret_cast<int*>(smem + dl::kOffPos);
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int b = blockIdx.z;
-    const int tt0 = blockIdx.x * dt::TT;
-    const int n0 = blockIdx.y * ncg * dt::kCols;
-    const int nchunks = min(ncg, (W2 - n0) / dt::kCols);
+    const TileMap tm = tile_map(ta, W2);
+    const int b = tm.b;
+    const int tt0 = tm.tt0;
+    const int n0 = tm.n0;
+    const int nchunks = tm.nchunks;
     const fp8_t* pool = ref_vals + (size_t)b * cap_ref * W2;
 
     // stage (c, h, k) -> slot ((2 c + h) KST + k) % NST. Wave w fills blocks w and w + 4
@@ -648,7 +686,8 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
         const int k2 = ahead(0, 0, 0, d, c2, h2);
         issue_w(c2, h2, k2, d);
     }
-    token_table<D>(sSlot, sKd, sPos, sRev, idx, m, b, tt0, self_slot, ref_idx, top_k, cap_ref, cap_tok, theta, err);
+    token_table<D>(sSlot, sKd, sPos, sRev, idx, m, b, tt0, tm.grp == 0, self_slot, ref_idx, top_k, cap_ref, cap_tok,
+                   theta, err);
     f16x8 zf[2][NKS];
     latent_frags<NKS, BITS>(zf, idx, m, b, tt0, self_slot, codes, code_bytes, scale, zmin, cap_tok);
     __syncthreads();
@@ -746,42 +785,60 @@ __global__ void prepare_decoder_kernel(const uint4* __restrict__ wd, uint4* __re
 
 }  // namespace
 
-// Workgroup grid: (token tiles, column groups, batch), one workgroup per CU. The
-// columns are split into groups so that the rounds of workgroups times the chunks per
-// workgroup (plus about half a chunk of set-up each) is smallest.
-static dim3 tiles_grid(const Shape& s, int B, int m, int* ncg_out) {
+// Workgroup grid, one workgroup per CU at a time. A run of chunks costs its length plus about
+// half a chunk of set-up (token table, latents, RoPE table). Either every tile is cut into runs
+// of one length (the length whose rounds of workgroups cost least), or the tiles that fill whole
+// rounds of CUs take all chunks in one run and the remaining tiles are cut finer, whichever
+// costs less.
+static TileMapArgs tiles_grid(const Shape& s, int B, int m, unsigned* nblocks) {
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
         ncu = 256;
     const int chunks = s.W2 / dt::kCols;
-    const long tiles = (long)((m + dt::TT - 1) / dt::TT) * B;
-    int best_ncg = chunks;
+    const int tpb = (m + dt::TT - 1) / dt::TT;
+    const long tiles = (long)tpb * B;
+    auto rounds_cost = [&](long ntiles, int ncg) {
+        const long groups = (chunks + ncg - 1) / ncg;
+        return (double)((ntiles * groups + ncu - 1) / ncu) * (ncg + 0.5);
+    };
+    TileMapArgs a{(int)tiles, chunks, 0, chunks, tpb};
     double best = 1e30;
     for (int ncg = chunks; ncg >= 1; --ncg) {
-        const long groups = (chunks + ncg - 1) / ncg;
-        const long rounds = (tiles * groups + ncu - 1) / ncu;
-        const double cost = (double)rounds * (ncg + 0.5);
-        if (cost < best - 1e-9) {
-            best = cost;
-            best_ncg = ncg;
+        const double c = rounds_cost(tiles, ncg);
+        if (c < best - 1e-9) {
+            best = c;
+            a.ncg1 = ncg;
         }
     }
-    *ncg_out = best_ncg;
-    return dim3((unsigned)((m + dt::TT - 1) / dt::TT), (unsigned)((chunks + best_ncg - 1) / best_ncg), (unsigned)B);
+    const long T1 = tiles / ncu * ncu, R = tiles - T1;
+    if (T1 > 0 && R > 0) {
+        const double c1 = (double)(T1 / ncu) * (chunks + 0.5);
+        for (int ncg = chunks; ncg >= 1; --ncg) {
+            const double c = c1 + rounds_cost(R, ncg);
+            if (c < best - 1e-9) {
+                best = c;
+                a = TileMapArgs{(int)T1, chunks, (int)R, ncg, tpb};
+            }
+        }
+    }
+    const long g1 = (chunks + a.ncg1 - 1) / a.ncg1, g2 = (chunks + a.ncg2 - 1) / a.ncg2;
+    *nblocks = (unsigned)(a.T1 * g1 + a.R * g2);
+    return a;
 }
 
 template <int NKS, int D, int BITS, typename OutT>
 static hipError_t tiles_impl(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd,
                              const void* wd16, void* out, hipStream_t st) {
-    int ncg = 0;
-    const dim3 grid = tiles_grid(s, c.B, m, &ncg);
+    unsigned nblocks = 0;
+    const TileMapArgs ta = tiles_grid(s, c.B, m, &nblocks);
+    const dim3 grid(nblocks);
     if (wd16) {
         auto kern = decode_tiles_dl_kernel<NKS, D, BITS, OutT>;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, dl::bytes);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, grid, dim3(dt::kThreads), dl::bytes, st, idx, m, ncg,
+        hipLaunchKernelGGL(kern, grid, dim3(dt::kThreads), dl::bytes, st, idx, m, ta,
                            static_cast<const fp8_t*>(c.ref_vals), c.self_slot, c.ref_idx, c.codes, c.code_bytes,
                            static_cast<const f16_t*>(c.scale), static_cast<const f16_t*>(c.zmin),
                            static_cast<const f16_t*>(wd16), s.W2, s.dk, s.top_k, c.cap_ref, c.cap_tok, s.theta,
@@ -791,7 +848,7 @@ static hipError_t tiles_impl(const Shape& s, const CacheView& c, const int* idx,
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, rr::bytes);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, grid, dim3(dt::kThreads), rr::bytes, st, idx, m, ncg,
+        hipLaunchKernelGGL(kern, grid, dim3(dt::kThreads), rr::bytes, st, idx, m, ta,
                            static_cast<const fp8_t*>(c.ref_vals), c.self_slot, c.ref_idx, c.codes, c.code_bytes,
                            static_cast<const f16_t*>(c.scale), static_cast<const f16_t*>(c.zmin),
                            static_cast<const bf16_t*>(wd), s.W2, s.dk, s.top_k, c.cap_ref, c.cap_tok, s.theta,
