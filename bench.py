@@ -105,6 +105,26 @@ def measured_traffic(kernel: str):
     return e.get("bytes_per_launch")
 
 
+def data_stats(kv, n_sample=128, seed=7):
+    """Statistics of the synthetic KV beside the ones the ResidualKV review page reports for real
+    models (section 1.2, Fig. 3(a) and 3(b)): the mean over tokens of the largest cosine
+    similarity to any earlier token, and the fraction of tokens whose most similar earlier token
+    lies more than 16 positions back. Computed on a seeded sample of positions."""
+    T = kv.shape[0]
+    rng = np.random.default_rng(seed)
+    pos = np.sort(rng.choice(np.arange(1, T), size=min(n_sample, T - 1), replace=False))
+    x = kv.astype(np.float32)
+    nrm = np.linalg.norm(x, axis=1)
+    nrm[nrm == 0] = 1.0
+    sims = (x[pos] @ x.T) / (nrm[pos, None] * nrm[None, :])
+    sims[np.arange(T)[None, :] >= pos[:, None]] = -np.inf  # earlier tokens only
+    best = np.argmax(sims, axis=1)
+    return {"mean_max_cosine": round(float(np.mean(sims[np.arange(pos.size), best])), 4),
+            "frac_best_match_beyond_16": round(float(np.mean(pos - best > 16)), 4),
+            "pages_real_models": {"mean_max_cosine": 0.92, "frac_best_match_beyond_16": 0.597},
+            "sample": f"{pos.size} seeded positions against their whole history"}
+
+
 def cpu_baseline(wl, kv, W, n_enc_sample=96, n_dec_sample=2048):
     """The oracle, untuned, on a bounded sample of the same step; scaled to tokens/s."""
     from oracle import OracleCodec
@@ -570,6 +590,7 @@ def main() -> int:
         "decode_selected_tok_s": round(idx_sel.shape[1] / (sel_ms * 1e-3), 1),
         "decode_selected_frac": args.select_frac,
         "per_kernel": per_kernel,
+        "data_stats": data_stats(kv_np),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
