@@ -105,6 +105,41 @@ def measured_traffic(kernel: str):
     return e.get("bytes_per_launch")
 
 
+def measured_peaks():
+    """What this machine reaches outside the codec, as context for the published peaks the
+    roofline uses: a 1 GiB device-to-device copy (read + write bytes) and a square bf16
+    GEMM through the vendor BLAS (8192^3, contiguous operands)."""
+    import torch
+
+    dev = "cuda"
+    out = {}
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    out["copy_GBps"] = round(2 * a.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del a, b
+    x = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    y = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    z = torch.matmul(x, y)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        z = torch.matmul(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    out["bf16_gemm_TFLOPs"] = round(2 * 8192 ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    del x, y, z
+    torch.cuda.empty_cache()
+    return out
+
+
 def data_stats(kv, n_sample=128, seed=7):
     """Statistics of the synthetic KV beside the ones the ResidualKV review page reports for real
     models (section 1.2, Fig. 3(a) and 3(b)): the mean over tokens of the largest cosine
@@ -591,6 +626,7 @@ def main() -> int:
         "decode_selected_frac": args.select_frac,
         "per_kernel": per_kernel,
         "data_stats": data_stats(kv_np),
+        "measured_peaks": measured_peaks(),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
