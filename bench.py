@@ -499,8 +499,8 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 5}))
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the codec runs on one GPU, "
-              "see the multi-GPU notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the codec and its "
+              "benchmark run on a single GPU", file=sys.stderr)
         return 2
 
     if args.workload != "llama-prefill":
