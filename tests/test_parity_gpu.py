@@ -88,6 +88,9 @@ CASES = {
     "batch3-int4": (5, dict(T=600, batch=3)),
     "batch2-fp16-latent": (5, dict(T=520, batch=2, bits=16)),
     "llama-shape-k2-fp16-latent": (2, dict(T=700, top_k=2, bits=16)),
+    # the largest k the boundary accepts: k_i up to 8 references, means of up to 8 FP8
+    # rows (k = 5, 6, 7 divide exactly), the restore form for k > 4
+    "llama-shape-k8": (2, dict(T=900, top_k=8)),
 }
 
 
@@ -244,6 +247,29 @@ def test_empty_pool_and_range_errors():
     assert gpu.cache.error_bits() & B.DEVERR_REF_CAPACITY
     assert gpu.cache.ref_count.item() == 8
     assert gpu.cache.ref_pos[0].tolist() == [0, 8, 16, 24, 32, 1, 9, 17]
+
+
+def test_empty_calls_change_nothing():
+    """Calls with no tokens (append and encode with n = 0, restore with m = 0) return
+    success and leave the cache as it was."""
+    wl = workload(2, T=256)
+    W = wl.make_weights()
+    gpu = GpuCodec(wl, W)
+    kv = wl.make_kv()
+    kv_dev = gpu.to_dev(kv[None])
+    gpu.prefill(kv_dev, wl.T)
+    torch.cuda.synchronize()
+    names = ("ref_vals", "ref_pos", "ref_norm2", "ref_count", "codes", "scale", "zmin", "ref_idx", "self_slot")
+    before = {n: getattr(gpu.cache, n).clone() for n in names}
+    none = torch.zeros((1, 0), dtype=torch.int32, device="cuda")
+    B.rkv_append_ref(gpu.cfg, gpu.cache, kv_dev, none, none)
+    B.rkv_encode(gpu.cfg, gpu.W, gpu.cache, kv_dev, none, none)
+    out = gpu.decode(np.zeros((1, 0), dtype=np.int32))
+    torch.cuda.synchronize()
+    assert out.shape == (1, 0, wl.two_dk)
+    assert gpu.cache.error_bits() == 0
+    for n in names:
+        assert torch.equal(before[n], getattr(gpu.cache, n)), n
 
 
 # ------------------------------------------------------------------ full sizes, sampled
