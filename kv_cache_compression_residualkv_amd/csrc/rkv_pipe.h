@@ -1,8 +1,7 @@
 // Multi-stage MFMA mainloop fed by direct global -> LDS loads (gfx950).
 //
-// A workgroup of 256 threads (4 wavefronts) computes a BM x BN tile of
-// A[BM x K] * B[BN x K]^T; both operands are K-contiguous rows read in stages of
-// 64 K values.
+// A workgroup of NW wavefronts computes a BM x BN tile of A[BM x K] * B[BN x K]^T;
+// both operands are K-contiguous rows read in stages of 64 K values.
 //
 // LDS layout of one operand stage. Rows are grouped by 16 and K by 32 (64 bytes of
 // a 16-bit row): each (row group, K step) is one 1 KB block holding its 16 rows at a
@@ -14,15 +13,12 @@
 // v_mfma_f32_16x16x32 (lane l: row l % 16, chunk l / 16) is then read from one block;
 // h makes every 16 lanes of the read cover all 64 LDS banks once (and every 8 lanes
 // 32 banks once).
-// FP8 rows (64 bytes per 64 K stage) use the same 1 KB block per row group with the
-// 16-byte granule m (K values 16 m .. +16) in place of the chunk; a bf16 fragment is
-// read as 8 bytes per lane and widened.
 //
-// Pipeline: NST stage slots form a ring. Stage s + NST - 1 is issued right after
-// the barrier that opens stage s, into the slot stage s - 1 used; before that
-// barrier every wavefront waits (s_waitcnt vmcnt) until its own loads of stage s
-// have landed, and the barrier then makes all of stage s visible. Only the
-// raw s_barrier is used: a workgroup fence would make the compiler wait for every
+// Pipeline (ring_mainloop_lrp): NST stage slots form a ring. In the middle of stage s
+// every wavefront waits (s_waitcnt vmcnt) until its own loads of stage s + 1 have
+// landed, a barrier makes them visible to all, and stage s + NST is issued into the
+// slot stage s used, whose fragments are all in registers by then. Only the raw
+// s_barrier is used: a workgroup fence would make the compiler wait for every
 // outstanding load, which is exactly what the ring is meant to avoid.
 #pragma once
 
@@ -32,7 +28,6 @@ namespace rkv {
 
 #define RKV_LDS __attribute__((address_space(3)))
 
-constexpr int kPipeThreads = 256;
 constexpr int kStageK = 64;
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -85,45 +80,6 @@ struct Op16 {
         const int lane = threadIdx.x & 63, r = lane & 15;
         return *reinterpret_cast<const typename Mma<T>::frag*>(slot + 2048 * g + 1024 * ks + 64 * r +
                                                                16 * swz(r, lane >> 4));
-    }
-};
-
-// An FP8 operand of R rows (R a multiple of 64): one 1 KB block per row group.
-template <int R>
-struct Op8 {
-    static constexpr int kLoads = R / 64;
-    static constexpr int kStageBytes = R * kStageK;
-    const char* src[kLoads];
-    template <class RowFn>
-    __device__ inline void init(RowFn&& row) {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) {
-            const int g = wave + 4 * u;
-            src[u] = reinterpret_cast<const char*>(row(16 * g + (lane >> 2))) + 16 * swz(lane >> 2, lane & 3);
-        }
-    }
-    __device__ inline void issue(int s, char* slot) const {
-        const int wave = wave_id();
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) dma16(src[u] + (size_t)s * kStageK, slot + 1024 * (wave + 4 * u));
-    }
-    // raw FP8 fragment of row group g, K step ks: K values 32 ks + 8 (lane / 16) .. +8
-    static __device__ inline uint2 frag_raw(const char* slot, int g, int ks) {
-        const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
-        const u32x2 v = lds_load<u32x2>(slot + 1024 * g + 64 * r + 16 * swz(r, 2 * ks + (q >> 1)) + 8 * (q & 1));
-        return make_uint2(v.x, v.y);
-    }
-    // exact widening of a raw fragment to bf16
-    static __device__ inline bf16x8 widen(uint2 v) {
-        const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, false);
-        const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, true);
-        const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.y, 1.0f, false);
-        const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.y, 1.0f, true);
-        bf16x8 f;
-        f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
-        f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
-        return f;
     }
 };
 
@@ -233,44 +189,6 @@ __device__ inline void ring_mainloop_lrp(const LA& a, const LB& b, int n_stages,
         mma(f0, acc);
         mma(f1, acc);
         on_block((n_stages - 1) / stages_per_block, acc, true);
-    }
-}
-
-// The ring mainloop. `a` and `b` issue their stage loads; `mma(slot_a, slot_b, acc)`
-// multiplies one resident stage; every `stages_per_block` stages `on_block(block, acc)`
-// sees the finished accumulators, which then restart from zero (the last block's
-// accumulators stay for the caller). LDS holds NST slots of (A stage, B stage).
-template <int NST, class LA, class LB, class Mm, class Acc, class OnBlock>
-__device__ inline void ring_mainloop(const LA& a, const LB& b, int n_stages, int stages_per_block, char* lds, Mm&& mma,
-                                     Acc& acc, OnBlock&& on_block) {
-    static_assert(NST >= 2 && NST <= 4, "2 to 4 stages");
-    constexpr int kSlot = LA::kStageBytes + LB::kStageBytes;
-    constexpr int kPer = LA::kLoads + LB::kLoads;
-#pragma unroll
-    for (int p = 0; p < NST - 1; ++p) {
-        if (p < n_stages) {
-            a.issue(p, lds + p * kSlot);
-            b.issue(p, lds + p * kSlot + LA::kStageBytes);
-        }
-    }
-    int kin = 0;
-    int slot = 0;
-    for (int s = 0; s < n_stages; ++s) {
-        const int ahead = min(NST - 2, n_stages - 1 - s);
-        wait_stage<NST, kPer>(ahead);
-        __builtin_amdgcn_s_barrier();
-        if (s + NST - 1 < n_stages) {
-            const int ns = slot == 0 ? NST - 1 : slot - 1;  // (s + NST - 1) mod NST
-            a.issue(s + NST - 1, lds + ns * kSlot);
-            b.issue(s + NST - 1, lds + ns * kSlot + LA::kStageBytes);
-        }
-        mma(lds + slot * kSlot, lds + slot * kSlot + LA::kStageBytes, acc);
-        slot = slot + 1 == NST ? 0 : slot + 1;
-        if (++kin == stages_per_block) {
-            kin = 0;
-            const bool last = s + 1 == n_stages;
-            on_block(s / stages_per_block, acc, last);
-        }
     }
 }
 
