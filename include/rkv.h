@@ -4,7 +4,7 @@
  * The codec follows the ResidualKV review page ("ResidualKV: 基于参考向量与残差的
  * KV Cache 压缩", review of arXiv 2602.08005v2):
  *   - a sparse pool of reference tokens stored directly in FP8 (section 2.4,
- *     section 2.6 fixed stride, section 2.7 step 4);
+ *     section 2.6 fixed or dynamic stride, section 2.7 step 4);
  *   - every other token stored as a per-token group-quantized latent residual
  *     z = f_c(kv) - f_c(mean of its k nearest references) (sections 2.2-2.4);
  *   - restore of selected tokens: dequantize, z W_d + mean, split K/V, RoPE at the
@@ -149,6 +149,23 @@ rkv_status rkv_record_bytes(const rkv_config* cfg, size_t out[6]);
 /* Workspace bytes rkv_encode needs for `batch` sequences of `n` tokens with a pool
  * capacity of cap_ref. Host-only; 0 on an invalid configuration. */
 size_t rkv_encode_workspace_bytes(const rkv_config* cfg, int32_t batch, int32_t n, int32_t cap_ref);
+
+/* Reference positions of the dynamic stride (ResidualKV review page, section 2.6):
+ *   p_0 = n_sink,  p_{m+1} = p_m + s0 + floor(alpha (p_m - n_sink)),  alpha = alpha_num / alpha_den,
+ * every p_m < limit, preceded by the sink positions 0 .. n_sink - 1 (below limit),
+ * which have no earlier token to be encoded against and so are stored directly.
+ * alpha_num = 0 gives the fixed stride s0 from n_sink. alpha is an exact rational
+ * so that the floor is exact (0.001 = 1/1000). The pages' Table VI counts at 262K
+ * (s0 = 10) are reproduced with n_sink = 0 and limit = 262144 - 256.
+ * Host-only. out: host memory for up to `cap` positions (ascending; may be NULL when
+ * cap = 0); *count receives the number of positions in the schedule.
+ * Returns RKV_ERR_INVALID_ARG for limit < 0, s0 < 1, n_sink < 0, alpha_num < 0,
+ * alpha_den < 1, cap < 0, count NULL or out NULL with cap > 0; RKV_ERR_CAPACITY when
+ * *count > cap (the first cap positions are written), so a call with cap = 0 asks
+ * for the size. The schedule is the caller's: pass the positions to rkv_append_ref
+ * and every other position to rkv_encode. */
+rkv_status rkv_reference_schedule(int32_t limit, int32_t s0, int32_t n_sink, int32_t alpha_num, int32_t alpha_den,
+                                  int32_t* out, int32_t cap, int32_t* count);
 
 /* Store tokens directly as references (section 2.7 step 4; FP8 storage, section 2.4).
  *   kv   [B, kv_len, W2] kv_dtype; rows [B, n] row of kv per token; pos [B, n] positions.

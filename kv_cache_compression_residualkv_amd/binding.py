@@ -42,6 +42,7 @@ EXPORTED = (
     "rkv_validate_config",
     "rkv_record_bytes",
     "rkv_encode_workspace_bytes",
+    "rkv_reference_schedule",
     "rkv_append_ref",
     "rkv_encode",
     "rkv_encode_ex",
@@ -122,6 +123,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.rkv_record_bytes.argtypes = [cfg_p, ctypes.POINTER(sz)]
     lib.rkv_encode_workspace_bytes.restype = sz
     lib.rkv_encode_workspace_bytes.argtypes = [cfg_p, i32, i32, i32]
+    lib.rkv_reference_schedule.restype = ctypes.c_int
+    lib.rkv_reference_schedule.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
     lib.rkv_append_ref.restype = ctypes.c_int
     lib.rkv_append_ref.argtypes = [cfg_p, c_p, vp, i32, vp, vp, i32, vp]
     lib.rkv_encode.restype = ctypes.c_int
@@ -222,6 +225,20 @@ def rkv_record_bytes(cfg: CodecConfig) -> Dict[str, int]:
 
 def rkv_encode_workspace_bytes(cfg: CodecConfig, batch: int, n: int, cap_ref: int) -> int:
     return int(load_library().rkv_encode_workspace_bytes(ctypes.byref(cfg.c_struct()), batch, n, cap_ref))
+
+
+def rkv_reference_schedule(limit: int, s0: int, n_sink: int, alpha_num: int, alpha_den: int) -> torch.Tensor:
+    """Reference positions of the dynamic stride (host int32 tensor, ascending)."""
+    lib = load_library()
+    count = ctypes.c_int32(0)
+    st = lib.rkv_reference_schedule(limit, s0, n_sink, alpha_num, alpha_den, None, 0, ctypes.byref(count))
+    if st not in (0, -3):
+        _check("rkv_reference_schedule", st)
+    out = torch.empty(count.value, dtype=torch.int32)
+    buf = ctypes.cast(out.data_ptr(), ctypes.POINTER(ctypes.c_int32)) if count.value else None
+    _check("rkv_reference_schedule",
+           lib.rkv_reference_schedule(limit, s0, n_sink, alpha_num, alpha_den, buf, count.value, ctypes.byref(count)))
+    return out
 
 
 def rkv_prepared_decoder_bytes(cfg: CodecConfig) -> int:

@@ -136,6 +136,23 @@ size_t rkv_encode_workspace_bytes(const rkv_config* cfg, int32_t batch, int32_t 
     return plan_encode(s, batch, n, cap_ref).total;
 }
 
+rkv_status rkv_reference_schedule(int32_t limit, int32_t s0, int32_t n_sink, int32_t alpha_num, int32_t alpha_den,
+                                  int32_t* out, int32_t cap, int32_t* count) {
+    if (!count || limit < 0 || s0 < 1 || n_sink < 0 || alpha_num < 0 || alpha_den < 1 || cap < 0 ||
+        (cap > 0 && !out))
+        return RKV_ERR_INVALID_ARG;
+    int64_t n = 0;
+    auto put = [&](int64_t p) {
+        if (n < cap) out[n] = (int32_t)p;
+        ++n;
+    };
+    for (int64_t p = 0; p < n_sink && p < limit; ++p) put(p);  // sink tokens
+    // gap s0 + floor(alpha (p - n_sink)) in integers: alpha_num (p - n_sink) < 2^62
+    for (int64_t p = n_sink; p < limit; p += s0 + (int64_t)alpha_num * (p - n_sink) / alpha_den) put(p);
+    *count = (int32_t)n;
+    return n > cap ? RKV_ERR_CAPACITY : RKV_OK;
+}
+
 rkv_status rkv_append_ref(const rkv_config* cfg, rkv_cache* cache, const void* kv, int32_t kv_len,
                           const int32_t* rows, const int32_t* pos, int32_t n, void* stream) {
     Shape s;

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from kv_cache_compression_residualkv_amd import binding as B
 from synth import workload
@@ -156,3 +157,32 @@ def test_entry_points_reject_bad_arguments_on_host(lib):
     assert lib.rkv_append_ref(ctypes.byref(c), ctypes.byref(cache), fake, 8, fake, fake, 0, None) == 0
     assert lib.rkv_encode(ctypes.byref(c), ctypes.byref(w), ctypes.byref(cache), fake, 8, fake, fake, 0, None, 0, None) == 0
     assert lib.rkv_decode_selected(ctypes.byref(c), ctypes.byref(w), ctypes.byref(cache), fake, 0, fake, 0, None) == 0
+
+
+@pytest.mark.parametrize(
+    "limit,s0,n_sink,num,den",
+    [(262144 - 256, 10, 0, 0, 1), (262144 - 256, 10, 0, 1, 1000), (262144 - 256, 10, 0, 2, 100),
+     (262144 - 256, 10, 0, 5, 100), (262144 - 256, 10, 0, 1, 10), (131072, 16, 4, 1, 1000),
+     (40, 3, 2, 1, 2), (300, 100, 0, 29, 100), (5, 8, 7, 1, 3), (0, 1, 0, 0, 1), (1, 1, 0, 0, 1),
+     (2 ** 31 - 1, 1000000, 0, 1, 1)],
+)
+def test_reference_schedule_matches_oracle(lib, limit, s0, n_sink, num, den):
+    from oracle.schedule import dynamic_reference_positions
+
+    got = B.rkv_reference_schedule(limit, s0, n_sink, num, den)
+    want = dynamic_reference_positions(limit, s0, n_sink, f"{num}/{den}")
+    assert got.dtype == torch.int32 and got.tolist() == want
+
+
+def test_reference_schedule_statuses(lib):
+    n = ctypes.c_int32(-1)
+    buf = (ctypes.c_int32 * 4)()
+    assert lib.rkv_reference_schedule(100, 10, 0, 0, 1, None, 0, ctypes.byref(n)) == -3 and n.value == 10
+    assert lib.rkv_reference_schedule(100, 10, 0, 0, 1, buf, 4, ctypes.byref(n)) == -3 and n.value == 10
+    assert list(buf) == [0, 10, 20, 30]
+    assert lib.rkv_reference_schedule(0, 10, 0, 0, 1, None, 0, ctypes.byref(n)) == 0 and n.value == 0
+    for args in [(-1, 10, 0, 0, 1), (100, 0, 0, 0, 1), (100, 10, -1, 0, 1), (100, 10, 0, -1, 1), (100, 10, 0, 1, 0)]:
+        assert lib.rkv_reference_schedule(*args, None, 0, ctypes.byref(n)) == -1, args
+    assert lib.rkv_reference_schedule(100, 10, 0, 0, 1, None, 4, ctypes.byref(n)) == -1
+    assert lib.rkv_reference_schedule(100, 10, 0, 0, 1, buf, -1, ctypes.byref(n)) == -1
+    assert lib.rkv_reference_schedule(100, 10, 0, 0, 1, buf, 4, None) == -1
