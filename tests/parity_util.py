@@ -13,7 +13,9 @@ Tolerances (stated for this codec):
   fp16 neighbour a few of its own ulps away; the exact and within-own-ulp
   fractions are reported;
 * restored K/V (fp32 output): max-abs error <= 2e-2 and RMS error relative to the
-  RMS of the oracle output <= 1e-3.
+  RMS of the oracle output <= 1e-3. End to end (GPU records against the oracle's),
+  a token with a permitted code difference is held instead to the bound its z~
+  difference gives through the linear decoder.
 """
 
 from __future__ import annotations
@@ -47,12 +49,19 @@ class GpuCodec:
     def to_dev(self, kv: np.ndarray) -> torch.Tensor:
         return torch.from_numpy(np.ascontiguousarray(kv)).to(self.cfg.kv_torch_dtype).to(self.device)
 
-    def prefill(self, kv_dev: torch.Tensor, T: int, ws=None):
-        """Bulk write of T tokens per sequence: references every stride-th token, encode the rest."""
+    def prefill(self, kv_dev: torch.Tensor, T: int, ws=None, refp=None):
+        """Bulk write of T tokens per sequence: references every stride-th token (or at
+        the ascending positions `refp`, a host int tensor), encode the rest."""
         wl = self.wl
-        refp = torch.arange(0, T, wl.stride, dtype=torch.int32, device=self.device)
         allp = torch.arange(T, dtype=torch.int32, device=self.device)
-        encp = allp[allp % wl.stride != 0].contiguous()
+        if refp is None:
+            refp = torch.arange(0, T, wl.stride, dtype=torch.int32, device=self.device)
+            encp = allp[allp % wl.stride != 0].contiguous()
+        else:
+            refp = refp.to(torch.int32).to(self.device)
+            is_ref = torch.zeros(T, dtype=torch.bool, device=self.device)
+            is_ref[refp.long()] = True
+            encp = allp[~is_ref].contiguous()
         Bn = self.batch
         B.rkv_append_ref(self.cfg, self.cache, kv_dev, refp.repeat(Bn, 1), refp.repeat(Bn, 1))
         return B.rkv_encode(self.cfg, self.W, self.cache, kv_dev, encp.repeat(Bn, 1), encp.repeat(Bn, 1), ws)
@@ -174,11 +183,15 @@ def kv_errors(out: np.ndarray, ref: np.ndarray):
 def assert_end_to_end(codec: OracleCodec, out: np.ndarray, orc, gpc, positions, what=""):
     """GPU restore vs the oracle's restore of the oracle's own records.
 
-    Tokens whose records agree (same codes, same stored step/min) must meet the K/V
-    bar. A token with a permitted code difference can differ by what the decoder
-    makes of that difference: the restore is linear in z~ with the same mean, and
-    RoPE is an isometry, so ||out_gpu - out_oracle|| <= ||W_d||_op ||z~_gpu - z~_oracle||
-    plus the arithmetic error. The RMS bar applies to all tokens together.
+    Tokens whose records agree (same codes, same stored step/min) must meet the
+    max-abs bar. A token whose records differ can differ by what the decoder makes
+    of that difference: the restore is linear in z~ with the same mean, and RoPE is
+    an isometry, so ||out_gpu - out_oracle|| <= ||W_d||_op ||z~_gpu - z~_oracle|| plus
+    the arithmetic error, checked token by token. The RMS bar applies to every token
+    whose integer codes agree (step/min within their ulp bar, fp16 latents): one
+    INT2 code off by one moves z~ by a whole quantization step, which a bar on
+    arithmetic error does not cover, so tokens with a permitted code difference are
+    held to the per-token bound alone.
     """
     pos = np.asarray(positions, dtype=np.int64)
     ref = codec.decode_selected(orc, pos)
@@ -192,7 +205,11 @@ def assert_end_to_end(codec: OracleCodec, out: np.ndarray, orc, gpc, positions, 
     same = dz == 0.0
     err = out.astype(np.float64) - ref
     ma_same = float(np.max(np.abs(err[same]))) if same.any() else 0.0
-    rms_rel = float(np.sqrt(np.mean(err ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
+    flip = np.zeros(pos.size, dtype=bool)
+    if codec.bits != 16 and enc.any():
+        flip[enc] = np.any(orc.q[pos[enc]] != gpc.q[pos[enc]], axis=1)
+    keep = ~flip
+    rms_rel = float(np.sqrt(np.mean(err[keep] ** 2)) / max(np.sqrt(np.mean(ref[keep] ** 2)), 1e-30)) if keep.any() else 0.0
     opn = np.linalg.norm(codec.W["Wd"], 2)
     tok_err = np.linalg.norm(err, axis=1)
     bound = opn * dz + KV_MAX_ABS
