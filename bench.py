@@ -47,11 +47,14 @@ KERNEL_NAMES = {
 }
 
 
-def algorithmic_work(wl, n_enc_decoded: int):
-    """Algorithmic flops and bytes per launch of each kernel for one step."""
+def algorithmic_work(wl, n_enc_decoded: int, refp=None):
+    """Algorithmic flops and bytes per launch of each kernel for one step (references every
+    stride-th token, or at the ascending positions refp)."""
     T, W2, d_ff, d_c, s = wl.T, wl.two_dk, wl.d_ff, wl.d_c, wl.stride
-    refp = np.arange(0, T, s)
-    encp = np.array([p for p in range(T) if p % s])
+    if refp is None:
+        refp = np.arange(0, T, s)
+    refp = np.asarray(refp, dtype=np.int64)
+    encp = np.setdiff1d(np.arange(T), refp)
     n_ref, n = refp.size, encp.size
     visible = np.searchsorted(refp, encp, side="left")  # references with position < token
     rec = d_c * wl.bits // 8 + (d_c // wl.group) * 4 + wl.top_k * 4
@@ -280,13 +283,23 @@ def run_other(args) -> int:
     if args.workload == "qwen-long":
         wl = workload(4)
         T, W2 = wl.T, wl.two_dk
-        print(f"[bench] generating {wl.name}: T={T} 2dk={W2}", file=sys.stderr, flush=True)
+        name, sched = wl.name, {"stride": wl.stride}
+        if args.alpha:
+            # dynamic stride (section 2.6) with Table VI's s0 = 10, no sink tokens and no
+            # reference among the last 256 positions
+            num, den = (int(v) for v in args.alpha.split("/"))
+            refp_np = rkv.rkv_reference_schedule(T - 256, 10, 0, num, den).numpy()
+            name = f"{wl.name}-dynamic-stride"
+            sched = {"schedule": "dynamic", "alpha": f"{num}/{den}", "s0": 10, "n_sink": 0, "tail_window": 256}
+        else:
+            refp_np = wl.ref_positions()
+        encp_np = np.setdiff1d(np.arange(T), refp_np).astype(np.int32)
+        print(f"[bench] generating {name}: T={T} 2dk={W2}, {refp_np.size} references", file=sys.stderr, flush=True)
         kv_np = wl.make_kv()
         W, cfg, weights, cache = setup(wl)
         kv = torch.from_numpy(kv_np).to(torch.bfloat16).to(dev)[None].contiguous()
-        refp_np = wl.ref_positions()
         refp = torch.from_numpy(refp_np).to(dev)[None].contiguous()
-        encp = torch.from_numpy(wl.enc_positions()).to(dev)[None].contiguous()
+        encp = torch.from_numpy(encp_np).to(dev)[None].contiguous()
         sel = torch.from_numpy(wl.make_selected(T)).to(dev)[None].contiguous()
         out = torch.empty((1, sel.shape[1], W2), dtype=torch.bfloat16, device=dev)
         n_ref, n = refp.shape[1], encp.shape[1]
@@ -319,7 +332,7 @@ def run_other(args) -> int:
         dec_ms = timed(stream, lambda: rkv.rkv_decode_selected(cfg, weights, cache, sel, out=out, stream=stream),
                        args.steps)
         m = sel.shape[1]
-        work = algorithmic_work(wl, n)
+        work = algorithmic_work(wl, n, refp_np)
         per_kernel = {p: dict(ms=round(tot[i], 4), **{k: v for k, v in roofline(work[p], tot[i]).items()
                                                       if k in ("bound", "achieved", "unit", "frac")})
                       for i, p in enumerate(("search", "select", "compress", "quantize"))}
@@ -334,10 +347,10 @@ def run_other(args) -> int:
             extra["cpu_baseline"] = dict(value=round((n + m) / (n * te + m * td), 2), unit="tokens/s", cores=cores,
                                          kind="oracle", encode_tok_s=round(1 / te, 2), decode_tok_s=round(1 / td, 2),
                                          sample=f"{ne} single-token encodes (full causal pool each) and {nd} restores")
-        line(wl.name, "tokens/s encoded and restored at the Qwen2.5-7B KV shape (bulk encode + 30 % restore)",
+        line(name, "tokens/s encoded and restored at the Qwen2.5-7B KV shape (bulk encode + 30 % restore)",
              (n + m) / ((enc_ms + dec_ms) * 1e-3), enc_ms + dec_ms,
-             {"T": T, "two_dk": W2, "d_ff": wl.d_ff, "d_c": wl.d_c, "bits": wl.bits, "stride": wl.stride,
-              "n_encode": n, "n_restore": m}, extra)
+             {"T": T, "two_dk": W2, "d_ff": wl.d_ff, "d_c": wl.d_c, "bits": wl.bits, **sched,
+              "n_ref": n_ref, "n_encode": n, "n_restore": m}, extra)
         return 0
 
     if args.workload == "llama-decode":
@@ -483,6 +496,8 @@ def main() -> int:
     ap.add_argument("--select-frac", type=float, default=0.3, help="read fraction for the extra selected-restore rate")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (HBM counter calibration)")
+    ap.add_argument("--alpha", default="", metavar="NUM/DEN",
+                    help="qwen-long only: dynamic-stride reference schedule with this alpha (e.g. 2/100)")
     ap.add_argument("--workload", default="llama-prefill",
                     choices=("llama-prefill", "qwen-long", "llama-decode", "batch16"),
                     help="llama-prefill (default, the headline step); the others measure the remaining "

@@ -19,5 +19,6 @@ from .binding import (  # noqa: F401
     rkv_encode_workspace_bytes,
     rkv_prepared_decoder_bytes,
     rkv_record_bytes,
+    rkv_reference_schedule,
     rkv_validate_config,
 )
