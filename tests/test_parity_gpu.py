@@ -91,6 +91,13 @@ CASES = {
     # the largest k the boundary accepts: k_i up to 8 references, means of up to 8 FP8
     # rows (k = 5, 6, 7 divide exactly), the restore form for k > 4
     "llama-shape-k8": (2, dict(T=900, top_k=8)),
+    # the trained codecs' shapes of Table I: Llama-3.1-8B d_ff = 3072, Qwen2.5-7B d_c = 384
+    # and d_ff = 3072 (a partial last quantizer tile, 12 latent K-steps in the restore),
+    # Qwen2.5-32B d_ff = 4096
+    "llama-table1-dff3072": (2, dict(T=1200, d_ff=3072)),
+    "qwen-table1-dc384-int2": (4, dict(T=1600, d_ff=3072, d_c=384)),
+    "qwen-table1-dc384-int4-batch2": (4, dict(T=700, d_ff=3072, d_c=384, bits=4, batch=2)),
+    "qwen32b-table1-dff4096": (2, dict(T=800, d_ff=4096)),
 }
 
 
@@ -183,9 +190,10 @@ def test_streaming_equals_bulk_and_is_deterministic():
 
 def test_few_token_calls_equal_bulk_batched():
     """Calls with at most 4 tokens per sequence (pool scan, one-wavefront GEMMs) write the
-    same records as one bulk call (tiled search and GEMMs), batch of 3, INT4 and INT2."""
-    for wid, T, bits in ((5, 300, 4), (4, 400, 2)):
-        wl = workload(wid, T=T, batch=3, bits=bits)
+    same records as one bulk call (tiled search and GEMMs), batch of 3, INT4 and INT2, and
+    at Table I's Qwen2.5-7B codec shape (d_c = 384, d_ff = 3072)."""
+    for wid, T, bits, over in ((5, 300, 4, {}), (4, 400, 2, {}), (4, 260, 2, dict(d_ff=3072, d_c=384))):
+        wl = workload(wid, T=T, batch=3, bits=bits, **over)
         W = wl.make_weights()
         _banner(f"few-token calls vs bulk: wid={wid} T={T} B=3 bits={bits}")
         kvs = np.stack([wl.make_kv(seq=b) for b in range(3)])
