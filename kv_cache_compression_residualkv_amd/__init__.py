@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     load_library,
     rkv_abi_version,
     rkv_append_ref,
+    rkv_decode_attend,
+    rkv_decode_attend_workspace_bytes,
     rkv_decode_selected,
     rkv_encode,
     rkv_encode_workspace_bytes,

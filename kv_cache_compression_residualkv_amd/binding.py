@@ -47,6 +47,8 @@ EXPORTED = (
     "rkv_encode",
     "rkv_encode_ex",
     "rkv_decode_selected",
+    "rkv_decode_attend_workspace_bytes",
+    "rkv_decode_attend",
     "rkv_prepared_decoder_bytes",
     "rkv_prepare_decoder",
 )
@@ -133,6 +135,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.rkv_encode_ex.argtypes = [cfg_p, w_p, c_p, vp, i32, vp, vp, i32, vp, sz, vp, ctypes.POINTER(vp)]
     lib.rkv_decode_selected.restype = ctypes.c_int
     lib.rkv_decode_selected.argtypes = [cfg_p, w_p, c_p, vp, i32, vp, i32, vp]
+    lib.rkv_decode_attend_workspace_bytes.restype = sz
+    lib.rkv_decode_attend_workspace_bytes.argtypes = [cfg_p, i32, i32, i32]
+    lib.rkv_decode_attend.restype = ctypes.c_int
+    lib.rkv_decode_attend.argtypes = [cfg_p, w_p, c_p, vp, i32, vp, i32, ctypes.c_float, vp, vp, sz, vp]
     lib.rkv_prepared_decoder_bytes.restype = sz
     lib.rkv_prepared_decoder_bytes.argtypes = [cfg_p]
     lib.rkv_prepare_decoder.restype = ctypes.c_int
@@ -376,3 +382,30 @@ def rkv_decode_selected(cfg: CodecConfig, weights: CodecWeights, cache: CodecCac
                                             ctypes.byref(cache._c), _ptr(idx), m, _ptr(out), odt, _stream(stream))
     _check("rkv_decode_selected", st)
     return out
+
+
+def rkv_decode_attend_workspace_bytes(cfg: CodecConfig, batch: int, m: int, n_q_heads: int) -> int:
+    return int(load_library().rkv_decode_attend_workspace_bytes(ctypes.byref(cfg.c_struct()), batch, m, n_q_heads))
+
+
+def rkv_decode_attend(cfg: CodecConfig, weights: CodecWeights, cache: CodecCache, idx: torch.Tensor,
+                      q: torch.Tensor, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Attention of q [B, H_q, D] (bf16, on the GPU) over the restored tokens idx [B, m].
+    Returns (out [B, H_q, D] fp32, the workspace used)."""
+    idx = idx.reshape(cache.batch, -1).to(torch.int32).contiguous()
+    m = idx.shape[1]
+    q = q.contiguous()
+    hq = q.shape[1]
+    if scale is None:
+        scale = 1.0 / float(cfg.head_dim) ** 0.5
+    if out is None:
+        out = torch.empty((cache.batch, hq, cfg.head_dim), dtype=torch.float32, device=q.device)
+    need = rkv_decode_attend_workspace_bytes(cfg, cache.batch, m, hq)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+    st = load_library().rkv_decode_attend(ctypes.byref(cfg.c_struct()), ctypes.byref(weights._c),
+                                          ctypes.byref(cache._c), _ptr(idx), m, _ptr(q), hq, float(scale), _ptr(out),
+                                          _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("rkv_decode_attend", st)
+    return out, workspace

@@ -229,6 +229,34 @@ rkv_status rkv_decode_selected(const rkv_config* cfg, const rkv_weights* w, cons
     return from_hip(launch_decode(s, c, idx, m, w->w_d, wd16, out, out_dtype, static_cast<hipStream_t>(stream)));
 }
 
+size_t rkv_decode_attend_workspace_bytes(const rkv_config* cfg, int32_t batch, int32_t m, int32_t n_q_heads) {
+    Shape s;
+    if (check_config(cfg, &s) != RKV_OK || batch <= 0 || m < 0 || !attend_supported(s, n_q_heads)) return 0;
+    return attend_workspace_bytes(s, batch, m);
+}
+
+rkv_status rkv_decode_attend(const rkv_config* cfg, const rkv_weights* w, const rkv_cache* cache,
+                             const int32_t* idx, int32_t m, const void* q, int32_t n_q_heads, float scale,
+                             float* out, void* workspace, size_t workspace_bytes, void* stream) {
+    Shape s;
+    rkv_status st = check_config(cfg, &s);
+    if (st != RKV_OK) return st;
+    CacheView c;
+    st = check_cache(s, cache, true, &c);
+    if (st != RKV_OK) return st;
+    if (m < 0 || n_q_heads <= 0 || n_q_heads % s.N != 0 || !(scale > 0.f) || !q || !out) return RKV_ERR_INVALID_ARG;
+    if (!attend_supported(s, n_q_heads)) return RKV_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(out)) return RKV_ERR_ALIGNMENT;
+    if (m > 0) {
+        if (!w || !w->w_d || !idx) return RKV_ERR_INVALID_ARG;
+        if (!aligned16(w->w_d) || (w->w_d_f16 && !aligned16(w->w_d_f16))) return RKV_ERR_ALIGNMENT;
+        if (!workspace || workspace_bytes < attend_workspace_bytes(s, c.B, m)) return RKV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return RKV_ERR_ALIGNMENT;
+    }
+    return from_hip(launch_attend(s, c, idx, m, m > 0 ? w->w_d : nullptr, m > 0 ? w->w_d_f16 : nullptr, q, n_q_heads,
+                                  scale, out, workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t rkv_prepared_decoder_bytes(const rkv_config* cfg) {
     Shape s;
     if (check_config(cfg, &s) != RKV_OK || s.f32) return 0;

@@ -1,0 +1,213 @@
+// Attention of one decoding query per head over the restored selected tokens
+// (ResidualKV review page, section 2.7: the sparse attention method picks the tokens,
+// the codec restores them, the layer attends over them).
+//
+//   out[b, h] = sum_j softmax_j(scale * q[b, h] . K[b, j, g]) V[b, j, g],  g = h / G,
+//
+// G = H_q / N query heads per KV head. Split over tokens (each workgroup one chunk of
+// kChunk tokens of one KV head), then one combine pass per (sequence, KV head):
+//   chunk pass: scores of the chunk's tokens for the G query heads (one thread per
+//     token reads its key row; the queries sit in LDS and are read as broadcasts),
+//     the chunk maximum and exp weights per head, then P V with 16 lanes per token
+//     row (16-byte value loads, 4 rows per wavefront at a time); writes the chunk's
+//     unnormalised output, maximum and weight sum;
+//   combine pass: rescales the chunks to the overall maximum and divides by the sum.
+// The key/value rows are bf16 [B, m, 2 d_k] (K heads, then V heads), as the restore
+// writes them. The pass reads each row once: it is bound by HBM bandwidth.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+
+#include "rkv_device.h"
+#include "rkv_internal.h"
+
+namespace rkv {
+namespace {
+
+constexpr int kChunk = 256;   // tokens per workgroup
+constexpr int kThreads = 256;  // one thread per token in the score pass
+constexpr int kMaxG = 8;       // query heads per KV head
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attend_chunk_kernel(const bf16_t* __restrict__ kv, int m, int W2, int dk,
+                                                                const bf16_t* __restrict__ q, int Hq, int G,
+                                                                float scale, float* __restrict__ part_o,
+                                                                float* __restrict__ part_ml, int nch) {
+    static_assert(D == 64 || D == 128, "head dimension");
+    __shared__ float sQ[kMaxG][D];
+    __shared__ float sP[kMaxG][kChunk];
+    __shared__ float sO[4][kMaxG][D];
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j0 = c * kChunk;
+    for (int e = tid; e < G * D; e += kThreads) {
+        const int h = e / D, d = e - h * D;
+        sQ[h][d] = (float)q[((size_t)b * Hq + (size_t)g * G + h) * D + d];
+    }
+    __syncthreads();
+
+    // scores: thread t takes token j0 + t
+    {
+        const int j = j0 + tid;
+        float s[kMaxG];
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) s[h] = 0.f;
+        if (j < m) {
+            const bf16_t* krow = kv + ((size_t)b * m + j) * W2 + (size_t)g * D;
+#pragma unroll 4
+            for (int d0 = 0; d0 < D; d0 += 8) {
+                float k8[8];
+                Load8<bf16_t>::run(krow + d0, k8);
+#pragma unroll
+                for (int h = 0; h < kMaxG; ++h) {
+                    if (h < G) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) s[h] = fmaf(k8[e], sQ[h][d0 + e], s[h]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h)
+            if (h < G) sP[h][tid] = j < m ? s[h] * scale : -INFINITY;
+    }
+    __syncthreads();
+
+    // per head: chunk maximum, weights exp(s - max), their sum (wave w: heads w, w + 4)
+    for (int h = wave; h < G; h += 4) {
+        float mx = -INFINITY;
+        for (int t = lane; t < kChunk; t += 64) mx = fmaxf(mx, sP[h][t]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        float sum = 0.f;
+        for (int t = lane; t < kChunk; t += 64) {
+            const float p = j0 + t < m ? expf(sP[h][t] - mx) : 0.f;
+            sP[h][t] = p;
+            sum += p;
+        }
+        sum = wave_sum(sum);
+        if (lane == 0) {
+            float* ml = part_ml + ((((size_t)b * (W2 / (2 * D)) + g) * nch + c) * kMaxG + h) * 2;
+            ml[0] = mx;
+            ml[1] = sum;
+        }
+    }
+    __syncthreads();
+
+    // P V: lane group r = lane / 16 takes row 16 i + 4 wave + r, lane % 16 its 8 dims
+    // (D = 64: lanes with (lane % 16) >= 8 hold no dims)
+    const int r = lane >> 4, dl = 8 * (lane & 15);
+    float acc[kMaxG][8];
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    if (dl < D) {
+        for (int i = 0; i < kChunk / 16; ++i) {
+            const int t = 16 * i + 4 * wave + r;
+            const int j = j0 + t;
+            if (j >= m) break;  // rows are taken in increasing t
+            float v8[8];
+            Load8<bf16_t>::run(kv + ((size_t)b * m + j) * W2 + dk + (size_t)g * D + dl, v8);
+#pragma unroll
+            for (int h = 0; h < kMaxG; ++h) {
+                if (h < G) {
+                    const float p = sP[h][t];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, v8[e], acc[h][e]);
+                }
+            }
+        }
+    }
+    // the four row groups of the wavefront, then the four wavefronts through LDS
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = acc[h][e];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            acc[h][e] = v;
+        }
+    if (r == 0 && dl < D) {
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h)
+            if (h < G)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sO[wave][h][dl + e] = acc[h][e];
+    }
+    __syncthreads();
+    for (int e = tid; e < G * D; e += kThreads) {
+        const int h = e / D, d = e - h * D;
+        const float o = (sO[0][h][d] + sO[1][h][d]) + (sO[2][h][d] + sO[3][h][d]);
+        part_o[((((size_t)b * (W2 / (2 * D)) + g) * nch + c) * kMaxG + h) * D + d] = o;
+    }
+}
+
+// out[b, g G + h, d] from the chunks of KV head g; no chunks (m = 0): zeros
+template <int D>
+__global__ __launch_bounds__(kThreads) void attend_combine_kernel(const float* __restrict__ part_o,
+                                                                  const float* __restrict__ part_ml, int N, int nch,
+                                                                  int Hq, int G, float* __restrict__ out) {
+    const int g = blockIdx.x, b = blockIdx.y;
+    const size_t base = ((size_t)b * N + g) * nch;
+    for (int e = threadIdx.x; e < G * D; e += kThreads) {
+        const int h = e / D, d = e - h * D;
+        float mx = -INFINITY;
+        for (int c = 0; c < nch; ++c) mx = fmaxf(mx, part_ml[((base + c) * kMaxG + h) * 2]);
+        float num = 0.f, den = 0.f;
+        for (int c = 0; c < nch; ++c) {
+            const float* ml = part_ml + ((base + c) * kMaxG + h) * 2;
+            const float w = expf(ml[0] - mx);
+            den = fmaf(ml[1], w, den);
+            num = fmaf(part_o[((base + c) * kMaxG + h) * D + d], w, num);
+        }
+        out[((size_t)b * Hq + (size_t)g * G + h) * D + d] = den > 0.f ? num / den : 0.f;
+    }
+}
+
+}  // namespace
+
+size_t attend_workspace_bytes(const Shape& s, int B, int m) {
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const size_t nch = (size_t)(m + kChunk - 1) / kChunk;
+    return up((size_t)B * m * s.W2 * sizeof(bf16_t)) + up((size_t)B * s.N * nch * kMaxG * s.D * sizeof(float)) +
+           up((size_t)B * s.N * nch * kMaxG * 2 * sizeof(float));
+}
+
+bool attend_supported(const Shape& s, int Hq) {
+    return !s.f32 && (s.D == 64 || s.D == 128) && Hq > 0 && Hq % s.N == 0 && Hq / s.N <= kMaxG;
+}
+
+hipError_t launch_attend(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd,
+                         const void* wd16, const void* q, int Hq, float scale, float* out, void* ws, hipStream_t st) {
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const int B = c.B, G = Hq / s.N;
+    const int nch = (m + kChunk - 1) / kChunk;
+    char* w = static_cast<char*>(ws);
+    bf16_t* kv = reinterpret_cast<bf16_t*>(w);
+    float* part_o = reinterpret_cast<float*>(w + up((size_t)B * m * s.W2 * sizeof(bf16_t)));
+    float* part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(part_o) +
+                                              up((size_t)B * s.N * nch * kMaxG * s.D * sizeof(float)));
+    if (m > 0) {
+        hipError_t e = launch_decode(s, c, idx, m, wd, wd16, kv, RKV_BF16, st);
+        if (e != hipSuccess) return e;
+        if (s.D == 64)
+            hipLaunchKernelGGL(attend_chunk_kernel<64>, dim3(nch, s.N, B), dim3(kThreads), 0, st, kv, m, s.W2, s.dk,
+                               static_cast<const bf16_t*>(q), Hq, G, scale, part_o, part_ml, nch);
+        else
+            hipLaunchKernelGGL(attend_chunk_kernel<128>, dim3(nch, s.N, B), dim3(kThreads), 0, st, kv, m, s.W2, s.dk,
+                               static_cast<const bf16_t*>(q), Hq, G, scale, part_o, part_ml, nch);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (s.D == 64)
+        hipLaunchKernelGGL(attend_combine_kernel<64>, dim3(s.N, B), dim3(kThreads), 0, st, part_o, part_ml, s.N, nch,
+                           Hq, G, out);
+    else
+        hipLaunchKernelGGL(attend_combine_kernel<128>, dim3(s.N, B), dim3(kThreads), 0, st, part_o, part_ml, s.N, nch,
+                           Hq, G, out);
+    return hipGetLastError();
+}
+
+}  // namespace rkv

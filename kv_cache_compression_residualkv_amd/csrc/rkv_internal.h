@@ -71,4 +71,11 @@ hipError_t launch_decode_tiles(const Shape& s, const CacheView& c, const int* id
 // W_d (bf16, [2 d_k][d_c]) -> the fp16 form the token-tile restore reads by direct loads
 hipError_t launch_prepare_decoder(const Shape& s, const void* wd, void* wd16, hipStream_t st);
 
+// Attention over the restored selected tokens (bf16 formats): restore into the
+// workspace, then split-token softmax attention for Hq query heads.
+bool attend_supported(const Shape& s, int Hq);
+size_t attend_workspace_bytes(const Shape& s, int B, int m);
+hipError_t launch_attend(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd,
+                         const void* wd16, const void* q, int Hq, float scale, float* out, void* ws, hipStream_t st);
+
 }  // namespace rkv

@@ -186,3 +186,18 @@ def test_reference_schedule_statuses(lib):
     assert lib.rkv_reference_schedule(100, 10, 0, 0, 1, None, 4, ctypes.byref(n)) == -1
     assert lib.rkv_reference_schedule(100, 10, 0, 0, 1, buf, -1, ctypes.byref(n)) == -1
     assert lib.rkv_reference_schedule(100, 10, 0, 0, 1, buf, 4, None) == -1
+
+
+def test_decode_attend_host_checks(lib):
+    cfg = B.CodecConfig.from_workload(workload(2))
+    w = B.rkv_decode_attend_workspace_bytes(cfg, 1, 39321, 32)
+    # bf16 rows of the restored tokens plus the per-chunk partials
+    assert w >= 39321 * cfg.two_dk * 2
+    assert B.rkv_decode_attend_workspace_bytes(cfg, 1, 0, 32) == 0
+    assert B.rkv_decode_attend_workspace_bytes(cfg, 1, 100, 30) == 0  # not a multiple of 8 KV heads
+    assert B.rkv_decode_attend_workspace_bytes(cfg, 1, 100, 72) == 0  # 9 query heads per KV head
+    assert B.rkv_decode_attend_workspace_bytes(B.CodecConfig.from_workload(workload(1)), 1, 100, 4) == 0
+    # argument checks run before anything touches a device: an empty cache struct
+    empty = B._Cache()
+    assert lib.rkv_decode_attend(ctypes.byref(cfg.c_struct()), None, ctypes.byref(empty), None, 4, None, 32,
+                                 ctypes.c_float(0.1), None, None, 0, None) == -1

@@ -1,0 +1,145 @@
+"""GPU parity of rkv_decode_attend: attention of one decoding query per head over the
+restored selected tokens (ResidualKV review page, section 2.7), against the oracle's
+textbook softmax attention (oracle.attention).
+
+The bar is taken on the GPU's records: the oracle restores the selected tokens from
+the records the GPU wrote, rounds them to bf16 (the precision the restored rows are
+held at between the restore and the attention) and attends in fp64. A restored
+value then differs from the oracle's by its restore error, and after the rounding
+by at most one bf16 step of the value; the output is a convex combination of the
+values, so its error is at most one bf16 step at the largest |V| plus the restore
+error (bar: that step + 1e-3), and its RMS error <= 1e-3 of the output's RMS.
+End to end (the oracle's own records, restore and attention) is printed too: the
+records may differ by the codes the code policy permits, which the pipeline tests
+check.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_residualkv_amd import binding as B
+from oracle import OracleCodec
+from oracle.attention import sparse_attention
+from oracle.formats import bf16_round
+from parity_util import GpuCodec, mirror_cache
+from synth import workload
+
+pytestmark = pytest.mark.gpu
+
+RMS_REL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    B.load_library()  # raises if librkv.so is missing: no fallback
+
+
+def _banner(msg):
+    print(f"\n[parity] {msg}", flush=True)
+
+
+def _query(wl, hq, seed):
+    """Seeded standard-normal queries [B, H_q, D], rounded to bf16."""
+    rng = np.random.default_rng([wl.wid, 7, seed])
+    q = torch.from_numpy(rng.standard_normal((wl.batch, hq, wl.head_dim)).astype(np.float32))
+    return q.to(torch.bfloat16)
+
+
+def _errors(got, want):
+    err = got.astype(np.float64) - want
+    return float(np.max(np.abs(err))), float(np.sqrt(np.mean(err ** 2)) / max(np.sqrt(np.mean(want ** 2)), 1e-30))
+
+
+def _oracle_attend(codec, cache, wl, sel, q, scale):
+    """Oracle attention and its max-abs bar (one bf16 step at the largest |V| + 1e-3)."""
+    kv = bf16_round(codec.decode_selected(cache, sel)) if sel.size else np.zeros((0, wl.two_dk))
+    kv = kv.reshape(sel.size, 2, wl.n_kv_heads, wl.head_dim)
+    vmax = float(np.max(np.abs(kv[:, 1]))) if sel.size else 0.0
+    bar = (2.0 ** (np.floor(np.log2(vmax)) - 7) if vmax > 0 else 0.0) + 1e-3
+    return sparse_attention(q, kv[:, 0], kv[:, 1], scale), bar
+
+
+# (workload, overrides, query heads, read-set sizes)
+CASES = {
+    "llama-shape-gqa4": (2, dict(T=1500), 32, [1, 5, 256, 257, 450]),
+    "qwen-shape-int2-gqa7": (4, dict(T=2000), 28, [3, 600]),
+    "batch3-int4-mha": (5, dict(T=700, batch=3), 8, [200]),
+    "batch2-fp16-latent-gqa8": (5, dict(T=520, batch=2, bits=16), 64, [300]),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_attend_parity(case):
+    wid, over, hq, sizes = CASES[case]
+    wl = workload(wid, **over)
+    T = wl.T
+    W = wl.make_weights()
+    _banner(f"attend {case}: T={T} B={wl.batch} H_q={hq} N={wl.n_kv_heads} m={sizes}")
+    gpu = GpuCodec(wl, W)
+    kvs = [wl.make_kv(seq=b) for b in range(wl.batch)]
+    gpu.prefill(gpu.to_dev(np.stack(kvs)), T)
+    torch.cuda.synchronize()
+    assert gpu.cache.error_bits() == 0
+    gpu.W.prepare_decoder(gpu.cfg)
+    codec = OracleCodec.from_workload(wl, W)
+    orcs = [codec.prefill(kvs[b], wl.stride, cap_ref=gpu.cap_ref) for b in range(wl.batch)]
+    gpcs = [mirror_cache(codec, gpu, b) for b in range(wl.batch)]
+    scale = 1.0 / np.sqrt(wl.head_dim)
+    for i, m in enumerate(sizes):
+        rng = np.random.default_rng([wid, 8, i])
+        sel = np.stack([np.sort(rng.choice(T, m, replace=False)) for _ in range(wl.batch)]).astype(np.int32)
+        q16 = _query(wl, hq, i)
+        out, _ = B.rkv_decode_attend(gpu.cfg, gpu.W, gpu.cache, torch.from_numpy(sel).cuda(), q16.cuda())
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        qn = q16.float().numpy().astype(np.float64)
+        for b in range(wl.batch):
+            want, bar = _oracle_attend(codec, gpcs[b], wl, sel[b], qn[b], scale)
+            ma, rr = _errors(out[b], want)
+            e2e, _ = _oracle_attend(codec, orcs[b], wl, sel[b], qn[b], scale)
+            ma2, rr2 = _errors(out[b], e2e)
+            print(f"[parity] attend {case} m={m} seq {b}: gpu records max_abs={ma:.3g} (bar {bar:.3g}) "
+                  f"rms_rel={rr:.3g}; end to end max_abs={ma2:.3g} rms_rel={rr2:.3g}", flush=True)
+            assert ma <= bar and rr <= RMS_REL, (case, m, b, ma, bar, rr)
+    assert gpu.cache.error_bits() == 0
+
+
+def test_attend_empty_selection_gives_zeros():
+    wl = workload(2, T=64)
+    gpu = GpuCodec(wl, wl.make_weights())
+    q = _query(wl, 32, 0).cuda()
+    out = torch.full((1, 32, wl.head_dim), 7.0, device="cuda")
+    B.rkv_decode_attend(gpu.cfg, gpu.W, gpu.cache, torch.zeros((1, 0), dtype=torch.int32, device="cuda"), q, out=out)
+    torch.cuda.synchronize()
+    assert not out.any()
+
+
+def test_attend_full_decode_read_set():
+    """The decode-side shape at full size: a 131072-token history and its 39322-token
+    read set, 32 query heads over 8 KV heads. The attention is checked against the
+    softmax average of the restored rows the restore writes in bf16 (rkv_decode_selected,
+    the same rows the call holds in its workspace; the restore itself is checked
+    against the oracle elsewhere), on every head."""
+    wl = workload(3)
+    T = wl.T
+    W = wl.make_weights()
+    _banner(f"attend at full size: T={T}: generating")
+    kv = wl.make_kv()
+    gpu = GpuCodec(wl, W)
+    gpu.prefill(gpu.to_dev(kv[None]), T)
+    torch.cuda.synchronize()
+    assert gpu.cache.error_bits() == 0
+    sel = wl.make_selected(T)[None].astype(np.int32)
+    q16 = _query(wl, 32, 99)
+    rows = gpu.decode(sel, out_dtype=torch.bfloat16, prepared=True)[0]
+    out, _ = B.rkv_decode_attend(gpu.cfg, gpu.W, gpu.cache, torch.from_numpy(sel).cuda(), q16.cuda())
+    torch.cuda.synchronize()
+    rows = rows.reshape(sel.shape[1], 2, wl.n_kv_heads, wl.head_dim).astype(np.float64)
+    want = sparse_attention(q16.float().numpy()[0].astype(np.float64), rows[:, 0], rows[:, 1], 1.0 / np.sqrt(128))
+    ma, rr = _errors(out.cpu().numpy()[0], want)
+    print(f"[parity] attend full size m={sel.shape[1]}: max_abs={ma:.3g} rms_rel={rr:.3g}", flush=True)
+    # same bf16 rows on both sides: only fp32 accumulation order and expf remain
+    assert ma <= 1e-4 and rr <= 1e-5, (ma, rr)
