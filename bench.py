@@ -420,13 +420,26 @@ def run_other(args) -> int:
         r_enc = torch.full((1, 1), T - 1, dtype=torch.int32, device=dev)
         p_enc = torch.full((1, 1), T + args.warmup + steps + 1, dtype=torch.int32, device=dev)
         enc_ms = timed(stream, lambda: rkv.rkv_encode(cfg, weights, cache, kv, r_enc, p_enc, ws, stream=stream), 20)
+        # restore + attention of one decoding query (32 query heads over the 8 KV heads of
+        # Llama-3.1-8B) in one call; the attention's share is the difference to the restore
+        hq = 32
+        q = torch.randn((1, hq, wl.head_dim), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16).to(dev)
+        att_out = torch.empty((1, hq, wl.head_dim), dtype=torch.float32, device=dev)
+        att_ws = torch.empty((rkv.rkv_decode_attend_workspace_bytes(cfg, 1, m, hq),), dtype=torch.uint8, device=dev)
+        att_ms = timed(stream, lambda: rkv.rkv_decode_attend(cfg, weights, cache, sels[0], q, out=att_out,
+                                                             workspace=att_ws, stream=stream), 20)
         for _, _, _, c_ in layers:
             assert c_.error_bits() == 0, c_.error_bits()
         dr = roofline(dec_work(wl, m), dec_ms)
+        # the attention reads each restored bf16 row once
+        ar = roofline(dict(flops=4.0 * m * hq * wl.head_dim, bytes=2.0 * m * W2), max(att_ms - dec_ms, 1e-6))
         extra = {"decode_tok_s": round(L * m / (step_ms * 1e-3), 1),
                  "per_layer": {"decode_selected_ms": round(dec_ms, 4),
                                "decode_selected": {k: v for k, v in dr.items() if k in ("bound", "achieved", "unit", "frac")},
-                               "encode_one_token_ms": round(enc_ms, 4)}}
+                               "encode_one_token_ms": round(enc_ms, 4),
+                               "decode_attend_ms": round(att_ms, 4), "attention_share_ms": round(att_ms - dec_ms, 4),
+                               "attention": {k: v for k, v in ar.items() if k in ("bound", "achieved", "unit", "frac")},
+                               "query_heads": hq}}
         if not args.no_cpu_baseline:
             print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
             te, td, cores, ne, nd = oracle_rates(wl, kv_np[:T], layers[0][0], refp_np, 4, 512, seconds_cap=10.0)

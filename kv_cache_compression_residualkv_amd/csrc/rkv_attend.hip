@@ -5,13 +5,14 @@
 //   out[b, h] = sum_j softmax_j(scale * q[b, h] . K[b, j, g]) V[b, j, g],  g = h / G,
 //
 // G = H_q / N query heads per KV head. Split over tokens (each workgroup one chunk of
-// kChunk tokens of one KV head), then one combine pass per (sequence, KV head):
+// kChunk tokens of one KV head), then one combine pass per (sequence, query head):
 //   chunk pass: scores of the chunk's tokens for the G query heads (one thread per
 //     token reads its key row; the queries sit in LDS and are read as broadcasts),
 //     the chunk maximum and exp weights per head, then P V with 16 lanes per token
 //     row (16-byte value loads, 4 rows per wavefront at a time); writes the chunk's
 //     unnormalised output, maximum and weight sum;
-//   combine pass: rescales the chunks to the overall maximum and divides by the sum.
+//   combine pass (one workgroup per query head): rescales the chunks to the overall
+//     maximum and divides by the sum.
 // The key/value rows are bf16 [B, m, 2 d_k] (K heads, then V heads), as the restore
 // writes them. The pass reads each row once: it is bound by HBM bandwidth.
 #include <hip/hip_runtime.h>
@@ -28,12 +29,13 @@ constexpr int kChunk = 256;   // tokens per workgroup
 constexpr int kThreads = 256;  // one thread per token in the score pass
 constexpr int kMaxG = 8;       // query heads per KV head
 
-template <int D>
+template <int D, int G>
 __global__ __launch_bounds__(kThreads) void attend_chunk_kernel(const bf16_t* __restrict__ kv, int m, int W2, int dk,
-                                                                const bf16_t* __restrict__ q, int Hq, int G,
-                                                                float scale, float* __restrict__ part_o,
+                                                                const bf16_t* __restrict__ q, int Hq, float scale,
+                                                                float* __restrict__ part_o,
                                                                 float* __restrict__ part_ml, int nch) {
     static_assert(D == 64 || D == 128, "head dimension");
+    static_assert(G >= 1 && G <= kMaxG, "query heads per KV head");
     __shared__ float sQ[kMaxG][D];
     __shared__ float sP[kMaxG][kChunk];
     __shared__ float sO[4][kMaxG][D];
@@ -49,27 +51,26 @@ __global__ __launch_bounds__(kThreads) void attend_chunk_kernel(const bf16_t* __
     // scores: thread t takes token j0 + t
     {
         const int j = j0 + tid;
-        float s[kMaxG];
+        float s[G];
 #pragma unroll
-        for (int h = 0; h < kMaxG; ++h) s[h] = 0.f;
-        if (j < m) {
-            const bf16_t* krow = kv + ((size_t)b * m + j) * W2 + (size_t)g * D;
-#pragma unroll 4
-            for (int d0 = 0; d0 < D; d0 += 8) {
-                float k8[8];
-                Load8<bf16_t>::run(krow + d0, k8);
+        for (int h = 0; h < G; ++h) s[h] = 0.f;
+        // rows past m read row m - 1 (their scores are replaced below): all loads in flight
+        const bf16_t* krow = kv + ((size_t)b * m + min(j, m - 1)) * W2 + (size_t)g * D;
+        uint4 raw[D / 8];
 #pragma unroll
-                for (int h = 0; h < kMaxG; ++h) {
-                    if (h < G) {
+        for (int u = 0; u < D / 8; ++u) raw[u] = *reinterpret_cast<const uint4*>(krow + 8 * u);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) s[h] = fmaf(k8[e], sQ[h][d0 + e], s[h]);
-                    }
-                }
+        for (int u = 0; u < D / 8; ++u) {
+            const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float kf = __uint_as_float((e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16));
+#pragma unroll
+                for (int h = 0; h < G; ++h) s[h] = fmaf(kf, sQ[h][8 * u + e], s[h]);
             }
         }
 #pragma unroll
-        for (int h = 0; h < kMaxG; ++h)
-            if (h < G) sP[h][tid] = j < m ? s[h] * scale : -INFINITY;
+        for (int h = 0; h < G; ++h) sP[h][tid] = j < m ? s[h] * scale : -INFINITY;
     }
     __syncthreads();
 
@@ -97,31 +98,31 @@ __global__ __launch_bounds__(kThreads) void attend_chunk_kernel(const bf16_t* __
     // P V: lane group r = lane / 16 takes row 16 i + 4 wave + r, lane % 16 its 8 dims
     // (D = 64: lanes with (lane % 16) >= 8 hold no dims)
     const int r = lane >> 4, dl = 8 * (lane & 15);
-    float acc[kMaxG][8];
+    float acc[G][8];
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     if (dl < D) {
+        // rows past m read row m - 1 with weight 0 (sP is 0 there), so every load of the
+        // loop can be in flight at once
+#pragma unroll
         for (int i = 0; i < kChunk / 16; ++i) {
             const int t = 16 * i + 4 * wave + r;
-            const int j = j0 + t;
-            if (j >= m) break;  // rows are taken in increasing t
+            const int j = min(j0 + t, m - 1);
             float v8[8];
             Load8<bf16_t>::run(kv + ((size_t)b * m + j) * W2 + dk + (size_t)g * D + dl, v8);
 #pragma unroll
-            for (int h = 0; h < kMaxG; ++h) {
-                if (h < G) {
-                    const float p = sP[h][t];
+            for (int h = 0; h < G; ++h) {
+                const float p = sP[h][t];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, v8[e], acc[h][e]);
-                }
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, v8[e], acc[h][e]);
             }
         }
     }
     // the four row groups of the wavefront, then the four wavefronts through LDS
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float v = acc[h][e];
@@ -131,10 +132,9 @@ __global__ __launch_bounds__(kThreads) void attend_chunk_kernel(const bf16_t* __
         }
     if (r == 0 && dl < D) {
 #pragma unroll
-        for (int h = 0; h < kMaxG; ++h)
-            if (h < G)
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sO[wave][h][dl + e] = acc[h][e];
+            for (int e = 0; e < 8; ++e) sO[wave][h][dl + e] = acc[h][e];
     }
     __syncthreads();
     for (int e = tid; e < G * D; e += kThreads) {
@@ -144,25 +144,77 @@ __global__ __launch_bounds__(kThreads) void attend_chunk_kernel(const bf16_t* __
     }
 }
 
-// out[b, g G + h, d] from the chunks of KV head g; no chunks (m = 0): zeros
+// out[b, hq, d] for one query head hq = g G + h per workgroup; no chunks (m = 0): zeros.
+// kCombThreads threads: thread (slice, d) sums the chunks slice, slice + S, ... of
+// dimension d (S = kCombThreads / D slices), after the block-wide maximum of the chunks'
+// maxima; the slices are then added through LDS.
+constexpr int kCombThreads = 512;
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void attend_combine_kernel(const float* __restrict__ part_o,
-                                                                  const float* __restrict__ part_ml, int N, int nch,
-                                                                  int Hq, int G, float* __restrict__ out) {
-    const int g = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(kCombThreads) void attend_combine_kernel(const float* __restrict__ part_o,
+                                                                      const float* __restrict__ part_ml, int N,
+                                                                      int nch, int Hq, int G, float* __restrict__ out) {
+    constexpr int S = kCombThreads / D;
+    __shared__ float sMax[kCombThreads / 64];
+    __shared__ float sNum[S][D];
+    __shared__ float sDen[S];
+    const int hq = blockIdx.x, b = blockIdx.y;
+    const int g = hq / G, h = hq - g * G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t base = ((size_t)b * N + g) * nch;
-    for (int e = threadIdx.x; e < G * D; e += kThreads) {
-        const int h = e / D, d = e - h * D;
-        float mx = -INFINITY;
-        for (int c = 0; c < nch; ++c) mx = fmaxf(mx, part_ml[((base + c) * kMaxG + h) * 2]);
-        float num = 0.f, den = 0.f;
-        for (int c = 0; c < nch; ++c) {
-            const float* ml = part_ml + ((base + c) * kMaxG + h) * 2;
-            const float w = expf(ml[0] - mx);
-            den = fmaf(ml[1], w, den);
-            num = fmaf(part_o[((base + c) * kMaxG + h) * D + d], w, num);
+    float mx = -INFINITY;
+    for (int c = tid; c < nch; c += kCombThreads) mx = fmaxf(mx, part_ml[((base + c) * kMaxG + h) * 2]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) sMax[wave] = mx;
+    __syncthreads();
+    mx = sMax[0];
+#pragma unroll
+    for (int w = 1; w < kCombThreads / 64; ++w) mx = fmaxf(mx, sMax[w]);
+    const int d = tid % D, sl = tid / D;
+    float num = 0.f, den = 0.f;
+#pragma unroll 4
+    for (int c = sl; c < nch; c += S) {
+        const float* ml = part_ml + ((base + c) * kMaxG + h) * 2;
+        const float w = expf(ml[0] - mx);
+        den = fmaf(ml[1], w, den);
+        num = fmaf(part_o[((base + c) * kMaxG + h) * D + d], w, num);
+    }
+    sNum[sl][d] = num;
+    if (d == 0) sDen[sl] = den;
+    __syncthreads();
+    if (tid < D) {
+        float n = 0.f, dd = 0.f;
+#pragma unroll
+        for (int k = 0; k < S; ++k) {
+            n += sNum[k][tid];
+            dd += sDen[k];
         }
-        out[((size_t)b * Hq + (size_t)g * G + h) * D + d] = den > 0.f ? num / den : 0.f;
+        out[((size_t)b * Hq + hq) * D + tid] = dd > 0.f ? n / dd : 0.f;
+    }
+}
+
+template <int D, int G>
+hipError_t chunk_launch(dim3 grid, hipStream_t st, const bf16_t* kv, int m, int W2, int dk, const void* q, int Hq,
+                        float scale, float* part_o, float* part_ml, int nch) {
+    hipLaunchKernelGGL((attend_chunk_kernel<D, G>), grid, dim3(kThreads), 0, st, kv, m, W2, dk,
+                       static_cast<const bf16_t*>(q), Hq, scale, part_o, part_ml, nch);
+    return hipSuccess;
+}
+
+template <int D>
+hipError_t chunk_g(int G, dim3 grid, hipStream_t st, const bf16_t* kv, int m, int W2, int dk, const void* q, int Hq,
+                   float scale, float* part_o, float* part_ml, int nch) {
+    switch (G) {
+        case 1: return chunk_launch<D, 1>(grid, st, kv, m, W2, dk, q, Hq, scale, part_o, part_ml, nch);
+        case 2: return chunk_launch<D, 2>(grid, st, kv, m, W2, dk, q, Hq, scale, part_o, part_ml, nch);
+        case 3: return chunk_launch<D, 3>(grid, st, kv, m, W2, dk, q, Hq, scale, part_o, part_ml, nch);
+        case 4: return chunk_launch<D, 4>(grid, st, kv, m, W2, dk, q, Hq, scale, part_o, part_ml, nch);
+        case 5: return chunk_launch<D, 5>(grid, st, kv, m, W2, dk, q, Hq, scale, part_o, part_ml, nch);
+        case 6: return chunk_launch<D, 6>(grid, st, kv, m, W2, dk, q, Hq, scale, part_o, part_ml, nch);
+        case 7: return chunk_launch<D, 7>(grid, st, kv, m, W2, dk, q, Hq, scale, part_o, part_ml, nch);
+        case 8: return chunk_launch<D, 8>(grid, st, kv, m, W2, dk, q, Hq, scale, part_o, part_ml, nch);
+        default: return hipErrorInvalidValue;
     }
 }
 
@@ -192,21 +244,18 @@ hipError_t launch_attend(const Shape& s, const CacheView& c, const int* idx, int
     if (m > 0) {
         hipError_t e = launch_decode(s, c, idx, m, wd, wd16, kv, RKV_BF16, st);
         if (e != hipSuccess) return e;
-        if (s.D == 64)
-            hipLaunchKernelGGL(attend_chunk_kernel<64>, dim3(nch, s.N, B), dim3(kThreads), 0, st, kv, m, s.W2, s.dk,
-                               static_cast<const bf16_t*>(q), Hq, G, scale, part_o, part_ml, nch);
-        else
-            hipLaunchKernelGGL(attend_chunk_kernel<128>, dim3(nch, s.N, B), dim3(kThreads), 0, st, kv, m, s.W2, s.dk,
-                               static_cast<const bf16_t*>(q), Hq, G, scale, part_o, part_ml, nch);
+        e = s.D == 64 ? chunk_g<64>(G, dim3(nch, s.N, B), st, kv, m, s.W2, s.dk, q, Hq, scale, part_o, part_ml, nch)
+                      : chunk_g<128>(G, dim3(nch, s.N, B), st, kv, m, s.W2, s.dk, q, Hq, scale, part_o, part_ml, nch);
+        if (e != hipSuccess) return e;
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (s.D == 64)
-        hipLaunchKernelGGL(attend_combine_kernel<64>, dim3(s.N, B), dim3(kThreads), 0, st, part_o, part_ml, s.N, nch,
-                           Hq, G, out);
+        hipLaunchKernelGGL(attend_combine_kernel<64>, dim3(Hq, B), dim3(kCombThreads), 0, st, part_o, part_ml, s.N,
+                           nch, Hq, G, out);
     else
-        hipLaunchKernelGGL(attend_combine_kernel<128>, dim3(s.N, B), dim3(kThreads), 0, st, part_o, part_ml, s.N, nch,
-                           Hq, G, out);
+        hipLaunchKernelGGL(attend_combine_kernel<128>, dim3(Hq, B), dim3(kCombThreads), 0, st, part_o, part_ml, s.N,
+                           nch, Hq, G, out);
     return hipGetLastError();
 }
 
