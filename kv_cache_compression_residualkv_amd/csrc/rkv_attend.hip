@@ -72,6 +72,19 @@ __global__ __launch_bounds__(kThreads) void attend_chunk_kernel(const bf16_t* __
 #pragma unroll
         for (int h = 0; h < G; ++h) sP[h][tid] = j < m ? s[h] * scale : -INFINITY;
     }
+    // P V operands: lane group r = lane / 16 takes row 16 i + 4 wave + r, lane % 16 its 8
+    // dims (D = 64: lanes with (lane % 16) >= 8 hold no dims). The value loads do not
+    // depend on the scores, so they are issued here and land during the softmax pass;
+    // rows past m read row m - 1 with weight 0 (sP is 0 there).
+    const int r = lane >> 4, dl = 8 * (lane & 15);
+    uint4 vraw[kChunk / 16];
+    if (dl < D) {
+#pragma unroll
+        for (int i = 0; i < kChunk / 16; ++i) {
+            const int j = min(j0 + 16 * i + 4 * wave + r, m - 1);
+            vraw[i] = *reinterpret_cast<const uint4*>(kv + ((size_t)b * m + j) * W2 + dk + (size_t)g * D + dl);
+        }
+    }
     __syncthreads();
 
     // per head: chunk maximum, weights exp(s - max), their sum (wave w: heads w, w + 4)
@@ -95,23 +108,19 @@ __global__ __launch_bounds__(kThreads) void attend_chunk_kernel(const bf16_t* __
     }
     __syncthreads();
 
-    // P V: lane group r = lane / 16 takes row 16 i + 4 wave + r, lane % 16 its 8 dims
-    // (D = 64: lanes with (lane % 16) >= 8 hold no dims)
-    const int r = lane >> 4, dl = 8 * (lane & 15);
     float acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     if (dl < D) {
-        // rows past m read row m - 1 with weight 0 (sP is 0 there), so every load of the
-        // loop can be in flight at once
 #pragma unroll
         for (int i = 0; i < kChunk / 16; ++i) {
             const int t = 16 * i + 4 * wave + r;
-            const int j = min(j0 + t, m - 1);
+            const uint32_t w4[4] = {vraw[i].x, vraw[i].y, vraw[i].z, vraw[i].w};
             float v8[8];
-            Load8<bf16_t>::run(kv + ((size_t)b * m + j) * W2 + dk + (size_t)g * D + dl, v8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v8[e] = __uint_as_float((e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16));
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 const float p = sP[h][t];
