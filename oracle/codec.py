@@ -218,6 +218,10 @@ class OracleCache:
         self.self_slot = np.full(cap_tok, -1, dtype=np.int32)
         self.ref_dist = np.full((cap_tok, top_k), np.nan)
         self.z = np.zeros((cap_tok, d_c), dtype=np.float64)  # unquantized latent, for checks
+        # max |f_c(kv)| + max |f_c(mean)|: the magnitude the two encoder outputs have before
+        # z takes their difference (the scale of the arithmetic error of any finite-precision
+        # evaluation of z), for checks
+        self.f_scale = np.zeros(cap_tok, dtype=np.float64)
 
 
 class OracleCodec:
@@ -300,12 +304,14 @@ class OracleCodec:
             xbar[t] = self.encoder_input(mean32)
         W = self.W
         # average-then-encode: z = f_c(kv_i) - f_c(mean_i)  (section 2.3, boxed equation)
-        z = swiglu_compressor(kv, W["Wc1"], W["Wc2"], W["Wc3"]) - swiglu_compressor(
-            xbar, W["Wc1"], W["Wc2"], W["Wc3"])
+        f_kv = swiglu_compressor(kv, W["Wc1"], W["Wc2"], W["Wc3"])
+        f_mean = swiglu_compressor(xbar, W["Wc1"], W["Wc2"], W["Wc3"])
+        z = f_kv - f_mean
         store = "f16" if self.mode == "bf16" else "f32"
         q, step, zmin = group_quantize(z, self.bits, self.group, store)
         for t, p in enumerate(pos):
             cache.z[p] = z[t]
+            cache.f_scale[p] = np.max(np.abs(f_kv[t])) + np.max(np.abs(f_mean[t]))
             if self.bits == 16:
                 cache.latent[p] = step[t]
             else:

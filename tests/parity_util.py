@@ -6,16 +6,23 @@ Tolerances (stated for this codec):
   the two sets agree within 1e-5 relative (a tie); such tokens are re-encoded by the
   oracle with the GPU's set before their codes are compared;
 * codes: identical in >= 99.99 % of coordinates, off by at most 1 elsewhere;
-* stored step / minimum: within 1 fp16 ulp (fp32 storage: 1e-5 relative);
-* fp16 latent (quantization off): every coordinate within 1 fp16 ulp of the
-  token's largest coordinate. z carries an absolute fp32 accumulation error at the
-  token's scale, so a coordinate near zero (whose own ulp is tiny) can round to an
-  fp16 neighbour a few of its own ulps away; the exact and within-own-ulp
-  fractions are reported;
+* stored step / minimum: within one storage ulp (fp16, or fp32 for the fp32 formats) plus
+  the fp32 arithmetic error of z carried into them: E for the minimum, 2 E / (2^b - 1)
+  for the step, with E = 64 * 2^-24 * (max|f_c(kv)| + max|f_c(mean)|) of the token (see
+  the fp16-latent bar below);
+* fp16 latent (quantization off): every coordinate within one fp16 ulp at the larger
+  of the two latents plus 64 * 2^-24 * (max|f_c(kv)| + max|f_c(mean)|) of its token
+  (the fp32 arithmetic error of the difference z = f_c(kv) - f_c(mean) scales with
+  the two outputs, not with z; derived from an fp32 evaluation on the CPU in
+  test_tolerance_derivation.py, which reaches 99.975 % within one own ulp and at most
+  16 * 2^-24 * that scale before rounding); the exact and within-own-ulp fractions are
+  reported;
 * restored K/V (fp32 output): max-abs error <= 2e-2 and RMS error relative to the
   RMS of the oracle output <= 1e-3. End to end (GPU records against the oracle's),
-  a token with a permitted code difference is held instead to the bound its z~
-  difference gives through the linear decoder.
+  a token whose records differ (a permitted code difference, or fp16 latents within
+  their bar) is held per coordinate to 2e-2 plus what its z~ difference becomes
+  through the linear decoder and the rotation: |W_d|^T |dz~|, the two coordinates of
+  a rotated key pair added.
 """
 
 from __future__ import annotations
@@ -29,6 +36,7 @@ from oracle.formats import FP8_E4M3FN_VALUES, unpack_codes
 
 TIE_REL = 1e-5
 CODE_EXACT_FRAC = 0.9999
+LATENT_ARITH_C = 64.0  # fp16-latent bar: multiples of 2^-24 * the token's encoder-output scale
 KV_MAX_ABS = 2e-2
 KV_RMS_REL = 1e-3
 
@@ -135,6 +143,15 @@ def fp16_ulp(x: np.ndarray) -> np.ndarray:
     return 2.0 ** (e - 10)
 
 
+def storage_ulp(x: np.ndarray, mode: str) -> np.ndarray:
+    """ulp of the stored per-group values: fp16 ('bf16' formats) or fp32 ('f32' formats)."""
+    if mode == "bf16":
+        return fp16_ulp(x)
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 23)
+
+
 def compare_codes(codec: OracleCodec, orc, gpc, positions):
     """Code / step / min agreement on the given (encoded, agreed) positions. Returns stats dict."""
     pos = np.asarray(positions, dtype=np.int64)
@@ -144,20 +161,21 @@ def compare_codes(codec: OracleCodec, orc, gpc, positions):
         d = np.abs(a - g)
         st["latent_exact_frac"] = float(np.mean(d == 0)) if d.size else 1.0
         st["latent_within_1ulp_frac"] = float(np.mean(d <= fp16_ulp(a))) if d.size else 1.0
-        # error measured in fp16 ulps of the token's largest coordinate
-        tok_ulp = fp16_ulp(np.max(np.abs(a), axis=1, keepdims=True)) if d.size else np.ones((1, 1))
-        st["latent_max_token_ulps"] = float(np.max(d / tok_ulp)) if d.size else 0.0
+        bar = fp16_ulp(np.maximum(np.abs(a), np.abs(g))) + LATENT_ARITH_C * 2.0 ** -24 * orc.f_scale[pos][:, None]
+        st["latent_max_bar_ratio"] = float(np.max(d / bar)) if d.size else 0.0
         return st
     qa, qg = orc.q[pos].astype(np.int32), gpc.q[pos].astype(np.int32)
     diff = np.abs(qa - qg)
     st["code_exact_frac"] = float(np.mean(diff == 0)) if diff.size else 1.0
     st["code_max_diff"] = int(diff.max()) if diff.size else 0
-    if codec.mode == "bf16":
-        st["step_max_ulps"] = float(np.max(np.abs(orc.step[pos] - gpc.step[pos]) / fp16_ulp(orc.step[pos])))
-        st["zmin_max_ulps"] = float(np.max(np.abs(orc.zmin[pos] - gpc.zmin[pos]) / fp16_ulp(orc.zmin[pos])))
-    else:
-        st["step_max_rel"] = float(np.max(np.abs(orc.step[pos] - gpc.step[pos]) / np.maximum(np.abs(orc.step[pos]), 1e-30)))
-        st["zmin_max_rel"] = float(np.max(np.abs(orc.zmin[pos] - gpc.zmin[pos]) / np.maximum(np.abs(orc.zmin[pos]), 1e-30)))
+    E = LATENT_ARITH_C * 2.0 ** -24 * orc.f_scale[pos][:, None]
+    so, sg, mo, mg = orc.step[pos], gpc.step[pos], orc.zmin[pos], gpc.zmin[pos]
+    step_bar = storage_ulp(np.maximum(np.abs(so), np.abs(sg)), codec.mode) + 2.0 * E / (2 ** codec.bits - 1)
+    zmin_bar = storage_ulp(np.maximum(np.abs(mo), np.abs(mg)), codec.mode) + E
+    st["step_max_bar_ratio"] = float(np.max(np.abs(so - sg) / step_bar)) if so.size else 0.0
+    st["zmin_max_bar_ratio"] = float(np.max(np.abs(mo - mg) / zmin_bar)) if mo.size else 0.0
+    st["step_max_ulps"] = float(np.max(np.abs(so - sg) / storage_ulp(so, codec.mode))) if so.size else 0.0
+    st["zmin_max_ulps"] = float(np.max(np.abs(mo - mg) / storage_ulp(mo, codec.mode))) if mo.size else 0.0
     return st
 
 
@@ -165,12 +183,10 @@ def assert_codes_ok(st):
     if "code_exact_frac" in st:
         assert st["code_exact_frac"] >= CODE_EXACT_FRAC, st
         assert st["code_max_diff"] <= 1, st
-    if "step_max_ulps" in st:
-        assert st["step_max_ulps"] <= 1.0 and st["zmin_max_ulps"] <= 1.0, st
-    if "step_max_rel" in st:
-        assert st["step_max_rel"] <= 1e-5 and st["zmin_max_rel"] <= 1e-5, st
-    if "latent_max_token_ulps" in st:
-        assert st["latent_max_token_ulps"] <= 1.0, st
+    if "step_max_bar_ratio" in st:
+        assert st["step_max_bar_ratio"] <= 1.0 and st["zmin_max_bar_ratio"] <= 1.0, st
+    if "latent_max_bar_ratio" in st:
+        assert st["latent_max_bar_ratio"] <= 1.0, st
 
 
 def kv_errors(out: np.ndarray, ref: np.ndarray):
@@ -180,18 +196,27 @@ def kv_errors(out: np.ndarray, ref: np.ndarray):
     return max_abs, rms_rel
 
 
+def decoder_bound(codec: OracleCodec, dz: np.ndarray) -> np.ndarray:
+    """Per-coordinate bound on the restored K|V difference that a latent difference dz
+    [n, d_c] causes: |W_d|^T |dz| (the decoder is linear, section 2.5), with the two
+    coordinates of every rotated key pair (j, j + D/2) added (RoPE mixes them, with
+    |cos|, |sin| <= 1)."""
+    g = np.abs(dz) @ np.abs(codec.W["Wd"])
+    k = g[:, : codec.dk].reshape(-1, codec.N, 2, codec.D // 2)
+    k = (k + k[:, :, ::-1, :]).reshape(-1, codec.dk)
+    return np.concatenate([k, g[:, codec.dk:]], axis=1)
+
+
 def assert_end_to_end(codec: OracleCodec, out: np.ndarray, orc, gpc, positions, what=""):
     """GPU restore vs the oracle's restore of the oracle's own records.
 
-    Tokens whose records agree (same codes, same stored step/min) must meet the
-    max-abs bar. A token whose records differ can differ by what the decoder makes
-    of that difference: the restore is linear in z~ with the same mean, and RoPE is
-    an isometry, so ||out_gpu - out_oracle|| <= ||W_d||_op ||z~_gpu - z~_oracle|| plus
-    the arithmetic error, checked token by token. The RMS bar applies to every token
-    whose integer codes agree (step/min within their ulp bar, fp16 latents): one
-    INT2 code off by one moves z~ by a whole quantization step, which a bar on
-    arithmetic error does not cover, so tokens with a permitted code difference are
-    held to the per-token bound alone.
+    Every coordinate must lie within 2e-2 plus what the token's z~ difference becomes
+    through the decoder (decoder_bound): for tokens whose records agree that is the
+    plain max-abs bar. The RMS bar applies to every token whose integer codes agree
+    (step/min within their ulp bar, fp16 latents within theirs): one INT2 code off by
+    one moves z~ by a whole quantization step, which a bar on arithmetic error does not
+    cover, so tokens with a permitted code difference are held to the per-coordinate
+    bound alone.
     """
     pos = np.asarray(positions, dtype=np.int64)
     ref = codec.decode_selected(orc, pos)
@@ -201,8 +226,8 @@ def assert_end_to_end(codec: OracleCodec, out: np.ndarray, orc, gpc, positions, 
     if enc.any():
         zt_o[enc] = codec.latent_tilde(orc, pos[enc])
         zt_g[enc] = codec.latent_tilde(gpc, pos[enc])
-    dz = np.linalg.norm(zt_o - zt_g, axis=1)
-    same = dz == 0.0
+    dz = zt_o - zt_g
+    same = np.all(dz == 0.0, axis=1)
     err = out.astype(np.float64) - ref
     ma_same = float(np.max(np.abs(err[same]))) if same.any() else 0.0
     flip = np.zeros(pos.size, dtype=bool)
@@ -210,11 +235,10 @@ def assert_end_to_end(codec: OracleCodec, out: np.ndarray, orc, gpc, positions, 
         flip[enc] = np.any(orc.q[pos[enc]] != gpc.q[pos[enc]], axis=1)
     keep = ~flip
     rms_rel = float(np.sqrt(np.mean(err[keep] ** 2)) / max(np.sqrt(np.mean(ref[keep] ** 2)), 1e-30)) if keep.any() else 0.0
-    opn = np.linalg.norm(codec.W["Wd"], 2)
-    tok_err = np.linalg.norm(err, axis=1)
-    bound = opn * dz + KV_MAX_ABS
+    bound = KV_MAX_ABS + decoder_bound(codec, dz)
+    excess = np.abs(err) - bound
     assert ma_same <= KV_MAX_ABS and rms_rel <= KV_RMS_REL, (what, ma_same, rms_rel)
-    assert np.all(tok_err[~same] <= bound[~same]), (what, np.max(tok_err[~same] - bound[~same]))
+    assert np.all(excess <= 0.0), (what, float(np.max(excess)))
     return ma_same, rms_rel, int((~same).sum())
 
 
