@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 2
+#define RKV_ABI_VERSION 3
 
 typedef enum {
     RKV_OK = 0,
@@ -129,7 +129,17 @@ typedef struct {
     int32_t* ref_idx;
     int32_t* self_slot;
     int32_t* err_word; /* optional (may be NULL) */
+    /* optional (may be NULL): device int32[RKV_STATS_WORDS] counters the encode adds to
+     * (atomic adds; the caller zeroes them when it wants a fresh count):
+     *   [0] tokens whose reference set was decided with exact distances because the
+     *       approximate scores at the set boundary lay within their rounding bound;
+     *   [1] tokens re-searched with exact distances over whole pool chunks because a
+     *       chunk's kept candidates could hide a nearer reference (near-equidistant
+     *       references). */
+    int32_t* stats;
 } rkv_cache;
+
+#define RKV_STATS_WORDS 2
 
 /* Version of this ABI (RKV_ABI_VERSION). */
 int32_t rkv_abi_version(void);

@@ -34,6 +34,8 @@ STATUS = {
     -6: "workspace missing or too small",
 }
 RKV_ENCODE_PHASES = 4
+RKV_STATS_WORDS = 2
+ABI_VERSION = 3
 DEVERR_EMPTY_POOL, DEVERR_POS_RANGE, DEVERR_REF_CAPACITY, DEVERR_IDX_RANGE, DEVERR_ROW_RANGE = 1, 2, 4, 8, 16
 
 EXPORTED = (
@@ -99,6 +101,7 @@ class _Cache(ctypes.Structure):
         ("ref_idx", ctypes.c_void_p),
         ("self_slot", ctypes.c_void_p),
         ("err_word", ctypes.c_void_p),
+        ("stats", ctypes.c_void_p),
     ]
 
 
@@ -294,7 +297,7 @@ class CodecCache:
     """Caller-owned cache arrays of one layer (torch tensors) + the rkv_cache struct."""
 
     def __init__(self, cfg: CodecConfig, batch: int, cap_ref: int, cap_tok: int, device="cuda",
-                 err_word: bool = True):
+                 err_word: bool = True, stats: bool = True):
         rb = rkv_record_bytes(cfg)
         self.cfg, self.batch, self.cap_ref, self.cap_tok = cfg, batch, cap_ref, cap_tok
         W2 = cfg.two_dk
@@ -304,23 +307,29 @@ class CodecCache:
         self.ref_norm2 = torch.zeros((batch, cap_ref), dtype=torch.float32, device=device)
         self.ref_count = torch.zeros((batch,), dtype=torch.int32, device=device)
         self.codes = torch.zeros((batch, cap_tok, rb["codes"]), dtype=torch.uint8, device=device)
-        if cfg.bits == 16:
-            self.scale = torch.zeros((batch, cap_tok, G), dtype=cfg.scale_torch_dtype, device=device)
-        else:
-            self.scale = torch.zeros((batch, cap_tok, G), dtype=cfg.scale_torch_dtype, device=device)
+        self.scale = torch.zeros((batch, cap_tok, G), dtype=cfg.scale_torch_dtype, device=device)
         self.zmin = torch.zeros_like(self.scale)
         self.ref_idx = torch.full((batch, cap_tok, cfg.top_k), -1, dtype=torch.int32, device=device)
         self.self_slot = torch.full((batch, cap_tok), -1, dtype=torch.int32, device=device)
         self.err_word = torch.zeros((1,), dtype=torch.int32, device=device) if err_word else None
+        self.stats = torch.zeros((RKV_STATS_WORDS,), dtype=torch.int32, device=device) if stats else None
         self._c = _Cache(
             batch, cap_ref, cap_tok, 0,
             _ptr(self.ref_vals), _ptr(self.ref_pos), _ptr(self.ref_norm2), _ptr(self.ref_count),
             _ptr(self.codes), _ptr(self.scale), _ptr(self.zmin), _ptr(self.ref_idx), _ptr(self.self_slot),
-            _ptr(self.err_word),
+            _ptr(self.err_word), _ptr(self.stats),
         )
 
     def error_bits(self) -> int:
         return int(self.err_word.item()) if self.err_word is not None else 0
+
+    def encode_stats(self) -> Dict[str, int]:
+        """The encode's counters (rkv_cache.stats): tokens whose set boundary needed exact
+        distances, and tokens re-searched exactly over whole pool chunks."""
+        if self.stats is None:
+            return {"exact_boundary": 0, "exact_rescan": 0}
+        v = self.stats.cpu().tolist()
+        return {"exact_boundary": int(v[0]), "exact_rescan": int(v[1])}
 
 
 # ------------------------------------------------------------------------------ entry points

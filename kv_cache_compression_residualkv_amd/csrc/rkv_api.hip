@@ -88,6 +88,7 @@ rkv_status check_cache(const Shape& s, const rkv_cache* c, bool need_records, Ca
     v->ref_idx = c->ref_idx;
     v->self_slot = c->self_slot;
     v->err = c->err_word;
+    v->stats = c->stats;
     v->code_bytes = code_bytes_of(s);
     return RKV_OK;
 }

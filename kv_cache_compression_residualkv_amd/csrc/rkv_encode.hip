@@ -79,6 +79,16 @@ __device__ inline float silu(float a) {
     return fmaf(fmaf(-q, d, a), r, q);
 }
 
+// One hidden value h = Swish(a) * g, rounded on its own: written as a plain product, the
+// compiler may fuse it into the difference h(kv) - h(mean) that follows (an FMA rounds
+// only once), so that one side is rounded and the other is not, and a token equal to its
+// reference mean would get a nonzero residual. The review page's z = f_c(kv) - f_c(mean)
+// (section 2.3) is exactly zero there, and so is this.
+__device__ inline float swiglu_h(float a, float g) {
+#pragma clang fp contract(off)
+    return silu(a) * g;
+}
+
 // grid: 8 * per blocks over MT x NT logical tiles (N tiles fastest, so the NT tiles
 // that read one A row block run back to back on one XCD).
 template <typename T>
@@ -137,10 +147,10 @@ __global__ __launch_bounds__(kGemmThreads) void swiglu_kernel(const T* __restric
         for (int c = 0; c < 2; ++c) {
             const f32x4 a = acc[i][c];
             const f32x4 g = acc[i][c + 2];
-            const float h0 = silu(a[0]) * g[0];
-            const float h1 = silu(a[1]) * g[1];
-            const float h2 = silu(a[2]) * g[2];
-            const float h3 = silu(a[3]) * g[3];
+            const float h0 = swiglu_h(a[0], g[0]);
+            const float h1 = swiglu_h(a[1], g[1]);
+            const float h2 = swiglu_h(a[2], g[2]);
+            const float h3 = swiglu_h(a[3], g[3]);
             const int cl = 32 * wn + 16 * c + (lane & 15);
             sH[tl * C::kHP + cl] = h0 - h1;
             sH[(tl + 1) * C::kHP + cl] = h2 - h3;
@@ -266,10 +276,10 @@ __global__ __launch_bounds__(g1r::kThreads) void swiglu_ring_kernel(const bf16_t
         for (int c = 0; c < 2; ++c) {
             const f32x4 a = acc[i][c];
             const f32x4 g = acc[i][c + 2];
-            const float h0 = silu(a[0]) * g[0];
-            const float h1 = silu(a[1]) * g[1];
-            const float h2 = silu(a[2]) * g[2];
-            const float h3 = silu(a[3]) * g[3];
+            const float h0 = swiglu_h(a[0], g[0]);
+            const float h1 = swiglu_h(a[1], g[1]);
+            const float h2 = swiglu_h(a[2], g[2]);
+            const float h3 = swiglu_h(a[3], g[3]);
             const int cl = 32 * wn + 16 * c + (lane & 15);
             sH[tl * g1r::kHP + cl] = h0 - h1;
             sH[(tl + 1) * g1r::kHP + cl] = h2 - h3;
@@ -760,10 +770,10 @@ __global__ __launch_bounds__(128) void swiglu_skinny_kernel(const bf16_t* __rest
     for (int i = 0; i < 2; ++i) {
         const f32x4 a = acc[i];
         const f32x4 g = xg[64 * i + lane];
-        const float h0 = silu(a[0]) * g[0];
-        const float h1 = silu(a[1]) * g[1];
-        const float h2 = silu(a[2]) * g[2];
-        const float h3 = silu(a[3]) * g[3];
+        const float h0 = swiglu_h(a[0], g[0]);
+        const float h1 = swiglu_h(a[1], g[1]);
+        const float h2 = swiglu_h(a[2], g[2]);
+        const float h3 = swiglu_h(a[3], g[3]);
         const int tl = 8 * i + 2 * (lane >> 4);
         const float d[2] = {h0 - h1, h2 - h3};
 #pragma unroll

@@ -29,6 +29,7 @@ struct CacheView {
     int* ref_idx;
     int* self_slot;
     int* err;
+    int* stats;        // optional encode counters (RKV_STATS_WORDS)
     size_t code_bytes;  // per token
 };
 
@@ -40,7 +41,7 @@ struct EncodePlan {
     size_t off_scores; // scan scores [B][n][cap_ref] (small only)
     int cap_q;         // items per queue of the bf16 search's work plan
     size_t off_tile_nblk, off_items, off_ctr;  // work plan: blocks per tile, item queues, counters
-    size_t off_part_score, off_part_slot, off_xbar, off_dh, total;
+    size_t off_part_score, off_part_slot, off_rescan, off_xbar, off_dh, total;
 };
 
 EncodePlan plan_encode(const Shape& s, int B, int n, int cap_ref);

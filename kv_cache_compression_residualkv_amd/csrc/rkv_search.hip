@@ -116,8 +116,9 @@ __global__ __launch_bounds__(kThreads) void search_kernel(
     const KvT* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
     const RefT* __restrict__ ref_vals, const int* __restrict__ ref_pos, const float* __restrict__ ref_norm2,
     const int* __restrict__ ref_count, int W2, int cap_ref, int blocks_per_chunk, int nsplit, int ntiles, int per,
-    float* __restrict__ part_score, int* __restrict__ part_slot) {
+    float* __restrict__ part_score, int* __restrict__ part_slot, int* __restrict__ rescan) {
     typedef SC<T> C;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) rescan[0] = 0;  // select's rescan queue
     extern __shared__ __align__(16) unsigned char smem_u8[];
     unsigned char* smem = smem_u8;
     T* lds = reinterpret_cast<T*>(smem);
@@ -423,7 +424,8 @@ struct SFrag {
 __global__ __launch_bounds__(256) void search_plan_kernel(const int* __restrict__ pos, int n,
                                                           const int* __restrict__ ref_pos,
                                                           const int* __restrict__ ref_count, int cap_ref, int ntiles,
-                                                          int* __restrict__ tile_nblk) {
+                                                          int* __restrict__ tile_nblk, int* __restrict__ rescan) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) rescan[0] = 0;  // select's rescan queue
     const int lane = threadIdx.x & 63;
     const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int b = blockIdx.y;
@@ -503,8 +505,9 @@ __global__ __launch_bounds__(256) void search_scan_kernel(const bf16_t* __restri
                                                           const int* __restrict__ ref_pos,
                                                           const float* __restrict__ ref_norm2,
                                                           const int* __restrict__ ref_count, int cap_ref,
-                                                          float* __restrict__ scores) {
+                                                          float* __restrict__ scores, int* __restrict__ rescan) {
     constexpr int W2 = 1024 * NC;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) rescan[0] = 0;  // select's rescan queue
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b = blockIdx.y;
     const int count = max(0, min(ref_count[b], cap_ref));
@@ -1018,14 +1021,114 @@ __device__ inline void gstore8<bf16_t>(bf16_t* p, const float* v) {
     *reinterpret_cast<bf16x8*>(p) = Mma<bf16_t>::from_float(v);
 }
 
+// 64-bit minimum over the wavefront
+__device__ inline uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o, 64);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o, 64);
+        const uint64_t w = ((uint64_t)hi << 32) | lo;
+        v = w < v ? w : v;
+    }
+    // the same in every lane: keep it in scalar registers
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Squared L2 distance of one reference row to the token row, summed by one lane alone
+// (eight partial sums over the columns, combined in a fixed tree): equal rows get equal
+// distances, so an exact tie is left to the slot order.
+template <typename KvT, typename RefT>
+__device__ inline float lane_dist(const KvT* __restrict__ x, const RefT* __restrict__ r, int W2) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int c = 0; c < W2; c += 8) {
+        float xv[8], rv[8];
+        Load8<KvT>::run(x + c, xv);
+        Load8<RefT>::run(r + c, rv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float d = xv[e] - rv[e];
+            a[e] = fmaf(d, d, a[e]);
+        }
+    }
+    return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+}
+
+// 8 ints in ascending order (the 19-comparator network)
+__device__ inline void sort8_i32(int (&k)[8]) {
+#define RKV_C(x, y)                          \
+    {                                        \
+        const int lo = min(k[x], k[y]);      \
+        const int hi = max(k[x], k[y]);      \
+        k[x] = lo;                           \
+        k[y] = hi;                           \
+    }
+    RKV_C(0, 2); RKV_C(1, 3); RKV_C(4, 6); RKV_C(5, 7);
+    RKV_C(0, 4); RKV_C(1, 5); RKV_C(2, 6); RKV_C(3, 7);
+    RKV_C(0, 1); RKV_C(2, 3); RKV_C(4, 5); RKV_C(6, 7);
+    RKV_C(2, 4); RKV_C(3, 5);
+    RKV_C(1, 4); RKV_C(3, 6);
+    RKV_C(1, 2); RKV_C(3, 4); RKV_C(5, 6);
+#undef RKV_C
+}
+
+// Reference mean of one token by one wavefront: fp32 sum in ascending slot order, one
+// correctly rounded division, rounded to the KV dtype for the encoder. slots[0..k_i-1]
+// hold the chosen slots in ascending order (the same in every lane).
+template <typename KvT, typename RefT>
+__device__ inline void write_mean(const RefT* __restrict__ pool, const int (&slots)[8], int k_i, int W2,
+                                  KvT* __restrict__ xrow, int lane) {
+    const float kf = (float)k_i;
+    const float rk = __fdiv_rn(1.0f, k_i > 0 ? kf : 1.0f);
+#pragma unroll 2
+    for (int c = 8 * lane; c < W2; c += 512) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (q < k_i) {
+                float v[8];
+                Load8<RefT>::run(pool + (size_t)slots[q] * W2 + c, v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += v[e];
+            }
+        }
+        if (k_i > 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if constexpr (std::is_same<RefT, fp8_t>::value) {
+                    acc[e] = div_small(acc[e], kf, rk);
+                } else {  // fp32 references: general sums, IEEE division
+                    acc[e] = __fdiv_rn(acc[e], kf);
+                }
+            }
+        }
+        gstore8<KvT>(xrow + c, acc);
+    }
+}
+
 // One wavefront per token; 4 tokens per block. Row accesses take 8 columns per lane
 // (chunks of 512 columns).
+//
+// Every chunk list holds the chunk's best 8 candidates by approximate score (rounded
+// down, ties by slot). Three cases decide the set:
+//  * the approximate boundary is clear of the rounding bound and no list can have
+//    dropped a member: the k_i best candidates by approximate score;
+//  * the boundary is ambiguous among the stored candidates: exact distances for the
+//    candidates the bounds cannot place (counted in stats[0]);
+//  * a full list's 8th score comes within the bound of the set's largest exact
+//    distance, so a slot the list dropped could belong to the set: the token goes to
+//    the rescan queue (rescan[0] entries of two words from rescan[2]: the token, and
+//    the mask of such lists | the number of lists << 8), and rescan_kernel writes its
+//    references and mean row (counted in stats[1]).
 template <typename KvT, typename RefT>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const KvT* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
     const RefT* __restrict__ ref_vals, const float* __restrict__ ref_norm2, const float* __restrict__ part_score,
     const int* __restrict__ part_slot, int nsplit, int nch_fixed, const int* __restrict__ tile_nblk, int bpc, int W2,
-    int cap_ref, int cap_tok, int top_k, int* __restrict__ ref_idx, KvT* __restrict__ xbar, int* err) {
+    int cap_ref, int cap_tok, int top_k, int* __restrict__ ref_idx, KvT* __restrict__ xbar, int* rescan, int* err,
+    int* stats) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int b = blockIdx.y;
@@ -1111,57 +1214,86 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         hi_in = fmaxf(hi_in, __shfl_xor(hi_in, o, 64));
         lo_out = fminf(lo_out, __shfl_xor(lo_out, o, 64));
     }
-    bool chosen = in_set;
-    if (k_i > 0 && lo_out <= hi_in) {
-        // ambiguous boundary. A candidate of the set whose score plus margin lies below
-        // every outside candidate's score minus margin is closer than all of them in
-        // exact arithmetic too, so it stays; one outside whose score minus margin lies
-        // above every set member's score plus margin stays out. Only the rest (of the
-        // best 8) get exact fp32 squared distances; the free places of the set go to
-        // the best of them by (exact distance, slot). This equals ranking all 8 exactly.
-        const bool sure_in = in_set && s + margin < lo_out;
-        const bool sure_out = !in_set && s - margin > hi_in;
-        const bool amb = id >= 0 && rank < kTop && !sure_in && !sure_out;
-        const unsigned long long am = __ballot(amb);
-        float dist = FLT_MAX;
-        for (unsigned long long mq = am; mq; mq &= mq - 1) {
-            const int src = __ffsll((long long)mq) - 1;
-            const int sq = __shfl(id, src, 64);
-            float acc = 0.f;
-            const RefT* r = pool + (size_t)sq * W2;
-            for (int c = 4 * lane; c < W2; c += 256) {
-                const float4 xv = Load4<KvT>::run(x + c);
-                const float4 rv = Load4<RefT>::run(r + c);
-                const float d0 = xv.x - rv.x, d1 = xv.y - rv.y, d2 = xv.z - rv.z, d3 = xv.w - rv.w;
-                acc += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
-            }
-            acc = wave_sum(acc);
-            if (lane == src) dist = acc;
-        }
-        int arank = 0;
-        for (unsigned long long mq = am; mq; mq &= mq - 1) {
-            const int src = __ffsll((long long)mq) - 1;
-            const float dj = __shfl(dist, src, 64);
-            const int ij = __shfl(key_id, src, 64);
-            arank += (dj < dist || (dj == dist && ij < key_id)) ? 1 : 0;
-        }
-        const int nsure = __popcll(__ballot(sure_in));
-        chosen = sure_in || (amb && arank < k_i - nsure);
+
+    // A slot a full list dropped scores at least the list's 8th (rounded-down) score. If
+    // it could belong to the set, its exact score is at most hi_in, so its distance is at
+    // most dmax = hi_in + ||x||^2 and ||r||^2 <= 2 ||x||^2 + 2 dmax; its rounding bound is
+    // then at most 2^-16 (3 ||x||^2 + 2 dmax), taken twice over here. A list whose 8th
+    // score minus that amount stays above hi_in cannot hide a member of the set.
+    bool hides = false;
+    if (k_i > 0 && lane < ncand && (lane & (kTop - 1)) == kTop - 1 && id >= 0) {
+        const float dmax = fmaxf(hi_in + xn, 0.f);
+        hides = s - 3.0517578125e-05f * (3.f * xn + 2.f * dmax) <= hi_in;  // 2^-15
     }
-    // chosen slots in ascending slot order
-    int srank = 0;
-    const unsigned long long cm = __ballot(chosen);
-    for (int j = 0; j < 64; ++j) {
-        if (!((cm >> j) & 1ull)) continue;
-        const int ij = __shfl(id, j, 64);
-        srank += (chosen && ij < id) ? 1 : 0;
-    }
-    // broadcast the chosen slots in order
-    int slots[8];
+    const unsigned long long hide_mask = __ballot(hides);
+
+    if (hide_mask) {
+        // the exact search over whole chunks runs in rescan_kernel, which then writes this
+        // token's references and mean row
+        if (lane == 0) {
+            const int slot = atomicAdd(&rescan[0], 1);
+            rescan[2 + 2 * slot] = b * n + t;
+            uint32_t cm = 0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const unsigned long long mq = __ballot(chosen && srank == q);
-        slots[q] = mq ? __shfl(id, __ffsll((long long)mq) - 1, 64) : -1;
+            for (int c = 0; c < 8; ++c) cm |= ((hide_mask >> (kTop * c + kTop - 1)) & 1ull) ? (1u << c) : 0u;
+            rescan[3 + 2 * slot] = (int)(cm | ((uint32_t)nch << 8));
+            if (stats) atomicAdd(&stats[1], 1);
+        }
+        return;
+    }
+    int slots[8];  // the chosen slots in ascending order, -1 padded (the same in every lane)
+    {
+        bool chosen = in_set;
+        if (k_i > 0 && lo_out <= hi_in) {
+            // ambiguous boundary. A candidate of the set whose score plus margin lies below
+            // every outside candidate's score minus margin is closer than all of them in
+            // exact arithmetic too, so it stays; one outside whose score minus margin lies
+            // above every set member's score plus margin has k_i closer candidates and
+            // stays out. The rest get exact fp32 squared distances; the free places of the
+            // set go to the best of them by (exact distance, slot).
+            if (lane == 0 && stats) atomicAdd(&stats[0], 1);
+            const bool sure_in = in_set && s + margin < lo_out;
+            const bool sure_out = !in_set && s - margin > hi_in;
+            const bool amb = id >= 0 && !sure_in && !sure_out;
+            const unsigned long long am = __ballot(amb);
+            float dist = FLT_MAX;
+            for (unsigned long long mq = am; mq; mq &= mq - 1) {
+                const int src = __ffsll((long long)mq) - 1;
+                const int sq = __shfl(id, src, 64);
+                float acc = 0.f;
+                const RefT* r = pool + (size_t)sq * W2;
+                for (int c = 4 * lane; c < W2; c += 256) {
+                    const float4 xv = Load4<KvT>::run(x + c);
+                    const float4 rv = Load4<RefT>::run(r + c);
+                    const float d0 = xv.x - rv.x, d1 = xv.y - rv.y, d2 = xv.z - rv.z, d3 = xv.w - rv.w;
+                    acc += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+                }
+                acc = wave_sum(acc);
+                if (lane == src) dist = acc;
+            }
+            int arank = 0;
+            for (unsigned long long mq = am; mq; mq &= mq - 1) {
+                const int src = __ffsll((long long)mq) - 1;
+                const float dj = __shfl(dist, src, 64);
+                const int ij = __shfl(key_id, src, 64);
+                arank += (dj < dist || (dj == dist && ij < key_id)) ? 1 : 0;
+            }
+            const int nsure = __popcll(__ballot(sure_in));
+            chosen = sure_in || (amb && arank < k_i - nsure);
+        }
+        // chosen slots in ascending slot order
+        int srank = 0;
+        const unsigned long long cm = __ballot(chosen);
+        for (int j = 0; j < 64; ++j) {
+            if (!((cm >> j) & 1ull)) continue;
+            const int ij = __shfl(id, j, 64);
+            srank += (chosen && ij < id) ? 1 : 0;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const unsigned long long mq = __ballot(chosen && srank == q);
+            slots[q] = mq ? __shfl(id, __ffsll((long long)mq) - 1, 64) : -1;
+        }
     }
     int* out_idx = ref_idx + ((size_t)b * cap_tok + p) * top_k;
     if (lane < top_k) {
@@ -1172,34 +1304,131 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         out_idx[lane] = v;
     }
     if (k_i == 0 && lane == 0) flag_error(err, DEVERR_EMPTY_POOL);
+    write_mean<KvT, RefT>(pool, slots, k_i, W2, xrow, lane);
+}
 
-    // reference mean: fp32 sum in ascending slot order, one correctly rounded division,
-    // rounded to the KV dtype for the encoder
-    const float kf = (float)k_i;
-    const float rk = __fdiv_rn(1.0f, k_i > 0 ? kf : 1.0f);
-#pragma unroll 2
-    for (int c = 8 * lane; c < W2; c += 512) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+// Exact search of the tokens select_kernel queued. One workgroup per queued token (grid-
+// stride over the queue): its four wavefronts compute exact squared distances, one lane
+// per reference row (lane_dist), over every visible slot of the chunks whose lists could
+// hide a member of the set and over the stored candidates of the other chunks; each
+// wavefront keeps the 8 smallest (distance, slot) keys, the four lists merge through
+// LDS, and wavefront 0 writes the k_i smallest as the token's references (ascending slot)
+// and its mean row. A chunk list that could hide a member holds 8 visible slots, so
+// k_i = top_k here.
+template <typename KvT, typename RefT>
+__global__ __launch_bounds__(256) void rescan_kernel(
+    const KvT* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
+    const RefT* __restrict__ ref_vals, const int* __restrict__ ref_pos, const int* __restrict__ ref_count,
+    const int* __restrict__ part_slot, int nsplit, int chunk_len, int W2, int cap_ref, int cap_tok, int top_k,
+    int* __restrict__ ref_idx, KvT* __restrict__ xbar, const int* __restrict__ rescan) {
+    __shared__ uint64_t s_best[4][8];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nq = rescan[0];
+    for (int e = blockIdx.x; e < nq; e += gridDim.x) {
+        const int code = rescan[2 + 2 * e];
+        const uint32_t info = (uint32_t)rescan[3 + 2 * e];
+        const int b = code / n, t = code - b * n;
+        const int row = rows[(size_t)b * n + t];
+        const int p = pos[(size_t)b * n + t];
+        const KvT* x = kv + ((size_t)b * kv_len + row) * W2;  // select queued only tokens with valid rows
+        const RefT* pool = ref_vals + (size_t)b * cap_ref * W2;
+        const int* rp = ref_pos + (size_t)b * cap_ref;
+        const uint32_t hmask = info & 0xFFu;
+        const int nch = (int)(info >> 8);
+        const int count = max(0, min(ref_count[b], cap_ref));
+        const int cl = chunk_len > 0 ? chunk_len : (count + nch - 1) / max(nch, 1);
+        uint64_t best[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            if (q < k_i) {
-                float v[8];
-                Load8<RefT>::run(pool + (size_t)slots[q] * W2 + c, v);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += v[e];
+        for (int q = 0; q < 8; ++q) best[q] = ~0ull;
+        uint64_t kth = ~0ull;
+        auto offer = [&](bool ok, int slot) {
+            uint64_t mine = ~0ull;
+            if (ok) {
+                const float d = lane_dist<KvT, RefT>(x, pool + (size_t)slot * W2, W2);
+                mine = ((uint64_t)__float_as_uint(d) << 32) | (uint32_t)slot;
             }
-        }
-        if (k_i > 1) {
+            // keys enter in ascending order, so at most 8 of them enter per call
+            for (;;) {
+                const uint64_t m = wave_min_u64(mine);
+                if (m >= kth) break;
+                uint64_t v = m;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if constexpr (std::is_same<RefT, fp8_t>::value) {
-                    acc[e] = div_small(acc[e], kf, rk);
-                } else {  // fp32 references: general sums, IEEE division
-                    acc[e] = __fdiv_rn(acc[e], kf);
+                for (int q = 0; q < 8; ++q) {
+                    const uint64_t lo = best[q] < v ? best[q] : v;
+                    const uint64_t hi = best[q] < v ? v : best[q];
+                    best[q] = lo;
+                    v = hi;
                 }
+                if (mine == m) mine = ~0ull;
+                kth = best[7];
+            }
+        };
+        // stored candidates of the lists that cannot hide a member (wavefront 0, a lane each)
+        if (wave == 0) {
+            const int c = lane / kTop;
+            const bool ok = lane < nch * kTop && !((hmask >> c) & 1u);
+            const int id = ok ? part_slot[((size_t)b * n + t) * nsplit * kTop + lane] : -1;
+            offer(id >= 0, id);
+        }
+        // every visible slot of the lists that could hide one
+        for (uint32_t mq = hmask; mq; mq &= mq - 1) {
+            const int c = __ffs(mq) - 1;
+            const int lo = c * cl, hi = min(count, lo + cl);
+            for (int s0 = lo + 64 * wave; s0 < hi; s0 += 256) {
+                const int sl = s0 + lane;
+                offer(sl < hi && rp[sl] < p, sl);
             }
         }
-        gstore8<KvT>(xrow + c, acc);
+        if (lane < 8) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (q == lane) s_best[wave][q] = best[q];
+        }
+        __syncthreads();
+        if (wave == 0) {
+            best[0] = ~0ull;
+#pragma unroll
+            for (int q = 1; q < 8; ++q) best[q] = ~0ull;
+            kth = ~0ull;
+            // the four lists (32 keys, one per lane) merge as one offer of precomputed keys
+            uint64_t mine = lane < 32 ? s_best[lane >> 3][lane & 7] : ~0ull;
+            for (;;) {
+                const uint64_t m = wave_min_u64(mine);
+                if (m >= kth) break;
+                uint64_t v = m;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint64_t lo = best[q] < v ? best[q] : v;
+                    const uint64_t hi = best[q] < v ? v : best[q];
+                    best[q] = lo;
+                    v = hi;
+                }
+                if (mine == m) mine = ~0ull;
+                kth = best[7];
+            }
+            const int k_i = top_k;
+            int sl8[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) sl8[q] = (q < k_i && best[q] != ~0ull) ? (int)(uint32_t)best[q] : INT_MAX;
+            sort8_i32(sl8);
+            int slots[8];
+            int kk = 0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                slots[q] = sl8[q] == INT_MAX ? -1 : sl8[q];
+                kk += slots[q] >= 0 ? 1 : 0;
+            }
+            int* out_idx = ref_idx + ((size_t)b * cap_tok + p) * top_k;
+            if (lane < top_k) {
+                int v = -1;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (q == lane) v = slots[q];
+                out_idx[lane] = v;
+            }
+            write_mean<KvT, RefT>(pool, slots, kk, W2, xbar + ((size_t)b * n + t) * W2, lane);
+        }
+        __syncthreads();
     }
 }
 
@@ -1235,6 +1464,8 @@ EncodePlan plan_encode(const Shape& s, int B, int n, int cap_ref) {
     off = up(off + tok * nsplit * kTop * sizeof(float));
     p.off_part_slot = off;
     off = up(off + tok * nsplit * kTop * sizeof(int));
+    p.off_rescan = off;  // select's rescan queue: count, spare word, then 2 words per token
+    off = up(off + (2 + 2 * tok) * sizeof(int));
     p.off_xbar = off;
     off = up(off + tok * s.W2 * (s.f32 ? 4 : 2));
     p.off_dh = off;
@@ -1258,7 +1489,7 @@ static hipError_t search_impl(const Shape& s, const CacheView& c, const EncodePl
     hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(kThreads), smem, st, static_cast<const KvT*>(kv), kv_len, rows,
                        pos, n, static_cast<const RefT*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count, s.W2,
                        c.cap_ref, p.chunk_slots, p.nsplit, ntiles, per, reinterpret_cast<float*>(w + p.off_part_score),
-                       reinterpret_cast<int*>(w + p.off_part_slot));
+                       reinterpret_cast<int*>(w + p.off_part_slot), reinterpret_cast<int*>(w + p.off_rescan));
     return hipGetLastError();
 }
 
@@ -1288,7 +1519,7 @@ static hipError_t search_ring_impl(const Shape& s, const CacheView& c, const Enc
     int* items = reinterpret_cast<int*>(w + p.off_items);
     int* ctr = reinterpret_cast<int*>(w + p.off_ctr);
     hipLaunchKernelGGL(search_plan_kernel, dim3((ntiles + 3) / 4, c.B), dim3(256), 0, st, pos, n, c.ref_pos,
-                       c.ref_count, c.cap_ref, ntiles, tile_nblk);
+                       c.ref_count, c.cap_ref, ntiles, tile_nblk, reinterpret_cast<int*>(w + p.off_rescan));
     hipLaunchKernelGGL(search_queue_kernel, dim3(1), dim3(512), 0, st, tile_nblk, c.B, ntiles, p.chunk_slots, p.cap_q,
                        items, ctr);
     // one workgroup per CU (the LDS of one fills a CU), never more than there are items
@@ -1313,11 +1544,11 @@ static hipError_t search_small_impl(const Shape& s, const CacheView& c, const En
     if (s.W2 == 2048) {
         hipLaunchKernelGGL(search_scan_kernel<2>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(kv), kv_len, rows,
                            pos, n, static_cast<const fp8_t*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count,
-                           c.cap_ref, scores);
+                           c.cap_ref, scores, reinterpret_cast<int*>(w + p.off_rescan));
     } else {
         hipLaunchKernelGGL(search_scan_kernel<1>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(kv), kv_len, rows,
                            pos, n, static_cast<const fp8_t*>(c.ref_vals), c.ref_pos, c.ref_norm2, c.ref_count,
-                           c.cap_ref, scores);
+                           c.cap_ref, scores, reinterpret_cast<int*>(w + p.off_rescan));
     }
     hipLaunchKernelGGL(search_small_topk_kernel, dim3(small_chunks(p), n, c.B), dim3(256), 0, st, scores, n,
                        c.ref_count, c.cap_ref,
@@ -1337,15 +1568,24 @@ template <typename KvT, typename RefT>
 static hipError_t select_impl(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
                               const int* rows, const int* pos, int n, void* ws, hipStream_t st) {
     char* w = static_cast<char*>(ws);
+    int* rescan = reinterpret_cast<int*>(w + p.off_rescan);
+    KvT* xbar = reinterpret_cast<KvT*>(w + p.off_xbar);
+    const int* part_slot = reinterpret_cast<const int*>(w + p.off_part_slot);
     const dim3 grid((n + 3) / 4, c.B);
     hipLaunchKernelGGL((select_kernel<KvT, RefT>), grid, dim3(kThreads), 0, st, static_cast<const KvT*>(kv), kv_len,
                        rows, pos, n, static_cast<const RefT*>(c.ref_vals), c.ref_norm2,
-                       reinterpret_cast<const float*>(w + p.off_part_score),
-                       reinterpret_cast<const int*>(w + p.off_part_slot), p.nsplit, p.small ? small_chunks(p) : p.nsplit,
+                       reinterpret_cast<const float*>(w + p.off_part_score), part_slot, p.nsplit,
+                       p.small ? small_chunks(p) : p.nsplit,
                        (s.f32 || p.small) ? nullptr : reinterpret_cast<const int*>(w + p.off_tile_nblk), p.chunk_slots,
-                       s.W2,
-                       c.cap_ref, c.cap_tok,
-                       s.top_k, c.ref_idx, reinterpret_cast<KvT*>(w + p.off_xbar), c.err);
+                       s.W2, c.cap_ref, c.cap_tok, s.top_k, c.ref_idx, xbar, rescan, c.err, c.stats);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // queued tokens (usually none): a grid of workgroups walks the queue
+    const int chunk_len = p.small ? 0 : p.chunk_slots * (s.f32 ? SC<float>::BM : s2::BM);
+    const int grid_r = (int)std::min<long long>(64, (long long)c.B * n);
+    hipLaunchKernelGGL((rescan_kernel<KvT, RefT>), dim3(grid_r), dim3(256), 0, st, static_cast<const KvT*>(kv),
+                       kv_len, rows, pos, n, static_cast<const RefT*>(c.ref_vals), c.ref_pos, c.ref_count, part_slot,
+                       p.nsplit, chunk_len, s.W2, c.cap_ref, c.cap_tok, s.top_k, c.ref_idx, xbar, rescan);
     return hipGetLastError();
 }
 

@@ -18,4 +18,6 @@ from .generators import (  # noqa: F401
     selected_subset,
     workload,
     WORKLOADS,
+    NearTieCase,
+    near_tie_kv,
 )

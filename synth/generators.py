@@ -216,3 +216,120 @@ def workload(wid: int, **overrides) -> WorkloadConfig:
     """Workload `wid`, with fields overridden (e.g. a shorter T for parity runs)."""
     cfg = WORKLOADS[wid]
     return cfg.replace(**overrides) if overrides else cfg
+
+
+# --------------------------------------------------------------------------------------
+# near-duplicate and near-equidistant references (adversarial inputs of the top-k search)
+# --------------------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class NearTieCase:
+    """kv rows [T, dim] with planted reference rows, and the tokens aimed at them.
+
+    exact_tokens: positions whose nearest references tie exactly (equal rows, or a token
+    halfway between two rows), so the lower-slot rule fixes the set; graded_tokens:
+    positions whose nearest references differ by steps far larger than any rounding;
+    below_fp32_tokens: positions whose k-th and (k+1)-th nearest references differ by
+    about 3e-10 of the distance, the nearer one at the higher slot (fp32 sums cannot
+    order them, fp64 can)."""
+
+    kv: np.ndarray
+    exact_tokens: np.ndarray
+    graded_tokens: np.ndarray
+    below_fp32_tokens: np.ndarray
+
+
+def _fp8_base_row(dim: int, rng: np.random.Generator) -> np.ndarray:
+    """A row of +-(1 + m/8), m = 0..6: exact in OCP e4m3 and bf16, and so is every
+    value within 0.25 of it on the grid used below."""
+    mag = 1.0 + rng.integers(0, 7, size=dim) / 8.0
+    sgn = np.where(rng.random(dim) < 0.5, -1.0, 1.0)
+    return (mag * sgn).astype(np.float32)
+
+
+def near_tie_kv(base: np.ndarray, stride: int, ref_slots: Dict[str, int], tok_start: int,
+                rng: np.random.Generator, n_dup: int = 12) -> NearTieCase:
+    """Plant near-duplicate reference rows into `base` (clustered rows [T, dim], values
+    exact in bf16), references at positions 0, stride, 2 stride, ...
+
+    ref_slots gives the first pool slot of each planted group ('dup', 'graded', 'pairs');
+    the tokens aimed at them take the non-reference positions from tok_start on (all
+    after every planted reference). Groups:
+      dup    - n_dup identical rows A, then n_dup rows A with one coordinate one FP8 step
+               up; tokens equal to A, and halfway between A and a shifted row;
+      graded - rows that agree with a token y on dim (10 + j) / 128 of its coordinates
+               (slot order ascending in j, so later slots are nearer);
+      pairs  - for 8 tokens: three rows nearer than a pair (P, Q) that differ only in
+               coordinate 0 (2^-9 against 0); the token's coordinate 0 is 2^-10 - 2^-17,
+               so Q (the higher slot) is nearer by 2^-25 at a distance near dim / 16.
+    """
+    kv = np.array(base, dtype=np.float32, copy=True)
+    T, dim = kv.shape
+    assert dim % 128 == 0 and dim >= 256
+    slot_pos = lambda m: m * stride  # noqa: E731
+    toks = [p for p in range(tok_start, T) if p % stride != 0]
+    ti = iter(toks)
+    exact, graded, below = [], [], []
+
+    # dup group
+    A = _fp8_base_row(dim, rng)
+    s0 = ref_slots["dup"]
+    for i in range(n_dup):
+        kv[slot_pos(s0 + i)] = A
+    for i in range(n_dup):
+        j = 3 + 7 * i
+        r = A.copy()
+        r[j] = A[j] + np.sign(A[j]) * 0.125  # one e4m3 step in [1, 2)
+        kv[slot_pos(s0 + n_dup + i)] = r
+    for _ in range(4):
+        p = next(ti)
+        kv[p] = A
+        exact.append(p)
+    for i in range(4):
+        j = 3 + 7 * i
+        p = next(ti)
+        y = A.copy()
+        y[j] = A[j] + np.sign(A[j]) * 0.0625  # halfway to the shifted row
+        kv[p] = y
+        exact.append(p)
+
+    # graded group
+    Bg = _fp8_base_row(dim, rng)
+    delta = np.where(rng.random(dim) < 0.5, -0.25, 0.25).astype(np.float32)
+    y = Bg + delta  # |y| in [0.75, 2.0]: exact in e4m3 and bf16
+    s0 = ref_slots["graded"]
+    for i in range(12):
+        r = Bg.copy()
+        L = dim * (10 + i) // 128
+        r[:L] = y[:L]
+        kv[slot_pos(s0 + i)] = r
+    p = next(ti)
+    kv[p] = y
+    graded.append(p)
+
+    # below-fp32 pairs
+    s0 = ref_slots["pairs"]
+    for m in range(8):
+        Bm = _fp8_base_row(dim, rng)
+        dm = np.where(rng.random(dim) < 0.5, -0.25, 0.25).astype(np.float32)
+        dm[:2] = 0.0
+        x = Bm + dm
+        x[0] = np.float32(2.0 ** -10 - 2.0 ** -17)
+        rows = []
+        for L in (dim * 75 // 256, dim * 62 // 256, dim * 50 // 256):  # nearer than the pair
+            r = Bm.copy()
+            r[2:2 + L] = x[2:2 + L]
+            r[0] = 0.0
+            rows.append(r)
+        P = Bm.copy()
+        P[0] = np.float32(2.0 ** -9)
+        Q = Bm.copy()
+        Q[0] = 0.0
+        rows += [P, Q]
+        for i, r in enumerate(rows):
+            kv[slot_pos(s0 + 5 * m + i)] = r
+        p = next(ti)
+        kv[p] = x
+        below.append(p)
+    return NearTieCase(kv, np.array(exact, np.int64), np.array(graded, np.int64), np.array(below, np.int64))

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(B.EXPORTED)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.rkv_abi_version() == 2
+    assert lib.rkv_abi_version() == 3
 
 
 def test_prepared_decoder_bytes(lib):

@@ -363,6 +363,71 @@ def test_streaming_equals_bulk():
     np.testing.assert_array_equal(codec.decode_selected(bulk, np.arange(T)), codec.decode_selected(stream, np.arange(T)))
 
 
+# ------------------------------------------------- re-encoding with given reference sets
+
+
+def test_ref_override_with_own_sets_reproduces_records():
+    # the parity tests re-encode a token with the GPU's (equally near) reference set; with
+    # the oracle's own sets that re-encode must reproduce its records bit for bit
+    codec, _ = small_codec(mode="bf16", bits=4)
+    T, s = 120, 8
+    kv = bf16_round(workload(2).replace(n_kv_heads=2, head_dim=16).make_kv(T=T))
+    bulk = codec.prefill(kv, s)
+    pos = np.array([p for p in range(1, T) if p % s][::3])
+    again = codec.prefill(kv, s)
+    codec.encode(again, kv[pos], pos, ref_override={int(p): bulk.ref_idx[p][bulk.ref_idx[p] >= 0] for p in pos})
+    for name in ("q", "step", "zmin", "ref_idx", "ref_dist", "z"):
+        assert np.array_equal(getattr(bulk, name), getattr(again, name), equal_nan=True), name
+
+
+def test_ref_override_uses_the_given_slots():
+    # another set than the search's: the stored slots, their distances and the mean the
+    # encoder sees all come from the given slots (section 2.2 mean equation, section 2.3)
+    codec, W = small_codec(mode="bf16", bits=4)
+    T, s = 120, 8
+    kv = bf16_round(workload(2).replace(n_kv_heads=2, head_dim=16).make_kv(T=T))
+    cache = codec.prefill(kv, s)
+    p = 101
+    given = [0, 3, 7, 11]  # descending order on purpose: stored ascending
+    codec.encode(cache, kv[p][None], [p], ref_override={p: given[::-1]})
+    assert cache.ref_idx[p].tolist() == given
+    np.testing.assert_array_equal(cache.ref_dist[p], np.sum((cache.ref_val[given] - kv[p][None]) ** 2, axis=1))
+    xbar = bf16_round(reference_mean32(cache.ref_val[given])).astype(np.float64)
+    z = (swiglu_compressor(kv[p][None], W["Wc1"], W["Wc2"], W["Wc3"])
+         - swiglu_compressor(xbar[None], W["Wc1"], W["Wc2"], W["Wc3"]))[0]
+    np.testing.assert_array_equal(cache.z[p], z)
+    searched = codec.prefill(kv, s)
+    assert not np.array_equal(searched.ref_idx[p], cache.ref_idx[p])
+    assert not np.array_equal(searched.z[p], cache.z[p])
+
+
+def test_near_tie_generator_plants_what_it_says():
+    # the adversarial search inputs of the GPU parity tests: planted rows are exact in FP8,
+    # equal rows tie at distance 0 (lower slots win), and each planted pair puts its nearer
+    # row at the higher slot, 2^-25 nearer
+    from synth import near_tie_kv
+
+    wl = workload(2, T=2200, stride=2)
+    c = near_tie_kv(wl.make_kv(), 2, {"dup": 600, "graded": 40, "pairs": 1030}, 2110, np.random.default_rng(7))
+    refp = np.arange(0, wl.T, 2)
+    rv = fp8_e4m3fn_decode(fp8_e4m3fn_encode(c.kv[refp]))
+    for m in list(range(600, 624)) + list(range(40, 52)) + list(range(1030, 1070)):
+        np.testing.assert_array_equal(rv[m], c.kv[refp[m]])
+    assert np.array_equal(bf16_round(c.kv), c.kv)
+    for p in c.exact_tokens:
+        slots, _ = topk_references(c.kv[p], rv, refp, refp.size, p, 4)
+        assert slots.tolist() == [600, 601, 602, 603]
+    slots, d = topk_references(c.kv[c.graded_tokens[0]], rv, refp, refp.size, c.graded_tokens[0], 4)
+    assert slots.tolist() == [48, 49, 50, 51] and np.all(np.diff(d) == -1.0)
+    for m, p in enumerate(c.below_fp32_tokens):
+        slots, _ = topk_references(c.kv[p], rv, refp, refp.size, p, 4)
+        base = 1030 + 5 * m
+        assert slots.tolist() == [base, base + 1, base + 2, base + 4]
+        dP = np.sum((rv[base + 3] - c.kv[p]) ** 2)
+        dQ = np.sum((rv[base + 4] - c.kv[p]) ** 2)
+        assert dP - dQ == 2.0 ** -25
+
+
 # ------------------------------------------------------------ storage accounting (section 3.3)
 
 

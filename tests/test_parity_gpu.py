@@ -98,6 +98,10 @@ CASES = {
     "qwen-table1-dc384-int2": (4, dict(T=1600, d_ff=3072, d_c=384)),
     "qwen-table1-dc384-int4-batch2": (4, dict(T=700, d_ff=3072, d_c=384, bits=4, batch=2)),
     "qwen32b-table1-dff4096": (2, dict(T=800, d_ff=4096)),
+    # head_dim 64 in the bf16 formats (16 KV heads x 64: the 2048-wide joint vector, RoPE
+    # pairs (j, j + 32), the restore's 64-column passes)
+    "d64-bf16-int4": (2, dict(T=1100, n_kv_heads=16, head_dim=64)),
+    "d64-bf16-fp16-latent": (2, dict(T=700, n_kv_heads=8, head_dim=64, d_c=256, bits=16)),
 }
 
 

@@ -68,6 +68,7 @@ CASES = {
     "qwen-shape-int2-gqa7": (4, dict(T=2000), 28, [3, 600]),
     "batch3-int4-mha": (5, dict(T=700, batch=3), 8, [200]),
     "batch2-fp16-latent-gqa8": (5, dict(T=520, batch=2, bits=16), 64, [300]),
+    "d64-bf16-gqa2": (2, dict(T=900, n_kv_heads=16, head_dim=64), 32, [7, 270]),
 }
 
 
