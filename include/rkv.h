@@ -219,6 +219,27 @@ rkv_status rkv_encode_ex(const rkv_config* cfg, const rkv_weights* w, rkv_cache*
                          int32_t kv_len, const int32_t* rows, const int32_t* pos, int32_t n, void* workspace,
                          size_t workspace_bytes, void* stream, void* const* events);
 
+/* Size of the static device scratch of rkv_encode_noalloc (per GPU). */
+#define RKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* rkv_encode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same call, the
+ * same kernels and the same results, with the workspace taken from a static device array
+ * of this library (RKV_NOALLOC_SCRATCH_BYTES, one copy per GPU, held until the process
+ * ends) instead of a caller buffer. Nothing is allocated or freed; the caller still
+ * passes every input and output. The first call on a device looks up that device's copy
+ * of the array (hipGetSymbolAddress, with the device current).
+ * Returns RKV_ERR_WORKSPACE, launching nothing, when the call needs more than
+ * RKV_NOALLOC_SCRATCH_BYTES (rkv_encode_workspace_bytes(cfg, B, n, cap_ref) > the
+ * limit: at the Llama-3.1-8B KV shape about 10.5 KB per token, so bulk calls of up to
+ * ~1500 tokens and any decode-time call); RKV_ERR_HIP if the array's address cannot be
+ * obtained; otherwise what rkv_encode returns. The scratch holds nothing a call needs
+ * from an earlier one (every part is written before it is read). All calls on one GPU
+ * share the array: calls that overlap on one GPU (different streams, or host threads
+ * without ordering) race and must be serialised by the caller. */
+rkv_status rkv_encode_noalloc(const rkv_config* cfg, const rkv_weights* w, rkv_cache* cache, const void* kv,
+                              int32_t kv_len, const int32_t* rows, const int32_t* pos, int32_t n, void* stream);
+
 /* Bytes of the prepared decoder of a "bf16" configuration: 2 * (2 d_k) * d_c. Host-only;
  * 0 on an invalid or "f32" configuration. */
 size_t rkv_prepared_decoder_bytes(const rkv_config* cfg);

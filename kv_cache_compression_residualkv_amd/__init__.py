@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     rkv_decode_attend_workspace_bytes,
     rkv_decode_selected,
     rkv_encode,
+    rkv_encode_noalloc,
     rkv_encode_workspace_bytes,
     rkv_prepared_decoder_bytes,
     rkv_record_bytes,

@@ -35,6 +35,7 @@ STATUS = {
 }
 RKV_ENCODE_PHASES = 4
 RKV_STATS_WORDS = 2
+RKV_NOALLOC_SCRATCH_BYTES = 16 << 20
 ABI_VERSION = 3
 DEVERR_EMPTY_POOL, DEVERR_POS_RANGE, DEVERR_REF_CAPACITY, DEVERR_IDX_RANGE, DEVERR_ROW_RANGE = 1, 2, 4, 8, 16
 
@@ -48,6 +49,7 @@ EXPORTED = (
     "rkv_append_ref",
     "rkv_encode",
     "rkv_encode_ex",
+    "rkv_encode_noalloc",
     "rkv_decode_selected",
     "rkv_decode_attend_workspace_bytes",
     "rkv_decode_attend",
@@ -136,6 +138,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.rkv_encode.argtypes = [cfg_p, w_p, c_p, vp, i32, vp, vp, i32, vp, sz, vp]
     lib.rkv_encode_ex.restype = ctypes.c_int
     lib.rkv_encode_ex.argtypes = [cfg_p, w_p, c_p, vp, i32, vp, vp, i32, vp, sz, vp, ctypes.POINTER(vp)]
+    lib.rkv_encode_noalloc.restype = ctypes.c_int
+    lib.rkv_encode_noalloc.argtypes = [cfg_p, w_p, c_p, vp, i32, vp, vp, i32, vp]
     lib.rkv_decode_selected.restype = ctypes.c_int
     lib.rkv_decode_selected.argtypes = [cfg_p, w_p, c_p, vp, i32, vp, i32, vp]
     lib.rkv_decode_attend_workspace_bytes.restype = sz
@@ -376,6 +380,17 @@ def rkv_encode(cfg: CodecConfig, weights: CodecWeights, cache: CodecCache, kv: t
         arr = (ctypes.c_void_p * len(events))(*events)
         _check("rkv_encode_ex", lib.rkv_encode_ex(*args, arr))
     return workspace
+
+
+def rkv_encode_noalloc(cfg: CodecConfig, weights: CodecWeights, cache: CodecCache, kv: torch.Tensor,
+                       rows: torch.Tensor, pos: torch.Tensor, stream=None) -> None:
+    """rkv_encode with the library's static device scratch instead of a workspace (no
+    allocation by the library; the argument tensors are the caller's)."""
+    kv, rows, pos = _rows_pos(kv, rows, pos, cache.batch)
+    st = load_library().rkv_encode_noalloc(ctypes.byref(cfg.c_struct()), ctypes.byref(weights._c),
+                                           ctypes.byref(cache._c), _ptr(kv), kv.shape[1], _ptr(rows), _ptr(pos),
+                                           rows.shape[1], _stream(stream))
+    _check("rkv_encode_noalloc", st)
 
 
 def rkv_decode_selected(cfg: CodecConfig, weights: CodecWeights, cache: CodecCache, idx: torch.Tensor,

@@ -19,7 +19,7 @@ LIB_NAME = "librkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["rkv_api.hip", "rkv_append.hip", "rkv_search.hip", "rkv_encode.hip", "rkv_decode.hip",
-           "rkv_decode_tiles.hip", "rkv_attend.hip"]
+           "rkv_decode_tiles.hip", "rkv_attend.hip", "rkv_noalloc.hip"]
 
 # Packed fp32 vector ops are kept out of the generated code (see the design notes).
 HIP_FLAGS = [

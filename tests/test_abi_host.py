@@ -201,3 +201,19 @@ def test_decode_attend_host_checks(lib):
     empty = B._Cache()
     assert lib.rkv_decode_attend(ctypes.byref(cfg.c_struct()), None, ctypes.byref(empty), None, 4, None, 32,
                                  ctypes.c_float(0.1), None, None, 0, None) == -1
+
+
+def test_encode_noalloc_host_checks(lib):
+    # argument checks before any device work: no configuration, no cache, a bad configuration
+    cfg = B.CodecConfig.from_workload(workload(2))
+    assert lib.rkv_encode_noalloc(None, None, None, None, 0, None, None, 1, None) == -1
+    assert lib.rkv_encode_noalloc(ctypes.byref(cfg.c_struct()), None, None, None, 0, None, None, 1, None) == -1
+    bad = cfg.c_struct()
+    bad.group = 16
+    c = B._Cache()
+    c.batch, c.cap_ref, c.cap_tok = 1, 8, 8
+    assert lib.rkv_encode_noalloc(ctypes.byref(bad), None, ctypes.byref(c), None, 0, None, None, 1, None) == -2
+    # the static scratch bounds the calls it serves
+    assert B.RKV_NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert B.rkv_encode_workspace_bytes(cfg, 1, 1400, 4096) <= B.RKV_NOALLOC_SCRATCH_BYTES
+    assert B.rkv_encode_workspace_bytes(cfg, 1, 4000, 4096) > B.RKV_NOALLOC_SCRATCH_BYTES
