@@ -274,13 +274,16 @@ size_t rkv_decode_attend_workspace_bytes(const rkv_config* cfg, int32_t batch, i
  * (consecutive query heads share KV head h / G):
  *   out[b, h] = sum_t softmax_t(scale * q[b, h] . K[b, t, h / G]) V[b, t, h / G]
  * over the m tokens idx[b, 0..m-1], K|V being exactly what rkv_decode_selected writes
- * (keys rotated at their own positions), held in bf16 in the workspace between the
- * restore and the attention. The query must already carry its own rotation.
+ * in bf16 (keys rotated at their own positions). Where the token-tile restore applies
+ * (top_k <= 4, d_c a multiple of 128) the restore and the attention run in one kernel and
+ * no restored row is written to memory; other shapes restore into the workspace first.
+ * The query must already carry its own rotation.
  *   q   [B, n_q_heads, head_dim] bf16 (device); out [B, n_q_heads, head_dim] fp32;
  *   scale > 0 (usually 1 / sqrt(head_dim)); m = 0 gives zeros.
  * "bf16" configurations, head_dim 64 or 128, G <= 8; RKV_ERR_UNSUPPORTED otherwise.
  * workspace: >= rkv_decode_attend_workspace_bytes(cfg, B, m, n_q_heads) bytes, 16-byte
- * aligned (may be NULL when m = 0). The restore's index rules and error bits apply. */
+ * aligned (may be NULL when m = 0): per-tile partial outputs, and room for the fp16
+ * decoder when w->w_d_f16 is NULL. The restore's index rules and error bits apply. */
 rkv_status rkv_decode_attend(const rkv_config* cfg, const rkv_weights* w, const rkv_cache* cache,
                              const int32_t* idx, int32_t m, const void* q, int32_t n_q_heads, float scale,
                              float* out, void* workspace, size_t workspace_bytes, void* stream);

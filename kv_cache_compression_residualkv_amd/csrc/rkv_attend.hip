@@ -4,15 +4,18 @@
 //
 //   out[b, h] = sum_j softmax_j(scale * q[b, h] . K[b, j, g]) V[b, j, g],  g = h / G,
 //
-// G = H_q / N query heads per KV head. Split over tokens (each workgroup one chunk of
-// kChunk tokens of one KV head), then one combine pass per (sequence, query head):
+// G = H_q / N query heads per KV head. Where the token-tile restore applies, the
+// attention runs inside it (restore_attend_kernel, rkv_decode_tiles.hip: no restored row
+// leaves the chip) and leaves one partial per token tile; otherwise the selected tokens
+// are restored into the workspace and split over tokens (each workgroup one chunk of
+// kChunk tokens of one KV head). Then one combine pass per (sequence, query head):
 //   chunk pass: scores of the chunk's tokens for the G query heads (one thread per
 //     token reads its key row; the queries sit in LDS and are read as broadcasts),
 //     the chunk maximum and exp weights per head, then P V with 16 lanes per token
 //     row (16-byte value loads, 4 rows per wavefront at a time); writes the chunk's
 //     unnormalised output, maximum and weight sum;
-//   combine pass (one workgroup per query head): rescales the chunks to the overall
-//     maximum and divides by the sum.
+//   combine pass (one workgroup per query head and 32 dimensions): rescales the chunks
+//     to the overall maximum and divides by the sum.
 // The key/value rows are bf16 [B, m, 2 d_k] (K heads, then V heads), as the restore
 // writes them. The pass reads each row once: it is bound by HBM bandwidth.
 #include <hip/hip_runtime.h>
@@ -27,7 +30,7 @@ namespace {
 
 constexpr int kChunk = 256;   // tokens per workgroup
 constexpr int kThreads = 256;  // one thread per token in the score pass
-constexpr int kMaxG = 8;       // query heads per KV head
+constexpr int kMaxG = kAttendMaxG;  // query heads per KV head
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void attend_chunk_kernel(const bf16_t* __restrict__ kv, int m, int W2, int dk,
@@ -153,21 +156,25 @@ __global__ __launch_bounds__(kThreads) void attend_chunk_kernel(const bf16_t* __
     }
 }
 
-// out[b, hq, d] for one query head hq = g G + h per workgroup; no chunks (m = 0): zeros.
-// kCombThreads threads: thread (slice, d) sums the chunks slice, slice + S, ... of
-// dimension d (S = kCombThreads / D slices), after the block-wide maximum of the chunks'
-// maxima; the slices are then added through LDS.
-constexpr int kCombThreads = 512;
+// out[b, hq, d] for query head hq = g G + h and 32 dimensions d0 .. d0 + 31 per workgroup
+// (no chunks, m = 0: zeros). The chunks' weights exp(m_c - M) and weighted sums l_c
+// exp(m_c - M) are formed once in LDS (M: the largest m_c); then thread (slice, d) adds
+// the chunks slice, slice + S, ... of dimension d (S = kCombThreads / 32 slices) and the
+// slices meet through LDS.
+constexpr int kCombThreads = 1024;
+constexpr int kCombDims = 32;
+constexpr int kCombMaxChunks = 2048;  // chunks whose weights fit the LDS table; more are recomputed
 
 template <int D>
 __global__ __launch_bounds__(kCombThreads) void attend_combine_kernel(const float* __restrict__ part_o,
                                                                       const float* __restrict__ part_ml, int N,
                                                                       int nch, int Hq, int G, float* __restrict__ out) {
-    constexpr int S = kCombThreads / D;
+    constexpr int S = kCombThreads / kCombDims;
     __shared__ float sMax[kCombThreads / 64];
-    __shared__ float sNum[S][D];
-    __shared__ float sDen[S];
-    const int hq = blockIdx.x, b = blockIdx.y;
+    __shared__ float sW[kCombMaxChunks];
+    __shared__ float sNum[S][kCombDims];
+    __shared__ float sDen[kCombThreads / 64];
+    const int hq = blockIdx.x, b = blockIdx.y, d0 = kCombDims * blockIdx.z;
     const int g = hq / G, h = hq - g * G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t base = ((size_t)b * N + g) * nch;
@@ -180,26 +187,34 @@ __global__ __launch_bounds__(kCombThreads) void attend_combine_kernel(const floa
     mx = sMax[0];
 #pragma unroll
     for (int w = 1; w < kCombThreads / 64; ++w) mx = fmaxf(mx, sMax[w]);
-    const int d = tid % D, sl = tid / D;
-    float num = 0.f, den = 0.f;
-#pragma unroll 4
-    for (int c = sl; c < nch; c += S) {
+    // chunk weights and the denominator
+    float den = 0.f;
+    for (int c = tid; c < nch; c += kCombThreads) {
         const float* ml = part_ml + ((base + c) * kMaxG + h) * 2;
         const float w = expf(ml[0] - mx);
+        if (c < kCombMaxChunks) sW[c] = w;
         den = fmaf(ml[1], w, den);
-        num = fmaf(part_o[((base + c) * kMaxG + h) * D + d], w, num);
+    }
+    den = wave_sum(den);
+    if (lane == 0) sDen[wave] = den;
+    __syncthreads();
+    const int d = tid % kCombDims, sl = tid / kCombDims;
+    float num = 0.f;
+#pragma unroll 4
+    for (int c = sl; c < nch; c += S) {
+        const float w = c < kCombMaxChunks ? sW[c] : expf(part_ml[((base + c) * kMaxG + h) * 2] - mx);
+        num = fmaf(part_o[((base + c) * kMaxG + h) * D + d0 + d], w, num);
     }
     sNum[sl][d] = num;
-    if (d == 0) sDen[sl] = den;
     __syncthreads();
-    if (tid < D) {
-        float n = 0.f, dd = 0.f;
+    if (tid < kCombDims) {
+        float n = 0.f;
 #pragma unroll
-        for (int k = 0; k < S; ++k) {
-            n += sNum[k][tid];
-            dd += sDen[k];
-        }
-        out[((size_t)b * Hq + hq) * D + tid] = dd > 0.f ? n / dd : 0.f;
+        for (int k = 0; k < S; ++k) n += sNum[k][tid];
+        float dd = 0.f;
+#pragma unroll
+        for (int w = 0; w < kCombThreads / 64; ++w) dd += sDen[w];
+        out[((size_t)b * Hq + hq) * D + d0 + tid] = dd > 0.f ? n / dd : 0.f;
     }
 }
 
@@ -229,12 +244,35 @@ hipError_t chunk_g(int G, dim3 grid, hipStream_t st, const bf16_t* kv, int m, in
 
 }  // namespace
 
-size_t attend_workspace_bytes(const Shape& s, int B, int m) {
+// The fused path (restore_attend_kernel, then the combine) serves every shape the
+// token-tile restore takes; other shapes restore into the workspace and run the chunk
+// kernel over the rows.
+static bool attend_fused(const Shape& s) { return decode_tiles_supported(s); }
+
+struct AttendWs {
+    size_t rows, part_o, part_ml, wprep, total;
+    int nch;
+};
+static AttendWs attend_ws(const Shape& s, int B, int m) {
     auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-    const size_t nch = (size_t)(m + kChunk - 1) / kChunk;
-    return up((size_t)B * m * s.W2 * sizeof(bf16_t)) + up((size_t)B * s.N * nch * kMaxG * s.D * sizeof(float)) +
-           up((size_t)B * s.N * nch * kMaxG * 2 * sizeof(float));
+    AttendWs w{};
+    if (m <= 0) return w;  // nothing restored: the combine writes zeros
+    const bool fused = attend_fused(s);
+    w.nch = fused ? restore_attend_tiles(m) : (m + kChunk - 1) / kChunk;
+    size_t off = 0;
+    w.rows = off;
+    if (!fused) off += up((size_t)B * m * s.W2 * sizeof(bf16_t));
+    w.part_o = off;
+    off += up((size_t)B * s.N * w.nch * kMaxG * s.D * sizeof(float));
+    w.part_ml = off;
+    off += up((size_t)B * s.N * w.nch * kMaxG * 2 * sizeof(float));
+    w.wprep = off;  // the fused path's prepared decoder when the caller has none
+    if (fused) off += up((size_t)2 * s.W2 * s.d_c);
+    w.total = off;
+    return w;
 }
+
+size_t attend_workspace_bytes(const Shape& s, int B, int m) { return attend_ws(s, B, m).total; }
 
 bool attend_supported(const Shape& s, int Hq) {
     return !s.f32 && (s.D == 64 || s.D == 128) && Hq > 0 && Hq % s.N == 0 && Hq / s.N <= kMaxG;
@@ -242,29 +280,39 @@ bool attend_supported(const Shape& s, int Hq) {
 
 hipError_t launch_attend(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd,
                          const void* wd16, const void* q, int Hq, float scale, float* out, void* ws, hipStream_t st) {
-    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
     const int B = c.B, G = Hq / s.N;
-    const int nch = (m + kChunk - 1) / kChunk;
+    const AttendWs L = attend_ws(s, B, m);
+    const int nch = L.nch;
     char* w = static_cast<char*>(ws);
-    bf16_t* kv = reinterpret_cast<bf16_t*>(w);
-    float* part_o = reinterpret_cast<float*>(w + up((size_t)B * m * s.W2 * sizeof(bf16_t)));
-    float* part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(part_o) +
-                                              up((size_t)B * s.N * nch * kMaxG * s.D * sizeof(float)));
+    float* part_o = reinterpret_cast<float*>(w + L.part_o);
+    float* part_ml = reinterpret_cast<float*>(w + L.part_ml);
     if (m > 0) {
-        hipError_t e = launch_decode(s, c, idx, m, wd, wd16, kv, RKV_BF16, st);
-        if (e != hipSuccess) return e;
-        e = s.D == 64 ? chunk_g<64>(G, dim3(nch, s.N, B), st, kv, m, s.W2, s.dk, q, Hq, scale, part_o, part_ml, nch)
-                      : chunk_g<128>(G, dim3(nch, s.N, B), st, kv, m, s.W2, s.dk, q, Hq, scale, part_o, part_ml, nch);
-        if (e != hipSuccess) return e;
-        e = hipGetLastError();
+        hipError_t e;
+        if (attend_fused(s)) {
+            if (!wd16) {
+                e = launch_prepare_decoder(s, wd, w + L.wprep, st);
+                if (e != hipSuccess) return e;
+                wd16 = w + L.wprep;
+            }
+            e = launch_restore_attend(s, c, idx, m, wd16, q, Hq, scale, part_o, part_ml, st);
+        } else {
+            bf16_t* kv = reinterpret_cast<bf16_t*>(w + L.rows);
+            e = launch_decode(s, c, idx, m, wd, wd16, kv, RKV_BF16, st);
+            if (e != hipSuccess) return e;
+            e = s.D == 64 ? chunk_g<64>(G, dim3(nch, s.N, B), st, kv, m, s.W2, s.dk, q, Hq, scale, part_o, part_ml, nch)
+                          : chunk_g<128>(G, dim3(nch, s.N, B), st, kv, m, s.W2, s.dk, q, Hq, scale, part_o, part_ml,
+                                         nch);
+            if (e == hipSuccess) e = hipGetLastError();
+        }
         if (e != hipSuccess) return e;
     }
+    const dim3 cgrid(Hq, B, s.D / kCombDims);
     if (s.D == 64)
-        hipLaunchKernelGGL(attend_combine_kernel<64>, dim3(Hq, B), dim3(kCombThreads), 0, st, part_o, part_ml, s.N,
-                           nch, Hq, G, out);
+        hipLaunchKernelGGL(attend_combine_kernel<64>, cgrid, dim3(kCombThreads), 0, st, part_o, part_ml, s.N, nch, Hq,
+                           G, out);
     else
-        hipLaunchKernelGGL(attend_combine_kernel<128>, dim3(Hq, B), dim3(kCombThreads), 0, st, part_o, part_ml, s.N,
-                           nch, Hq, G, out);
+        hipLaunchKernelGGL(attend_combine_kernel<128>, cgrid, dim3(kCombThreads), 0, st, part_o, part_ml, s.N, nch, Hq,
+                           G, out);
     return hipGetLastError();
 }
 

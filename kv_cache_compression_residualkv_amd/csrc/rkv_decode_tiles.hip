@@ -276,14 +276,14 @@ __device__ inline void latent_frags(f16x8 (&zf)[2][NKS], const int* __restrict__
 
 // RoPE table: cos / sin of every token's pair angles (two threads per token). The phase
 // in revolutions is reduced to [-1/2, 1/2] in fp64, then sin / cos in fp32.
-template <int D>
+template <int D, int RP = dt::kRopeP>
 __device__ inline void rope_table(float* sRope, const int* sPos, const double* sRev) {
     const int tid = threadIdx.x, tk = tid >> 1;
     const double pp = (double)sPos[tk];
     for (int j = (tid & 1) * 32; j < (tid & 1) * 32 + 32 && j < D / 2; ++j) {
         const double r = pp * sRev[j];
         const float fr = (float)(r - rint(r));
-        *reinterpret_cast<float2*>(sRope + 2 * (tk * dt::kRopeP + j)) =
+        *reinterpret_cast<float2*>(sRope + 2 * (tk * RP + j)) =
             make_float2(__builtin_amdgcn_cosf(fr), __builtin_amdgcn_sinf(fr));
     }
 }
@@ -316,14 +316,15 @@ __device__ inline MeanForm mean_form(const int* sKd) {
     return f;
 }
 
-// End of pass h of a chunk starting at column col0: reference mean (two FP8 MFMAs per
-// output tile against the slices in R: row r = q * TT + token, 64 bytes, tile t at 16-byte
-// position t ^ ((r / 4) % 4)), RoPE on key columns, store. An invalid index has a zero
-// latent and empty slots: its row is zero already.
-template <int D, bool kFused, typename OutT>
-__device__ inline void finish_pass(f32x4 (&acc)[2][4], const unsigned char* R, const float* sRope, int h, int col0,
-                                   bool rope, const MeanForm& mf, int tt0, int m, int b, int W2,
-                                   OutT* __restrict__ out) {
+// End of pass h of a chunk: reference mean (two FP8 MFMAs per output tile against the
+// slices in R: row r = q * TT + token, 64 bytes, tile t at 16-byte position
+// t ^ ((r / 4) % 4)) and, on key columns, RoPE (sRope rows of RP float2). After it the
+// lane holds, for its token 32 wave + 16 gr + lane % 16, columns 16 chunk_tile(h, lt) +
+// 4 (lane / 16) + e of the chunk in acc[gr][lt][e]. An invalid index has a zero latent and
+// empty slots: its row is zero already.
+template <int D, bool kFused, int RP = dt::kRopeP>
+__device__ inline void pass_values(f32x4 (&acc)[2][4], const unsigned char* R, const float* sRope, int h, bool rope,
+                                   const MeanForm& mf) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, mrow = lane & 15;
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
@@ -352,7 +353,7 @@ __device__ inline void finish_pass(f32x4 (&acc)[2][4], const unsigned char* R, c
 #pragma unroll
             for (int lt = 0; lt < 2; ++lt) {
                 const int jt = D == 128 ? 2 * h + lt : lt;
-                const float* rp = sRope + 2 * (tk * dt::kRopeP + 16 * jt + 4 * g);
+                const float* rp = sRope + 2 * (tk * RP + 16 * jt + 4 * g);
                 const float4 q01 = *reinterpret_cast<const float4*>(rp);
                 const float4 q23 = *reinterpret_cast<const float4*>(rp + 4);
                 const float cs[4] = {q01.x, q01.z, q23.x, q23.z};
@@ -365,12 +366,25 @@ __device__ inline void finish_pass(f32x4 (&acc)[2][4], const unsigned char* R, c
                 }
             }
         }
-        const int t = tt0 + tk;
+    }
+}
+
+// End of pass h of a chunk starting at column col0: pass_values, then the rows' store.
+template <int D, bool kFused, typename OutT>
+__device__ inline void finish_pass(f32x4 (&acc)[2][4], const unsigned char* R, const float* sRope, int h, int col0,
+                                   bool rope, const MeanForm& mf, int tt0, int m, int b, int W2,
+                                   OutT* __restrict__ out) {
+    pass_values<D, kFused>(acc, R, sRope, h, rope, mf);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, mrow = lane & 15;
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr) {
+        const int t = tt0 + 32 * wave + 16 * gr + mrow;
         if (t < m) {
             OutT* o = out + ((size_t)b * m + t) * W2 + col0 + 4 * g;
 #pragma unroll
             for (int lt = 0; lt < 4; ++lt)
-                store_row4<OutT>(o + 16 * chunk_tile<D>(h, lt), a[lt][0], a[lt][1], a[lt][2], a[lt][3]);
+                store_row4<OutT>(o + 16 * chunk_tile<D>(h, lt), acc[gr][lt][0], acc[gr][lt][1], acc[gr][lt][2],
+                                 acc[gr][lt][3]);
         }
     }
 }
@@ -772,6 +786,368 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
     }
 }
 
+// ---- restore fused with the attention of one decoding query per head --------------------
+// (review page section 2.7: the layer attends over the restored selected tokens.) A
+// workgroup takes a token tile and a run of "units": unit u is the K chunk u (columns
+// 128 u ..) and the V chunk u (columns d_k + 128 u ..), i.e. one KV head at D = 128 and
+// two at D = 64; the run does K u, V u, K u + 1, V u + 1, ... on the pipeline of
+// decode_tiles_dl_kernel. A pass's restored values (after the reference mean and, on
+// keys, RoPE) go to LDS in bf16, the precision the restored rows have in the unfused
+// path, instead of to memory:
+//   K pass: scores s[g][t] += q_g . K[t] over the pass's 64 columns, straight from the
+//           accumulators (a lane holds 16 of a token's columns; the four lanes of a token
+//           add their parts); when a head's key columns are done, the tile's softmax:
+//           m = max_t scale s, p = exp(scale s - m), l = sum_t p (wave reductions, the
+//           four wavefronts through LDS);
+//   V pass: the values go to LDS in bf16 and o[g][d] = sum_t p[g][t] V[t][d] for the
+//           pass's 64 columns, a thread per (query head, 8 columns, 16 tokens) with
+//           16-byte reads, the 8 token groups added by shuffles.
+// Each (tile, KV head, query head) leaves (o, m, l); attend_combine_kernel rescales the
+// tiles to the overall maximum and divides by the sum.
+namespace fa {
+template <int D>
+struct L {
+    static constexpr int G = kAttendMaxG;  // room for the largest query-head group
+    static constexpr int NST = dl::NST;
+    static constexpr int kRP = D / 2 + 2;        // float2 pitch of a token's RoPE row
+    static constexpr int kKP = dt::kHalf + 8;    // bf16 pitch of a key row of the pass (144 B)
+    static constexpr int kVP = dt::TT + 8;       // f16 pitch of a value column (272 B)
+    static constexpr int kQP = D + 8;            // bf16 pitch of a query row
+    static constexpr int kPP = dt::TT + 8;       // f16 pitch of a weight row
+    static constexpr int kNH = D == 64 ? 2 : 1;  // KV heads of a unit
+    static constexpr int kOffW = 0;
+    static constexpr int kOffRef = kOffW + NST * dl::kWStage;
+    static constexpr int kOffSlot = kOffRef + dt::kRefBuf;
+    static constexpr int kOffKd = kOffSlot + dt::TT * dt::kRefs * 4;
+    static constexpr int kOffRope = kOffKd + dt::TT * 4;
+    // keys of the pass [TT][kKP] bf16, or values of the pass transposed [64][kVP] f16
+    static constexpr int kOffKV = kOffRope + dt::TT * kRP * 8;
+    static constexpr int kKVBytes = dt::TT * kKP * 2 > 64 * kVP * 2 ? dt::TT * kKP * 2 : 64 * kVP * 2;
+    static constexpr int kOffQ = kOffKV + kKVBytes;                 // bf16 [kNH][G][kQP]
+    static constexpr int kOffP = kOffQ + kNH * G * kQP * 2;         // f16 weights [kNH][G][kPP]
+    static constexpr int kOffS = kOffP + kNH * G * kPP * 2;         // fp32 partial scores [G][TT]
+    static constexpr int kOffRed = kOffS + G * dt::TT * 4;          // fp32 [max, sum][4 waves][8]
+    static constexpr int bytes = kOffRed + 2 * 4 * 8 * 4;
+    static constexpr int kOffRev = kOffRef;
+    static constexpr int kOffPos = kOffRef + 64 * 8;
+    static_assert(bytes <= 160 * 1024, "LDS budget");
+    // the MFMA operand reads of query / weight rows G .. 15 (unused output columns) stay
+    // inside the allocation
+    static_assert(kOffRed + 2 * 4 * 8 * 4 >= kOffP + (kNH * G + 8) * kPP * 2, "operand over-read");
+};
+}  // namespace fa
+
+template <int NKS, int D, int BITS>
+__global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
+    const int* __restrict__ idx, int m, TileMapArgs ta, const fp8_t* __restrict__ ref_vals,
+    const int* __restrict__ self_slot, const int* __restrict__ ref_idx, const uint8_t* __restrict__ codes,
+    size_t code_bytes, const f16_t* __restrict__ scale, const f16_t* __restrict__ zmin, const f16_t* __restrict__ w16,
+    int W2, int dk, int top_k, int cap_ref, int cap_tok, double theta, const bf16_t* __restrict__ q, int G,
+    float qscale, float* __restrict__ part_o, float* __restrict__ part_ml, int* err) {
+    typedef fa::L<D> Ly;
+    constexpr int d_c = 32 * NKS;
+    constexpr int KST = d_c / kStageK;
+    constexpr int NST = Ly::NST;
+    static_assert(KST >= 2 && 2 * KST < 64, "stage shape");
+    static_assert(D == 64 || D == 128, "head dimension");
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char* sW = smem + Ly::kOffW;
+    unsigned char* sRef = smem + Ly::kOffRef;
+    int* sSlot = reinterpret_cast<int*>(smem + Ly::kOffSlot);
+    int* sKd = reinterpret_cast<int*>(smem + Ly::kOffKd);
+    float* sRope = reinterpret_cast<float*>(smem + Ly::kOffRope);
+    unsigned char* sKV = smem + Ly::kOffKV;
+    unsigned char* sQ = smem + Ly::kOffQ;
+    unsigned char* sP = smem + Ly::kOffP;
+    float* sS = reinterpret_cast<float*>(smem + Ly::kOffS);
+    float* sRed = reinterpret_cast<float*>(smem + Ly::kOffRed);
+    double* sRev = reinterpret_cast<double*>(smem + Ly::kOffRev);
+    int* sPos = reinterpret_cast<int*>(smem + Ly::kOffPos);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int N = dk / D, nK = dk / dt::kCols;
+    const int Hq = N * G;
+    // units play the part of the restore's chunks in the tile map (dk / 128 of them, as
+    // restore_attend_impl built the grid)
+    const TileMap tm = tile_map(ta, dk);
+    const int b = tm.b, tt0 = tm.tt0, tile = tt0 / dt::TT;
+    const int u0 = tm.n0 / dt::kCols;
+    const int nchunks = 2 * tm.nchunks;
+    const int ntiles = ta.tpb;
+    const fp8_t* pool = ref_vals + (size_t)b * cap_ref * W2;
+    auto chunk_col = [&](int c) {
+        const int u = u0 + (c >> 1);
+        return (c & 1) ? dk + dt::kCols * u : dt::kCols * u;
+    };
+
+    const int wv = wave_id(), lr = lane >> 2;
+    int rowoff[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) rowoff[h][u] = 16 * chunk_tile<D>(h, (wv + 4 * u) >> 1) + lr;
+    const f16_t* wswz = w16 + 8 * swz(lr, lane & 3);
+    auto issue_w = [&](int c, int h, int k, int slot) {
+        c = min(c, nchunks - 1);  // past the end: any readable stage (never used)
+        unsigned char* dst = sW + slot * dl::kWStage;
+        const f16_t* src = wswz + (size_t)chunk_col(c) * d_c + k * kStageK;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int blk = wv + 4 * u;
+            dma16(src + (size_t)rowoff[h][u] * d_c + 32 * (blk & 1), dst + 1024 * blk);
+        }
+    };
+    const uint8_t* zero = g_zero_slice;
+    auto issue_refs = [&](int c, int h) {
+        const int col = chunk_col(c);
+        int sl[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = 16 * (8 * wv + u) + lr;
+            sl[u] = sSlot[(r & (dt::TT - 1)) * dt::kRefs + (r >> 7)];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = 8 * wv + u, r = 16 * j + lr;
+            const int ts = (lane & 3) ^ ((r >> 2) & 3);
+            const uint8_t* src = sl[u] >= 0 ? reinterpret_cast<const uint8_t*>(pool) + (size_t)sl[u] * W2 + col +
+                                                  16 * chunk_tile<D>(h, ts)
+                                            : zero + 16 * ts;
+            dma16(src, sRef + 1024 * j);
+        }
+    };
+    auto ahead = [](int c, int h, int k, int d, int& c2, int& h2) {
+        const int du = (k + d) / KST;
+        c2 = c + ((h + du) >> 1);
+        h2 = (h + du) & 1;
+        return (k + d) % KST;
+    };
+
+#pragma unroll
+    for (int d = 0; d < NST; ++d) {
+        int c2, h2;
+        const int k2 = ahead(0, 0, 0, d, c2, h2);
+        issue_w(c2, h2, k2, d);
+    }
+    token_table<D>(sSlot, sKd, sPos, sRev, idx, m, b, tt0, tm.grp == 0, self_slot, ref_idx, top_k, cap_ref, cap_tok,
+                   theta, err);
+    f16x8 zf[2][NKS];
+    latent_frags<NKS, BITS>(zf, idx, m, b, tt0, self_slot, codes, code_bytes, scale, zmin, cap_tok);
+    __syncthreads();
+    rope_table<D, Ly::kRP>(sRope, sPos, sRev);
+    const MeanForm mf = mean_form(sKd);
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    typedef typename Mma<f16_t>::frag Frag;
+    auto read_frags = [&](Frag (&f)[4], int slot, int kh) {
+        const char* sp = reinterpret_cast<const char*>(sW + slot * dl::kWStage);
+#pragma unroll
+        for (int lt = 0; lt < 4; ++lt) f[lt] = Op16<64>::frag<f16_t>(sp, lt, kh);
+    };
+    auto mma = [&](f32x4 (&acc)[2][4], const Frag (&f)[4], int ks) {
+#pragma unroll
+        for (int lt = 0; lt < 4; ++lt) {
+            acc[0][lt] = Mma<f16_t>::step(acc[0][lt], f[lt], zf[0][ks]);
+            acc[1][lt] = Mma<f16_t>::step(acc[1][lt], f[lt], zf[1][ks]);
+        }
+    };
+
+    // queries of a unit, bf16 [kNH][G][kQP] (consecutive query heads share a KV head)
+    auto stage_q = [&](int u) {
+        for (int e = tid; e < Ly::kNH * G * D; e += dt::kThreads) {
+            const int r = e / D, d = e - r * D;  // r = hh G + g
+            const int hq = Ly::kNH * u * G + r;
+            reinterpret_cast<bf16_t*>(sQ)[r * Ly::kQP + d] = q[((size_t)b * Hq + hq) * D + d];
+        }
+    };
+    stage_q(u0);  // the main loop's barriers order it before the first score pass
+
+    const int g4 = lane >> 4, mrow = lane & 15;
+    float* sMax = sRed;
+    float* sSum = sRed + 32;
+
+    // The attention part of the end of pass (c, h), on MFMA: wavefront w takes its own 32
+    // tokens (two tiles of 16) in the scores and output columns 16 w .. + 16 of the pass in
+    // P V; the query heads are the 16-wide N side (columns G .. 15 unused).
+    auto attend_pass = [&](f32x4(&acc)[2][4], int c, int h) {
+        const bool isK = (c & 1) == 0;
+        const int u = u0 + (c >> 1);
+        const int hh = D == 128 ? 0 : h;  // KV head of the unit in this pass
+        const int head = Ly::kNH * u + hh;
+        // head dimension of local column block lt (16 columns of the pass)
+        auto dim0 = [&](int lt) { return D == 128 ? 16 * chunk_tile<D>(h, lt) : 16 * lt; };
+        const unsigned char* qrow = sQ + (hh * G) * Ly::kQP * 2;
+        unsigned char* prow = sP + (hh * G) * Ly::kPP * 2;
+        if (isK) {
+            // keys, rounded to bf16 as the restore writes them, to LDS [token][column]
+#pragma unroll
+            for (int gr = 0; gr < 2; ++gr) {
+                unsigned char* row = sKV + (32 * wave + 16 * gr + mrow) * Ly::kKP * 2;
+#pragma unroll
+                for (int lt = 0; lt < 4; ++lt) {
+                    const f32x2 lo = {acc[gr][lt][0], acc[gr][lt][1]}, hi = {acc[gr][lt][2], acc[gr][lt][3]};
+                    const bf16x2 x = __builtin_convertvector(lo, bf16x2), y = __builtin_convertvector(hi, bf16x2);
+                    *reinterpret_cast<uint2*>(row + 2 * (16 * lt + 4 * g4)) =
+                        make_uint2(*reinterpret_cast<const uint32_t*>(&x), *reinterpret_cast<const uint32_t*>(&y));
+                }
+            }
+            lds_barrier();
+            // scores S[t][g] = K[t] . q_g over the pass's 64 columns: 2 K-steps x 2 token tiles
+            const bool first = D == 128 && h == 0;  // the head's first of two key passes
+            const bool last = D == 64 || h == 1;    // the head's key columns all in
+            f32x4 st[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int lc = 32 * ks + 8 * g4;  // the lane's 8 columns of the K-step
+                const bf16x8 qb = lds_load<bf16x8>(qrow + mrow * Ly::kQP * 2 + 2 * (dim0(lc >> 4) + (lc & 15)));
+#pragma unroll
+                for (int tl = 0; tl < 2; ++tl) {
+                    const bf16x8 kb = lds_load<bf16x8>(sKV + (32 * wave + 16 * tl + mrow) * Ly::kKP * 2 + 2 * lc);
+                    st[tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, st[tl], 0, 0, 0);
+                }
+            }
+            // lane: query head mrow, tokens 32 w + 16 tl + 4 g4 + r
+            const bool gv = mrow < G;
+            float* srow = sS + mrow * dt::TT + 32 * wave + 4 * g4;
+            if (first) {
+                if (gv) {
+#pragma unroll
+                    for (int tl = 0; tl < 2; ++tl) *reinterpret_cast<f32x4*>(srow + 16 * tl) = st[tl];
+                }
+            }
+            if (last) {
+                if (D == 128 && gv) {
+#pragma unroll
+                    for (int tl = 0; tl < 2; ++tl) st[tl] += *reinterpret_cast<const f32x4*>(srow + 16 * tl);
+                }
+                // the tile's softmax per query head
+                float mxl = -INFINITY;
+#pragma unroll
+                for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bool ok = gv && tt0 + 32 * wave + 16 * tl + 4 * g4 + r < m;
+                        st[tl][r] = ok ? st[tl][r] * qscale : -INFINITY;
+                        mxl = fmaxf(mxl, st[tl][r]);
+                    }
+                mxl = fmaxf(mxl, __shfl_xor(mxl, 16, 64));
+                mxl = fmaxf(mxl, __shfl_xor(mxl, 32, 64));
+                if (g4 == 0 && gv) sMax[wave * 8 + mrow] = mxl;
+                lds_barrier();
+                const float mx = gv ? fmaxf(fmaxf(sMax[mrow], sMax[8 + mrow]), fmaxf(sMax[16 + mrow], sMax[24 + mrow]))
+                                    : 0.f;
+                float sum = 0.f;
+                f16_t pw[2][4];
+#pragma unroll
+                for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float p = st[tl][r] == -INFINITY ? 0.f : expf(st[tl][r] - mx);
+                        sum += p;
+                        pw[tl][r] = (f16_t)p;
+                    }
+                if (gv) {
+#pragma unroll
+                    for (int tl = 0; tl < 2; ++tl) {
+                        const f16x2 a = {pw[tl][0], pw[tl][1]}, bq = {pw[tl][2], pw[tl][3]};
+                        *reinterpret_cast<uint2*>(prow + mrow * Ly::kPP * 2 + 2 * (32 * wave + 16 * tl + 4 * g4)) =
+                            make_uint2(*reinterpret_cast<const uint32_t*>(&a), *reinterpret_cast<const uint32_t*>(&bq));
+                    }
+                }
+                sum += __shfl_xor(sum, 16, 64);
+                sum += __shfl_xor(sum, 32, 64);
+                if (g4 == 0 && gv) sSum[wave * 8 + mrow] = sum;
+                lds_barrier();
+                if (wave == 0 && g4 == 0 && gv) {
+                    float* ml = part_ml + ((((size_t)b * N + head) * ntiles + tile) * kAttendMaxG + mrow) * 2;
+                    ml[0] = mx;
+                    ml[1] = (sSum[mrow] + sSum[8 + mrow]) + (sSum[16 + mrow] + sSum[24 + mrow]);
+                }
+            }
+            // the queries of the next unit once this one's last key pass is done (the next
+            // score pass is a whole pass of barriers away)
+            if (last && (c >> 1) + 1 < tm.nchunks) stage_q(u + 1);
+        } else {
+            // values to LDS transposed, [column][token] f16 (bf16 first, as the restore writes
+            // them; bf16 -> f16 is exact in the normal range)
+            f16_t* vt = reinterpret_cast<f16_t*>(sKV);
+#pragma unroll
+            for (int gr = 0; gr < 2; ++gr) {
+                const int tk = 32 * wave + 16 * gr + mrow;
+#pragma unroll
+                for (int lt = 0; lt < 4; ++lt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        vt[(16 * lt + 4 * g4 + e) * Ly::kVP + tk] = (f16_t)(float)(bf16_t)acc[gr][lt][e];
+            }
+            lds_barrier();
+            // out^T[column][g] = sum_t V[t][column] P[g][t]: 4 K-steps of 32 tokens
+            f32x4 o = zero4();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const f16x8 va = lds_load<f16x8>(sKV + ((16 * wave + mrow) * Ly::kVP + 32 * ks + 8 * g4) * 2);
+                const f16x8 pb = lds_load<f16x8>(prow + (mrow * Ly::kPP + 32 * ks + 8 * g4) * 2);
+                o = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o, 0, 0, 0);
+            }
+            // lane: query head mrow, columns 16 w + 4 g4 + r of the pass
+            if (mrow < G) {
+                const int d = dim0(wave) + 4 * g4;
+                float* po = part_o + ((((size_t)b * N + head) * ntiles + tile) * kAttendMaxG + mrow) * D + d;
+                *reinterpret_cast<f32x4*>(po) = o;
+            }
+        }
+    };
+
+    Frag f0[4], f1[4];
+    read_frags(f0, 0, 0);
+    int slot = 0;
+    f32x4 acc[2][4];
+    for (int c = 0; c < nchunks; ++c) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[gr][i] = zero4();
+#pragma unroll
+            for (int k = 0; k < KST; ++k) {
+                read_frags(f1, slot, 1);
+                mma(acc, f0, 2 * k);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (k >= 1 && k <= NST - 1) wait_vmcnt<2 * (NST - 2) + 8>();
+                else wait_vmcnt<2 * (NST - 2)>();
+                lds_barrier();
+                const int next = slot + 1 == NST ? 0 : slot + 1;
+                read_frags(f0, next, 0);
+                mma(acc, f1, 2 * k + 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_lgkm0();
+                {
+                    int c2, h2;
+                    const int k2 = ahead(c, h, k, NST, c2, h2);
+                    issue_w(c2, h2, k2, slot);
+                }
+                if (k == 0) issue_refs(c, h);
+                __builtin_amdgcn_sched_barrier(0);
+                slot = next;
+            }
+            wait_vmcnt<2 * (KST - 1)>();
+            lds_barrier();
+            const bool isK = (c & 1) == 0;
+            if (mf.fused) pass_values<D, true, Ly::kRP>(acc, sRef, sRope, h, isK, mf);
+            else pass_values<D, false, Ly::kRP>(acc, sRef, sRope, h, isK, mf);
+            attend_pass(acc, c, h);
+            // the slices and the staged values are read: the next pass may refill them
+            lds_barrier();
+        }
+    }
+}
+
 // rkv_prepare_decoder: W_d bf16 -> fp16, each 8 latent values in the fragment order
 // 0 4 1 5 2 6 3 7 (the conversion form 1 applies in LDS, so both forms multiply the same
 // operands in the same order).
@@ -825,6 +1201,42 @@ static TileMapArgs tiles_grid(const Shape& s, int B, int m, unsigned* nblocks) {
     const long g1 = (chunks + a.ncg1 - 1) / a.ncg1, g2 = (chunks + a.ncg2 - 1) / a.ncg2;
     *nblocks = (unsigned)(a.T1 * g1 + a.R * g2);
     return a;
+}
+
+template <int NKS, int D, int BITS>
+static hipError_t restore_attend_impl(int G, const Shape& s, const CacheView& c, const int* idx, int m,
+                                      const void* wd16, const void* q, float qscale, float* part_o, float* part_ml,
+                                      hipStream_t st) {
+    // the tile map over units (K chunk + V chunk of 128 columns): a run of units costs two
+    // chunks per unit
+    Shape su = s;
+    su.W2 = s.dk;  // units as the map's chunks
+    unsigned nblocks = 0;
+    const TileMapArgs ta = tiles_grid(su, c.B, m, &nblocks);
+    typedef fa::L<D> Ly;
+    auto kern = restore_attend_kernel<NKS, D, BITS>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, Ly::bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(dt::kThreads), Ly::bytes, st, idx, m, ta,
+                       static_cast<const fp8_t*>(c.ref_vals), c.self_slot, c.ref_idx, c.codes, c.code_bytes,
+                       static_cast<const f16_t*>(c.scale), static_cast<const f16_t*>(c.zmin),
+                       static_cast<const f16_t*>(wd16), s.W2, s.dk, s.top_k, c.cap_ref, c.cap_tok, s.theta,
+                       static_cast<const bf16_t*>(q), G, qscale, part_o, part_ml, c.err);
+    return hipGetLastError();
+}
+
+template <int D, int BITS>
+static hipError_t restore_attend_dc(int G, const Shape& s, const CacheView& c, const int* idx, int m,
+                                    const void* wd16, const void* q, float qscale, float* part_o, float* part_ml,
+                                    hipStream_t st) {
+    switch (s.d_c / 32) {
+        case 4: return restore_attend_impl<4, D, BITS>(G, s, c, idx, m, wd16, q, qscale, part_o, part_ml, st);
+        case 8: return restore_attend_impl<8, D, BITS>(G, s, c, idx, m, wd16, q, qscale, part_o, part_ml, st);
+        case 12: return restore_attend_impl<12, D, BITS>(G, s, c, idx, m, wd16, q, qscale, part_o, part_ml, st);
+        case 16: return restore_attend_impl<16, D, BITS>(G, s, c, idx, m, wd16, q, qscale, part_o, part_ml, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int NKS, int D, int BITS, typename OutT>
@@ -894,6 +1306,22 @@ hipError_t launch_decode_tiles(const Shape& s, const CacheView& c, const int* id
     if (out_dtype == RKV_F32) return tiles_d<float>(s, c, idx, m, wd, wd16, out, st);
     return tiles_d<bf16_t>(s, c, idx, m, wd, wd16, out, st);
 }
+
+hipError_t launch_restore_attend(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd16,
+                                 const void* q, int Hq, float qscale, float* part_o, float* part_ml, hipStream_t st) {
+    if (m <= 0) return hipSuccess;
+    const int G = Hq / s.N;
+    if (s.D == 64) {
+        if (s.bits == 4) return restore_attend_dc<64, 4>(G, s, c, idx, m, wd16, q, qscale, part_o, part_ml, st);
+        if (s.bits == 16) return restore_attend_dc<64, 16>(G, s, c, idx, m, wd16, q, qscale, part_o, part_ml, st);
+        return restore_attend_dc<64, 2>(G, s, c, idx, m, wd16, q, qscale, part_o, part_ml, st);
+    }
+    if (s.bits == 4) return restore_attend_dc<128, 4>(G, s, c, idx, m, wd16, q, qscale, part_o, part_ml, st);
+    if (s.bits == 16) return restore_attend_dc<128, 16>(G, s, c, idx, m, wd16, q, qscale, part_o, part_ml, st);
+    return restore_attend_dc<128, 2>(G, s, c, idx, m, wd16, q, qscale, part_o, part_ml, st);
+}
+
+int restore_attend_tiles(int m) { return (m + dt::TT - 1) / dt::TT; }
 
 hipError_t launch_prepare_decoder(const Shape& s, const void* wd, void* wd16, hipStream_t st) {
     const size_t n8 = (size_t)s.W2 * s.d_c / 8;

@@ -41,7 +41,7 @@ struct EncodePlan {
     size_t off_scores; // scan scores [B][n][cap_ref] (small only)
     int cap_q;         // items per queue of the bf16 search's work plan
     size_t off_tile_nblk, off_items, off_ctr;  // work plan: blocks per tile, item queues, counters
-    size_t off_part_score, off_part_slot, off_rescan, off_xbar, off_dh, total;
+    size_t off_part_score, off_part_slot, off_rescan, off_rescan_part, off_xbar, off_dh, total;
 };
 
 EncodePlan plan_encode(const Shape& s, int B, int n, int cap_ref);
@@ -71,6 +71,15 @@ hipError_t launch_decode_tiles(const Shape& s, const CacheView& c, const int* id
                                const void* wd16, void* out, int out_dtype, hipStream_t st);
 // W_d (bf16, [2 d_k][d_c]) -> the fp16 form the token-tile restore reads by direct loads
 hipError_t launch_prepare_decoder(const Shape& s, const void* wd, void* wd16, hipStream_t st);
+
+// Restore fused with the attention (token-tile restore shapes): per (sequence, KV head,
+// token tile of restore_attend_tiles(m), query head in the group) the tile's
+// unnormalised output part_o [.. D], maximum and weight sum part_ml [.. 2], both strided
+// by kAttendMaxG query heads; wd16 = the prepared fp16 W_d.
+constexpr int kAttendMaxG = 8;
+int restore_attend_tiles(int m);
+hipError_t launch_restore_attend(const Shape& s, const CacheView& c, const int* idx, int m, const void* wd16,
+                                 const void* q, int Hq, float qscale, float* part_o, float* part_ml, hipStream_t st);
 
 // Attention over the restored selected tokens (bf16 formats): restore into the
 // workspace, then split-token softmax attention for Hq query heads.

@@ -46,6 +46,19 @@ constexpr int kThreads = 256;
 constexpr int kTop = 8;  // candidates kept per token
 constexpr int kTok = 128;  // tokens per search tile
 
+// select's rescan queue (int words of the workspace): [0] queued tokens, [1] spare,
+// [2, 2 + kRqPar) arrival counters of the parallel rescans, then two words per queued
+// token from kRqHead. The first kRqPar queued tokens are rescanned in kRqParts parts, one
+// workgroup each, whose partial top-8 lists (off_rescan_part) the last part merges.
+constexpr int kRqPar = 64;
+constexpr int kRqParts = 64;
+constexpr int kRqHead = 2 + kRqPar;
+// clears the queue head and the arrival counters (block (0, 0) of the first kernel of an
+// encode; at least kRqHead threads)
+__device__ inline void reset_rescan(int* rescan) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kRqHead) rescan[threadIdx.x] = 0;
+}
+
 template <typename T>
 struct SC {
     static constexpr int BM = std::is_same<T, float>::value ? 128 : 256;  // pool slots per block
@@ -118,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void search_kernel(
     const int* __restrict__ ref_count, int W2, int cap_ref, int blocks_per_chunk, int nsplit, int ntiles, int per,
     float* __restrict__ part_score, int* __restrict__ part_slot, int* __restrict__ rescan) {
     typedef SC<T> C;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) rescan[0] = 0;  // select's rescan queue
+    reset_rescan(rescan);
     extern __shared__ __align__(16) unsigned char smem_u8[];
     unsigned char* smem = smem_u8;
     T* lds = reinterpret_cast<T*>(smem);
@@ -425,7 +438,7 @@ __global__ __launch_bounds__(256) void search_plan_kernel(const int* __restrict_
                                                           const int* __restrict__ ref_pos,
                                                           const int* __restrict__ ref_count, int cap_ref, int ntiles,
                                                           int* __restrict__ tile_nblk, int* __restrict__ rescan) {
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) rescan[0] = 0;  // select's rescan queue
+    reset_rescan(rescan);
     const int lane = threadIdx.x & 63;
     const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int b = blockIdx.y;
@@ -507,7 +520,7 @@ __global__ __launch_bounds__(256) void search_scan_kernel(const bf16_t* __restri
                                                           const int* __restrict__ ref_count, int cap_ref,
                                                           float* __restrict__ scores, int* __restrict__ rescan) {
     constexpr int W2 = 1024 * NC;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) rescan[0] = 0;  // select's rescan queue
+    reset_rescan(rescan);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b = blockIdx.y;
     const int count = max(0, min(ref_count[b], cap_ref));
@@ -1119,9 +1132,9 @@ __device__ inline void write_mean(const RefT* __restrict__ pool, const int (&slo
 //    candidates the bounds cannot place (counted in stats[0]);
 //  * a full list's 8th score comes within the bound of the set's largest exact
 //    distance, so a slot the list dropped could belong to the set: the token goes to
-//    the rescan queue (rescan[0] entries of two words from rescan[2]: the token, and
-//    the mask of such lists | the number of lists << 8), and rescan_kernel writes its
-//    references and mean row (counted in stats[1]).
+//    the rescan queue (two words from rescan[kRqHead]: the token, and the mask of such
+//    lists | the number of lists << 8), and rescan_kernel writes its references and
+//    mean row (counted in stats[1]).
 template <typename KvT, typename RefT>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const KvT* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
@@ -1215,15 +1228,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         lo_out = fminf(lo_out, __shfl_xor(lo_out, o, 64));
     }
 
-    // A slot a full list dropped scores at least the list's 8th (rounded-down) score. If
-    // it could belong to the set, its exact score is at most hi_in, so its distance is at
-    // most dmax = hi_in + ||x||^2 and ||r||^2 <= 2 ||x||^2 + 2 dmax; its rounding bound is
-    // then at most 2^-16 (3 ||x||^2 + 2 dmax), taken twice over here. A list whose 8th
-    // score minus that amount stays above hi_in cannot hide a member of the set.
+    // A slot a full list dropped ranks after the list's 8th on the same rounded-down keys,
+    // so its approximate score is at least the 8th's stored score, and its exact score at
+    // least that minus its accumulation error, 2^-17 (||x||^2 + ||r||^2). If it could
+    // belong to the set its exact score is at most hi_in, so its distance is at most
+    // dmax = hi_in + ||x||^2 and ||r||^2 <= 2 ||x||^2 + 2 dmax. A list whose 8th score minus
+    // 2^-17 (3 ||x||^2 + 2 dmax) (rounded up to 1e-5, for the score's own rounding) stays
+    // above hi_in cannot hide a member of the set.
     bool hides = false;
     if (k_i > 0 && lane < ncand && (lane & (kTop - 1)) == kTop - 1 && id >= 0) {
         const float dmax = fmaxf(hi_in + xn, 0.f);
-        hides = s - 3.0517578125e-05f * (3.f * xn + 2.f * dmax) <= hi_in;  // 2^-15
+        hides = s - 1.0e-5f * (3.f * xn + 2.f * dmax) <= hi_in;
     }
     const unsigned long long hide_mask = __ballot(hides);
 
@@ -1232,11 +1247,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         // token's references and mean row
         if (lane == 0) {
             const int slot = atomicAdd(&rescan[0], 1);
-            rescan[2 + 2 * slot] = b * n + t;
+            rescan[kRqHead + 2 * slot] = b * n + t;
             uint32_t cm = 0;
 #pragma unroll
             for (int c = 0; c < 8; ++c) cm |= ((hide_mask >> (kTop * c + kTop - 1)) & 1ull) ? (1u << c) : 0u;
-            rescan[3 + 2 * slot] = (int)(cm | ((uint32_t)nch << 8));
+            rescan[kRqHead + 1 + 2 * slot] = (int)(cm | ((uint32_t)nch << 8));
             if (stats) atomicAdd(&stats[1], 1);
         }
         return;
@@ -1307,127 +1322,206 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     write_mean<KvT, RefT>(pool, slots, k_i, W2, xrow, lane);
 }
 
-// Exact search of the tokens select_kernel queued. One workgroup per queued token (grid-
-// stride over the queue): its four wavefronts compute exact squared distances, one lane
-// per reference row (lane_dist), over every visible slot of the chunks whose lists could
-// hide a member of the set and over the stored candidates of the other chunks; each
-// wavefront keeps the 8 smallest (distance, slot) keys, the four lists merge through
-// LDS, and wavefront 0 writes the k_i smallest as the token's references (ascending slot)
-// and its mean row. A chunk list that could hide a member holds 8 visible slots, so
-// k_i = top_k here.
+// wave-uniform ascending list best[0..7] of (distance, slot) keys: merge one key per lane
+__device__ inline void offer_keys(uint64_t (&best)[8], uint64_t mine) {
+    uint64_t kth = best[7];
+    // keys enter in ascending order, so at most 8 of them enter per call
+    for (;;) {
+        const uint64_t m = wave_min_u64(mine);
+        if (m >= kth) break;
+        uint64_t v = m;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint64_t lo = best[q] < v ? best[q] : v;
+            const uint64_t hi = best[q] < v ? v : best[q];
+            best[q] = lo;
+            v = hi;
+        }
+        if (mine == m) mine = ~0ull;
+        kth = best[7];
+    }
+}
+
+// exact (distance, slot) key of one reference row, or none
+template <typename KvT, typename RefT>
+__device__ inline uint64_t exact_key(bool ok, const KvT* x, const RefT* pool, int slot, int W2) {
+    if (!ok) return ~0ull;
+    const float d = lane_dist<KvT, RefT>(x, pool + (size_t)slot * W2, W2);
+    return ((uint64_t)__float_as_uint(d) << 32) | (uint32_t)slot;
+}
+
+// the four wavefronts' lists merged through LDS; the result in wavefront 0
+__device__ inline void merge_waves(uint64_t (&best)[8], uint64_t (*s_best)[8]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane < 8) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (q == lane) s_best[wave][q] = best[q];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) best[q] = ~0ull;
+        offer_keys(best, lane < 32 ? s_best[lane >> 3][lane & 7] : ~0ull);
+    }
+}
+
+// The token's references (the top_k smallest keys of `best`, in ascending slot order) and
+// mean row, by wavefront 0.
+template <typename KvT, typename RefT>
+__device__ inline void write_set(const uint64_t (&best)[8], int top_k, const RefT* pool, int W2, int* out_idx,
+                                 KvT* xrow) {
+    const int lane = threadIdx.x & 63;
+    int sl8[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) sl8[q] = (q < top_k && best[q] != ~0ull) ? (int)(uint32_t)best[q] : INT_MAX;
+    sort8_i32(sl8);
+    int slots[8];
+    int kk = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        slots[q] = sl8[q] == INT_MAX ? -1 : sl8[q];
+        kk += slots[q] >= 0 ? 1 : 0;
+    }
+    if (lane < top_k) {
+        int v = -1;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (q == lane) v = slots[q];
+        out_idx[lane] = v;
+    }
+    write_mean<KvT, RefT>(pool, slots, kk, W2, xrow, lane);
+}
+
+// Exact search of the tokens select_kernel queued: exact squared distances (one lane per
+// reference row, lane_dist) over every visible slot of the chunks whose lists could hide
+// a member of the set and over the stored candidates of the other chunks; the top_k
+// smallest (distance, slot) keys are the token's references (ascending slot) and give its
+// mean row. A chunk list that could hide a member holds 8 visible slots, so k_i = top_k.
+//   queued tokens 0 .. kRqPar - 1: kRqParts parts each (work item = token x part, spread
+//     over the grid); a part scans its share of the slots and writes its best 8 keys to
+//     part_keys; the part that arrives last (an atomic counter per token, after a device
+//     fence) merges the kRqParts lists and writes the result;
+//   later queued tokens: one workgroup each scans all of the token's slots.
 template <typename KvT, typename RefT>
 __global__ __launch_bounds__(256) void rescan_kernel(
     const KvT* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
     const RefT* __restrict__ ref_vals, const int* __restrict__ ref_pos, const int* __restrict__ ref_count,
     const int* __restrict__ part_slot, int nsplit, int chunk_len, int W2, int cap_ref, int cap_tok, int top_k,
-    int* __restrict__ ref_idx, KvT* __restrict__ xbar, const int* __restrict__ rescan) {
+    int* __restrict__ ref_idx, KvT* __restrict__ xbar, int* __restrict__ rescan, uint64_t* __restrict__ part_keys) {
     __shared__ uint64_t s_best[4][8];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nq = rescan[0];
-    for (int e = blockIdx.x; e < nq; e += gridDim.x) {
-        const int code = rescan[2 + 2 * e];
-        const uint32_t info = (uint32_t)rescan[3 + 2 * e];
-        const int b = code / n, t = code - b * n;
-        const int row = rows[(size_t)b * n + t];
-        const int p = pos[(size_t)b * n + t];
-        const KvT* x = kv + ((size_t)b * kv_len + row) * W2;  // select queued only tokens with valid rows
-        const RefT* pool = ref_vals + (size_t)b * cap_ref * W2;
-        const int* rp = ref_pos + (size_t)b * cap_ref;
-        const uint32_t hmask = info & 0xFFu;
-        const int nch = (int)(info >> 8);
-        const int count = max(0, min(ref_count[b], cap_ref));
-        const int cl = chunk_len > 0 ? chunk_len : (count + nch - 1) / max(nch, 1);
-        uint64_t best[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) best[q] = ~0ull;
-        uint64_t kth = ~0ull;
-        auto offer = [&](bool ok, int slot) {
-            uint64_t mine = ~0ull;
-            if (ok) {
-                const float d = lane_dist<KvT, RefT>(x, pool + (size_t)slot * W2, W2);
-                mine = ((uint64_t)__float_as_uint(d) << 32) | (uint32_t)slot;
-            }
-            // keys enter in ascending order, so at most 8 of them enter per call
-            for (;;) {
-                const uint64_t m = wave_min_u64(mine);
-                if (m >= kth) break;
-                uint64_t v = m;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const uint64_t lo = best[q] < v ? best[q] : v;
-                    const uint64_t hi = best[q] < v ? v : best[q];
-                    best[q] = lo;
-                    v = hi;
-                }
-                if (mine == m) mine = ~0ull;
-                kth = best[7];
-            }
-        };
+    const int npar = min(nq, kRqPar);
+
+    // the scan of queued token e: its chunks' slots as one list of S slots (hiding chunks in
+    // order), parts [part S / P, (part + 1) S / P); part 0 also offers the stored candidates
+    struct Tok {
+        int b, t, p, nch, cl, count;
+        uint32_t hmask;
+        const KvT* x;
+        const RefT* pool;
+        const int* rp;
+    };
+    auto token = [&](int e) {
+        Tok k;
+        const int code = rescan[kRqHead + 2 * e];
+        const uint32_t info = (uint32_t)rescan[kRqHead + 1 + 2 * e];
+        k.b = code / n;
+        k.t = code - k.b * n;
+        const int row = rows[(size_t)k.b * n + k.t];
+        k.p = pos[(size_t)k.b * n + k.t];
+        k.x = kv + ((size_t)k.b * kv_len + row) * W2;  // select queued only tokens with valid rows
+        k.pool = ref_vals + (size_t)k.b * cap_ref * W2;
+        k.rp = ref_pos + (size_t)k.b * cap_ref;
+        k.hmask = info & 0xFFu;
+        k.nch = (int)(info >> 8);
+        k.count = max(0, min(ref_count[k.b], cap_ref));
+        k.cl = chunk_len > 0 ? chunk_len : (k.count + k.nch - 1) / max(k.nch, 1);
+        return k;
+    };
+    auto scan_len = [&](const Tok& k) {
+        int S = 0;
+        for (uint32_t mq = k.hmask; mq; mq &= mq - 1) {
+            const int c = __ffs(mq) - 1;
+            S += max(0, min(k.count, (c + 1) * k.cl) - c * k.cl);
+        }
+        return S;
+    };
+    // slot of position i of the scan list
+    auto scan_slot = [&](const Tok& k, int i) {
+        for (uint32_t mq = k.hmask; mq; mq &= mq - 1) {
+            const int c = __ffs(mq) - 1;
+            const int len = max(0, min(k.count, (c + 1) * k.cl) - c * k.cl);
+            if (i < len) return c * k.cl + i;
+            i -= len;
+        }
+        return -1;
+    };
+    auto offer_stored = [&](const Tok& k, uint64_t (&best)[8]) {
         // stored candidates of the lists that cannot hide a member (wavefront 0, a lane each)
         if (wave == 0) {
             const int c = lane / kTop;
-            const bool ok = lane < nch * kTop && !((hmask >> c) & 1u);
-            const int id = ok ? part_slot[((size_t)b * n + t) * nsplit * kTop + lane] : -1;
-            offer(id >= 0, id);
+            const bool ok = lane < k.nch * kTop && !((k.hmask >> c) & 1u);
+            const int id = ok ? part_slot[((size_t)k.b * n + k.t) * nsplit * kTop + lane] : -1;
+            offer_keys(best, exact_key<KvT, RefT>(id >= 0, k.x, k.pool, id, W2));
         }
-        // every visible slot of the lists that could hide one
-        for (uint32_t mq = hmask; mq; mq &= mq - 1) {
-            const int c = __ffs(mq) - 1;
-            const int lo = c * cl, hi = min(count, lo + cl);
-            for (int s0 = lo + 64 * wave; s0 < hi; s0 += 256) {
-                const int sl = s0 + lane;
-                offer(sl < hi && rp[sl] < p, sl);
-            }
+    };
+    auto scan = [&](const Tok& k, int lo, int hi, uint64_t (&best)[8]) {
+        for (int i0 = lo + 64 * wave; i0 < hi; i0 += 256) {
+            const int i = i0 + lane;
+            const int sl = i < hi ? scan_slot(k, i) : -1;
+            offer_keys(best, exact_key<KvT, RefT>(sl >= 0 && k.rp[sl] < k.p, k.x, k.pool, sl, W2));
         }
-        if (lane < 8) {
+    };
+
+    // parallel rescans
+    for (int w = blockIdx.x; w < npar * kRqParts; w += gridDim.x) {
+        const int e = w / kRqParts, part = w - e * kRqParts;
+        const Tok k = token(e);
+        const int S = scan_len(k);
+        uint64_t best[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) best[q] = ~0ull;
+        if (part == 0) offer_stored(k, best);
+        scan(k, (int)((long long)S * part / kRqParts), (int)((long long)S * (part + 1) / kRqParts), best);
+        merge_waves(best, s_best);
+        uint64_t* mine = part_keys + ((size_t)e * kRqParts + part) * 8;
+        if (wave == 0 && lane < 8) {
 #pragma unroll
             for (int q = 0; q < 8; ++q)
-                if (q == lane) s_best[wave][q] = best[q];
+                if (q == lane) mine[q] = best[q];
+        }
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) s_last = atomicAdd(&rescan[2 + e], 1) == kRqParts - 1;
+        __syncthreads();
+        if (s_last) {
+            __threadfence();
+            if (wave == 0) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) best[q] = ~0ull;
+                const uint64_t* all = part_keys + (size_t)e * kRqParts * 8;
+                for (int j = 0; j < kRqParts * 8; j += 64) offer_keys(best, all[j + lane]);
+                write_set<KvT, RefT>(best, top_k, k.pool, W2, ref_idx + ((size_t)k.b * cap_tok + k.p) * top_k,
+                                     xbar + ((size_t)k.b * n + k.t) * W2);
+            }
         }
         __syncthreads();
-        if (wave == 0) {
-            best[0] = ~0ull;
+    }
+    // later queued tokens: one workgroup each
+    for (int e = npar + blockIdx.x; e < nq; e += gridDim.x) {
+        const Tok k = token(e);
+        uint64_t best[8];
 #pragma unroll
-            for (int q = 1; q < 8; ++q) best[q] = ~0ull;
-            kth = ~0ull;
-            // the four lists (32 keys, one per lane) merge as one offer of precomputed keys
-            uint64_t mine = lane < 32 ? s_best[lane >> 3][lane & 7] : ~0ull;
-            for (;;) {
-                const uint64_t m = wave_min_u64(mine);
-                if (m >= kth) break;
-                uint64_t v = m;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const uint64_t lo = best[q] < v ? best[q] : v;
-                    const uint64_t hi = best[q] < v ? v : best[q];
-                    best[q] = lo;
-                    v = hi;
-                }
-                if (mine == m) mine = ~0ull;
-                kth = best[7];
-            }
-            const int k_i = top_k;
-            int sl8[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) sl8[q] = (q < k_i && best[q] != ~0ull) ? (int)(uint32_t)best[q] : INT_MAX;
-            sort8_i32(sl8);
-            int slots[8];
-            int kk = 0;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                slots[q] = sl8[q] == INT_MAX ? -1 : sl8[q];
-                kk += slots[q] >= 0 ? 1 : 0;
-            }
-            int* out_idx = ref_idx + ((size_t)b * cap_tok + p) * top_k;
-            if (lane < top_k) {
-                int v = -1;
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    if (q == lane) v = slots[q];
-                out_idx[lane] = v;
-            }
-            write_mean<KvT, RefT>(pool, slots, kk, W2, xbar + ((size_t)b * n + t) * W2, lane);
-        }
+        for (int q = 0; q < 8; ++q) best[q] = ~0ull;
+        offer_stored(k, best);
+        scan(k, 0, scan_len(k), best);
+        merge_waves(best, s_best);
+        if (wave == 0)
+            write_set<KvT, RefT>(best, top_k, k.pool, W2, ref_idx + ((size_t)k.b * cap_tok + k.p) * top_k,
+                                 xbar + ((size_t)k.b * n + k.t) * W2);
         __syncthreads();
     }
 }
@@ -1464,8 +1558,10 @@ EncodePlan plan_encode(const Shape& s, int B, int n, int cap_ref) {
     off = up(off + tok * nsplit * kTop * sizeof(float));
     p.off_part_slot = off;
     off = up(off + tok * nsplit * kTop * sizeof(int));
-    p.off_rescan = off;  // select's rescan queue: count, spare word, then 2 words per token
-    off = up(off + (2 + 2 * tok) * sizeof(int));
+    p.off_rescan = off;  // select's rescan queue (kRqHead words, then 2 per token)
+    off = up(off + (kRqHead + 2 * tok) * sizeof(int));
+    p.off_rescan_part = off;  // partial lists of the parallel rescans
+    off = up(off + (size_t)kRqPar * kRqParts * 8 * sizeof(uint64_t));
     p.off_xbar = off;
     off = up(off + tok * s.W2 * (s.f32 ? 4 : 2));
     p.off_dh = off;
@@ -1582,10 +1678,11 @@ static hipError_t select_impl(const Shape& s, const CacheView& c, const EncodePl
     if (e != hipSuccess) return e;
     // queued tokens (usually none): a grid of workgroups walks the queue
     const int chunk_len = p.small ? 0 : p.chunk_slots * (s.f32 ? SC<float>::BM : s2::BM);
-    const int grid_r = (int)std::min<long long>(64, (long long)c.B * n);
+    const int grid_r = (int)std::min<long long>(256, (long long)c.B * n * kRqParts);
     hipLaunchKernelGGL((rescan_kernel<KvT, RefT>), dim3(grid_r), dim3(256), 0, st, static_cast<const KvT*>(kv),
                        kv_len, rows, pos, n, static_cast<const RefT*>(c.ref_vals), c.ref_pos, c.ref_count, part_slot,
-                       p.nsplit, chunk_len, s.W2, c.cap_ref, c.cap_tok, s.top_k, c.ref_idx, xbar, rescan);
+                       p.nsplit, chunk_len, s.W2, c.cap_ref, c.cap_tok, s.top_k, c.ref_idx, xbar, rescan,
+                       reinterpret_cast<uint64_t*>(w + p.off_rescan_part));
     return hipGetLastError();
 }
 

@@ -191,8 +191,16 @@ def test_reference_schedule_statuses(lib):
 def test_decode_attend_host_checks(lib):
     cfg = B.CodecConfig.from_workload(workload(2))
     w = B.rkv_decode_attend_workspace_bytes(cfg, 1, 39321, 32)
-    # bf16 rows of the restored tokens plus the per-chunk partials
-    assert w >= 39321 * cfg.two_dk * 2
+    # the fused restore + attention keeps the restored rows on chip: the workspace holds
+    # the per-tile partial outputs (308 tiles of 128 tokens x 8 KV heads x 8 query-head
+    # slots x (D + 2) floats) and room for the fp16 decoder (2 * 2d_k * d_c bytes)
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    tiles = (39321 + 127) // 128
+    assert w == up(tiles * 8 * 8 * 128 * 4) + up(tiles * 8 * 8 * 2 * 4) + up(2 * cfg.two_dk * cfg.d_c)
+    assert w < 39321 * cfg.two_dk * 2 // 10
+    # k = 8 is outside the token-tile restore: the rows go through the workspace
+    cfg8 = B.CodecConfig.from_workload(workload(2, top_k=8))
+    assert B.rkv_decode_attend_workspace_bytes(cfg8, 1, 39321, 32) >= 39321 * cfg.two_dk * 2
     assert B.rkv_decode_attend_workspace_bytes(cfg, 1, 0, 32) == 0
     assert B.rkv_decode_attend_workspace_bytes(cfg, 1, 100, 30) == 0  # not a multiple of 8 KV heads
     assert B.rkv_decode_attend_workspace_bytes(cfg, 1, 100, 72) == 0  # 9 query heads per KV head

@@ -69,6 +69,11 @@ CASES = {
     "batch3-int4-mha": (5, dict(T=700, batch=3), 8, [200]),
     "batch2-fp16-latent-gqa8": (5, dict(T=520, batch=2, bits=16), 64, [300]),
     "d64-bf16-gqa2": (2, dict(T=900, n_kv_heads=16, head_dim=64), 32, [7, 270]),
+    # no prepared decoder: the call converts W_d into its workspace first
+    "llama-shape-unprepared-gqa2": (2, dict(T=700), 16, [129]),
+    # k = 8 is outside the token-tile restore: restore into the workspace, then the
+    # chunk kernel over the rows
+    "llama-shape-k8-unfused-gqa4": (2, dict(T=900, top_k=8), 32, [300]),
 }
 
 
@@ -84,7 +89,8 @@ def test_attend_parity(case):
     gpu.prefill(gpu.to_dev(np.stack(kvs)), T)
     torch.cuda.synchronize()
     assert gpu.cache.error_bits() == 0
-    gpu.W.prepare_decoder(gpu.cfg)
+    if "unprepared" not in case:
+        gpu.W.prepare_decoder(gpu.cfg)
     codec = OracleCodec.from_workload(wl, W)
     orcs = [codec.prefill(kvs[b], wl.stride, cap_ref=gpu.cap_ref) for b in range(wl.batch)]
     gpcs = [mirror_cache(codec, gpu, b) for b in range(wl.batch)]
@@ -121,9 +127,10 @@ def test_attend_empty_selection_gives_zeros():
 def test_attend_full_decode_read_set():
     """The decode-side shape at full size: a 131072-token history and its 39322-token
     read set, 32 query heads over 8 KV heads. The attention is checked against the
-    softmax average of the restored rows the restore writes in bf16 (rkv_decode_selected,
-    the same rows the call holds in its workspace; the restore itself is checked
-    against the oracle elsewhere), on every head."""
+    softmax average of the restored rows the restore writes in bf16 (rkv_decode_selected;
+    the call stages the same bf16 values on chip; the restore itself is checked against
+    the oracle elsewhere), on every head: the only differences are the fp32 summation
+    order and the fp16 weights of the P V product."""
     wl = workload(3)
     T = wl.T
     W = wl.make_weights()
@@ -142,5 +149,8 @@ def test_attend_full_decode_read_set():
     want = sparse_attention(q16.float().numpy()[0].astype(np.float64), rows[:, 0], rows[:, 1], 1.0 / np.sqrt(128))
     ma, rr = _errors(out.cpu().numpy()[0], want)
     print(f"[parity] attend full size m={sel.shape[1]}: max_abs={ma:.3g} rms_rel={rr:.3g}", flush=True)
-    # same bf16 rows on both sides: only fp32 accumulation order and expf remain
-    assert ma <= 1e-4 and rr <= 1e-5, (ma, rr)
+    # same bf16 rows on both sides; the kernel feeds its softmax weights to the P V product
+    # in fp16 (relative error <= 2^-11 each) and normalises by their fp32 sum, so the output,
+    # a convex combination of the values, moves by at most 2^-11 max|V| (plus fp32 sums)
+    vmax = float(np.max(np.abs(rows[:, 1])))
+    assert ma <= 2.0 ** -11 * vmax + 1e-6 and rr <= 2.0 ** -11, (ma, rr, vmax)
