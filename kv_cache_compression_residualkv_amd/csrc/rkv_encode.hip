@@ -195,7 +195,10 @@ namespace g1r {
 constexpr int kThreads = 512;
 constexpr int BM = 256, BN = 256, NST = 2;
 constexpr int kHid = BN / 2;  // hidden columns per tile
-constexpr int kHP = kHid + 4;  // fp32 pitch of the dH staging tile
+// fp32 pitch of the dH staging tile: the epilogue's 4-byte stores (rows tl, tl + 2 in one
+// half wavefront) land 24 banks apart and its 16-byte reloads (rows t, t + 1 in one pass)
+// an odd number of 16-byte slots apart, so neither has bank conflicts
+constexpr int kHP = kHid + 12;
 constexpr size_t kRing = (size_t)NST * (BM + BN) * kStageK * 2;
 constexpr size_t kEpi = (size_t)(BM / 2) * kHP * sizeof(float);
 constexpr size_t bytes = kRing > kEpi ? kRing : kEpi;
