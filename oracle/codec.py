@@ -16,7 +16,9 @@ Readings where the page is silent (each is listed in the design notes):
   in ascending slot order;
 * the reference mean is accumulated in fp32, in ascending slot order, then divided
   by k_i (IEEE fp32 division); the encoder sees it rounded to the KV dtype (bf16
-  for bf16 KV), the decoder adds the fp32 mean;
+  for bf16 KV), the decoder adds the fp32 mean; in the mean-projection form (an
+  option, not on the page) the encoder instead takes f_c(mean)'s first-layer
+  pre-activations as the average of the references' own, with no rounding of the mean;
 * Swish is SiLU (beta = 1), no biases anywhere (section 2.3, section 2.5);
 * a group is 32 consecutive latent coordinates; the two stored values are the step
   Delta and the group minimum; round() is round-half-to-even; codes are clamped to
@@ -97,6 +99,44 @@ def swiglu_compressor(x: np.ndarray, Wc1: np.ndarray, Wc2: np.ndarray, Wc3: np.n
     b = x @ np.asarray(Wc2, dtype=np.float64)
     swish = a / (1.0 + np.exp(-a))
     return (swish * b) @ np.asarray(Wc3, dtype=np.float64)
+
+
+def reference_projections(refs: np.ndarray, Wc1: np.ndarray, Wc2: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """First-layer pre-activations of each reference, r_j W_c1 and r_j W_c2, in fp64.
+
+    The mean-projection form of the encoder (not on the pages; an algebraic identity of
+    the compressor of section 2.3): the first layer of f_c is linear, so the mean's
+    pre-activations are the mean of the references' pre-activations,
+    mean_i W = (1/k_i) sum_j r_j W, and r_j W can be computed once per reference when it
+    enters the pool. refs: [k, 2d_k] stored reference values. Returns two [k, d_ff] arrays.
+    """
+    refs = np.asarray(refs, dtype=np.float64)
+    return refs @ np.asarray(Wc1, dtype=np.float64), refs @ np.asarray(Wc2, dtype=np.float64)
+
+
+def averaged_preactivations(p1: np.ndarray, p2: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """(1/k_i) sum_j of the chosen references' projections (ascending slot order), fp64.
+
+    An empty set gives zeros (the zero mean of an empty pool)."""
+    p1 = np.asarray(p1, dtype=np.float64)
+    p2 = np.asarray(p2, dtype=np.float64)
+    k_i = p1.shape[0]
+    if k_i == 0:
+        return np.zeros(p1.shape[1]), np.zeros(p2.shape[1])
+    a1 = np.zeros(p1.shape[1])
+    a2 = np.zeros(p2.shape[1])
+    for j in range(k_i):
+        a1 = a1 + p1[j]
+        a2 = a2 + p2[j]
+    return a1 / k_i, a2 / k_i
+
+
+def swiglu_from_preactivations(a1: np.ndarray, a2: np.ndarray, Wc3: np.ndarray) -> np.ndarray:
+    """(Swish(a1) * a2) W_c3 in fp64: the compressor of section 2.3 after its first layer."""
+    a1 = np.asarray(a1, dtype=np.float64)
+    a2 = np.asarray(a2, dtype=np.float64)
+    swish = a1 / (1.0 + np.exp(-a1))
+    return (swish * a2) @ np.asarray(Wc3, dtype=np.float64)
 
 
 def linear_decoder(z: np.ndarray, Wd: np.ndarray) -> np.ndarray:
@@ -231,10 +271,16 @@ class OracleCodec:
     'Wd': [d_c, 2dk]} (float arrays holding the stored weight values).
     mode: 'f32' (fp32 KV, fp32 references, fp32 step/min) or 'bf16' (bf16 KV, FP8
     references, fp16 step/min).
+    mean_projection: the encoder's f_c(mean) takes its first-layer pre-activations as the
+    average of the chosen references' own pre-activations (reference_projections), so
+    the mean is never rounded to the KV dtype; otherwise (default) the encoder sees the
+    fp32 mean rounded to the KV dtype.
     """
 
     def __init__(self, n_kv_heads: int, head_dim: int, d_ff: int, d_c: int, top_k: int,
-                 bits: int, group: int, mode: str, rope_theta: float, weights: Dict[str, np.ndarray]):
+                 bits: int, group: int, mode: str, rope_theta: float, weights: Dict[str, np.ndarray],
+                 mean_projection: bool = False):
+        self.mean_projection = bool(mean_projection)
         self.N, self.D = n_kv_heads, head_dim
         self.dk = n_kv_heads * head_dim
         self.two_dk = 2 * self.dk
@@ -244,9 +290,9 @@ class OracleCodec:
         self.W = {k: np.asarray(v, dtype=np.float64) for k, v in weights.items()}
 
     @classmethod
-    def from_workload(cls, cfg, weights) -> "OracleCodec":
+    def from_workload(cls, cfg, weights, mean_projection: bool = False) -> "OracleCodec":
         return cls(cfg.n_kv_heads, cfg.head_dim, cfg.d_ff, cfg.d_c, cfg.top_k, cfg.bits,
-                   cfg.group, cfg.mode, cfg.rope_theta, weights)
+                   cfg.group, cfg.mode, cfg.rope_theta, weights, mean_projection=mean_projection)
 
     def new_cache(self, cap_ref: int, cap_tok: int) -> OracleCache:
         return OracleCache(self.two_dk, self.d_c, self.top_k, self.group, self.bits,
@@ -287,7 +333,9 @@ class OracleCodec:
         kv = np.asarray(kv, dtype=np.float64).reshape(-1, self.two_dk)
         pos = list(int(p) for p in pos)
         n = len(pos)
+        W = self.W
         xbar = np.zeros((n, self.two_dk))
+        a_mean = (np.zeros((n, self.d_ff)), np.zeros((n, self.d_ff)))
         for t, p in enumerate(pos):
             if ref_override is not None and p in ref_override:
                 slots = np.sort(np.asarray(ref_override[p], dtype=np.int64))
@@ -300,12 +348,18 @@ class OracleCodec:
             cache.ref_idx[p, : slots.size] = slots
             cache.ref_dist[p] = np.nan
             cache.ref_dist[p, : slots.size] = dist
-            mean32 = reference_mean32(cache.ref_val[slots]) if slots.size else np.zeros(self.two_dk, np.float32)
-            xbar[t] = self.encoder_input(mean32)
-        W = self.W
+            if self.mean_projection:
+                p1, p2 = reference_projections(cache.ref_val[slots], W["Wc1"], W["Wc2"])
+                a_mean[0][t], a_mean[1][t] = averaged_preactivations(p1, p2)
+            else:
+                mean32 = reference_mean32(cache.ref_val[slots]) if slots.size else np.zeros(self.two_dk, np.float32)
+                xbar[t] = self.encoder_input(mean32)
         # average-then-encode: z = f_c(kv_i) - f_c(mean_i)  (section 2.3, boxed equation)
         f_kv = swiglu_compressor(kv, W["Wc1"], W["Wc2"], W["Wc3"])
-        f_mean = swiglu_compressor(xbar, W["Wc1"], W["Wc2"], W["Wc3"])
+        if self.mean_projection:
+            f_mean = swiglu_from_preactivations(a_mean[0], a_mean[1], W["Wc3"])
+        else:
+            f_mean = swiglu_compressor(xbar, W["Wc1"], W["Wc2"], W["Wc3"])
         z = f_kv - f_mean
         store = "f16" if self.mode == "bf16" else "f32"
         q, step, zmin = group_quantize(z, self.bits, self.group, store)

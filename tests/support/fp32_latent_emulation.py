@@ -33,19 +33,48 @@ def hidden_f32(x: np.ndarray, W) -> np.ndarray:
     return (a / (np.float32(1.0) + np.exp(-a))) * b
 
 
-def emulate(wl, T: int, hidden_round=None):
+def projected_mean_hidden_f32(cache, enc, W) -> np.ndarray:
+    """The mean's hidden values in the mean-projection form, in fp32: each reference's
+    pre-activations r W_c1, r W_c2 (sgemm), summed over the token's references in
+    ascending slot order, divided by k, then SiLU(a1) * a2."""
+    W1 = np.asarray(W["Wc1"], dtype=np.float32)
+    W2 = np.asarray(W["Wc2"], dtype=np.float32)
+    out = np.zeros((len(enc), W1.shape[1]), dtype=np.float32)
+    for t, p in enumerate(enc):
+        sl = cache.ref_idx[p][cache.ref_idx[p] >= 0]
+        if sl.size == 0:
+            continue
+        r = cache.ref_val[sl].astype(np.float32)
+        p1, p2 = r @ W1, r @ W2
+        a1 = np.zeros(W1.shape[1], dtype=np.float32)
+        a2 = np.zeros(W1.shape[1], dtype=np.float32)
+        for j in range(sl.size):
+            a1 = a1 + p1[j]
+            a2 = a2 + p2[j]
+        a1 = a1 / np.float32(sl.size)
+        a2 = a2 / np.float32(sl.size)
+        out[t] = (a1 / (np.float32(1.0) + np.exp(-a1))) * a2
+    return out
+
+
+def emulate(wl, T: int, hidden_round=None, mean_projection: bool = False):
     """Oracle cache of the workload at T tokens, and the fp32 evaluation of z for its
-    encoded tokens. hidden_round (optional) rounds the hidden difference before W_c3.
+    encoded tokens. hidden_round (optional) rounds the hidden difference before W_c3;
+    mean_projection evaluates both with the encoder's mean-projection form.
 
     Returns (positions, z64 [n, d_c], z32 [n, d_c], f_scale [n])."""
     W = wl.make_weights()
     kv = wl.make_kv(T=T).astype(np.float64)
-    codec = OracleCodec.from_workload(wl.replace(T=T), W)
+    codec = OracleCodec.from_workload(wl.replace(T=T), W, mean_projection=mean_projection)
     cache = codec.prefill(kv, wl.stride)
     enc = wl.enc_positions(T)
-    xbar = np.stack([codec.encoder_input(reference_mean32(cache.ref_val[cache.ref_idx[p][cache.ref_idx[p] >= 0]]))
-                     for p in enc])
-    dh = hidden_f32(kv[enc], W) - hidden_f32(xbar, W)
+    if mean_projection:
+        h_mean = projected_mean_hidden_f32(cache, enc, W)
+    else:
+        xbar = np.stack([codec.encoder_input(reference_mean32(cache.ref_val[cache.ref_idx[p][cache.ref_idx[p] >= 0]]))
+                         for p in enc])
+        h_mean = hidden_f32(xbar, W)
+    dh = hidden_f32(kv[enc], W) - h_mean
     if hidden_round is not None:
         dh = hidden_round(dh.astype(np.float64)).astype(np.float32)
     z32 = (dh @ np.asarray(W["Wc3"], dtype=np.float32)).astype(np.float64)

@@ -60,3 +60,21 @@ def test_stored_step_and_minimum_bars_hold_for_fp32_pipeline():
         print(wl.name, st)
         assert st["code_exact_frac"] >= 0.9999 and st["code_max_diff"] <= 1, st
         assert st["step_max_bar_ratio"] <= 1.0 and st["zmin_max_bar_ratio"] <= 1.0, st
+
+
+def test_mean_projection_form_meets_the_same_bars():
+    # the encoder's mean-projection form (the mean's pre-activations averaged from the
+    # references' own, no rounding of the mean): an fp32 evaluation of it stays within
+    # the same derived bars, for the fp16 latent and for the quantized records
+    wl = workload(2, bits=16)
+    _, z64, z32, fs = emulate(wl, 500, mean_projection=True)
+    st = summarize(z64, z32, fs, C_BAR)
+    print(st)
+    assert st["max_pre_round_err_over_u_scale"] <= C_BAR / 2, st
+    assert st["within_bar_frac"] == 1.0, st
+    wl = workload(2)
+    _, z64, z32, fs = emulate(wl, 500, mean_projection=True)
+    st = quantized_agreement(z64, z32, fs, wl.bits, "f16", C_BAR)
+    print(st)
+    assert st["code_exact_frac"] >= 0.9999 and st["code_max_diff"] <= 1, st
+    assert st["step_max_bar_ratio"] <= 1.0 and st["zmin_max_bar_ratio"] <= 1.0, st
