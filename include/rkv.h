@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 3
+#define RKV_ABI_VERSION 4
 
 typedef enum {
     RKV_OK = 0,
@@ -97,9 +97,20 @@ typedef struct {
     int32_t ref_dtype;    /* rkv_dtype */
     int32_t scale_dtype;  /* rkv_dtype */
     int32_t weight_dtype; /* rkv_dtype */
-    int32_t reserved;
+    int32_t flags;        /* RKV_FLAG_* (0: the default forms)             */
     double rope_theta;  /* RoPE base theta                               */
 } rkv_config;
+
+/* rkv_config.flags.
+ * RKV_FLAG_MEAN_PROJECTION: the encoder's f_c(mean) takes its first-layer
+ *   pre-activations as the average of the chosen references' own. The first layer of f_c
+ *   is linear (section 2.3, compressor equation), so mean W = (1/k_i) sum_j r_j W: each
+ *   reference is multiplied by [W_c1 | W_c2] once (rkv_cache.ref_proj) instead of every
+ *   token's mean, which removes the mean rows from the SwiGLU GEMM. The mean is then never
+ *   rounded to kv_dtype (the default form rounds it), so codes can differ from the default
+ *   form's within the code-flip allowance. "bf16" formats only (RKV_ERR_UNSUPPORTED
+ *   otherwise); the restore is unchanged. Not on the pages: an identity of the method. */
+#define RKV_FLAG_MEAN_PROJECTION 1
 
 /* Codec weights of one layer, nn.Linear layout (see above), weight_dtype.
  * w_d_f16 is optional (NULL, or a buffer filled by rkv_prepare_decoder from this w_d):
@@ -137,6 +148,15 @@ typedef struct {
      *       chunk's kept candidates could hide a nearer reference (near-equidistant
      *       references). */
     int32_t* stats;
+    /* RKV_FLAG_MEAN_PROJECTION only (NULL otherwise):
+     *   ref_proj   [B, cap_ref, d_ff, 2] fp32, 16-byte aligned: per pool slot and hidden
+     *              column j, (r W_c1)_j and (r W_c2)_j of the stored reference r;
+     *   proj_count [B] int32: slots whose projection is current. The caller zeroes it
+     *              whenever it resets ref_count; rkv_encode projects slots
+     *              [proj_count, ref_count) and then sets proj_count = ref_count
+     *              (a proj_count above ref_count re-projects the whole pool). */
+    float* ref_proj;
+    int32_t* proj_count;
 } rkv_cache;
 
 #define RKV_STATS_WORDS 2
@@ -193,7 +213,10 @@ rkv_status rkv_append_ref(const rkv_config* cfg, rkv_cache* cache, const void* k
  * For each token: the k_i = min(top_k, #{slots with ref_pos < pos}) references with
  * the smallest squared L2 distance to kv (ties: lower slot) over the stored
  * reference values; their fp32 mean (ascending-slot sum, one IEEE division), rounded
- * to kv_dtype for the encoder; z = f_c(kv) - f_c(mean) with
+ * to kv_dtype for the encoder (with RKV_FLAG_MEAN_PROJECTION: f_c(mean)'s
+ * pre-activations are the fp32 ascending-slot sum of the references' rows of
+ * ref_proj, divided by k_i, after the pool's new slots are projected; ref_proj and
+ * proj_count must then be set, RKV_ERR_INVALID_ARG otherwise); z = f_c(kv) - f_c(mean) with
  * f_c(x) = (SiLU(x W_c1) * x W_c2) W_c3; then per group of 32 coordinates:
  * Delta = (max - min)/(2^b - 1), stored Delta and min in scale_dtype,
  * q = clamp(rint((z - min)/Delta), 0, 2^b - 1) (q = 0 when the stored Delta is 0);

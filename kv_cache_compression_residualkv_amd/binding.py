@@ -36,7 +36,8 @@ STATUS = {
 RKV_ENCODE_PHASES = 4
 RKV_STATS_WORDS = 2
 RKV_NOALLOC_SCRATCH_BYTES = 16 << 20
-ABI_VERSION = 3
+ABI_VERSION = 4
+RKV_FLAG_MEAN_PROJECTION = 1
 DEVERR_EMPTY_POOL, DEVERR_POS_RANGE, DEVERR_REF_CAPACITY, DEVERR_IDX_RANGE, DEVERR_ROW_RANGE = 1, 2, 4, 8, 16
 
 EXPORTED = (
@@ -77,7 +78,7 @@ class _Config(ctypes.Structure):
         ("ref_dtype", ctypes.c_int32),
         ("scale_dtype", ctypes.c_int32),
         ("weight_dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
     ]
 
@@ -104,6 +105,8 @@ class _Cache(ctypes.Structure):
         ("self_slot", ctypes.c_void_p),
         ("err_word", ctypes.c_void_p),
         ("stats", ctypes.c_void_p),
+        ("ref_proj", ctypes.c_void_p),
+        ("proj_count", ctypes.c_void_p),
     ]
 
 
@@ -188,10 +191,12 @@ class CodecConfig:
     group: int = 32
     mode: str = "bf16"  # 'bf16': bf16 KV/weights, FP8 refs, fp16 scale/min; 'f32': all fp32
     rope_theta: float = 1.0e4
+    mean_projection: bool = False  # RKV_FLAG_MEAN_PROJECTION
 
     @classmethod
-    def from_workload(cls, w) -> "CodecConfig":
-        return cls(w.n_kv_heads, w.head_dim, w.d_ff, w.d_c, w.top_k, w.bits, w.group, w.mode, w.rope_theta)
+    def from_workload(cls, w, mean_projection: bool = False) -> "CodecConfig":
+        return cls(w.n_kv_heads, w.head_dim, w.d_ff, w.d_c, w.top_k, w.bits, w.group, w.mode, w.rope_theta,
+                   mean_projection)
 
     @property
     def two_dk(self) -> int:
@@ -217,7 +222,7 @@ class CodecConfig:
             RKV_F32 if f32 else RKV_FP8_E4M3,
             RKV_F32 if f32 else RKV_F16,
             RKV_F32 if f32 else RKV_BF16,
-            0,
+            RKV_FLAG_MEAN_PROJECTION if self.mean_projection else 0,
             float(self.rope_theta),
         )
 
@@ -317,11 +322,15 @@ class CodecCache:
         self.self_slot = torch.full((batch, cap_tok), -1, dtype=torch.int32, device=device)
         self.err_word = torch.zeros((1,), dtype=torch.int32, device=device) if err_word else None
         self.stats = torch.zeros((RKV_STATS_WORDS,), dtype=torch.int32, device=device) if stats else None
+        # the mean-projection form's per-reference projections and their count
+        self.ref_proj = (torch.zeros((batch, cap_ref, cfg.d_ff, 2), dtype=torch.float32, device=device)
+                         if cfg.mean_projection else None)
+        self.proj_count = torch.zeros((batch,), dtype=torch.int32, device=device) if cfg.mean_projection else None
         self._c = _Cache(
             batch, cap_ref, cap_tok, 0,
             _ptr(self.ref_vals), _ptr(self.ref_pos), _ptr(self.ref_norm2), _ptr(self.ref_count),
             _ptr(self.codes), _ptr(self.scale), _ptr(self.zmin), _ptr(self.ref_idx), _ptr(self.self_slot),
-            _ptr(self.err_word), _ptr(self.stats),
+            _ptr(self.err_word), _ptr(self.stats), _ptr(self.ref_proj), _ptr(self.proj_count),
         )
 
     def error_bits(self) -> int:

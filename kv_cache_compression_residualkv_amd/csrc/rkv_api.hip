@@ -32,12 +32,15 @@ rkv_status check_config(const rkv_config* cfg, Shape* out) {
     if (dtype_size(cfg->kv_dtype) == 0 || dtype_size(cfg->ref_dtype) == 0 || dtype_size(cfg->scale_dtype) == 0 ||
         dtype_size(cfg->weight_dtype) == 0)
         return RKV_ERR_INVALID_ARG;
+    if (cfg->flags & ~RKV_FLAG_MEAN_PROJECTION) return RKV_ERR_INVALID_ARG;
     if (cfg->bits != 2 && cfg->bits != 4 && cfg->bits != 16) return RKV_ERR_UNSUPPORTED;
     const bool f32 = cfg->kv_dtype == RKV_F32 && cfg->ref_dtype == RKV_F32 && cfg->scale_dtype == RKV_F32 &&
                      cfg->weight_dtype == RKV_F32;
     const bool bf16 = cfg->kv_dtype == RKV_BF16 && cfg->ref_dtype == RKV_FP8_E4M3 && cfg->scale_dtype == RKV_F16 &&
                       cfg->weight_dtype == RKV_BF16;
     if (!f32 && !bf16) return RKV_ERR_UNSUPPORTED;
+    const bool mproj = (cfg->flags & RKV_FLAG_MEAN_PROJECTION) != 0;
+    if (mproj && f32) return RKV_ERR_UNSUPPORTED;
     const int D = cfg->head_dim;
     if (D != 64 && D != 128) return RKV_ERR_UNSUPPORTED;
     const long dk = (long)cfg->n_kv_heads * D;
@@ -60,6 +63,7 @@ rkv_status check_config(const rkv_config* cfg, Shape* out) {
         out->group = cfg->group;
         out->G = cfg->d_c / cfg->group;
         out->f32 = f32;
+        out->mproj = mproj;
         out->theta = cfg->rope_theta;
     }
     return RKV_OK;
@@ -89,6 +93,8 @@ rkv_status check_cache(const Shape& s, const rkv_cache* c, bool need_records, Ca
     v->self_slot = c->self_slot;
     v->err = c->err_word;
     v->stats = c->stats;
+    v->ref_proj = c->ref_proj;
+    v->proj_count = c->proj_count;
     v->code_bytes = code_bytes_of(s);
     return RKV_OK;
 }
@@ -186,6 +192,8 @@ rkv_status rkv_encode_ex(const rkv_config* cfg, const rkv_weights* w, rkv_cache*
     if (!aligned16(kv) || !aligned16(w->w_c1) || !aligned16(w->w_c2) || !aligned16(w->w_c3))
         return RKV_ERR_ALIGNMENT;
     if (n > cache->cap_tok) return RKV_ERR_CAPACITY;
+    if (s.mproj && (!c.ref_proj || !c.proj_count)) return RKV_ERR_INVALID_ARG;
+    if (s.mproj && !aligned16(c.ref_proj)) return RKV_ERR_ALIGNMENT;
     const EncodePlan p = plan_encode(s, c.B, n, c.cap_ref);
     if (!workspace || workspace_bytes < p.total) return RKV_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RKV_ERR_ALIGNMENT;
@@ -198,7 +206,8 @@ rkv_status rkv_encode_ex(const rkv_config* cfg, const rkv_weights* w, rkv_cache*
     if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess) e = launch_select(s, c, p, kv, kv_len, rows, pos, n, workspace, hs);
     if (e == hipSuccess) e = mark(2);
-    if (e == hipSuccess) e = launch_swiglu(s, c, p, kv, kv_len, rows, n, w->w_c1, w->w_c2, workspace, hs);
+    if (e == hipSuccess && s.mproj) e = launch_project_refs(s, c, w->w_c1, w->w_c2, hs);
+    if (e == hipSuccess) e = launch_swiglu(s, c, p, kv, kv_len, rows, pos, n, w->w_c1, w->w_c2, workspace, hs);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess) e = launch_latent_quant(s, c, p, pos, n, w->w_c3, workspace, hs);
     if (e == hipSuccess) e = mark(4);

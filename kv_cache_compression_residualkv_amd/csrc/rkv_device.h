@@ -116,6 +116,18 @@ __device__ inline float4 fp8x4_to_f32(uint32_t w) {
     return make_float4(lo[0], lo[1], hi[0], hi[1]);
 }
 
+// Eight FP8 values (two words) widened exactly to bf16
+__device__ inline bf16x8 widen8(uint32_t x, uint32_t y) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)y, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)y, 1.0f, true);
+    bf16x8 f;
+    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+    f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+    return f;
+}
+
 template <>
 struct Load8<fp8_t> {
     static __device__ inline void run(const fp8_t* p, float* o) {

@@ -19,6 +19,8 @@
 //                       through LDS into coalesced record writes.
 #include <float.h>
 
+#include <algorithm>
+
 #include "rkv_device.h"
 #include "rkv_gemm.h"
 #include "rkv_internal.h"
@@ -203,6 +205,13 @@ constexpr size_t kRing = (size_t)NST * (BM + BN) * kStageK * 2;
 constexpr size_t kEpi = (size_t)(BM / 2) * kHP * sizeof(float);
 constexpr size_t bytes = kRing > kEpi ? kRing : kEpi;
 static_assert(bytes <= 160 * 1024, "LDS budget");
+// mean-projection form: all BM rows are tokens (kv rows only); a table of each token's
+// reference count and slots follows the (larger) dH staging tile
+constexpr int kTab = 9;  // ints per token: count (-1: no kv row), then up to 8 slots
+constexpr size_t kEpiP = (size_t)BM * kHP * sizeof(float);
+constexpr size_t kOffTab = kRing > kEpiP ? kRing : kEpiP;
+constexpr size_t bytesP = kOffTab + (size_t)BM * kTab * sizeof(int);
+static_assert(bytesP <= 160 * 1024, "LDS budget");
 }  // namespace g1r
 
 struct G1Frag {
@@ -210,12 +219,69 @@ struct G1Frag {
     bf16x8 b[4];
 };
 
+// The mean's hidden values of the mean-projection form for one token and hidden column:
+// a = (sum over the token's slots, ascending, of [r W_c1, r W_c2]) / k, h = SiLU(a1) a2,
+// from the KMAX loaded projections v[q] of its padded slot list (entries q >= k repeat a
+// valid slot and are masked out of the sum). k = 0: the zero mean, h = 0.
+template <int KMAX>
+__device__ inline float mean_h_from(const f32x2 (&v)[KMAX], int k) {
+    float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < KMAX; ++q) {
+        a1 += q < k ? v[q][0] : 0.f;
+        a2 += q < k ? v[q][1] : 0.f;
+    }
+    if (k > 1) {
+        a1 = __fdiv_rn(a1, (float)k);
+        a2 = __fdiv_rn(a2, (float)k);
+    }
+    return swiglu_h(a1, a2);
+}
+
+template <int KMAX>
+__device__ inline void load_proj(f32x2 (&v)[KMAX], const float* __restrict__ proj_b, const int* tab, int d_ff,
+                                 int col) {
+#pragma unroll
+    for (int q = 0; q < KMAX; ++q)
+        v[q] = *reinterpret_cast<const f32x2*>(proj_b + ((size_t)tab[1 + q] * d_ff + col) * 2);
+}
+
+// Token table of the mean-projection form: count (-1 when the token has no kv row or its
+// position is out of range: dH = 0, the selection kernel has flagged it) and the slots,
+// padded to 8 with the first slot (slot 0 for an empty set) so that every load is valid.
+__device__ inline void token_entry(int* tab, const int* __restrict__ rows, const int* __restrict__ pos,
+                                   const int* __restrict__ ref_idx, int kv_len, int cap_tok, int top_k, int b, int n,
+                                   int t) {
+    const int kr = rows[(size_t)b * n + t];
+    const int p = pos[(size_t)b * n + t];
+    int k = -1;
+    if (kr >= 0 && kr < kv_len && p >= 0 && p < cap_tok) {
+        const int* ri = ref_idx + ((size_t)b * cap_tok + p) * top_k;
+        k = 0;
+        for (int q = 0; q < top_k; ++q) {
+            const int sl = ri[q];
+            if (sl >= 0) tab[1 + k++] = sl;
+        }
+    }
+    const int pad = k > 0 ? tab[1] : 0;
+    for (int q = max(k, 0); q < 8; ++q) tab[1 + q] = pad;
+    tab[0] = k;
+}
+
+// kProj = false: A rows alternate kv_i / mean_i of one token (128 tokens per tile).
+// kProj = true (mean-projection form): A rows are kv rows only (256 tokens per tile) and
+// the mean's hidden values come from the references' projections (proj) in the epilogue.
+template <bool kProj, int KMAX>
 __global__ __launch_bounds__(g1r::kThreads) void swiglu_ring_kernel(const bf16_t* __restrict__ kv, int kv_len,
                                                                     const int* __restrict__ rows, int n,
                                                                     const bf16_t* __restrict__ xbar,
                                                                     const bf16_t* __restrict__ w1,
                                                                     const bf16_t* __restrict__ w2, int W2, int d_ff,
-                                                                    bf16_t* __restrict__ dh, int MT, int NT, int per) {
+                                                                    bf16_t* __restrict__ dh, int MT, int NT, int per,
+                                                                    const int* __restrict__ pos,
+                                                                    const int* __restrict__ ref_idx,
+                                                                    const float* __restrict__ proj, int cap_ref,
+                                                                    int cap_tok, int top_k) {
     extern __shared__ __align__(16) unsigned char smem_u8[];
     char* smem = reinterpret_cast<char*>(smem_u8);
     const int tile = xcd_tile(blockIdx.x, per);
@@ -224,20 +290,33 @@ __global__ __launch_bounds__(g1r::kThreads) void swiglu_ring_kernel(const bf16_t
     const int b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
-    const int tok0 = mt * (g1r::BM / 2);
+    constexpr int kTok = kProj ? g1r::BM : g1r::BM / 2;  // tokens per tile
+    const int tok0 = mt * kTok;
     const int j0 = nt * g1r::kHid;
 
-    // A rows alternate kv_i / mean_i of one token. Rows past n repeat the last token;
-    // a kv row index outside [0, kv_len) reads the token's mean row instead (dH = 0;
-    // the selection kernel has flagged the token).
+    // Rows past n repeat the last token. A kv row index outside [0, kv_len) reads the
+    // token's mean row instead (dH = 0; the selection kernel has flagged the token); in the
+    // mean-projection form it reads row 0 and the token's table entry zeroes dH.
     Op16<g1r::BM, 8> la;
     la.init([&](int r) {
-        const int t = min(tok0 + (r >> 1), n - 1);
-        const bf16_t* mrow = xbar + ((size_t)b * n + t) * W2;
-        if (r & 1) return mrow;
-        const int kr = rows[(size_t)b * n + t];
-        return (kr >= 0 && kr < kv_len) ? kv + ((size_t)b * kv_len + kr) * W2 : mrow;
+        if constexpr (kProj) {
+            const int t = min(tok0 + r, n - 1);
+            const int kr = rows[(size_t)b * n + t];
+            return kv + ((size_t)b * kv_len + ((kr >= 0 && kr < kv_len) ? kr : 0)) * W2;
+        } else {
+            const int t = min(tok0 + (r >> 1), n - 1);
+            const bf16_t* mrow = xbar + ((size_t)b * n + t) * W2;
+            if (r & 1) return mrow;
+            const int kr = rows[(size_t)b * n + t];
+            return (kr >= 0 && kr < kv_len) ? kv + ((size_t)b * kv_len + kr) * W2 : mrow;
+        }
     });
+    int* sTab = reinterpret_cast<int*>(smem + g1r::kOffTab);
+    if constexpr (kProj) {
+        // read by the epilogue only, after the barriers of the main loop and its end
+        if (tid < kTok && tok0 + tid < n)
+            token_entry(sTab + g1r::kTab * tid, rows, pos, ref_idx, kv_len, cap_tok, top_k, b, n, tok0 + tid);
+    }
     // B tile rows in groups of 64: [c1 32q .. +32, c2 32q .. +32] for q = 0..3, so that
     // wave wn's 64 rows hold matching W_c1 (tiles j = 0, 1) and W_c2 (j = 2, 3) columns;
     // columns past d_ff repeat the last one (not stored)
@@ -269,30 +348,67 @@ __global__ __launch_bounds__(g1r::kThreads) void swiglu_ring_kernel(const bf16_t
     ring_mainloop_lrp<g1r::NST, G1Frag, 12, 32>(la, lb, ns, ns, smem, load, mma, acc,
                                         [](int, f32x4(&)[8][4], bool) {});
 
-    // epilogue: rows 4g+0/4g+1 of a tile are kv/mean of one token, 4g+2/4g+3 of the next
     __syncthreads();
-    float* sH = reinterpret_cast<float*>(smem);  // [BM/2 tokens][kHP]
+    float* sH = reinterpret_cast<float*>(smem);  // [tokens][kHP]
+    if constexpr (kProj) {
+        // epilogue: row 4 g + e of a tile is one token; its mean's hidden values from the
+        // projections of its references
+        // (every load of a 16-row block is issued before the sums that use it)
+        const float* proj_b = proj + (size_t)b * cap_ref * d_ff * 2;
+        int cols[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int tl = 64 * wm + 8 * i + 2 * (lane >> 4);
+        for (int c = 0; c < 2; ++c) cols[c] = min(j0 + 32 * wn + 16 * c + (lane & 15), d_ff - 1);
+        constexpr int EB = KMAX > 4 ? 2 : 4;  // rows of a 16-row block per batch of loads
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const f32x4 a = acc[i][c];
-            const f32x4 g = acc[i][c + 2];
-            const float h0 = swiglu_h(a[0], g[0]);
-            const float h1 = swiglu_h(a[1], g[1]);
-            const float h2 = swiglu_h(a[2], g[2]);
-            const float h3 = swiglu_h(a[3], g[3]);
-            const int cl = 32 * wn + 16 * c + (lane & 15);
-            sH[tl * g1r::kHP + cl] = h0 - h1;
-            sH[(tl + 1) * g1r::kHP + cl] = h2 - h3;
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int e0 = 0; e0 < 4; e0 += EB) {
+                f32x2 v[EB][2][KMAX];
+                int kk[EB];
+#pragma unroll
+                for (int u = 0; u < EB; ++u) {
+                    const int tl = 128 * wm + 16 * i + 4 * (lane >> 4) + e0 + u;
+                    const int* tab = sTab + g1r::kTab * (tok0 + tl < n ? tl : 0);
+                    kk[u] = tok0 + tl < n ? tab[0] : -1;
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) load_proj<KMAX>(v[u][c], proj_b, tab, d_ff, cols[c]);
+                }
+#pragma unroll
+                for (int u = 0; u < EB; ++u) {
+                    const int tl = 128 * wm + 16 * i + 4 * (lane >> 4) + e0 + u;
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const float hk = swiglu_h(acc[i][c][e0 + u], acc[i][c + 2][e0 + u]);
+                        const float hm = mean_h_from<KMAX>(v[u][c], kk[u]);
+                        sH[tl * g1r::kHP + 32 * wn + 16 * c + (lane & 15)] = kk[u] >= 0 ? hk - hm : 0.f;
+                    }
+                }
+            }
+        }
+    } else {
+        // epilogue: rows 4g+0/4g+1 of a tile are kv/mean of one token, 4g+2/4g+3 of the next
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int tl = 64 * wm + 8 * i + 2 * (lane >> 4);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const f32x4 a = acc[i][c];
+                const f32x4 g = acc[i][c + 2];
+                const float h0 = swiglu_h(a[0], g[0]);
+                const float h1 = swiglu_h(a[1], g[1]);
+                const float h2 = swiglu_h(a[2], g[2]);
+                const float h3 = swiglu_h(a[3], g[3]);
+                const int cl = 32 * wn + 16 * c + (lane & 15);
+                sH[tl * g1r::kHP + cl] = h0 - h1;
+                sH[(tl + 1) * g1r::kHP + cl] = h2 - h3;
+            }
         }
     }
     __syncthreads();
     // coalesced store: each job = 8 consecutive columns of one token, split into the
     // three bf16 planes hi + mid + lo
     constexpr int kCh = g1r::kHid / 8;
-    constexpr int kJobs = (g1r::BM / 2) * kCh;
+    constexpr int kJobs = kTok * kCh;
     for (int jb = tid; jb < kJobs; jb += g1r::kThreads) {
         const int tl = jb / kCh, ch = jb - tl * kCh;
         const int t = tok0 + tl;
@@ -796,6 +912,200 @@ __global__ __launch_bounds__(128) void swiglu_skinny_kernel(const bf16_t* __rest
     }
 }
 
+// Mean-projection form of swiglu_skinny_kernel: A rows are the kv rows of the (up to 16)
+// tokens; wavefront 0's epilogue takes each token's mean hidden values from the
+// projections of its references.
+struct SkFrag1P {
+    bf16x8 a;
+    bf16x8 b;
+};
+
+__global__ __launch_bounds__(128) void swiglu_skinny_proj_kernel(
+    const bf16_t* __restrict__ kv, int kv_len, const int* __restrict__ rows, const int* __restrict__ pos, int n,
+    const int* __restrict__ ref_idx, const float* __restrict__ proj, int cap_ref, int cap_tok, int top_k,
+    const bf16_t* __restrict__ w1, const bf16_t* __restrict__ w2, int W2, int d_ff, bf16_t* __restrict__ dh) {
+    extern __shared__ __align__(16) unsigned char smem_u8[];
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    char* ring = reinterpret_cast<char*>(smem_u8) + wave * sk::ring1;
+    const int j0 = 16 * blockIdx.x;
+    SoloOp16<16> la;
+    la.init([&](int r) {
+        const int t = min(r, n - 1);
+        const int kr = rows[(size_t)b * n + t];
+        return kv + ((size_t)b * kv_len + ((kr >= 0 && kr < kv_len) ? kr : 0)) * W2;
+    });
+    SoloOp16<16> lb;
+    const bf16_t* wsel = wave == 0 ? w1 : w2;
+    lb.init([&](int r) { return wsel + (size_t)min(j0 + r, d_ff - 1) * W2; });
+    f32x4 acc = zero4();
+    auto load = [&](SkFrag1P& f, const char* sa, const char* sb, int ks) {
+        f.b = Op16<16, 1>::template frag<bf16_t>(sb, 0, ks);
+        f.a = Op16<16, 1>::template frag<bf16_t>(sa, 0, ks);
+    };
+    auto mma = [&](const SkFrag1P& f) { acc = Mma<bf16_t>::step(acc, f.a, f.b); };
+    skinny_ring<sk::NST1, SkFrag1P>(la, lb, W2 / kStageK, ring, load, mma);
+    // wavefront 1's W_c2 accumulators -> LDS (its own ring, which it has finished reading),
+    // and the token table after them
+    f32x4* xg = reinterpret_cast<f32x4*>(reinterpret_cast<char*>(smem_u8) + sk::ring1);
+    int* sTab = reinterpret_cast<int*>(xg + 64);
+    if (wave == 1) {
+        xg[lane] = acc;
+        if (lane < 16 && lane < n) token_entry(sTab + g1r::kTab * lane, rows, pos, ref_idx, kv_len, cap_tok, top_k, b, n, lane);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // row 4 (lane / 16) + e is token 4 (lane / 16) + e; lane: hidden column j0 + lane % 16
+    const int col = j0 + (lane & 15);
+    const float* proj_b = proj + (size_t)b * cap_ref * d_ff * 2;
+    const f32x4 g = xg[lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int t = 4 * (lane >> 4) + e;
+        if (t >= n || col >= d_ff) continue;
+        const int* tab = sTab + g1r::kTab * t;
+        f32x2 v[8];
+        load_proj<8>(v, proj_b, tab, d_ff, col);
+        const int k = tab[0];
+        const float x = k >= 0 ? swiglu_h(acc[e], g[e]) - mean_h_from<8>(v, k) : 0.f;
+        const float hi = (float)(bf16_t)x;
+        const float r1 = x - hi;
+        const float mi = (float)(bf16_t)r1;
+        const float r2 = r1 - mi;
+        bf16_t* dst = dh + ((size_t)b * n + t) * 3 * d_ff + col;
+        dst[0] = (bf16_t)hi;
+        dst[d_ff] = (bf16_t)mi;
+        dst[2 * d_ff] = (bf16_t)r2;
+    }
+}
+
+// ---------------------------------------------------------------- reference projections
+// Mean-projection form: every stored reference r gets [r W_c1, r W_c2] once (fp32, hidden
+// column j at [2 j], [2 j + 1] of its row), so that the encoder can average them instead
+// of multiplying every token's mean (the first layer of f_c is linear, section 2.3).
+// Tile: 128 pool slots x 128 W rows (64 hidden columns of W_c1 and the same of W_c2),
+// four wavefronts of 64 x 64. The FP8 slots go through registers (widened exactly to
+// bf16 into the ring layout of rkv_pipe.h); W rows arrive by direct loads. The slots to
+// project, [proj_count, ref_count), are known on the device only: workgroups walk the
+// slot tiles with a stride of gridDim.y and stop at the first tile past the end.
+namespace pj {
+constexpr int kThreads = 256;
+constexpr int BM = 128, BN = 128;
+constexpr int kHid = BN / 2;
+constexpr int kMaxMT = 32;
+constexpr int kStageA = BM * kStageK * 2;  // bf16
+constexpr int kSlot = kStageA + BN * kStageK * 2;
+constexpr size_t bytes = 2 * (size_t)kSlot;
+}  // namespace pj
+
+__global__ __launch_bounds__(pj::kThreads) void project_refs_kernel(const fp8_t* __restrict__ ref_vals,
+                                                                    const int* __restrict__ ref_count,
+                                                                    const int* __restrict__ proj_count, int cap_ref,
+                                                                    const bf16_t* __restrict__ w1,
+                                                                    const bf16_t* __restrict__ w2, int W2, int d_ff,
+                                                                    float* __restrict__ proj) {
+    extern __shared__ __align__(16) unsigned char smem_u8[];
+    char* smem = reinterpret_cast<char*>(smem_u8);
+    const int b = blockIdx.z;
+    const int hi = min(ref_count[b], cap_ref);
+    const int pc = proj_count[b];
+    const int lo = (pc >= 0 && pc <= hi) ? pc : 0;
+    if (lo + (int)blockIdx.y * pj::BM >= hi) return;
+    const int j0 = blockIdx.x * pj::kHid;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    // W rows in groups of 64: [c1 32 q .. + 32, c2 32 q .. + 32]: wave wn's 64 rows hold
+    // W_c1 (tiles j = 0, 1) and W_c2 (j = 2, 3) of hidden columns j0 + 32 wn ..
+    Op16<pj::BN, 4> lb;
+    lb.init([&](int r) {
+        const int q = r >> 6, e = r & 63;
+        const int col = min(j0 + 32 * q + (e & 31), d_ff - 1);
+        return (e < 32) ? w1 + (size_t)col * W2 : w2 + (size_t)col * W2;
+    });
+    // A: thread -> slot row ar = tid % 128, K half ah = tid / 128 (32 FP8 values of a stage)
+    const int ar = tid & (pj::BM - 1), ah = tid >> 7;
+    const int ns = W2 / kStageK;
+    const fp8_t* pool = ref_vals + (size_t)b * cap_ref * W2;
+    float* out_b = proj + (size_t)b * cap_ref * d_ff * 2;
+    for (int mt = blockIdx.y;; mt += gridDim.y) {
+        const int s0 = lo + mt * pj::BM;
+        if (s0 >= hi) break;
+        const uint8_t* arow =
+            reinterpret_cast<const uint8_t*>(pool + (size_t)min(s0 + ar, hi - 1) * W2) + 32 * ah;
+        f32x4 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+        uint4 ra[2];
+        auto load_a = [&](int st) {
+            const uint4* src = reinterpret_cast<const uint4*>(arow + (size_t)st * kStageK);
+            ra[0] = src[0];
+            ra[1] = src[1];
+        };
+        // chunk c = 4 ah + u (8 values) of row ar -> block 2 (ar / 16) + ah, row ar % 16,
+        // position swz(ar % 16, u)
+        auto store_a = [&](char* slot) {
+            char* blk = slot + 1024 * (2 * (ar >> 4) + ah) + 64 * (ar & 15);
+            const uint32_t w[8] = {ra[0].x, ra[0].y, ra[0].z, ra[0].w, ra[1].x, ra[1].y, ra[1].z, ra[1].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                *reinterpret_cast<bf16x8*>(blk + 16 * swz(ar & 15, u)) = widen8(w[2 * u], w[2 * u + 1]);
+        };
+        load_a(0);
+        lb.issue(0, smem + pj::kStageA);
+        for (int st = 0; st < ns; ++st) {
+            char* slot = smem + (st & 1) * pj::kSlot;
+            store_a(slot);
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (st + 1 < ns) {
+                load_a(st + 1);
+                lb.issue(st + 1, smem + ((st + 1) & 1) * pj::kSlot + pj::kStageA);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 fa[4], fb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fa[i] = Op16<pj::BM, 4>::template frag<bf16_t>(slot, 4 * wm + i, ks);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    fb[j] = Op16<pj::BN, 4>::template frag<bf16_t>(slot + pj::kStageA, 4 * wn + j, ks);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = Mma<bf16_t>::step(acc[i][j], fa[i], fb[j]);
+            }
+            __syncthreads();
+        }
+        // row 64 wm + 16 i + 4 (lane / 16) + e is slot s0 + row; tiles j and j + 2 are the
+        // W_c1 and W_c2 columns j0 + 32 wn + 16 j + lane % 16
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int slot = s0 + 64 * wm + 16 * i + 4 * (lane >> 4) + e;
+                if (slot >= hi) continue;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int col = j0 + 32 * wn + 16 * j + (lane & 15);
+                    if (col >= d_ff) continue;
+                    f32x2 v;
+                    v[0] = acc[i][j][e];
+                    v[1] = acc[i][j + 2][e];
+                    *reinterpret_cast<f32x2*>(out_b + ((size_t)slot * d_ff + col) * 2) = v;
+                }
+            }
+    }
+}
+
+// proj_count = ref_count once the projections of the new slots are written
+__global__ void projections_done_kernel(const int* __restrict__ ref_count, int* __restrict__ proj_count, int B,
+                                        int cap_ref) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) proj_count[b] = min(ref_count[b], cap_ref);
+}
+
 struct SkFrag2 {
     bf16x8 a;
     bf16x8 b[2];
@@ -859,21 +1169,39 @@ static hipError_t swiglu_impl(const Shape& s, const CacheView& c, const EncodePl
 }
 
 static hipError_t swiglu_ring_impl(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv,
-                                   int kv_len, const int* rows, int n, const void* w1, const void* w2, void* ws,
-                                   hipStream_t st) {
-    const size_t smem = g1r::bytes;
-    auto kern = swiglu_ring_kernel;
+                                   int kv_len, const int* rows, const int* pos, int n, const void* w1, const void* w2,
+                                   void* ws, hipStream_t st) {
+    const size_t smem = s.mproj ? g1r::bytesP : g1r::bytes;
+    auto kern = !s.mproj ? swiglu_ring_kernel<false, 4>
+                         : (s.top_k <= 4 ? swiglu_ring_kernel<true, 4> : swiglu_ring_kernel<true, 8>);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     char* w = static_cast<char*>(ws);
-    const int MT = (2 * n + g1r::BM - 1) / g1r::BM;
+    const int MT = ((s.mproj ? n : 2 * n) + g1r::BM - 1) / g1r::BM;
     const int NT = (s.d_ff + g1r::kHid - 1) / g1r::kHid;
     const int per = xcd_per(MT * NT);
     hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(g1r::kThreads), smem, st, static_cast<const bf16_t*>(kv), kv_len,
-                       rows, n, reinterpret_cast<const bf16_t*>(w + p.off_xbar), static_cast<const bf16_t*>(w1),
-                       static_cast<const bf16_t*>(w2), s.W2, s.d_ff, reinterpret_cast<bf16_t*>(w + p.off_dh), MT, NT,
-                       per);
+                       rows, n, s.mproj ? nullptr : reinterpret_cast<const bf16_t*>(w + p.off_xbar),
+                       static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w2), s.W2, s.d_ff,
+                       reinterpret_cast<bf16_t*>(w + p.off_dh), MT, NT, per, pos, c.ref_idx, c.ref_proj, c.cap_ref,
+                       c.cap_tok, s.top_k);
+    return hipGetLastError();
+}
+
+hipError_t launch_project_refs(const Shape& s, const CacheView& c, const void* w1, const void* w2, hipStream_t st) {
+    if (s.f32 || !s.mproj) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(project_refs_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)pj::bytes);
+    if (e != hipSuccess) return e;
+    const int mt = std::min((c.cap_ref + pj::BM - 1) / pj::BM, pj::kMaxMT);
+    hipLaunchKernelGGL(project_refs_kernel, dim3(s.d_ff / pj::kHid, mt, c.B), dim3(pj::kThreads), pj::bytes, st,
+                       static_cast<const fp8_t*>(c.ref_vals), c.ref_count, c.proj_count, c.cap_ref,
+                       static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w2), s.W2, s.d_ff, c.ref_proj);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(projections_done_kernel, dim3((c.B + 63) / 64), dim3(64), 0, st, c.ref_count, c.proj_count,
+                       c.B, c.cap_ref);
     return hipGetLastError();
 }
 
@@ -885,8 +1213,20 @@ static bool skinny(const Shape& s, int n) {
 }
 
 hipError_t launch_swiglu(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
-                         const int* rows, int n, const void* w1, const void* w2, void* ws, hipStream_t st) {
+                         const int* rows, const int* pos, int n, const void* w1, const void* w2, void* ws,
+                         hipStream_t st) {
     if (s.f32) return swiglu_impl<float>(s, c, p, kv, kv_len, rows, n, w1, w2, ws, st);
+    if (skinny(s, n) && s.mproj) {
+        char* w = static_cast<char*>(ws);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(swiglu_skinny_proj_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sk::bytes1);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(swiglu_skinny_proj_kernel, dim3(s.d_ff / 16, c.B), dim3(128), sk::bytes1, st,
+                           static_cast<const bf16_t*>(kv), kv_len, rows, pos, n, c.ref_idx, c.ref_proj, c.cap_ref,
+                           c.cap_tok, s.top_k, static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w2), s.W2,
+                           s.d_ff, reinterpret_cast<bf16_t*>(w + p.off_dh));
+        return hipGetLastError();
+    }
     if (skinny(s, n)) {
         char* w = static_cast<char*>(ws);
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(swiglu_skinny_kernel),
@@ -898,7 +1238,7 @@ hipError_t launch_swiglu(const Shape& s, const CacheView& c, const EncodePlan& p
                            static_cast<const bf16_t*>(w2), s.W2, s.d_ff, reinterpret_cast<bf16_t*>(w + p.off_dh));
         return hipGetLastError();
     }
-    return swiglu_ring_impl(s, c, p, kv, kv_len, rows, n, w1, w2, ws, st);
+    return swiglu_ring_impl(s, c, p, kv, kv_len, rows, pos, n, w1, w2, ws, st);
 }
 
 template <typename T, typename ScT>

@@ -14,6 +14,7 @@ struct Shape {
     int N, D, dk, W2;  // heads, head dim, d_k = N*D, W2 = 2*d_k
     int d_ff, d_c, top_k, bits, group, G;  // G = d_c / group
     bool f32;          // true: "f32" formats, false: "bf16" formats
+    bool mproj;        // RKV_FLAG_MEAN_PROJECTION: f_c(mean) from the references' projections
     double theta;
 };
 
@@ -30,6 +31,8 @@ struct CacheView {
     int* self_slot;
     int* err;
     int* stats;        // optional encode counters (RKV_STATS_WORDS)
+    float* ref_proj;   // [B][cap_ref][d_ff][2] (mean-projection form)
+    int* proj_count;   // [B] (mean-projection form)
     size_t code_bytes;  // per token
 };
 
@@ -55,8 +58,14 @@ hipError_t launch_search(const Shape& s, const CacheView& c, const EncodePlan& p
 hipError_t launch_select(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
                          const int* rows, const int* pos, int n, void* ws, hipStream_t st);
 
+// kv_len rows of kv; pos [B][n] (the records' positions, read by the mean-projection form)
 hipError_t launch_swiglu(const Shape& s, const CacheView& c, const EncodePlan& p, const void* kv, int kv_len,
-                         const int* rows, int n, const void* w1, const void* w2, void* ws, hipStream_t st);
+                         const int* rows, const int* pos, int n, const void* w1, const void* w2, void* ws,
+                         hipStream_t st);
+
+// Mean-projection form: project pool slots [proj_count, ref_count) of every sequence into
+// ref_proj ([r W_c1, r W_c2] per hidden column, fp32), then set proj_count = ref_count.
+hipError_t launch_project_refs(const Shape& s, const CacheView& c, const void* w1, const void* w2, hipStream_t st);
 
 hipError_t launch_latent_quant(const Shape& s, const CacheView& c, const EncodePlan& p, const int* pos, int n,
                                const void* w3, void* ws, hipStream_t st);

@@ -400,17 +400,6 @@ __device__ inline void dma4(const void* g, void* lds) {
     __builtin_amdgcn_global_load_lds(g, (RKV_LDS void*)lds, 4, 0, 0);
 }
 
-// Eight FP8 values (two words) widened exactly to bf16
-__device__ inline bf16x8 widen8(uint32_t x, uint32_t y) {
-    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, false);
-    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, true);
-    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)y, 1.0f, false);
-    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)y, 1.0f, true);
-    bf16x8 f;
-    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
-    f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
-    return f;
-}
 
 // LDS layout of a ring slot: the FP8 pool stage (256 rows x 64 K bytes) as 16 blocks of
 // 16 rows at a 64-byte pitch, the 16-byte granule m of row r at position m ^ h(r); the
@@ -1089,10 +1078,12 @@ __device__ inline void sort8_i32(int (&k)[8]) {
 
 // Reference mean of one token by one wavefront: fp32 sum in ascending slot order, one
 // correctly rounded division, rounded to the KV dtype for the encoder. slots[0..k_i-1]
-// hold the chosen slots in ascending order (the same in every lane).
+// hold the chosen slots in ascending order (the same in every lane). A null row: the
+// encoder takes the mean from the references' projections and needs no mean row.
 template <typename KvT, typename RefT>
 __device__ inline void write_mean(const RefT* __restrict__ pool, const int (&slots)[8], int k_i, int W2,
                                   KvT* __restrict__ xrow, int lane) {
+    if (!xrow) return;
     const float kf = (float)k_i;
     const float rk = __fdiv_rn(1.0f, k_i > 0 ? kf : 1.0f);
 #pragma unroll 2
@@ -1150,7 +1141,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     const int p = pos[(size_t)b * n + t];
     const bool row_ok = row >= 0 && row < kv_len;
     const bool pos_ok = p >= 0 && p < cap_tok;
-    KvT* xrow = xbar + ((size_t)b * n + t) * W2;
+    KvT* xrow = xbar ? xbar + ((size_t)b * n + t) * W2 : nullptr;
     if (!row_ok || !pos_ok) {
         if (lane == 0) flag_error(err, (row_ok ? 0 : DEVERR_ROW_RANGE) | (pos_ok ? 0 : DEVERR_POS_RANGE));
         const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -1505,7 +1496,7 @@ __global__ __launch_bounds__(256) void rescan_kernel(
                 const uint64_t* all = part_keys + (size_t)e * kRqParts * 8;
                 for (int j = 0; j < kRqParts * 8; j += 64) offer_keys(best, all[j + lane]);
                 write_set<KvT, RefT>(best, top_k, k.pool, W2, ref_idx + ((size_t)k.b * cap_tok + k.p) * top_k,
-                                     xbar + ((size_t)k.b * n + k.t) * W2);
+                                     xbar ? xbar + ((size_t)k.b * n + k.t) * W2 : nullptr);
             }
         }
         __syncthreads();
@@ -1521,7 +1512,7 @@ __global__ __launch_bounds__(256) void rescan_kernel(
         merge_waves(best, s_best);
         if (wave == 0)
             write_set<KvT, RefT>(best, top_k, k.pool, W2, ref_idx + ((size_t)k.b * cap_tok + k.p) * top_k,
-                                 xbar + ((size_t)k.b * n + k.t) * W2);
+                                 xbar ? xbar + ((size_t)k.b * n + k.t) * W2 : nullptr);
         __syncthreads();
     }
 }
@@ -1562,8 +1553,8 @@ EncodePlan plan_encode(const Shape& s, int B, int n, int cap_ref) {
     off = up(off + (kRqHead + 2 * tok) * sizeof(int));
     p.off_rescan_part = off;  // partial lists of the parallel rescans
     off = up(off + (size_t)kRqPar * kRqParts * 8 * sizeof(uint64_t));
-    p.off_xbar = off;
-    off = up(off + tok * s.W2 * (s.f32 ? 4 : 2));
+    p.off_xbar = off;  // mean rows (none in the mean-projection form)
+    if (!s.mproj) off = up(off + tok * s.W2 * (s.f32 ? 4 : 2));
     p.off_dh = off;
     // dH: fp32 rows (fp32 formats) or three bf16 planes per row (bf16 formats)
     off = up(off + tok * s.d_ff * (s.f32 ? 4 : 6));
@@ -1665,7 +1656,7 @@ static hipError_t select_impl(const Shape& s, const CacheView& c, const EncodePl
                               const int* rows, const int* pos, int n, void* ws, hipStream_t st) {
     char* w = static_cast<char*>(ws);
     int* rescan = reinterpret_cast<int*>(w + p.off_rescan);
-    KvT* xbar = reinterpret_cast<KvT*>(w + p.off_xbar);
+    KvT* xbar = s.mproj ? nullptr : reinterpret_cast<KvT*>(w + p.off_xbar);
     const int* part_slot = reinterpret_cast<const int*>(w + p.off_part_slot);
     const dim3 grid((n + 3) / 4, c.B);
     hipLaunchKernelGGL((select_kernel<KvT, RefT>), grid, dim3(kThreads), 0, st, static_cast<const KvT*>(kv), kv_len,

@@ -44,9 +44,10 @@ KV_RMS_REL = 1e-3
 class GpuCodec:
     """One layer of the codec on the GPU for a workload (batch of sequences)."""
 
-    def __init__(self, wl, weights_math, batch=None, cap_ref=None, cap_tok=None, device="cuda"):
+    def __init__(self, wl, weights_math, batch=None, cap_ref=None, cap_tok=None, device="cuda",
+                 mean_projection=False):
         self.wl = wl
-        self.cfg = B.CodecConfig.from_workload(wl)
+        self.cfg = B.CodecConfig.from_workload(wl, mean_projection=mean_projection)
         self.W = B.CodecWeights.from_math(weights_math, self.cfg, device)
         self.batch = batch or wl.batch
         self.cap_tok = cap_tok or wl.T

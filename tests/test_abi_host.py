@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(B.EXPORTED)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.rkv_abi_version() == 3
+    assert lib.rkv_abi_version() == 4
 
 
 def test_prepared_decoder_bytes(lib):
@@ -225,3 +225,33 @@ def test_encode_noalloc_host_checks(lib):
     assert B.RKV_NOALLOC_SCRATCH_BYTES == 16 << 20
     assert B.rkv_encode_workspace_bytes(cfg, 1, 1400, 4096) <= B.RKV_NOALLOC_SCRATCH_BYTES
     assert B.rkv_encode_workspace_bytes(cfg, 1, 4000, 4096) > B.RKV_NOALLOC_SCRATCH_BYTES
+
+
+def test_mean_projection_flag_host_checks(lib):
+    # RKV_FLAG_MEAN_PROJECTION: "bf16" formats only; unknown flag bits are invalid
+    cfg = B.CodecConfig.from_workload(workload(2), mean_projection=True)
+    assert B.rkv_validate_config(cfg) == 0
+    f32 = B.CodecConfig.from_workload(workload(1), mean_projection=True)
+    assert B.rkv_validate_config(f32) == -2
+    bad = B.CodecConfig.from_workload(workload(2)).c_struct()
+    bad.flags = 2
+    assert lib.rkv_validate_config(ctypes.byref(bad)) == -1
+    # no mean rows in the workspace: smaller by n * 2 d_k bf16 values (up to alignment)
+    plain = B.CodecConfig.from_workload(workload(2))
+    wp, wq = B.rkv_encode_workspace_bytes(plain, 1, 28672, 4096), B.rkv_encode_workspace_bytes(cfg, 1, 28672, 4096)
+    assert wp - wq == 28672 * 2048 * 2
+    # the encode needs ref_proj and proj_count, 16-byte aligned, before anything is launched
+    fake = 1 << 20
+    cache = B._Cache()
+    cache.batch, cache.cap_ref, cache.cap_tok = 1, 8, 8
+    for f in ("ref_vals", "ref_pos", "ref_norm2", "ref_count", "codes", "scale", "zmin", "ref_idx", "self_slot"):
+        setattr(cache, f, fake)
+    w = B._Weights(fake, fake, fake, fake)
+    c = cfg.c_struct()
+    args = (ctypes.byref(c), ctypes.byref(w), ctypes.byref(cache), fake, 4, fake, fake, 2, fake, 1 << 30, None)
+    assert lib.rkv_encode(*args) == -1
+    cache.ref_proj, cache.proj_count = fake + 8, fake
+    assert lib.rkv_encode(*args) == -4
+    cache.ref_proj, cache.proj_count = fake, None
+    assert lib.rkv_encode(*args) == -1
+
