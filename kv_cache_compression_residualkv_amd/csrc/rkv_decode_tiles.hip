@@ -42,7 +42,7 @@ constexpr int kCols = 128;          // output columns per chunk
 constexpr int kHalf = 64;           // output columns per pass (4 MFMA tiles of 16)
 constexpr int kRefs = 4;            // reference slots per token (k <= 4)
 constexpr int kRefBuf = TT * kRefs * kHalf;  // FP8 reference slices of one pass
-constexpr int kRopeP = 66;                   // float2 (cos, sin) pitch of a token's RoPE row
+constexpr int kRotBytes = 64 * 8;            // float2 [64]: revolutions per position, split hi + lo
 }  // namespace dt
 
 // LDS layout of form 1 (register-staged W_d)
@@ -55,31 +55,30 @@ constexpr int kOffW = 0;
 constexpr int kOffRef = kOffW + kWSlots * kWBuf;       // two pass buffers
 constexpr int kOffSlot = kOffRef + 2 * dt::kRefBuf;    // int [TT][kRefs]; -1: none
 constexpr int kOffKd = kOffSlot + dt::TT * dt::kRefs * 4;  // int [TT]: divisor of the slot sum
-constexpr int kOffRope = kOffKd + dt::TT * 4;          // float2 [TT][kRopeP]
-constexpr int bytes = kOffRope + dt::TT * dt::kRopeP * 8;
-// set-up tables that live in the reference buffers until their first fill
-constexpr int kOffRev = kOffRef;                       // double [64]
-constexpr int kOffPos = kOffRef + 64 * 8;              // int [TT]
+constexpr int kOffRot = kOffKd + dt::TT * 4;           // RoPE frequencies (rope_cs)
+constexpr int bytes = kOffRot + dt::kRotBytes;
+// set-up table that lives in the reference buffers until their first fill
+constexpr int kOffPos = kOffRef;                       // int [TT]
 static_assert(bytes <= 160 * 1024, "LDS budget");
 }  // namespace rr
 
 // LDS layout of form 2 (prepared fp16 W_d by direct loads)
 namespace dl {
-constexpr int NST = 4;                           // W_d stages in flight
+constexpr int NST = 8;                           // W_d stages in flight
 constexpr int kWStage = dt::kHalf * kStageK * 2;  // 8 KB
 constexpr int kOffW = 0;
 constexpr int kOffRef = kOffW + NST * kWStage;
 constexpr int kOffSlot = kOffRef + dt::kRefBuf;
 constexpr int kOffKd = kOffSlot + dt::TT * dt::kRefs * 4;
-constexpr int kOffRope = kOffKd + dt::TT * 4;
-constexpr int bytes = kOffRope + dt::TT * dt::kRopeP * 8;
-constexpr int kOffRev = kOffRef;
-constexpr int kOffPos = kOffRef + 64 * 8;
+constexpr int kOffRot = kOffKd + dt::TT * 4;
+constexpr int bytes = kOffRot + dt::kRotBytes;
+constexpr int kOffPos = kOffRef;
 static_assert(bytes <= 160 * 1024, "LDS budget");
 }  // namespace dl
 
 // 64 zero bytes: the slices of an empty reference slot
 __device__ __align__(16) uint8_t g_zero_slice[64];
+
 
 // Workgroup barrier for LDS traffic only: a fence would also wait for every
 // outstanding global load, including the reference slices fetched for the next chunk.
@@ -165,10 +164,10 @@ __device__ constexpr int chunk_tile(int h, int lt) {
 // empty slot, read as zeros) and the divisor of their sum. k_i = 1, 2 or 4 references
 // fill the slots by repetition (slot sum / 4 is their mean exactly); k_i = 3 leaves one
 // slot empty and divides by 3. A reference token restores its own stored row (k = 1).
-// Also the position of every token and, for the RoPE table, the revolutions per position
-// of the pair frequencies theta^(-2j/D) / (2 pi).
+// Also the position of every token and, for RoPE, the revolutions per position of the
+// pair frequencies theta^(-2j/D) / (2 pi).
 template <int D>
-__device__ inline void token_table(int* sSlot, int* sKd, int* sPos, double* sRev, const int* __restrict__ idx, int m,
+__device__ inline void token_table(int* sSlot, int* sKd, int* sPos, float* sRot, const int* __restrict__ idx, int m,
                                    int b, int tt0, bool flag, const int* __restrict__ self_slot,
                                    const int* __restrict__ ref_idx, int top_k, int cap_ref, int cap_tok, double theta,
                                    int* err) {
@@ -217,7 +216,13 @@ __device__ inline void token_table(int* sSlot, int* sKd, int* sPos, double* sRev
         sKd[tid] = n == 3 ? 3 : 4;
         sPos[tid] = max(p, 0);
     }
-    if (tid < D / 2) sRev[tid] = pow(theta, -2.0 * (double)tid / (double)D) * 0.15915494309189535;
+    if (tid < D / 2) {
+        // revolutions per position of pair j, theta^(-2j/D) / (2 pi), as hi + lo in fp32
+        const double r = pow(theta, -2.0 * (double)tid / (double)D) * 0.15915494309189535;
+        const float hi = (float)r;
+        sRot[2 * tid] = hi;
+        sRot[2 * tid + 1] = (float)(r - (double)hi);
+    }
 }
 
 // This lane's two tokens (MFMA column groups of wavefront `wave`): the latent as fp16
@@ -274,18 +279,39 @@ __device__ inline void latent_frags(f16x8 (&zf)[2][NKS], const int* __restrict__
     }
 }
 
-// RoPE table: cos / sin of every token's pair angles (two threads per token). The phase
-// in revolutions is reduced to [-1/2, 1/2] in fp64, then sin / cos in fp32.
-template <int D, int RP = dt::kRopeP>
-__device__ inline void rope_table(float* sRope, const int* sPos, const double* sRev) {
-    const int tid = threadIdx.x, tk = tid >> 1;
-    const double pp = (double)sPos[tk];
-    for (int j = (tid & 1) * 32; j < (tid & 1) * 32 + 32 && j < D / 2; ++j) {
-        const double r = pp * sRev[j];
-        const float fr = (float)(r - rint(r));
-        *reinterpret_cast<float2*>(sRope + 2 * (tk * RP + j)) =
-            make_float2(__builtin_amdgcn_cosf(fr), __builtin_amdgcn_sinf(fr));
-    }
+// cos and sin of the RoPE angle of one token and pair frequency: pos times the pair's
+// revolutions per position rev = hi + lo (fp32 split of the fp64 value), reduced in
+// double-float arithmetic: x = pos hi with its rounding error ex from an FMA (exact),
+// x minus its nearest integer (exact), plus ex and pos lo; the result, within about
+// 2^-24 revolutions of the exact phase in [-1/2, 1/2], goes to the hardware sine and
+// cosine of revolutions. pos < 2^24 is exact in fp32. Contraction stays off: fused into
+// x - rint(x), the product would enter unrounded and count ex twice.
+__device__ inline void rope_cs(float pos, float hi, float lo, float& c, float& s) {
+#pragma clang fp contract(off)
+    const float x = pos * hi;
+    const float ex = fmaf(pos, hi, -x);
+    const float f = (x - __builtin_rintf(x)) + fmaf(pos, lo, ex);
+    c = __builtin_amdgcn_cosf(f);
+    s = __builtin_amdgcn_sinf(f);
+}
+
+// Rotation of one RoPE pair (element e of v1, v2) by the angle with cosine c and sine s. Every restore
+// path rotates through this one function with contraction off, so all of them round
+// alike (the compiler may otherwise fuse either product into the sum differently in
+// each context).
+__device__ inline void rope_rotate(f32x4& v1, f32x4& v2, int e, float c, float s) {
+#pragma clang fp contract(off)
+    const float a = v1[e], b = v2[e];
+    v1[e] = a * c - b * s;
+    v2[e] = b * c + a * s;
+}
+
+// A lane's two token positions (MFMA column groups gr of wavefront `wave`), from the
+// set-up table sPos, as fp32.
+__device__ inline void lane_positions(float (&posf)[2], const int* sPos) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, mrow = lane & 15;
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr) posf[gr] = (float)sPos[32 * wave + 16 * gr + mrow];
 }
 
 // Form of this wavefront's reference mean. When every token averages its four slots the
@@ -318,13 +344,14 @@ __device__ inline MeanForm mean_form(const int* sKd) {
 
 // End of pass h of a chunk: reference mean (two FP8 MFMAs per output tile against the
 // slices in R: row r = q * TT + token, 64 bytes, tile t at 16-byte position
-// t ^ ((r / 4) % 4)) and, on key columns, RoPE (sRope rows of RP float2). After it the
+// t ^ ((r / 4) % 4)) and, on key columns, RoPE (rope_cs at the lane's token positions
+// posf, frequencies in sRot). After it the
 // lane holds, for its token 32 wave + 16 gr + lane % 16, columns 16 chunk_tile(h, lt) +
 // 4 (lane / 16) + e of the chunk in acc[gr][lt][e]. An invalid index has a zero latent and
 // empty slots: its row is zero already.
-template <int D, bool kFused, int RP = dt::kRopeP>
-__device__ inline void pass_values(f32x4 (&acc)[2][4], const unsigned char* R, const float* sRope, int h, bool rope,
-                                   const MeanForm& mf) {
+template <int D, bool kFused>
+__device__ inline void pass_values(f32x4 (&acc)[2][4], const unsigned char* R, const float* sRot,
+                                   const float (&posf)[2], int h, bool rope, const MeanForm& mf) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, mrow = lane & 15;
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
@@ -353,17 +380,15 @@ __device__ inline void pass_values(f32x4 (&acc)[2][4], const unsigned char* R, c
 #pragma unroll
             for (int lt = 0; lt < 2; ++lt) {
                 const int jt = D == 128 ? 2 * h + lt : lt;
-                const float* rp = sRope + 2 * (tk * RP + 16 * jt + 4 * g);
-                const float4 q01 = *reinterpret_cast<const float4*>(rp);
-                const float4 q23 = *reinterpret_cast<const float4*>(rp + 4);
-                const float cs[4] = {q01.x, q01.z, q23.x, q23.z};
-                const float sn[4] = {q01.y, q01.w, q23.y, q23.w};
+                const f32x4 r01 = lds_load<f32x4>(sRot + 2 * (16 * jt + 4 * g));
+                const f32x4 r23 = lds_load<f32x4>(sRot + 2 * (16 * jt + 4 * g) + 4);
+                const float rh[4] = {r01[0], r01[2], r23[0], r23[2]};
+                const float rl[4] = {r01[1], r01[3], r23[1], r23[3]};
+                float cs[4], sn[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x1 = a[lt][e], x2 = a[lt + 2][e];
-                    a[lt][e] = x1 * cs[e] - x2 * sn[e];
-                    a[lt + 2][e] = x2 * cs[e] + x1 * sn[e];
-                }
+                for (int e = 0; e < 4; ++e) rope_cs(posf[gr], rh[e], rl[e], cs[e], sn[e]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rope_rotate(a[lt], a[lt + 2], e, cs[e], sn[e]);
             }
         }
     }
@@ -371,10 +396,10 @@ __device__ inline void pass_values(f32x4 (&acc)[2][4], const unsigned char* R, c
 
 // End of pass h of a chunk starting at column col0: pass_values, then the rows' store.
 template <int D, bool kFused, typename OutT>
-__device__ inline void finish_pass(f32x4 (&acc)[2][4], const unsigned char* R, const float* sRope, int h, int col0,
-                                   bool rope, const MeanForm& mf, int tt0, int m, int b, int W2,
-                                   OutT* __restrict__ out) {
-    pass_values<D, kFused>(acc, R, sRope, h, rope, mf);
+__device__ inline void finish_pass(f32x4 (&acc)[2][4], const unsigned char* R, const float* sRot,
+                                   const float (&posf)[2], int h, int col0, bool rope, const MeanForm& mf, int tt0,
+                                   int m, int b, int W2, OutT* __restrict__ out) {
+    pass_values<D, kFused>(acc, R, sRot, posf, h, rope, mf);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, mrow = lane & 15;
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
@@ -444,8 +469,7 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
     unsigned char* sRef = smem + rr::kOffRef;
     int* sSlot = reinterpret_cast<int*>(smem + rr::kOffSlot);
     int* sKd = reinterpret_cast<int*>(smem + rr::kOffKd);
-    float* sRope = reinterpret_cast<float*>(smem + rr::kOffRope);
-    double* sRev = reinterpret_cast<double*>(smem + rr::kOffRev);
+    float* sRot = reinterpret_cast<float*>(smem + rr::kOffRot);
     int* sPos = reinterpret_cast<int*>(smem + rr::kOffPos);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -487,7 +511,7 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
     load_ahead(wa, 0, 0, 0, 0);
     load_ahead(wb, 0, 0, 0, 1);
 
-    token_table<D>(sSlot, sKd, sPos, sRev, idx, m, b, tt0, tm.grp == 0, self_slot, ref_idx, top_k, cap_ref, cap_tok,
+    token_table<D>(sSlot, sKd, sPos, sRot, idx, m, b, tt0, tm.grp == 0, self_slot, ref_idx, top_k, cap_ref, cap_tok,
                    theta, err);
     f16x8 zf[2][NKS];
     latent_frags<NKS, BITS>(zf, idx, m, b, tt0, self_slot, codes, code_bytes, scale, zmin, cap_tok);
@@ -498,7 +522,8 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
     store_w(wb, 1);
     load_ahead(wb, 0, 0, 0, 3);
     __syncthreads();
-    if (n0 < dk) rope_table<D>(sRope, sPos, sRev);
+    float posf[2];
+    lane_positions(posf, sPos);
     const MeanForm mf = mean_form(sKd);
 
     // ---- reference slices of a pass -> LDS buffer (pass % 2), in the layout finish_pass
@@ -603,8 +628,8 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
             // ---- pass (c, h) done (one branch per pass on the mean's form)
             const int col0 = n0 + dt::kCols * c;
             const unsigned char* R = sRef + h * dt::kRefBuf;
-            if (mf.fused) finish_pass<D, true, OutT>(acc, R, sRope, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
-            else finish_pass<D, false, OutT>(acc, R, sRope, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
+            if (mf.fused) finish_pass<D, true, OutT>(acc, R, sRot, posf, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
+            else finish_pass<D, false, OutT>(acc, R, sRot, posf, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
         }
     }
 }
@@ -632,8 +657,7 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
     unsigned char* sRef = smem + dl::kOffRef;
     int* sSlot = reinterpret_cast<int*>(smem + dl::kOffSlot);
     int* sKd = reinterpret_cast<int*>(smem + dl::kOffKd);
-    float* sRope = reinterpret_cast<float*>(smem + dl::kOffRope);
-    double* sRev = reinterpret_cast<double*>(smem + dl::kOffRev);
+    float* sRot = reinterpret_cast<float*>(smem + dl::kOffRot);
     int* sPos = reinterpret_cast<int*>(smem + dl::kOffPos);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -700,14 +724,15 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
         const int k2 = ahead(0, 0, 0, d, c2, h2);
         issue_w(c2, h2, k2, d);
     }
-    token_table<D>(sSlot, sKd, sPos, sRev, idx, m, b, tt0, tm.grp == 0, self_slot, ref_idx, top_k, cap_ref, cap_tok,
+    token_table<D>(sSlot, sKd, sPos, sRot, idx, m, b, tt0, tm.grp == 0, self_slot, ref_idx, top_k, cap_ref, cap_tok,
                    theta, err);
     f16x8 zf[2][NKS];
     latent_frags<NKS, BITS>(zf, idx, m, b, tt0, self_slot, codes, code_bytes, scale, zmin, cap_tok);
     __syncthreads();
-    if (n0 < dk) rope_table<D>(sRope, sPos, sRev);
+    float posf[2];
+    lane_positions(posf, sPos);
     const MeanForm mf = mean_form(sKd);
-    // the set-up tables in the reference buffer are read; W_d stages 0 .. NST - 1 landed
+    // the set-up table in the reference buffer is read; W_d stages 0 .. NST - 1 landed
     wait_vmcnt<0>();
     __syncthreads();
 
@@ -778,8 +803,10 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
             wait_vmcnt<2 * (KST - 1)>();
             lds_barrier();
             const int col0 = n0 + dt::kCols * c;
-            if (mf.fused) finish_pass<D, true, OutT>(acc, sRef, sRope, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
-            else finish_pass<D, false, OutT>(acc, sRef, sRope, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
+            if (mf.fused)
+                finish_pass<D, true, OutT>(acc, sRef, sRot, posf, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
+            else
+                finish_pass<D, false, OutT>(acc, sRef, sRot, posf, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
             // the slices are read: the next pass may refill the buffer
             lds_barrier();
         }
@@ -809,7 +836,6 @@ template <int D>
 struct L {
     static constexpr int G = kAttendMaxG;  // room for the largest query-head group
     static constexpr int NST = dl::NST;
-    static constexpr int kRP = D / 2 + 2;        // float2 pitch of a token's RoPE row
     static constexpr int kKP = dt::kHalf + 8;    // bf16 pitch of a key row of the pass (144 B)
     static constexpr int kVP = dt::TT + 8;       // f16 pitch of a value column (272 B)
     static constexpr int kQP = D + 8;            // bf16 pitch of a query row
@@ -819,17 +845,16 @@ struct L {
     static constexpr int kOffRef = kOffW + NST * dl::kWStage;
     static constexpr int kOffSlot = kOffRef + dt::kRefBuf;
     static constexpr int kOffKd = kOffSlot + dt::TT * dt::kRefs * 4;
-    static constexpr int kOffRope = kOffKd + dt::TT * 4;
+    static constexpr int kOffRot = kOffKd + dt::TT * 4;
     // keys of the pass [TT][kKP] bf16, or values of the pass transposed [64][kVP] f16
-    static constexpr int kOffKV = kOffRope + dt::TT * kRP * 8;
+    static constexpr int kOffKV = kOffRot + dt::kRotBytes;
     static constexpr int kKVBytes = dt::TT * kKP * 2 > 64 * kVP * 2 ? dt::TT * kKP * 2 : 64 * kVP * 2;
     static constexpr int kOffQ = kOffKV + kKVBytes;                 // bf16 [kNH][G][kQP]
     static constexpr int kOffP = kOffQ + kNH * G * kQP * 2;         // f16 weights [kNH][G][kPP]
     static constexpr int kOffS = kOffP + kNH * G * kPP * 2;         // fp32 partial scores [G][TT]
     static constexpr int kOffRed = kOffS + G * dt::TT * 4;          // fp32 [max, sum][4 waves][8]
     static constexpr int bytes = kOffRed + 2 * 4 * 8 * 4;
-    static constexpr int kOffRev = kOffRef;
-    static constexpr int kOffPos = kOffRef + 64 * 8;
+    static constexpr int kOffPos = kOffRef;
     static_assert(bytes <= 160 * 1024, "LDS budget");
     // the MFMA operand reads of query / weight rows G .. 15 (unused output columns) stay
     // inside the allocation
@@ -855,13 +880,12 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
     unsigned char* sRef = smem + Ly::kOffRef;
     int* sSlot = reinterpret_cast<int*>(smem + Ly::kOffSlot);
     int* sKd = reinterpret_cast<int*>(smem + Ly::kOffKd);
-    float* sRope = reinterpret_cast<float*>(smem + Ly::kOffRope);
+    float* sRot = reinterpret_cast<float*>(smem + Ly::kOffRot);
     unsigned char* sKV = smem + Ly::kOffKV;
     unsigned char* sQ = smem + Ly::kOffQ;
     unsigned char* sP = smem + Ly::kOffP;
     float* sS = reinterpret_cast<float*>(smem + Ly::kOffS);
     float* sRed = reinterpret_cast<float*>(smem + Ly::kOffRed);
-    double* sRev = reinterpret_cast<double*>(smem + Ly::kOffRev);
     int* sPos = reinterpret_cast<int*>(smem + Ly::kOffPos);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -929,12 +953,13 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
         const int k2 = ahead(0, 0, 0, d, c2, h2);
         issue_w(c2, h2, k2, d);
     }
-    token_table<D>(sSlot, sKd, sPos, sRev, idx, m, b, tt0, tm.grp == 0, self_slot, ref_idx, top_k, cap_ref, cap_tok,
+    token_table<D>(sSlot, sKd, sPos, sRot, idx, m, b, tt0, tm.grp == 0, self_slot, ref_idx, top_k, cap_ref, cap_tok,
                    theta, err);
     f16x8 zf[2][NKS];
     latent_frags<NKS, BITS>(zf, idx, m, b, tt0, self_slot, codes, code_bytes, scale, zmin, cap_tok);
     __syncthreads();
-    rope_table<D, Ly::kRP>(sRope, sPos, sRev);
+    float posf[2];
+    lane_positions(posf, sPos);
     const MeanForm mf = mean_form(sKd);
     wait_vmcnt<0>();
     __syncthreads();
@@ -1139,8 +1164,8 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
             wait_vmcnt<2 * (KST - 1)>();
             lds_barrier();
             const bool isK = (c & 1) == 0;
-            if (mf.fused) pass_values<D, true, Ly::kRP>(acc, sRef, sRope, h, isK, mf);
-            else pass_values<D, false, Ly::kRP>(acc, sRef, sRope, h, isK, mf);
+            if (mf.fused) pass_values<D, true>(acc, sRef, sRot, posf, h, isK, mf);
+            else pass_values<D, false>(acc, sRef, sRot, posf, h, isK, mf);
             attend_pass(acc, c, h);
             // the slices and the staged values are read: the next pass may refill them
             lds_barrier();
