@@ -243,8 +243,10 @@ __device__ inline float seg16_max(float v) {
 
 // s / k correctly rounded for the reference-mean sums: s is a sum of at most 8 FP8
 // e4m3fn values (a multiple of 2^-9, |s| <= 8 * 448) and k = 1..8. With rk = RN(1/k),
-// one residual correction q + (s - q k) rk gives the IEEE quotient for every such s and
-// k (checked exhaustively against the correctly rounded division, all 2^22 sums x 8 k).
+// q = s rk and one FMA correction of the residual, q + (s - q k) rk (Markstein's
+// correction step for division on FMA hardware), give the IEEE quotient for every such
+// s and k: checked exhaustively against the correctly rounded division, all 2^22 sums
+// x 8 k (tests/support/exact_div_check.c).
 __device__ inline float div_small(float s, float k, float rk) {
     const float q = s * rk;
     const float e = fmaf(-q, k, s);

@@ -25,6 +25,7 @@
 #include "rkv_gemm.h"
 #include "rkv_internal.h"
 #include "rkv_pipe.h"
+#include "rkv_swish.h"
 
 namespace rkv {
 
@@ -61,35 +62,6 @@ struct G1LoadB {
     __device__ inline void load(int s) { t.load_rows(row, s * kKC); }
     __device__ inline void store(T* lds, int P) const { t.store(lds, P); }
 };
-
-// Swish(a) = a / (1 + e^-a) in fp32. e^-a = 2^t with t = -a log2(e): log2(e) is split
-// into L + Lc and the product's rounding error recovered by an FMA, so t is carried to
-// about 2^-40 relative before the hardware 2^x (v_exp_f32); the quotient takes the
-// hardware reciprocal and one residual correction (a few ulp in all, against ~0.5 ulp
-// for expf and an IEEE divide, at a third of the instructions). Below a = -87 the
-// value is under 1e-35 in magnitude and the argument is clamped so that 1 + e^-a stays
-// finite.
-__device__ inline float silu(float a) {
-    a = fmaxf(a, -87.0f);
-    const float L = 1.44269502f, Lc = 1.92596299e-8f;
-    const float t = -a * L;
-    const float tl = fmaf(-a, Lc, fmaf(-a, L, -t));
-    const float e = __builtin_amdgcn_exp2f(t) * fmaf(tl, 0.693147181f, 1.0f);
-    const float d = 1.0f + e;
-    const float r = __builtin_amdgcn_rcpf(d);
-    const float q = a * r;
-    return fmaf(fmaf(-q, d, a), r, q);
-}
-
-// One hidden value h = Swish(a) * g, rounded on its own: written as a plain product, the
-// compiler may fuse it into the difference h(kv) - h(mean) that follows (an FMA rounds
-// only once), so that one side is rounded and the other is not, and a token equal to its
-// reference mean would get a nonzero residual. The review page's z = f_c(kv) - f_c(mean)
-// (section 2.3) is exactly zero there, and so is this.
-__device__ inline float swiglu_h(float a, float g) {
-#pragma clang fp contract(off)
-    return silu(a) * g;
-}
 
 // grid: 8 * per blocks over MT x NT logical tiles (N tiles fastest, so the NT tiles
 // that read one A row block run back to back on one XCD).
