@@ -67,12 +67,12 @@ namespace dl {
 constexpr int NST = 8;                           // W_d stages in flight
 constexpr int kWStage = dt::kHalf * kStageK * 2;  // 8 KB
 constexpr int kOffW = 0;
-constexpr int kOffRef = kOffW + NST * kWStage;
-constexpr int kOffSlot = kOffRef + dt::kRefBuf;
+constexpr int kOffRef = kOffW + NST * kWStage;   // two pass buffers (pass h of a chunk: buffer h)
+constexpr int kOffSlot = kOffRef + 2 * dt::kRefBuf;
 constexpr int kOffKd = kOffSlot + dt::TT * dt::kRefs * 4;
 constexpr int kOffRot = kOffKd + dt::TT * 4;
-constexpr int bytes = kOffRot + dt::kRotBytes;
-constexpr int kOffPos = kOffRef;
+constexpr int kOffPos = kOffRot + dt::kRotBytes;  // int [TT]
+constexpr int bytes = kOffPos + dt::TT * 4;
 static_assert(bytes <= 160 * 1024, "LDS budget");
 }  // namespace dl
 
@@ -158,126 +158,173 @@ __device__ constexpr int chunk_tile(int h, int lt) {
     return D == 128 ? 2 * h + (lt & 1) + 4 * (lt >> 1) : 4 * h + lt;
 }
 
-// ---- set-up shared by both forms ------------------------------------------------------
-
+// ---- set-up shared by every restore kernel ------------------------------------------------
+// Everything a workgroup needs before its first pass, in two rounds of independent global
+// loads: the token indices (round 1), then what hangs off an index, i.e. the self slot,
+// the reference slots and the record (round 2). Addresses are clamped to valid memory and
+// validity is applied after the loads, so no load waits behind a branch or a wait for an
+// earlier one.
+//
 // Token table (threads 0..TT-1, one token each): four reference slots per token (-1: an
 // empty slot, read as zeros) and the divisor of their sum. k_i = 1, 2 or 4 references
 // fill the slots by repetition (slot sum / 4 is their mean exactly); k_i = 3 leaves one
 // slot empty and divides by 3. A reference token restores its own stored row (k = 1).
 // Also the position of every token and, for RoPE, the revolutions per position of the
 // pair frequencies theta^(-2j/D) / (2 pi).
-template <int D>
-__device__ inline void token_table(int* sSlot, int* sKd, int* sPos, float* sRot, const int* __restrict__ idx, int m,
-                                   int b, int tt0, bool flag, const int* __restrict__ self_slot,
-                                   const int* __restrict__ ref_idx, int top_k, int cap_ref, int cap_tok, double theta,
-                                   int* err) {
-    const int tid = threadIdx.x;
-    if (tid < dt::TT) {
-        const int t = tt0 + tid;
-        int p = -1;
-        if (t < m) {
-            p = idx[(size_t)b * m + t];
-            if (p < 0 || p >= cap_tok) {
-                if (flag) flag_error(err, DEVERR_IDX_RANGE);
-                p = -1;
-            }
+//
+// Latents: this lane's two tokens (MFMA column groups of token group tg, tokens 32 tg ..
+// + 32 of the tile) as fp16 fragments of every K-step (zero for a reference token or an
+// invalid index).
+template <int NKS, int BITS>
+struct TileSetup {
+    typedef typename std::conditional<BITS == 16, u32x4, uint32_t>::type Word;
+    int tt, tp, tss, tr[dt::kRefs];        // token table: thread tid % TT's token
+    int lt[2], lp[2], lss[2];              // the lane's two latent tokens
+    Word cw[2][NKS];                       // their code words (BITS 2 / 4) or fp16 values
+    uint32_t st2[2][NKS / 2], zm2[2][NKS / 2];  // their steps and minima (fp16 pairs)
+
+    // a loaded value used here on every path: the compiler cannot sink its load into the
+    // branch that needs it (with a wait of its own), so a round's loads share one wait
+    template <typename T>
+    static __device__ inline void pin(const T& v) {
+        asm volatile("" ::"v"(v));
+    }
+
+    // round 1: the token indices (positions past m read index m - 1 and are dropped later)
+    __device__ inline void index(const int* __restrict__ idx, int m, int b, int tt0, int tg) {
+        const int tid = threadIdx.x, lane = tid & 63, mrow = lane & 15;
+        tt = tt0 + (tid & (dt::TT - 1));
+        tp = idx[(size_t)b * m + min(tt, m - 1)];
+#pragma unroll
+        for (int gr = 0; gr < 2; ++gr) {
+            lt[gr] = tt0 + 32 * tg + 16 * gr + mrow;
+            lp[gr] = idx[(size_t)b * m + min(lt[gr], m - 1)];
         }
-        const size_t ro = (size_t)b * cap_tok + max(p, 0);
-        const int ss = self_slot[ro];
-        int r[dt::kRefs];
+        pin(tp);
+        pin(lp[0]);
+        pin(lp[1]);
+    }
+
+    // round 2: what hangs off an index, at the index clamped into the sequence's records
+    __device__ inline void fetch(const int* __restrict__ self_slot, const int* __restrict__ ref_idx, int top_k,
+                                 const uint8_t* __restrict__ codes, size_t code_bytes,
+                                 const f16_t* __restrict__ scale, const f16_t* __restrict__ zmin, int b,
+                                 int cap_tok) {
+        const int lane = threadIdx.x & 63, g = lane >> 4;
+        {
+            const size_t ro = (size_t)b * cap_tok + min(max(tp, 0), cap_tok - 1);
+            tss = self_slot[ro];
 #pragma unroll
-        for (int q = 0; q < dt::kRefs; ++q) r[q] = (q < top_k) ? ref_idx[ro * top_k + q] : -1;
-        int sl[dt::kRefs], n = 0;
+            for (int q = 0; q < dt::kRefs; ++q) tr[q] = ref_idx[ro * top_k + min(q, top_k - 1)];
+        }
 #pragma unroll
-        for (int q = 0; q < dt::kRefs; ++q) sl[q] = -1;
-        if (p >= 0) {
-            if (ss >= 0) {
-                sl[0] = min(ss, cap_ref - 1);
-                n = 1;
+        for (int gr = 0; gr < 2; ++gr) {
+            const size_t ro = (size_t)b * cap_tok + min(max(lp[gr], 0), cap_tok - 1);
+            lss[gr] = self_slot[ro];
+            const uint8_t* rec = codes + ro * code_bytes;
+            if constexpr (BITS == 16) {
+                // unquantized record: d_c fp16 values in latent order, 8 per lane and K-step
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) cw[gr][ks] = *reinterpret_cast<const u32x4*>(rec + 64 * ks + 16 * g);
             } else {
 #pragma unroll
-                for (int q = 0; q < dt::kRefs; ++q)
-                    if (r[q] >= 0) {
-                        // compact the valid entries
+                for (int ks = 0; ks < NKS; ++ks) {
+                    if constexpr (BITS == 4) cw[gr][ks] = *reinterpret_cast<const uint32_t*>(rec + 16 * ks + 4 * g);
+                    else cw[gr][ks] = *reinterpret_cast<const uint16_t*>(rec + 8 * ks + 2 * g);
+                }
+                const uint32_t* sp = reinterpret_cast<const uint32_t*>(scale + ro * NKS);
+                const uint32_t* zp = reinterpret_cast<const uint32_t*>(zmin + ro * NKS);
 #pragma unroll
-                        for (int u = 0; u < dt::kRefs; ++u)
-                            if (u == n) sl[u] = min(r[q], cap_ref - 1);
-                        ++n;
-                    }
+                for (int u = 0; u < NKS / 2; ++u) {
+                    st2[gr][u] = sp[u];
+                    zm2[gr][u] = zp[u];
+                }
             }
         }
-        if (n == 1) sl[1] = sl[2] = sl[3] = sl[0];
-        if (n == 2) {
-            sl[2] = sl[0];
-            sl[3] = sl[1];
-        }
+        pin(tss);
 #pragma unroll
-        for (int q = 0; q < dt::kRefs; ++q) sSlot[tid * dt::kRefs + q] = sl[q];
-        sKd[tid] = n == 3 ? 3 : 4;
-        sPos[tid] = max(p, 0);
+        for (int q = 0; q < dt::kRefs; ++q) pin(tr[q]);
+#pragma unroll
+        for (int gr = 0; gr < 2; ++gr) pin(lss[gr]);
     }
-    if (tid < D / 2) {
-        // revolutions per position of pair j, theta^(-2j/D) / (2 pi), as hi + lo in fp32
-        const double r = pow(theta, -2.0 * (double)tid / (double)D) * 0.15915494309189535;
-        const float hi = (float)r;
-        sRot[2 * tid] = hi;
-        sRot[2 * tid + 1] = (float)(r - (double)hi);
-    }
-}
 
-// This lane's two tokens (MFMA column groups of wavefront `wave`): the latent as fp16
-// fragments of every K-step (zero for a reference token or an invalid index).
-template <int NKS, int BITS>
-__device__ inline void latent_frags(f16x8 (&zf)[2][NKS], const int* __restrict__ idx, int m, int b, int tt0,
-                                    const int* __restrict__ self_slot, const uint8_t* __restrict__ codes,
-                                    size_t code_bytes, const f16_t* __restrict__ scale,
-                                    const f16_t* __restrict__ zmin, int cap_tok) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, mrow = lane & 15;
+    // the token table (threads 0..TT-1) and the RoPE frequencies; an index outside
+    // [0, cap_tok) raises DEVERR_IDX_RANGE (when flag) and restores a zero row
+    template <int D>
+    __device__ inline void table(int* sSlot, int* sKd, int* sPos, float* sRot, int m, int cap_ref, int cap_tok,
+                                 int top_k, bool flag, int* err) const {
+        const int tid = threadIdx.x;
+        if (tid < dt::TT) {
+            const bool in = tt < m;
+            const bool bad = in && (tp < 0 || tp >= cap_tok);
+            if (bad && flag) flag_error(err, DEVERR_IDX_RANGE);
+            const int p = (in && !bad) ? tp : -1;
+            int sl[dt::kRefs], n = 0;
 #pragma unroll
-    for (int gr = 0; gr < 2; ++gr) {
-        const int t = tt0 + 32 * wave + 16 * gr + mrow;
-        int p = t < m ? idx[(size_t)b * m + t] : -1;
-        if (p >= cap_tok) p = -1;
-        const size_t ro = (size_t)b * cap_tok + max(p, 0);
-        const bool enc = p >= 0 && self_slot[ro] < 0;
-        const uint8_t* rec = codes + ro * code_bytes;
-        if constexpr (BITS == 16) {
-            // unquantized record: d_c fp16 values in latent order; 8 of them per lane
-            // and K-step, reordered 0 4 1 5 2 6 3 7 to match the decoder's fragments
+            for (int q = 0; q < dt::kRefs; ++q) sl[q] = -1;
+            if (p >= 0) {
+                if (tss >= 0) {
+                    sl[0] = min(tss, cap_ref - 1);
+                    n = 1;
+                } else {
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                u32x4 w = *reinterpret_cast<const u32x4*>(rec + 64 * ks + 16 * g);
-                if (!enc) w = u32x4{0u, 0u, 0u, 0u};
-                const u32x4 o = {(w[0] & 0xFFFFu) | (w[2] << 16), (w[0] >> 16) | (w[2] & 0xFFFF0000u),
-                                 (w[1] & 0xFFFFu) | (w[3] << 16), (w[1] >> 16) | (w[3] & 0xFFFF0000u)};
-                zf[gr][ks] = *reinterpret_cast<const f16x8*>(&o);
+                    for (int q = 0; q < dt::kRefs; ++q)
+                        if (q < top_k && tr[q] >= 0) {
+                            // compact the valid entries
+#pragma unroll
+                            for (int u = 0; u < dt::kRefs; ++u)
+                                if (u == n) sl[u] = min(tr[q], cap_ref - 1);
+                            ++n;
+                        }
+                }
             }
-            continue;
-        }
-        uint32_t cw[NKS];
+            if (n == 1) sl[1] = sl[2] = sl[3] = sl[0];
+            if (n == 2) {
+                sl[2] = sl[0];
+                sl[3] = sl[1];
+            }
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            if constexpr (BITS == 4) cw[ks] = *reinterpret_cast<const uint32_t*>(rec + 16 * ks + 4 * g);
-            else cw[ks] = *reinterpret_cast<const uint16_t*>(rec + 8 * ks + 2 * g);
+            for (int q = 0; q < dt::kRefs; ++q) sSlot[tid * dt::kRefs + q] = sl[q];
+            sKd[tid] = n == 3 ? 3 : 4;
+            sPos[tid] = max(p, 0);
         }
-        const uint32_t* sp = reinterpret_cast<const uint32_t*>(scale + ro * NKS);
-        const uint32_t* zp = reinterpret_cast<const uint32_t*>(zmin + ro * NKS);
-        uint32_t st2[NKS / 2], zm2[NKS / 2];
-#pragma unroll
-        for (int u = 0; u < NKS / 2; ++u) {
-            st2[u] = sp[u];
-            zm2[u] = zp[u];
-        }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const uint32_t sh = (ks & 1) ? (st2[ks >> 1] >> 16) : (st2[ks >> 1] & 0xFFFFu);
-            const uint32_t zh = (ks & 1) ? (zm2[ks >> 1] >> 16) : (zm2[ks >> 1] & 0xFFFFu);
-            const uint32_t svp = enc ? (sh | (sh << 16)) : 0u, zvp = enc ? (zh | (zh << 16)) : 0u;
-            zf[gr][ks] = dequant8<BITS>(enc ? cw[ks] : 0u, *reinterpret_cast<const f16x2*>(&svp),
-                                        *reinterpret_cast<const f16x2*>(&zvp));
+        if (tid < D / 2) {
+            // revolutions per position of pair j, theta^(-2j/D) / (2 pi), as hi + lo in fp32
+            const double r = pow(theta_, -2.0 * (double)tid / (double)D) * 0.15915494309189535;
+            const float hi = (float)r;
+            sRot[2 * tid] = hi;
+            sRot[2 * tid + 1] = (float)(r - (double)hi);
         }
     }
-}
+
+    __device__ inline void latents(f16x8 (&zf)[2][NKS], int m, int cap_tok) const {
+#pragma unroll
+        for (int gr = 0; gr < 2; ++gr) {
+            const bool enc = lt[gr] < m && lp[gr] >= 0 && lp[gr] < cap_tok && lss[gr] < 0;
+            if constexpr (BITS == 16) {
+                // reordered 0 4 1 5 2 6 3 7 to match the decoder's fragments
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    u32x4 w = cw[gr][ks];
+                    if (!enc) w = u32x4{0u, 0u, 0u, 0u};
+                    const u32x4 o = {(w[0] & 0xFFFFu) | (w[2] << 16), (w[0] >> 16) | (w[2] & 0xFFFF0000u),
+                                     (w[1] & 0xFFFFu) | (w[3] << 16), (w[1] >> 16) | (w[3] & 0xFFFF0000u)};
+                    zf[gr][ks] = *reinterpret_cast<const f16x8*>(&o);
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const uint32_t sh = (ks & 1) ? (st2[gr][ks >> 1] >> 16) : (st2[gr][ks >> 1] & 0xFFFFu);
+                    const uint32_t zh = (ks & 1) ? (zm2[gr][ks >> 1] >> 16) : (zm2[gr][ks >> 1] & 0xFFFFu);
+                    const uint32_t svp = enc ? (sh | (sh << 16)) : 0u, zvp = enc ? (zh | (zh << 16)) : 0u;
+                    zf[gr][ks] = dequant8<BITS>(enc ? (uint32_t)cw[gr][ks] : 0u, *reinterpret_cast<const f16x2*>(&svp),
+                                                *reinterpret_cast<const f16x2*>(&zvp));
+                }
+            }
+        }
+    }
+    double theta_;
+};
 
 // cos and sin of the RoPE angle of one token and pair frequency: pos times the pair's
 // revolutions per position rev = hi + lo (fp32 split of the fp64 value), reduced in
@@ -306,15 +353,15 @@ __device__ inline void rope_rotate(f32x4& v1, f32x4& v2, int e, float c, float s
     v2[e] = b * c + a * s;
 }
 
-// A lane's two token positions (MFMA column groups gr of wavefront `wave`), from the
+// A lane's two token positions (MFMA column groups gr of token group tg), from the
 // set-up table sPos, as fp32.
-__device__ inline void lane_positions(float (&posf)[2], const int* sPos) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, mrow = lane & 15;
+__device__ inline void lane_positions(float (&posf)[2], const int* sPos, int tg) {
+    const int lane = threadIdx.x & 63, mrow = lane & 15;
 #pragma unroll
-    for (int gr = 0; gr < 2; ++gr) posf[gr] = (float)sPos[32 * wave + 16 * gr + mrow];
+    for (int gr = 0; gr < 2; ++gr) posf[gr] = (float)sPos[32 * tg + 16 * gr + mrow];
 }
 
-// Form of this wavefront's reference mean. When every token averages its four slots the
+// Form of the reference mean of token group tg. When every token averages its four slots the
 // 1/4 rides in the selection matrix (fused); otherwise the slot sum is divided exactly per
 // token. Selection matrix of the reference MFMA (A operand, 16 x 32 FP8): output row r
 // takes K entries (q, r) of the step's two slots q; K entry 8 (lane / 16) + j of this lane
@@ -325,13 +372,13 @@ struct MeanForm {
     long sel;
     bool fused;
 };
-__device__ inline MeanForm mean_form(const int* sKd) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, mrow = lane & 15;
+__device__ inline MeanForm mean_form(const int* sKd, int tg) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, mrow = lane & 15;
     MeanForm f;
     bool all4 = true;
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
-        const int k = sKd[32 * wave + 16 * gr + mrow];
+        const int k = sKd[32 * tg + 16 * gr + mrow];
         all4 = all4 && k == 4;
         f.kd[gr] = (float)k;
         f.rkd[gr] = __fdiv_rn(1.0f, f.kd[gr]);
@@ -342,74 +389,91 @@ __device__ inline MeanForm mean_form(const int* sKd) {
     return f;
 }
 
-// End of pass h of a chunk: reference mean (two FP8 MFMAs per output tile against the
-// slices in R: row r = q * TT + token, 64 bytes, tile t at 16-byte position
-// t ^ ((r / 4) % 4)) and, on key columns, RoPE (rope_cs at the lane's token positions
-// posf, frequencies in sRot). After it the
-// lane holds, for its token 32 wave + 16 gr + lane % 16, columns 16 chunk_tile(h, lt) +
-// 4 (lane / 16) + e of the chunk in acc[gr][lt][e]. An invalid index has a zero latent and
-// empty slots: its row is zero already.
-template <int D, bool kFused>
-__device__ inline void pass_values(f32x4 (&acc)[2][4], const unsigned char* R, const float* sRot,
-                                   const float (&posf)[2], int h, bool rope, const MeanForm& mf) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, mrow = lane & 15;
+// A pass of a chunk for NT of its four 16-column tiles: local tiles lt(i) = i (NT = 4) or
+// ch + 2 i (NT = 2, column half ch), tokens 32 tg .. + 32 of the tile. The lane holds, for
+// its token 32 tg + 16 gr + lane % 16, columns 16 chunk_tile(h, lt(i)) + 4 (lane / 16) + e
+// of the chunk in acc[gr][i][e]. Every restore path and tile set rounds alike: the
+// accumulators start from the reference mean (pass_mean), the W_d product accumulates on
+// top, then pass_rope rotates key columns.
+template <int NT>
+__device__ constexpr int pass_tile(int ch, int i) {
+    return NT == 4 ? i : ch + 2 * i;
+}
+
+// The reference mean as the accumulators' initial value: two FP8 MFMAs per output tile
+// against the slices in R (row r = q * TT + token, 64 bytes, tile t at 16-byte position
+// t ^ ((r / 4) % 4)); with the 1/4 in the selection matrix (fused form) that is the mean,
+// otherwise the slot sum divided exactly by the token's k. An invalid index has empty
+// slots: zero.
+template <bool kFused, int NT>
+__device__ inline void pass_mean(f32x4 (&acc)[2][NT], const unsigned char* R, const MeanForm& mf, int ch, int tg) {
+    static_assert(NT == 2 || NT == 4, "tile set");
+    const int lane = threadIdx.x & 63, g = lane >> 4, mrow = lane & 15;
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
-        const int tk = 32 * wave + 16 * gr + mrow;
-        f32x4 (&a)[4] = acc[gr];
+        const int tk = 32 * tg + 16 * gr + mrow;
 #pragma unroll
-        for (int lt = 0; lt < 4; ++lt) {
+        for (int i = 0; i < NT; ++i) {
+            const int lt = pass_tile<NT>(ch, i);
             long v[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int r = (2 * hh + (g >> 1)) * dt::TT + tk;
                 v[hh] = *reinterpret_cast<const long*>(R + r * dt::kHalf + 16 * (lt ^ ((r >> 2) & 3)) + 8 * (g & 1));
             }
-            if constexpr (kFused) {
-                a[lt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(mf.sel, v[0], a[lt], 0, 0, 0);
-                a[lt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(mf.sel, v[1], a[lt], 0, 0, 0);
-            } else {
-                f32x4 sm = zero4();
-                sm = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(mf.sel, v[0], sm, 0, 0, 0);
-                sm = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(mf.sel, v[1], sm, 0, 0, 0);
+            f32x4 sm = zero4();
+            sm = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(mf.sel, v[0], sm, 0, 0, 0);
+            sm = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(mf.sel, v[1], sm, 0, 0, 0);
+            if constexpr (!kFused) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) a[lt][e] += div_small(sm[e], mf.kd[gr], mf.rkd[gr]);
+                for (int e = 0; e < 4; ++e) sm[e] = div_small(sm[e], mf.kd[gr], mf.rkd[gr]);
             }
-        }
-        if (rope) {
-#pragma unroll
-            for (int lt = 0; lt < 2; ++lt) {
-                const int jt = D == 128 ? 2 * h + lt : lt;
-                const f32x4 r01 = lds_load<f32x4>(sRot + 2 * (16 * jt + 4 * g));
-                const f32x4 r23 = lds_load<f32x4>(sRot + 2 * (16 * jt + 4 * g) + 4);
-                const float rh[4] = {r01[0], r01[2], r23[0], r23[2]};
-                const float rl[4] = {r01[1], r01[3], r23[1], r23[3]};
-                float cs[4], sn[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) rope_cs(posf[gr], rh[e], rl[e], cs[e], sn[e]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) rope_rotate(a[lt], a[lt + 2], e, cs[e], sn[e]);
-            }
+            acc[gr][i] = sm;
         }
     }
 }
 
-// End of pass h of a chunk starting at column col0: pass_values, then the rows' store.
-template <int D, bool kFused, typename OutT>
-__device__ inline void finish_pass(f32x4 (&acc)[2][4], const unsigned char* R, const float* sRot,
-                                   const float (&posf)[2], int h, int col0, bool rope, const MeanForm& mf, int tt0,
-                                   int m, int b, int W2, OutT* __restrict__ out) {
-    pass_values<D, kFused>(acc, R, sRot, posf, h, rope, mf);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, mrow = lane & 15;
+// RoPE of a key pass: rope_cs at the lane's token positions posf (frequencies in sRot), on
+// the pairs of local tiles (lt, lt + 2).
+template <int D, int NT>
+__device__ inline void pass_rope(f32x4 (&acc)[2][NT], const float* sRot, const float (&posf)[2], int h, int ch) {
+    const int lane = threadIdx.x & 63, g = lane >> 4;
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
-        const int t = tt0 + 32 * wave + 16 * gr + mrow;
+#pragma unroll
+        for (int pr = 0; pr < NT / 2; ++pr) {
+            const int i0 = NT == 4 ? pr : 0, i1 = NT == 4 ? pr + 2 : 1;
+            const int lt = pass_tile<NT>(ch, i0);
+            const int jt = D == 128 ? 2 * h + lt : lt;
+            const f32x4 r01 = lds_load<f32x4>(sRot + 2 * (16 * jt + 4 * g));
+            const f32x4 r23 = lds_load<f32x4>(sRot + 2 * (16 * jt + 4 * g) + 4);
+            const float rh[4] = {r01[0], r01[2], r23[0], r23[2]};
+            const float rl[4] = {r01[1], r01[3], r23[1], r23[3]};
+            float cs[4], sn[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rope_cs(posf[gr], rh[e], rl[e], cs[e], sn[e]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rope_rotate(acc[gr][i0], acc[gr][i1], e, cs[e], sn[e]);
+        }
+    }
+}
+
+// End of pass h of a chunk starting at column col0: RoPE on key columns, then the rows'
+// store.
+template <int D, typename OutT, int NT>
+__device__ inline void finish_rows(f32x4 (&acc)[2][NT], const float* sRot, const float (&posf)[2], int h, int col0,
+                                   bool rope, int tt0, int m, int b, int W2, OutT* __restrict__ out, int ch, int tg) {
+    if (rope) pass_rope<D, NT>(acc, sRot, posf, h, ch);
+    const int lane = threadIdx.x & 63, g = lane >> 4, mrow = lane & 15;
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr) {
+        const int t = tt0 + 32 * tg + 16 * gr + mrow;
         if (t < m) {
             OutT* o = out + ((size_t)b * m + t) * W2 + col0 + 4 * g;
 #pragma unroll
-            for (int lt = 0; lt < 4; ++lt)
-                store_row4<OutT>(o + 16 * chunk_tile<D>(h, lt), acc[gr][lt][0], acc[gr][lt][1], acc[gr][lt][2],
-                                 acc[gr][lt][3]);
+            for (int i = 0; i < NT; ++i)
+                store_row4<OutT>(o + 16 * chunk_tile<D>(h, pass_tile<NT>(ch, i)), acc[gr][i][0], acc[gr][i][1],
+                                 acc[gr][i][2], acc[gr][i][3]);
         }
     }
 }
@@ -511,10 +575,15 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
     load_ahead(wa, 0, 0, 0, 0);
     load_ahead(wb, 0, 0, 0, 1);
 
-    token_table<D>(sSlot, sKd, sPos, sRot, idx, m, b, tt0, tm.grp == 0, self_slot, ref_idx, top_k, cap_ref, cap_tok,
-                   theta, err);
     f16x8 zf[2][NKS];
-    latent_frags<NKS, BITS>(zf, idx, m, b, tt0, self_slot, codes, code_bytes, scale, zmin, cap_tok);
+    {
+        TileSetup<NKS, BITS> su;
+        su.theta_ = theta;
+        su.index(idx, m, b, tt0, tid >> 6);
+        su.fetch(self_slot, ref_idx, top_k, codes, code_bytes, scale, zmin, b, cap_tok);
+        su.template table<D>(sSlot, sKd, sPos, sRot, m, cap_ref, cap_tok, top_k, tm.grp == 0, err);
+        su.latents(zf, m, cap_tok);
+    }
 
     // ---- stages 0 and 1 into LDS slots 0 and 1, stages 2 and 3 into the registers
     store_w(wa, 0);
@@ -523,12 +592,12 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
     load_ahead(wb, 0, 0, 0, 3);
     __syncthreads();
     float posf[2];
-    lane_positions(posf, sPos);
-    const MeanForm mf = mean_form(sKd);
+    lane_positions(posf, sPos, tid >> 6);
+    const MeanForm mf = mean_form(sKd, tid >> 6);
 
-    // ---- reference slices of a pass -> LDS buffer (pass % 2), in the layout finish_pass
+    // ---- reference slices of a pass -> LDS buffer (pass % 2), in the layout pass_mean
     // reads. Thread t moves slices 256 u + t (u = 0..7): row 64 u + t / 4, tile t % 4;
-    // they travel through registers two stages ahead like W_d.
+    // they travel through registers, stored one stage after their fetch.
     auto load_ref = [&](int c, int h, int u) -> uint4 {
         c = min(c, nchunks - 1);  // past the end: any readable slice (never used)
         const int r = 64 * u + (tid >> 2), q = r >> 7, tk = r & (dt::TT - 1);
@@ -542,9 +611,10 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
         const int r = 64 * u + (tid >> 2);
         *reinterpret_cast<uint4*>(sRef + buf * dt::kRefBuf + r * dt::kHalf + 16 * ((tid & 3) ^ ((r >> 2) & 3))) = v;
     };
-    // slices of the next pass fetched in stage k of a pass (all 8 spread over the stages)
-    constexpr int NP = (rr::kPieces + KST - 1) / KST;
-    auto piece_lo = [](int k) { return rr::kPieces * k / KST; };
+    // slices of the next pass fetched in stages 0 .. KST - 2 of a pass (all 8 spread over
+    // them) and stored one stage later, so a pass's slices are in LDS when it starts
+    constexpr int NP = (rr::kPieces + KST - 2) / (KST - 1);
+    auto piece_lo = [](int k) { return rr::kPieces * k / (KST - 1); };
 
     // the set-up tables in the reference buffers are read; pass 0's slices go in directly
     __syncthreads();
@@ -575,19 +645,19 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
     for (int c = 0; c < nchunks; ++c) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            // pass p = 2 c + h; its slices are in buffer h, the next pass's go to 1 - h
-#pragma unroll
-            for (int gr = 0; gr < 2; ++gr)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[gr][i] = zero4();
+            // pass p = 2 c + h; its slices are in buffer h (stored by the previous pass, the
+            // last of them before its final barrier), the next pass's go to 1 - h
+            if (mf.fused) pass_mean<true, 4>(acc, sRef + h * dt::kRefBuf, mf, 0, tid >> 6);
+            else pass_mean<false, 4>(acc, sRef + h * dt::kRefBuf, mf, 0, tid >> 6);
 #pragma unroll
             for (int k = 0; k < KST; ++k) {
                 // stage x: fragments of stage x + 1 (resident since the last barrier); stage
                 // x + 2 registers -> LDS and stage x + 4 -> those registers; the slices
-                // fetched two stages ago -> LDS and the next ones -> those registers
+                // fetched in the stage before -> LDS and the next ones -> the other registers
                 Frag (&cur)[2][4] = (k % 2 == 0) ? fa : fb;
                 Frag (&nxt)[2][4] = (k % 2 == 0) ? fb : fa;
                 uint4 (&rg)[NP] = (k % 2 == 0) ? ra : rb;
+                uint4 (&rp)[NP] = (k % 2 == 0) ? rb : ra;
                 const int s1 = slot == 2 ? 0 : slot + 1, s2 = slot == 0 ? 2 : slot - 1;
                 read_frags(nxt, s1);
                 if (k % 2 == 0) {
@@ -598,20 +668,19 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
                     load_ahead(wb, c, h, k, 4);
                 }
                 {
-                    // slices fetched in stage k - 2 (of this pass, or of the previous one)
-                    const bool prev = k < 2;
-                    const int kf = prev ? k + KST - 2 : k - 2;
-                    const bool have = !prev || c > 0 || h > 0;
-                    if (have) {
+                    // the next pass's slices: those fetched in stage k - 1 -> LDS, stage k's
+                    // share -> registers (past the last pass: any readable slices, never read)
+                    if (k >= 1) {
 #pragma unroll
                         for (int u = 0; u < NP; ++u)
-                            if (piece_lo(kf) + u < piece_lo(kf + 1))
-                                store_ref(rg[u], prev ? h : 1 - h, piece_lo(kf) + u);
+                            if (piece_lo(k - 1) + u < piece_lo(k)) store_ref(rp[u], 1 - h, piece_lo(k - 1) + u);
                     }
                     const int cn = c + h, hn = 1 - h;  // the next pass
+                    if (k + 1 < KST) {
 #pragma unroll
-                    for (int u = 0; u < NP; ++u)
-                        if (piece_lo(k) + u < piece_lo(k + 1)) rg[u] = load_ref(cn, hn, piece_lo(k) + u);
+                        for (int u = 0; u < NP; ++u)
+                            if (piece_lo(k) + u < piece_lo(k + 1)) rg[u] = load_ref(cn, hn, piece_lo(k) + u);
+                    }
                 }
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh) {
@@ -625,11 +694,9 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
                 slot = s1;
                 lds_barrier();
             }
-            // ---- pass (c, h) done (one branch per pass on the mean's form)
+            // ---- pass (c, h) done
             const int col0 = n0 + dt::kCols * c;
-            const unsigned char* R = sRef + h * dt::kRefBuf;
-            if (mf.fused) finish_pass<D, true, OutT>(acc, R, sRot, posf, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
-            else finish_pass<D, false, OutT>(acc, R, sRot, posf, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
+            finish_rows<D, OutT, 4>(acc, sRot, posf, h, col0, col0 < dk, tt0, m, b, W2, out, 0, tid >> 6);
         }
     }
 }
@@ -639,10 +706,39 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
 // no registers are staged and no VALU converts, and every wait on those loads is
 // counted here. W_d: a ring of NST stages of 64 rows x 64 latent values, each 8 blocks of
 // 16 rows x 32 values (1 KB) in the chunk-swizzled layout of rkv_pipe.h; stage x is
-// issued NST stages ahead into the slot stage x - NST used. Reference slices: one buffer,
-// fetched at the start of each pass (after the previous pass's epilogue has read it).
+// issued NST stages ahead into the slot stage x - NST used. Reference slices: two buffers
+// (pass h of a chunk reads buffer h); a pass's slices are fetched at the start of the pass
+// before it, so the gather has a whole pass to land.
+//
+// Eight wavefronts, two per SIMD: wavefront w takes the tile's tokens 32 (w % 4) .. + 32
+// (token group tg) and, of a pass's four 16-column tiles, the column half ch = w / 4
+// (local tiles ch and ch + 2, one RoPE pair). The two wavefronts of a SIMD hold the same
+// latent fragments and different columns, so LDS reads per stage equal a four-wavefront
+// layout's, while each SIMD has two independent instruction streams: with one per SIMD
+// the fragment reads and the pass epilogue run at their latency, not their throughput.
+namespace w8 {
+constexpr int kThreads = 2 * dt::kThreads;
+}
+
+// L2 warm-up of a run's W_d rows (run_bytes at run): the workgroups of an XCD (the
+// hardware places workgroup i on XCD i % 8) take one share each, so every XCD's L2 holds
+// the run before its passes ask for it; without it, after other work has cycled the
+// caches, each stage's first request goes to HBM, whose latency the W_d ring cannot cover.
+// NL loads of 1 KB per wavefront (NW wavefronts) land in the LDS sink, which the caller
+// does not read before younger loads overwrite it.
+template <int NL, int NW>
+__device__ inline void warm_w(const char* run, size_t run_bytes, unsigned char* sink) {
+    const int lane = threadIdx.x & 63, wv = wave_id();
+    const int J = max(1, (int)((gridDim.x + 7) >> 3));
+    const size_t share = (run_bytes + J - 1) / J;
+    const size_t first = (size_t)((blockIdx.x >> 3) % J) * share;
+#pragma unroll
+    for (int u = 0; u < NL; ++u)
+        dma16(run + min(first + (size_t)(NW * u + wv) * 1024 + 16 * lane, run_bytes - 16), sink + 1024 * wv);
+}
+constexpr int kWarm = 8;  // warm-up loads per wavefront of the restore (64 KB per workgroup)
 template <int NKS, int D, int BITS, typename OutT>
-__global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
+__global__ __launch_bounds__(w8::kThreads) void decode_tiles_dl_kernel(
     const int* __restrict__ idx, int m, TileMapArgs ta, const fp8_t* __restrict__ ref_vals, const int* __restrict__ self_slot,
     const int* __restrict__ ref_idx, const uint8_t* __restrict__ codes, size_t code_bytes,
     const f16_t* __restrict__ scale, const f16_t* __restrict__ zmin, const f16_t* __restrict__ w16, int W2, int dk,
@@ -650,7 +746,7 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
     constexpr int d_c = 32 * NKS;
     constexpr int KST = d_c / kStageK;  // W_d stages per pass
     constexpr int NST = dl::NST;
-    static_assert(KST >= 2 && 2 * KST < 64, "stage shape");
+    static_assert(KST >= 2 && 2 * KST + 3 < 64 && NST + 6 + kWarm < 64, "stage shape");
     static_assert(D == 64 || D == 128, "head dimension");
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char* sW = smem + dl::kOffW;
@@ -668,46 +764,29 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
     const int nchunks = tm.nchunks;
     const fp8_t* pool = ref_vals + (size_t)b * cap_ref * W2;
 
-    // stage (c, h, k) -> slot ((2 c + h) KST + k) % NST. Wave w fills blocks w and w + 4
-    // (block 2 lt + kh: row group lt = local MFMA tile, K half kh); lane l fetches row
-    // l / 4, chunk swz(l / 4, l % 4). rowoff[h][u]: the lane's output column in pass h.
-    const int wv = wave_id(), lr = lane >> 2;
-    int rowoff[2][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) rowoff[h][u] = 16 * chunk_tile<D>(h, (wv + 4 * u) >> 1) + lr;
-    const f16_t* wbase = w16 + (size_t)n0 * d_c + 8 * swz(lr, lane & 3);
+    const int wv = wave_id(), tg = wv & 3, ch = wv >> 2, lr = lane >> 2;
+    // stage (c, h, k) -> slot ((2 c + h) KST + k) % NST. Wave w fills block w = 2 lt + kh
+    // (row group lt = local MFMA tile, K half kh); lane l fetches row l / 4, chunk
+    // swz(l / 4, l % 4). rowoff[h]: the lane's output column in pass h.
+    const int rowoff[2] = {16 * chunk_tile<D>(0, wv >> 1) + lr, 16 * chunk_tile<D>(1, wv >> 1) + lr};
+    const f16_t* wbase = w16 + (size_t)n0 * d_c + 8 * swz(lr, lane & 3) + 32 * (wv & 1);
     auto issue_w = [&](int c, int h, int k, int slot) {
         c = min(c, nchunks - 1);  // past the end: any readable stage (never used)
-        unsigned char* dst = sW + slot * dl::kWStage;
-        const f16_t* src = wbase + (size_t)dt::kCols * c * d_c + k * kStageK;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int blk = wv + 4 * u;
-            dma16(src + (size_t)rowoff[h][u] * d_c + 32 * (blk & 1), dst + 1024 * blk);
-        }
+        dma16(wbase + ((size_t)dt::kCols * c + rowoff[h]) * d_c + k * kStageK, sW + slot * dl::kWStage + 1024 * wv);
     };
-    // slices of pass p: DMA j (wave w issues 8 w .. + 8) fills rows 16 j .. + 16; lane l
-    // fills row 16 j + l / 4 at 16-byte position l % 4 with its tile (l % 4) ^ ((row / 4) % 4)
-    const uint8_t* zero = g_zero_slice;
-    auto issue_refs = [&](int c, int h) {
-        const int col = n0 + dt::kCols * c;
-        int sl[8];
+    // slices of a pass: DMA j (wave w issues 4 w .. + 4) fills rows 16 j .. + 16, i.e. slot
+    // q = w / 2 of tokens 16 (j % 8) .. + 16; lane l fills row 16 j + l / 4 at 16-byte
+    // position l % 4 with its tile ts = (l % 4) ^ ((row / 4) % 4). The tile's column offset
+    // splits into a part of the pass, 16 chunk_tile(h, 0), and a part of the lane; rsrc[u]
+    // holds the lane's slot row plus that lane part (null: an empty slot, read from the
+    // zero slice), set once the token table is built.
+    const int ts_l = (lane & 3) ^ ((lr >> 2) & 3);
+    const uint8_t* zsrc = g_zero_slice + 16 * ts_l;
+    const uint8_t* rsrc[4];
+    auto issue_refs = [&](int c, int h, unsigned char* buf) {
+        const size_t off = (size_t)n0 + dt::kCols * c + 16 * chunk_tile<D>(h, 0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int r = 16 * (8 * wv + u) + lr;
-            sl[u] = sSlot[(r & (dt::TT - 1)) * dt::kRefs + (r >> 7)];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int j = 8 * wv + u, r = 16 * j + lr;
-            const int ts = (lane & 3) ^ ((r >> 2) & 3);
-            const uint8_t* src = sl[u] >= 0 ? reinterpret_cast<const uint8_t*>(pool) + (size_t)sl[u] * W2 + col +
-                                                  16 * chunk_tile<D>(h, ts)
-                                            : zero + 16 * ts;
-            dma16(src, sRef + 1024 * j);
-        }
+        for (int u = 0; u < 4; ++u) dma16(rsrc[u] ? rsrc[u] + off : zsrc, buf + 1024 * (4 * wv + u));
     };
     // stage (c, h, k) + d of the run
     auto ahead = [](int c, int h, int k, int d, int& c2, int& h2) {
@@ -724,69 +803,102 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
         const int k2 = ahead(0, 0, 0, d, c2, h2);
         issue_w(c2, h2, k2, d);
     }
-    token_table<D>(sSlot, sKd, sPos, sRot, idx, m, b, tt0, tm.grp == 0, self_slot, ref_idx, top_k, cap_ref, cap_tok,
-                   theta, err);
     f16x8 zf[2][NKS];
-    latent_frags<NKS, BITS>(zf, idx, m, b, tt0, self_slot, codes, code_bytes, scale, zmin, cap_tok);
-    __syncthreads();
+    TileSetup<NKS, BITS> su;
+    su.theta_ = theta;
+    su.index(idx, m, b, tt0, tg);
+    su.fetch(self_slot, ref_idx, top_k, codes, code_bytes, scale, zmin, b, cap_tok);
+    su.template table<D>(sSlot, sKd, sPos, sRot, m, cap_ref, cap_tok, top_k, tm.grp == 0, err);
+    // (no workgroup fence here or below: it would wait for every load in flight)
+    lds_barrier();
+    // slices of the first pass, as soon as the slot table stands (they follow every W_d
+    // stage of the prologue; the latents' loads may still be in flight)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int sl = sSlot[(16 * (4 * (wv & 1) + u) + lr) * dt::kRefs + (wv >> 1)];
+        const int lane_tile = chunk_tile<D>(0, ts_l) - chunk_tile<D>(0, 0);
+        rsrc[u] = sl >= 0 ? reinterpret_cast<const uint8_t*>(pool) + (size_t)sl * W2 + 16 * lane_tile : nullptr;
+    }
+    issue_refs(0, 0, sRef);
+    // the second slice buffer is the warm-up's sink: the slices of pass 1 (younger loads,
+    // so they land later) overwrite it before anything reads it
+    {
+        const char* run = reinterpret_cast<const char*>(w16 + (size_t)n0 * d_c);
+        warm_w<kWarm, 8>(run, (size_t)nchunks * dt::kCols * d_c * 2, sRef + dt::kRefBuf);
+    }
+    su.latents(zf, m, cap_tok);
     float posf[2];
-    lane_positions(posf, sPos);
-    const MeanForm mf = mean_form(sKd);
-    // the set-up table in the reference buffer is read; W_d stages 0 .. NST - 1 landed
-    wait_vmcnt<0>();
-    __syncthreads();
+    lane_positions(posf, sPos, tg);
+    const MeanForm mf = mean_form(sKd, tg);
+    // W_d stages 0 .. NST - 1 and the set-up's loads have landed once at most the first
+    // pass's 4 slice loads and the warm-up's are in flight; the barrier makes every
+    // wavefront's stages visible
+    wait_vmcnt<4 + kWarm>();
+    lds_barrier();
 
-    // one K-step of W_d fragments (4 tiles)
+    // one K-step of this wavefront's W_d fragments (its 2 tiles)
     typedef typename Mma<f16_t>::frag Frag;
-    auto read_frags = [&](Frag (&f)[4], int slot, int kh) {
+    auto read_frags = [&](Frag (&f)[2], int slot, int kh) {
         const char* sp = reinterpret_cast<const char*>(sW + slot * dl::kWStage);
 #pragma unroll
-        for (int lt = 0; lt < 4; ++lt) f[lt] = Op16<64>::frag<f16_t>(sp, lt, kh);
+        for (int i = 0; i < 2; ++i) f[i] = Op16<64>::frag<f16_t>(sp, pass_tile<2>(ch, i), kh);
     };
-    auto mma = [&](f32x4 (&acc)[2][4], const Frag (&f)[4], int ks) {
+    auto mma = [&](f32x4 (&acc)[2][2], const Frag (&f)[2], int ks) {
 #pragma unroll
-        for (int lt = 0; lt < 4; ++lt) {
-            acc[0][lt] = Mma<f16_t>::step(acc[0][lt], f[lt], zf[0][ks]);
-            acc[1][lt] = Mma<f16_t>::step(acc[1][lt], f[lt], zf[1][ks]);
+        for (int i = 0; i < 2; ++i) {
+            acc[0][i] = Mma<f16_t>::step(acc[0][i], f[i], zf[0][ks]);
+            acc[1][i] = Mma<f16_t>::step(acc[1][i], f[i], zf[1][ks]);
         }
     };
-    // Per stage x (K-steps 0 and 1, fragments f0 and f1):
+    // Per pass: wait for its slices (fetched a pass ahead), barrier, the reference mean into
+    // the accumulators, then the stages. Per stage x (K-steps 0 and 1, fragments f0, f1):
     //   read f1(x) | MFMA f0(x) | wait stage x + 1, barrier | read f0(x + 1) | MFMA f1(x) |
     //   f0(x + 1) in registers, then refill slot x with stage x + NST (and, in a pass's
-    //   first stage, fetch its reference slices).
+    //   first stage, fetch the next pass's reference slices).
     // The direct loads go out right after an explicit wait on the fragment reads: the
     // compiler treats a pending direct load as an access to both LDS and memory and turns
     // its next wait on LDS reads into a full one, so none of its waits may fall behind one.
-    Frag f0[4], f1[4];
+    Frag f0[2], f1[2];
     read_frags(f0, 0, 0);
     int slot = 0;
 
-    f32x4 acc[2][4];
+    f32x4 acc[2][2];
     for (int c = 0; c < nchunks; ++c) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int gr = 0; gr < 2; ++gr)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[gr][i] = zero4();
+            const bool first = c == 0 && h == 0;
+            // this pass's slices: issued at the start of the previous pass (by the set-up for
+            // the first, followed by the warm-up), followed by that pass's later W_d stages (1
+            // load each)
+            if (first) wait_vmcnt<kWarm>();
+            else wait_vmcnt<KST - 1>();
+            lds_barrier();
+            if (mf.fused) pass_mean<true, 2>(acc, sRef + h * dt::kRefBuf, mf, ch, tg);
+            else pass_mean<false, 2>(acc, sRef + h * dt::kRefBuf, mf, ch, tg);
 #pragma unroll
             for (int k = 0; k < KST; ++k) {
                 read_frags(f1, slot, 1);
                 mma(acc, f0, 2 * k);
-                // the four fragment reads go out before the eight MFMAs that cover them
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                // the two fragment reads go out before the four MFMAs that cover them
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
                 __builtin_amdgcn_sched_barrier(0);
-                // stage x + 1 must have landed: the loads issued after it are stages x + 2 ..
-                // x + NST - 1 and, from the pass's second stage on, its 8 reference loads
-                if (k >= 1 && k <= NST - 1) wait_vmcnt<2 * (NST - 2) + 8>();
-                else wait_vmcnt<2 * (NST - 2)>();
+                // stage x + 1 must have landed. Issued after it (per wavefront): stages x + 2
+                // .. x + NST - 1 (1 load each) and, from a pass's second stage on, the 4 slice
+                // loads of its first stage; in the first pass also the set-up's slice and
+                // warm-up loads (stage x + 1 < NST came with the prologue), so there stage 0
+                // counts 4 + kWarm more and stages 1 .. NST - 2 count 8 + kWarm more. A count
+                // below the true one only waits longer.
+                if (first && k == 0) wait_vmcnt<NST - 2 + 4 + kWarm>();
+                else if (first && k <= NST - 2) wait_vmcnt<NST - 2 + 8 + kWarm>();
+                else if (k >= 1 && k <= NST - 1) wait_vmcnt<NST - 2 + 4>();
+                else wait_vmcnt<NST - 2>();
                 lds_barrier();
                 const int next = slot + 1 == NST ? 0 : slot + 1;
                 read_frags(f0, next, 0);
                 mma(acc, f1, 2 * k + 1);
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
                 __builtin_amdgcn_sched_barrier(0);
                 wait_lgkm0();
                 {
@@ -794,21 +906,16 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_dl_kernel(
                     const int k2 = ahead(c, h, k, NST, c2, h2);
                     issue_w(c2, h2, k2, slot);
                 }
-                if (k == 0) issue_refs(c, h);
+                // the next pass's slices go to the other buffer, last read by the mean at
+                // the previous pass's start; past the last pass they reload the last chunk's
+                // into a buffer nobody reads, which keeps the counts uniform
+                if (k == 0) issue_refs(h == 0 ? c : min(c + 1, nchunks - 1), 1 - h, sRef + (1 - h) * dt::kRefBuf);
                 __builtin_amdgcn_sched_barrier(0);
                 slot = next;
             }
-            // ---- pass (c, h) done: its reference slices have landed once at most the
-            // W_d loads issued after them (2 per later stage of the pass) are in flight
-            wait_vmcnt<2 * (KST - 1)>();
-            lds_barrier();
+            // ---- pass (c, h) done: RoPE on key columns, then the rows' store
             const int col0 = n0 + dt::kCols * c;
-            if (mf.fused)
-                finish_pass<D, true, OutT>(acc, sRef, sRot, posf, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
-            else
-                finish_pass<D, false, OutT>(acc, sRef, sRot, posf, h, col0, col0 < dk, mf, tt0, m, b, W2, out);
-            // the slices are read: the next pass may refill the buffer
-            lds_barrier();
+            finish_rows<D, OutT, 2>(acc, sRot, posf, h, col0, col0 < dk, tt0, m, b, W2, out, ch, tg);
         }
     }
 }
@@ -842,8 +949,8 @@ struct L {
     static constexpr int kPP = dt::TT + 8;       // f16 pitch of a weight row
     static constexpr int kNH = D == 64 ? 2 : 1;  // KV heads of a unit
     static constexpr int kOffW = 0;
-    static constexpr int kOffRef = kOffW + NST * dl::kWStage;
-    static constexpr int kOffSlot = kOffRef + dt::kRefBuf;
+    static constexpr int kOffRef = kOffW + NST * dl::kWStage;  // two pass buffers (pass h: buffer h)
+    static constexpr int kOffSlot = kOffRef + 2 * dt::kRefBuf;
     static constexpr int kOffKd = kOffSlot + dt::TT * dt::kRefs * 4;
     static constexpr int kOffRot = kOffKd + dt::TT * 4;
     // keys of the pass [TT][kKP] bf16, or values of the pass transposed [64][kVP] f16
@@ -873,7 +980,7 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
     constexpr int d_c = 32 * NKS;
     constexpr int KST = d_c / kStageK;
     constexpr int NST = Ly::NST;
-    static_assert(KST >= 2 && 2 * KST < 64, "stage shape");
+    static_assert(KST >= 2 && 4 * KST + 6 < 64 && 2 * NST + 12 < 64, "stage shape");
     static_assert(D == 64 || D == 128, "head dimension");
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char* sW = smem + Ly::kOffW;
@@ -921,24 +1028,14 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
             dma16(src + (size_t)rowoff[h][u] * d_c + 32 * (blk & 1), dst + 1024 * blk);
         }
     };
-    const uint8_t* zero = g_zero_slice;
-    auto issue_refs = [&](int c, int h) {
-        const int col = chunk_col(c);
-        int sl[8];
+    // the reference slices as in decode_tiles_dl_kernel (rsrc set after the token table)
+    const int ts_l = (lane & 3) ^ ((lr >> 2) & 3);
+    const uint8_t* zsrc = g_zero_slice + 16 * ts_l;
+    const uint8_t* rsrc[8];
+    auto issue_refs = [&](int c, int h, unsigned char* buf) {
+        const size_t off = (size_t)chunk_col(c) + 16 * chunk_tile<D>(h, 0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int r = 16 * (8 * wv + u) + lr;
-            sl[u] = sSlot[(r & (dt::TT - 1)) * dt::kRefs + (r >> 7)];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int j = 8 * wv + u, r = 16 * j + lr;
-            const int ts = (lane & 3) ^ ((r >> 2) & 3);
-            const uint8_t* src = sl[u] >= 0 ? reinterpret_cast<const uint8_t*>(pool) + (size_t)sl[u] * W2 + col +
-                                                  16 * chunk_tile<D>(h, ts)
-                                            : zero + 16 * ts;
-            dma16(src, sRef + 1024 * j);
-        }
+        for (int u = 0; u < 8; ++u) dma16(rsrc[u] ? rsrc[u] + off : zsrc, buf + 1024 * (8 * wv + u));
     };
     auto ahead = [](int c, int h, int k, int d, int& c2, int& h2) {
         const int du = (k + d) / KST;
@@ -953,16 +1050,32 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
         const int k2 = ahead(0, 0, 0, d, c2, h2);
         issue_w(c2, h2, k2, d);
     }
-    token_table<D>(sSlot, sKd, sPos, sRot, idx, m, b, tt0, tm.grp == 0, self_slot, ref_idx, top_k, cap_ref, cap_tok,
-                   theta, err);
     f16x8 zf[2][NKS];
-    latent_frags<NKS, BITS>(zf, idx, m, b, tt0, self_slot, codes, code_bytes, scale, zmin, cap_tok);
-    __syncthreads();
+    TileSetup<NKS, BITS> su;
+    su.theta_ = theta;
+    su.index(idx, m, b, tt0, tid >> 6);
+    su.fetch(self_slot, ref_idx, top_k, codes, code_bytes, scale, zmin, b, cap_tok);
+    su.template table<D>(sSlot, sKd, sPos, sRot, m, cap_ref, cap_tok, top_k, tm.grp == 0, err);
+    // (no workgroup fence here or below: it would wait for every load in flight)
+    lds_barrier();
     float posf[2];
-    lane_positions(posf, sPos);
-    const MeanForm mf = mean_form(sKd);
-    wait_vmcnt<0>();
-    __syncthreads();
+    lane_positions(posf, sPos, tid >> 6);
+    const MeanForm mf = mean_form(sKd, tid >> 6);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int sl = sSlot[(16 * u + lr) * dt::kRefs + wv];
+        const int lane_tile = chunk_tile<D>(0, ts_l) - chunk_tile<D>(0, 0);
+        rsrc[u] = sl >= 0 ? reinterpret_cast<const uint8_t*>(pool) + (size_t)sl * W2 + 16 * lane_tile : nullptr;
+    }
+    // the token positions live in the first slice buffer: read by all before its fill
+    lds_barrier();
+    issue_refs(0, 0, sRef);
+    su.latents(zf, m, cap_tok);
+    // W_d stages 0 .. NST - 1 and the set-up's loads have landed once at most the first
+    // pass's 8 slice loads are in flight; the barrier makes every wavefront's stages visible
+    // (this kernel measured slower with the restore's W_d warm-up, so it has none)
+    wait_vmcnt<8>();
+    lds_barrier();
 
     typedef typename Mma<f16_t>::frag Frag;
     auto read_frags = [&](Frag (&f)[4], int slot, int kh) {
@@ -1131,10 +1244,14 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
     for (int c = 0; c < nchunks; ++c) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int gr = 0; gr < 2; ++gr)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[gr][i] = zero4();
+            const bool first = c == 0 && h == 0;
+            // this pass's slices: issued at the start of the previous pass (by the set-up for
+            // the first), followed by that pass's later W_d stages (2 loads each)
+            if (first) wait_vmcnt<0>();
+            else wait_vmcnt<2 * (KST - 1)>();
+            lds_barrier();
+            if (mf.fused) pass_mean<true, 4>(acc, sRef + h * dt::kRefBuf, mf, 0, wave);
+            else pass_mean<false, 4>(acc, sRef + h * dt::kRefBuf, mf, 0, wave);
 #pragma unroll
             for (int k = 0; k < KST; ++k) {
                 read_frags(f1, slot, 1);
@@ -1142,7 +1259,10 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
                 __builtin_amdgcn_sched_barrier(0);
-                if (k >= 1 && k <= NST - 1) wait_vmcnt<2 * (NST - 2) + 8>();
+                // counts as in decode_tiles_dl_kernel (2 W_d loads per stage, 8 per slice batch)
+                if (first && k == 0) wait_vmcnt<2 * (NST - 2) + 8>();
+                else if (first && k <= NST - 2) wait_vmcnt<2 * (NST - 2) + 16>();
+                else if (k >= 1 && k <= NST - 1) wait_vmcnt<2 * (NST - 2) + 8>();
                 else wait_vmcnt<2 * (NST - 2)>();
                 lds_barrier();
                 const int next = slot + 1 == NST ? 0 : slot + 1;
@@ -1157,17 +1277,14 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
                     const int k2 = ahead(c, h, k, NST, c2, h2);
                     issue_w(c2, h2, k2, slot);
                 }
-                if (k == 0) issue_refs(c, h);
+                if (k == 0) issue_refs(h == 0 ? c : min(c + 1, nchunks - 1), 1 - h, sRef + (1 - h) * dt::kRefBuf);
                 __builtin_amdgcn_sched_barrier(0);
                 slot = next;
             }
-            wait_vmcnt<2 * (KST - 1)>();
-            lds_barrier();
             const bool isK = (c & 1) == 0;
-            if (mf.fused) pass_values<D, true>(acc, sRef, sRot, posf, h, isK, mf);
-            else pass_values<D, false>(acc, sRef, sRot, posf, h, isK, mf);
+            if (isK) pass_rope<D, 4>(acc, sRot, posf, h, 0);
             attend_pass(acc, c, h);
-            // the slices and the staged values are read: the next pass may refill them
+            // the staged values are read: the next pass may refill them
             lds_barrier();
         }
     }
@@ -1275,7 +1392,7 @@ static hipError_t tiles_impl(const Shape& s, const CacheView& c, const int* idx,
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, dl::bytes);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, grid, dim3(dt::kThreads), dl::bytes, st, idx, m, ta,
+        hipLaunchKernelGGL(kern, grid, dim3(w8::kThreads), dl::bytes, st, idx, m, ta,
                            static_cast<const fp8_t*>(c.ref_vals), c.self_slot, c.ref_idx, c.codes, c.code_bytes,
                            static_cast<const f16_t*>(c.scale), static_cast<const f16_t*>(c.zmin),
                            static_cast<const f16_t*>(wd16), s.W2, s.dk, s.top_k, c.cap_ref, c.cap_tok, s.theta,
