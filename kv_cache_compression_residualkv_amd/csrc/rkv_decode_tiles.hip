@@ -924,18 +924,18 @@ __global__ __launch_bounds__(w8::kThreads) void decode_tiles_dl_kernel(
 // (review page section 2.7: the layer attends over the restored selected tokens.) A
 // workgroup takes a token tile and a run of "units": unit u is the K chunk u (columns
 // 128 u ..) and the V chunk u (columns d_k + 128 u ..), i.e. one KV head at D = 128 and
-// two at D = 64; the run does K u, V u, K u + 1, V u + 1, ... on the pipeline of
-// decode_tiles_dl_kernel. A pass's restored values (after the reference mean and, on
-// keys, RoPE) go to LDS in bf16, the precision the restored rows have in the unfused
-// path, instead of to memory:
-//   K pass: scores s[g][t] += q_g . K[t] over the pass's 64 columns, straight from the
-//           accumulators (a lane holds 16 of a token's columns; the four lanes of a token
-//           add their parts); when a head's key columns are done, the tile's softmax:
+// two at D = 64; the run does K u, V u, K u + 1, V u + 1, ... on the pipeline and with the
+// eight wavefronts of decode_tiles_dl_kernel. A pass's restored values (after the
+// reference mean and, on keys, RoPE) go to LDS in bf16, the precision the restored rows
+// have in the unfused path, instead of to memory:
+//   K pass: the keys to LDS [token][column]; the four wavefronts of column half 0 take
+//           the scores s[g][t] = q_g . K[t] of their 32 tokens on MFMA (query heads on the
+//           16-wide side); when a head's key columns are done, the tile's softmax:
 //           m = max_t scale s, p = exp(scale s - m), l = sum_t p (wave reductions, the
-//           four wavefronts through LDS);
-//   V pass: the values go to LDS in bf16 and o[g][d] = sum_t p[g][t] V[t][d] for the
-//           pass's 64 columns, a thread per (query head, 8 columns, 16 tokens) with
-//           16-byte reads, the 8 token groups added by shuffles.
+//           four token groups through LDS), p to LDS in fp16;
+//   V pass: the values to LDS transposed [column][token] in fp16 and o[g][d] =
+//           sum_t p[g][t] V[t][d] on MFMA: wavefront w takes 16 columns and half the
+//           tokens, the two halves added through LDS.
 // Each (tile, KV head, query head) leaves (o, m, l); attend_combine_kernel rescales the
 // tiles to the overall maximum and divides by the sum.
 namespace fa {
@@ -970,7 +970,7 @@ struct L {
 }  // namespace fa
 
 template <int NKS, int D, int BITS>
-__global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
+__global__ __launch_bounds__(w8::kThreads) void restore_attend_kernel(
     const int* __restrict__ idx, int m, TileMapArgs ta, const fp8_t* __restrict__ ref_vals,
     const int* __restrict__ self_slot, const int* __restrict__ ref_idx, const uint8_t* __restrict__ codes,
     size_t code_bytes, const f16_t* __restrict__ scale, const f16_t* __restrict__ zmin, const f16_t* __restrict__ w16,
@@ -980,7 +980,7 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
     constexpr int d_c = 32 * NKS;
     constexpr int KST = d_c / kStageK;
     constexpr int NST = Ly::NST;
-    static_assert(KST >= 2 && 4 * KST + 6 < 64 && 2 * NST + 12 < 64, "stage shape");
+    static_assert(KST >= 2 && 2 * KST + 3 < 64 && NST + 6 < 64, "stage shape");
     static_assert(D == 64 || D == 128, "head dimension");
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char* sW = smem + Ly::kOffW;
@@ -995,8 +995,8 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
     float* sRed = reinterpret_cast<float*>(smem + Ly::kOffRed);
     int* sPos = reinterpret_cast<int*>(smem + Ly::kOffPos);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int N = dk / D, nK = dk / dt::kCols;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int N = dk / D;
     const int Hq = N * G;
     // units play the part of the restore's chunks in the tile map (dk / 128 of them, as
     // restore_attend_impl built the grid)
@@ -1011,31 +1011,23 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
         return (c & 1) ? dk + dt::kCols * u : dt::kCols * u;
     };
 
-    const int wv = wave_id(), lr = lane >> 2;
-    int rowoff[2][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) rowoff[h][u] = 16 * chunk_tile<D>(h, (wv + 4 * u) >> 1) + lr;
-    const f16_t* wswz = w16 + 8 * swz(lr, lane & 3);
+    // the restore's layout and streams as in decode_tiles_dl_kernel: wavefront w takes token
+    // group tg = w % 4 and column half ch = w / 4 of each pass, fills W_d block w of every
+    // stage and 4 of the 32 slice blocks of every pass
+    const int wv = wave_id(), tg = wv & 3, ch = wv >> 2, lr = lane >> 2;
+    const int rowoff[2] = {16 * chunk_tile<D>(0, wv >> 1) + lr, 16 * chunk_tile<D>(1, wv >> 1) + lr};
+    const f16_t* wswz = w16 + 8 * swz(lr, lane & 3) + 32 * (wv & 1);
     auto issue_w = [&](int c, int h, int k, int slot) {
         c = min(c, nchunks - 1);  // past the end: any readable stage (never used)
-        unsigned char* dst = sW + slot * dl::kWStage;
-        const f16_t* src = wswz + (size_t)chunk_col(c) * d_c + k * kStageK;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int blk = wv + 4 * u;
-            dma16(src + (size_t)rowoff[h][u] * d_c + 32 * (blk & 1), dst + 1024 * blk);
-        }
+        dma16(wswz + ((size_t)chunk_col(c) + rowoff[h]) * d_c + k * kStageK, sW + slot * dl::kWStage + 1024 * wv);
     };
-    // the reference slices as in decode_tiles_dl_kernel (rsrc set after the token table)
     const int ts_l = (lane & 3) ^ ((lr >> 2) & 3);
     const uint8_t* zsrc = g_zero_slice + 16 * ts_l;
-    const uint8_t* rsrc[8];
+    const uint8_t* rsrc[4];
     auto issue_refs = [&](int c, int h, unsigned char* buf) {
         const size_t off = (size_t)chunk_col(c) + 16 * chunk_tile<D>(h, 0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) dma16(rsrc[u] ? rsrc[u] + off : zsrc, buf + 1024 * (8 * wv + u));
+        for (int u = 0; u < 4; ++u) dma16(rsrc[u] ? rsrc[u] + off : zsrc, buf + 1024 * (4 * wv + u));
     };
     auto ahead = [](int c, int h, int k, int d, int& c2, int& h2) {
         const int du = (k + d) / KST;
@@ -1053,17 +1045,17 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
     f16x8 zf[2][NKS];
     TileSetup<NKS, BITS> su;
     su.theta_ = theta;
-    su.index(idx, m, b, tt0, tid >> 6);
+    su.index(idx, m, b, tt0, tg);
     su.fetch(self_slot, ref_idx, top_k, codes, code_bytes, scale, zmin, b, cap_tok);
     su.template table<D>(sSlot, sKd, sPos, sRot, m, cap_ref, cap_tok, top_k, tm.grp == 0, err);
     // (no workgroup fence here or below: it would wait for every load in flight)
     lds_barrier();
     float posf[2];
-    lane_positions(posf, sPos, tid >> 6);
-    const MeanForm mf = mean_form(sKd, tid >> 6);
+    lane_positions(posf, sPos, tg);
+    const MeanForm mf = mean_form(sKd, tg);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int sl = sSlot[(16 * u + lr) * dt::kRefs + wv];
+    for (int u = 0; u < 4; ++u) {
+        const int sl = sSlot[(16 * (4 * (wv & 1) + u) + lr) * dt::kRefs + (wv >> 1)];
         const int lane_tile = chunk_tile<D>(0, ts_l) - chunk_tile<D>(0, 0);
         rsrc[u] = sl >= 0 ? reinterpret_cast<const uint8_t*>(pool) + (size_t)sl * W2 + 16 * lane_tile : nullptr;
     }
@@ -1072,28 +1064,27 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
     issue_refs(0, 0, sRef);
     su.latents(zf, m, cap_tok);
     // W_d stages 0 .. NST - 1 and the set-up's loads have landed once at most the first
-    // pass's 8 slice loads are in flight; the barrier makes every wavefront's stages visible
-    // (this kernel measured slower with the restore's W_d warm-up, so it has none)
-    wait_vmcnt<8>();
+    // pass's 4 slice loads are in flight; the barrier makes every wavefront's stages visible
+    wait_vmcnt<4>();
     lds_barrier();
 
     typedef typename Mma<f16_t>::frag Frag;
-    auto read_frags = [&](Frag (&f)[4], int slot, int kh) {
+    auto read_frags = [&](Frag (&f)[2], int slot, int kh) {
         const char* sp = reinterpret_cast<const char*>(sW + slot * dl::kWStage);
 #pragma unroll
-        for (int lt = 0; lt < 4; ++lt) f[lt] = Op16<64>::frag<f16_t>(sp, lt, kh);
+        for (int i = 0; i < 2; ++i) f[i] = Op16<64>::frag<f16_t>(sp, pass_tile<2>(ch, i), kh);
     };
-    auto mma = [&](f32x4 (&acc)[2][4], const Frag (&f)[4], int ks) {
+    auto mma = [&](f32x4 (&acc)[2][2], const Frag (&f)[2], int ks) {
 #pragma unroll
-        for (int lt = 0; lt < 4; ++lt) {
-            acc[0][lt] = Mma<f16_t>::step(acc[0][lt], f[lt], zf[0][ks]);
-            acc[1][lt] = Mma<f16_t>::step(acc[1][lt], f[lt], zf[1][ks]);
+        for (int i = 0; i < 2; ++i) {
+            acc[0][i] = Mma<f16_t>::step(acc[0][i], f[i], zf[0][ks]);
+            acc[1][i] = Mma<f16_t>::step(acc[1][i], f[i], zf[1][ks]);
         }
     };
 
     // queries of a unit, bf16 [kNH][G][kQP] (consecutive query heads share a KV head)
     auto stage_q = [&](int u) {
-        for (int e = tid; e < Ly::kNH * G * D; e += dt::kThreads) {
+        for (int e = tid; e < Ly::kNH * G * D; e += w8::kThreads) {
             const int r = e / D, d = e - r * D;  // r = hh G + g
             const int hq = Ly::kNH * u * G + r;
             reinterpret_cast<bf16_t*>(sQ)[r * Ly::kQP + d] = q[((size_t)b * Hq + hq) * D + d];
@@ -1105,10 +1096,13 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
     float* sMax = sRed;
     float* sSum = sRed + 32;
 
-    // The attention part of the end of pass (c, h), on MFMA: wavefront w takes its own 32
-    // tokens (two tiles of 16) in the scores and output columns 16 w .. + 16 of the pass in
-    // P V; the query heads are the 16-wide N side (columns G .. 15 unused).
-    auto attend_pass = [&](f32x4(&acc)[2][4], int c, int h) {
+    // The attention part of the end of pass (c, h), on MFMA. Every wavefront stages its own
+    // values (its 32 tokens, its 2 column tiles); the wavefronts of column half 0 then take
+    // the scores of their 32 tokens (two tiles of 16) and the softmax, and in P V wavefront w
+    // takes output columns 16 (w % 4) .. + 16 of the pass over the tokens 64 (w / 4) .. + 64,
+    // the two token halves added through the score buffer (free in value passes). The query
+    // heads are the 16-wide N side (columns G .. 15 unused).
+    auto attend_pass = [&](f32x4(&acc)[2][2], int c, int h) {
         const bool isK = (c & 1) == 0;
         const int u = u0 + (c >> 1);
         const int hh = D == 128 ? 0 : h;  // KV head of the unit in this pass
@@ -1117,87 +1111,94 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
         auto dim0 = [&](int lt) { return D == 128 ? 16 * chunk_tile<D>(h, lt) : 16 * lt; };
         const unsigned char* qrow = sQ + (hh * G) * Ly::kQP * 2;
         unsigned char* prow = sP + (hh * G) * Ly::kPP * 2;
+        const bool gv = mrow < G;
         if (isK) {
             // keys, rounded to bf16 as the restore writes them, to LDS [token][column]
 #pragma unroll
             for (int gr = 0; gr < 2; ++gr) {
-                unsigned char* row = sKV + (32 * wave + 16 * gr + mrow) * Ly::kKP * 2;
+                unsigned char* row = sKV + (32 * tg + 16 * gr + mrow) * Ly::kKP * 2;
 #pragma unroll
-                for (int lt = 0; lt < 4; ++lt) {
-                    const f32x2 lo = {acc[gr][lt][0], acc[gr][lt][1]}, hi = {acc[gr][lt][2], acc[gr][lt][3]};
+                for (int i = 0; i < 2; ++i) {
+                    const int lt = pass_tile<2>(ch, i);
+                    const f32x2 lo = {acc[gr][i][0], acc[gr][i][1]}, hi = {acc[gr][i][2], acc[gr][i][3]};
                     const bf16x2 x = __builtin_convertvector(lo, bf16x2), y = __builtin_convertvector(hi, bf16x2);
                     *reinterpret_cast<uint2*>(row + 2 * (16 * lt + 4 * g4)) =
                         make_uint2(*reinterpret_cast<const uint32_t*>(&x), *reinterpret_cast<const uint32_t*>(&y));
                 }
             }
             lds_barrier();
-            // scores S[t][g] = K[t] . q_g over the pass's 64 columns: 2 K-steps x 2 token tiles
             const bool first = D == 128 && h == 0;  // the head's first of two key passes
             const bool last = D == 64 || h == 1;    // the head's key columns all in
+            // lane: query head mrow, tokens 32 tg + 16 tl + 4 g4 + r
+            float* srow = sS + mrow * dt::TT + 32 * tg + 4 * g4;
             f32x4 st[2] = {zero4(), zero4()};
+            if (ch == 0) {
+                // scores S[t][g] = K[t] . q_g over the pass's 64 columns: 2 K-steps x 2 token tiles
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int lc = 32 * ks + 8 * g4;  // the lane's 8 columns of the K-step
-                const bf16x8 qb = lds_load<bf16x8>(qrow + mrow * Ly::kQP * 2 + 2 * (dim0(lc >> 4) + (lc & 15)));
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int lc = 32 * ks + 8 * g4;  // the lane's 8 columns of the K-step
+                    const bf16x8 qb = lds_load<bf16x8>(qrow + mrow * Ly::kQP * 2 + 2 * (dim0(lc >> 4) + (lc & 15)));
 #pragma unroll
-                for (int tl = 0; tl < 2; ++tl) {
-                    const bf16x8 kb = lds_load<bf16x8>(sKV + (32 * wave + 16 * tl + mrow) * Ly::kKP * 2 + 2 * lc);
-                    st[tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, st[tl], 0, 0, 0);
+                    for (int tl = 0; tl < 2; ++tl) {
+                        const bf16x8 kb =
+                            lds_load<bf16x8>(sKV + (32 * tg + 16 * tl + mrow) * Ly::kKP * 2 + 2 * lc);
+                        st[tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, st[tl], 0, 0, 0);
+                    }
                 }
-            }
-            // lane: query head mrow, tokens 32 w + 16 tl + 4 g4 + r
-            const bool gv = mrow < G;
-            float* srow = sS + mrow * dt::TT + 32 * wave + 4 * g4;
-            if (first) {
-                if (gv) {
+                if (first && gv) {
 #pragma unroll
                     for (int tl = 0; tl < 2; ++tl) *reinterpret_cast<f32x4*>(srow + 16 * tl) = st[tl];
                 }
             }
             if (last) {
-                if (D == 128 && gv) {
-#pragma unroll
-                    for (int tl = 0; tl < 2; ++tl) st[tl] += *reinterpret_cast<const f32x4*>(srow + 16 * tl);
-                }
                 // the tile's softmax per query head
-                float mxl = -INFINITY;
+                if (ch == 0) {
+                    if (D == 128 && gv) {
 #pragma unroll
-                for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const bool ok = gv && tt0 + 32 * wave + 16 * tl + 4 * g4 + r < m;
-                        st[tl][r] = ok ? st[tl][r] * qscale : -INFINITY;
-                        mxl = fmaxf(mxl, st[tl][r]);
+                        for (int tl = 0; tl < 2; ++tl) st[tl] += *reinterpret_cast<const f32x4*>(srow + 16 * tl);
                     }
-                mxl = fmaxf(mxl, __shfl_xor(mxl, 16, 64));
-                mxl = fmaxf(mxl, __shfl_xor(mxl, 32, 64));
-                if (g4 == 0 && gv) sMax[wave * 8 + mrow] = mxl;
-                lds_barrier();
-                const float mx = gv ? fmaxf(fmaxf(sMax[mrow], sMax[8 + mrow]), fmaxf(sMax[16 + mrow], sMax[24 + mrow]))
-                                    : 0.f;
-                float sum = 0.f;
-                f16_t pw[2][4];
+                    float mxl = -INFINITY;
 #pragma unroll
-                for (int tl = 0; tl < 2; ++tl)
+                    for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float p = st[tl][r] == -INFINITY ? 0.f : expf(st[tl][r] - mx);
-                        sum += p;
-                        pw[tl][r] = (f16_t)p;
-                    }
-                if (gv) {
-#pragma unroll
-                    for (int tl = 0; tl < 2; ++tl) {
-                        const f16x2 a = {pw[tl][0], pw[tl][1]}, bq = {pw[tl][2], pw[tl][3]};
-                        *reinterpret_cast<uint2*>(prow + mrow * Ly::kPP * 2 + 2 * (32 * wave + 16 * tl + 4 * g4)) =
-                            make_uint2(*reinterpret_cast<const uint32_t*>(&a), *reinterpret_cast<const uint32_t*>(&bq));
-                    }
+                        for (int r = 0; r < 4; ++r) {
+                            const bool ok = gv && tt0 + 32 * tg + 16 * tl + 4 * g4 + r < m;
+                            st[tl][r] = ok ? st[tl][r] * qscale : -INFINITY;
+                            mxl = fmaxf(mxl, st[tl][r]);
+                        }
+                    mxl = fmaxf(mxl, __shfl_xor(mxl, 16, 64));
+                    mxl = fmaxf(mxl, __shfl_xor(mxl, 32, 64));
+                    if (g4 == 0 && gv) sMax[tg * 8 + mrow] = mxl;
                 }
-                sum += __shfl_xor(sum, 16, 64);
-                sum += __shfl_xor(sum, 32, 64);
-                if (g4 == 0 && gv) sSum[wave * 8 + mrow] = sum;
                 lds_barrier();
-                if (wave == 0 && g4 == 0 && gv) {
+                float mx = 0.f;
+                if (ch == 0) {
+                    mx = gv ? fmaxf(fmaxf(sMax[mrow], sMax[8 + mrow]), fmaxf(sMax[16 + mrow], sMax[24 + mrow])) : 0.f;
+                    float sum = 0.f;
+                    f16_t pw[2][4];
+#pragma unroll
+                    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float p = st[tl][r] == -INFINITY ? 0.f : expf(st[tl][r] - mx);
+                            sum += p;
+                            pw[tl][r] = (f16_t)p;
+                        }
+                    if (gv) {
+#pragma unroll
+                        for (int tl = 0; tl < 2; ++tl) {
+                            const f16x2 a = {pw[tl][0], pw[tl][1]}, bq = {pw[tl][2], pw[tl][3]};
+                            *reinterpret_cast<uint2*>(prow + mrow * Ly::kPP * 2 + 2 * (32 * tg + 16 * tl + 4 * g4)) =
+                                make_uint2(*reinterpret_cast<const uint32_t*>(&a),
+                                           *reinterpret_cast<const uint32_t*>(&bq));
+                        }
+                    }
+                    sum += __shfl_xor(sum, 16, 64);
+                    sum += __shfl_xor(sum, 32, 64);
+                    if (g4 == 0 && gv) sSum[tg * 8 + mrow] = sum;
+                }
+                lds_barrier();
+                if (wv == 0 && g4 == 0 && gv) {
                     float* ml = part_ml + ((((size_t)b * N + head) * ntiles + tile) * kAttendMaxG + mrow) * 2;
                     ml[0] = mx;
                     ml[1] = (sSum[mrow] + sSum[8 + mrow]) + (sSum[16 + mrow] + sSum[24 + mrow]);
@@ -1212,64 +1213,71 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
             f16_t* vt = reinterpret_cast<f16_t*>(sKV);
 #pragma unroll
             for (int gr = 0; gr < 2; ++gr) {
-                const int tk = 32 * wave + 16 * gr + mrow;
+                const int tk = 32 * tg + 16 * gr + mrow;
 #pragma unroll
-                for (int lt = 0; lt < 4; ++lt)
+                for (int i = 0; i < 2; ++i) {
+                    const int lt = pass_tile<2>(ch, i);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        vt[(16 * lt + 4 * g4 + e) * Ly::kVP + tk] = (f16_t)(float)(bf16_t)acc[gr][lt][e];
+                        vt[(16 * lt + 4 * g4 + e) * Ly::kVP + tk] = (f16_t)(float)(bf16_t)acc[gr][i][e];
+                }
             }
             lds_barrier();
-            // out^T[column][g] = sum_t V[t][column] P[g][t]: 4 K-steps of 32 tokens
+            // out^T[column][g] = sum_t V[t][column] P[g][t] over this wavefront's 2 K-steps of
+            // 32 tokens; lane: query head mrow, columns 16 tg + 4 g4 + r of the pass
             f32x4 o = zero4();
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const f16x8 va = lds_load<f16x8>(sKV + ((16 * wave + mrow) * Ly::kVP + 32 * ks + 8 * g4) * 2);
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int ks = 2 * ch + k2;
+                const f16x8 va = lds_load<f16x8>(sKV + ((16 * tg + mrow) * Ly::kVP + 32 * ks + 8 * g4) * 2);
                 const f16x8 pb = lds_load<f16x8>(prow + (mrow * Ly::kPP + 32 * ks + 8 * g4) * 2);
                 o = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o, 0, 0, 0);
             }
-            // lane: query head mrow, columns 16 w + 4 g4 + r of the pass
-            if (mrow < G) {
-                const int d = dim0(wave) + 4 * g4;
+            f32x4* red = reinterpret_cast<f32x4*>(sS) + tg * 64 + lane;
+            if (ch == 1) *red = o;
+            lds_barrier();
+            if (ch == 0 && gv) {
+                o += *red;
+                const int d = dim0(tg) + 4 * g4;
                 float* po = part_o + ((((size_t)b * N + head) * ntiles + tile) * kAttendMaxG + mrow) * D + d;
                 *reinterpret_cast<f32x4*>(po) = o;
             }
         }
     };
 
-    Frag f0[4], f1[4];
+    Frag f0[2], f1[2];
     read_frags(f0, 0, 0);
     int slot = 0;
-    f32x4 acc[2][4];
+    f32x4 acc[2][2];
     for (int c = 0; c < nchunks; ++c) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const bool first = c == 0 && h == 0;
             // this pass's slices: issued at the start of the previous pass (by the set-up for
-            // the first), followed by that pass's later W_d stages (2 loads each)
+            // the first), followed by that pass's later W_d stages (1 load each)
             if (first) wait_vmcnt<0>();
-            else wait_vmcnt<2 * (KST - 1)>();
+            else wait_vmcnt<KST - 1>();
             lds_barrier();
-            if (mf.fused) pass_mean<true, 4>(acc, sRef + h * dt::kRefBuf, mf, 0, wave);
-            else pass_mean<false, 4>(acc, sRef + h * dt::kRefBuf, mf, 0, wave);
+            if (mf.fused) pass_mean<true, 2>(acc, sRef + h * dt::kRefBuf, mf, ch, tg);
+            else pass_mean<false, 2>(acc, sRef + h * dt::kRefBuf, mf, ch, tg);
 #pragma unroll
             for (int k = 0; k < KST; ++k) {
                 read_frags(f1, slot, 1);
                 mma(acc, f0, 2 * k);
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
                 __builtin_amdgcn_sched_barrier(0);
-                // counts as in decode_tiles_dl_kernel (2 W_d loads per stage, 8 per slice batch)
-                if (first && k == 0) wait_vmcnt<2 * (NST - 2) + 8>();
-                else if (first && k <= NST - 2) wait_vmcnt<2 * (NST - 2) + 16>();
-                else if (k >= 1 && k <= NST - 1) wait_vmcnt<2 * (NST - 2) + 8>();
-                else wait_vmcnt<2 * (NST - 2)>();
+                // counts as in decode_tiles_dl_kernel without its warm-up
+                if (first && k == 0) wait_vmcnt<NST - 2 + 4>();
+                else if (first && k <= NST - 2) wait_vmcnt<NST - 2 + 8>();
+                else if (k >= 1 && k <= NST - 1) wait_vmcnt<NST - 2 + 4>();
+                else wait_vmcnt<NST - 2>();
                 lds_barrier();
                 const int next = slot + 1 == NST ? 0 : slot + 1;
                 read_frags(f0, next, 0);
                 mma(acc, f1, 2 * k + 1);
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
                 __builtin_amdgcn_sched_barrier(0);
                 wait_lgkm0();
                 {
@@ -1282,7 +1290,7 @@ __global__ __launch_bounds__(dt::kThreads) void restore_attend_kernel(
                 slot = next;
             }
             const bool isK = (c & 1) == 0;
-            if (isK) pass_rope<D, 4>(acc, sRot, posf, h, 0);
+            if (isK) pass_rope<D, 2>(acc, sRot, posf, h, ch);
             attend_pass(acc, c, h);
             // the staged values are read: the next pass may refill them
             lds_barrier();
@@ -1360,7 +1368,7 @@ static hipError_t restore_attend_impl(int G, const Shape& s, const CacheView& c,
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Ly::bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(dt::kThreads), Ly::bytes, st, idx, m, ta,
+    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(w8::kThreads), Ly::bytes, st, idx, m, ta,
                        static_cast<const fp8_t*>(c.ref_vals), c.self_slot, c.ref_idx, c.codes, c.code_bytes,
                        static_cast<const f16_t*>(c.scale), static_cast<const f16_t*>(c.zmin),
                        static_cast<const f16_t*>(wd16), s.W2, s.dk, s.top_k, c.cap_ref, c.cap_tok, s.theta,
