@@ -269,7 +269,8 @@ size_t rkv_prepared_decoder_bytes(const rkv_config* cfg);
 
 /* Prepare the linear decoder W_d (section 2.5, the f_d of the boxed equation) for the
  * restore: w_d_f16 receives w->w_d ([2 d_k, d_c] bf16) as fp16, in a device layout of
- * this library (each run of 8 latent values reordered for the restore's MFMA operand).
+ * this library (the runs of 8 latent values of a row permuted, and each reordered, for the
+ * restore's MFMA operand).
  * Every bf16 in the fp16 normal range converts exactly; smaller ones round toward zero.
  * w_d_f16: >= rkv_prepared_decoder_bytes(cfg) bytes of device memory, 16-byte aligned,
  * caller-owned; valid for as long as w_d is unchanged. Stream-ordered on `stream`.

@@ -173,15 +173,15 @@ __device__ constexpr int chunk_tile(int h, int lt) {
 // pair frequencies theta^(-2j/D) / (2 pi).
 //
 // Latents: this lane's two tokens (MFMA column groups of token group tg, tokens 32 tg ..
-// + 32 of the tile) as fp16 fragments of every K-step (zero for a reference token or an
-// invalid index).
+// + 32 of the tile) as fp16 fragments of every K-step in the latent order above (zero for
+// a reference token or an invalid index).
 template <int NKS, int BITS>
 struct TileSetup {
     typedef typename std::conditional<BITS == 16, u32x4, uint32_t>::type Word;
     int tt, tp, tss, tr[dt::kRefs];        // token table: thread tid % TT's token
     int lt[2], lp[2], lss[2];              // the lane's two latent tokens
     Word cw[2][NKS];                       // their code words (BITS 2 / 4) or fp16 values
-    uint32_t st2[2][NKS / 2], zm2[2][NKS / 2];  // their steps and minima (fp16 pairs)
+    uint32_t st[2][NKS / 4], zm[2][NKS / 4];  // their groups' steps and minima (fp16 bits)
 
     // a loaded value used here on every path: the compiler cannot sink its load into the
     // branch that needs it (with a wait of its own), so a round's loads share one wait
@@ -217,27 +217,45 @@ struct TileSetup {
 #pragma unroll
             for (int q = 0; q < dt::kRefs; ++q) tr[q] = ref_idx[ro * top_k + min(q, top_k - 1)];
         }
+        constexpr int d_c = 32 * NKS;
 #pragma unroll
         for (int gr = 0; gr < 2; ++gr) {
             const size_t ro = (size_t)b * cap_tok + min(max(lp[gr], 0), cap_tok - 1);
             lss[gr] = self_slot[ro];
             const uint8_t* rec = codes + ro * code_bytes;
             if constexpr (BITS == 16) {
-                // unquantized record: d_c fp16 values in latent order, 8 per lane and K-step
+                // unquantized record: d_c fp16 values in latent order; K-step ks of lane
+                // group g: values d_c / 4 g + 8 ks .. + 8
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) cw[gr][ks] = *reinterpret_cast<const u32x4*>(rec + 64 * ks + 16 * g);
+                for (int ks = 0; ks < NKS; ++ks)
+                    cw[gr][ks] = *reinterpret_cast<const u32x4*>(rec + (d_c / 2) * g + 16 * ks);
             } else {
+                if constexpr (BITS == 4) {
+                    // 8 codes of K-step ks in one word: the lane's NKS words are contiguous
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    if constexpr (BITS == 4) cw[gr][ks] = *reinterpret_cast<const uint32_t*>(rec + 16 * ks + 4 * g);
-                    else cw[gr][ks] = *reinterpret_cast<const uint16_t*>(rec + 8 * ks + 2 * g);
+                    for (int j = 0; j < NKS / 4; ++j) {
+                        const u32x4 w = *reinterpret_cast<const u32x4*>(rec + (d_c / 8) * g + 16 * j);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) cw[gr][4 * j + i] = w[i];
+                    }
+                } else {
+                    // 8 codes of K-step ks in 16 bits
+#pragma unroll
+                    for (int j = 0; j < NKS / 4; ++j) {
+                        const uint2 w = *reinterpret_cast<const uint2*>(rec + (d_c / 16) * g + 8 * j);
+                        cw[gr][4 * j + 0] = w.x & 0xFFFFu;
+                        cw[gr][4 * j + 1] = w.x >> 16;
+                        cw[gr][4 * j + 2] = w.y & 0xFFFFu;
+                        cw[gr][4 * j + 3] = w.y >> 16;
+                    }
                 }
-                const uint32_t* sp = reinterpret_cast<const uint32_t*>(scale + ro * NKS);
-                const uint32_t* zp = reinterpret_cast<const uint32_t*>(zmin + ro * NKS);
+                // the lane's quantizer groups (NKS / 4 g .. + NKS / 4)
+                const uint16_t* sp = reinterpret_cast<const uint16_t*>(scale + ro * NKS) + (NKS / 4) * g;
+                const uint16_t* zp = reinterpret_cast<const uint16_t*>(zmin + ro * NKS) + (NKS / 4) * g;
 #pragma unroll
-                for (int u = 0; u < NKS / 2; ++u) {
-                    st2[gr][u] = sp[u];
-                    zm2[gr][u] = zp[u];
+                for (int j = 0; j < NKS / 4; ++j) {
+                    st[gr][j] = sp[j];
+                    zm[gr][j] = zp[j];
                 }
             }
         }
@@ -314,8 +332,8 @@ struct TileSetup {
             } else {
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
-                    const uint32_t sh = (ks & 1) ? (st2[gr][ks >> 1] >> 16) : (st2[gr][ks >> 1] & 0xFFFFu);
-                    const uint32_t zh = (ks & 1) ? (zm2[gr][ks >> 1] >> 16) : (zm2[gr][ks >> 1] & 0xFFFFu);
+                    // K-step ks of lane group g lies in the lane's quantizer group ks / 4
+                    const uint32_t sh = st[gr][ks >> 2], zh = zm[gr][ks >> 2];
                     const uint32_t svp = enc ? (sh | (sh << 16)) : 0u, zvp = enc ? (zh | (zh << 16)) : 0u;
                     zf[gr][ks] = dequant8<BITS>(enc ? (uint32_t)cw[gr][ks] : 0u, *reinterpret_cast<const f16x2*>(&svp),
                                                 *reinterpret_cast<const f16x2*>(&zvp));
@@ -513,9 +531,16 @@ __device__ inline TileMap tile_map(const TileMapArgs& a, int W2) {
     return m;
 }
 
-// One workgroup per tile_map entry. NKS = d_c / 32 latent K-steps (step ks
-// covers latent coordinates 32 ks .. +32, i.e. quantizer group ks); D = head dimension;
-// BITS = 4 or 2 (quantized records) or 16 (fp16 latents).
+// One workgroup per tile_map entry. NKS = d_c / 32 latent K-steps of 32 coordinates; D =
+// head dimension; BITS = 4 or 2 (quantized records) or 16 (fp16 latents).
+//
+// Latent order of the contraction. In K-step ks the MFMA operand positions 8 g .. 8 g + 7
+// (lane group g = lane / 16) carry the latent coordinates d_c / 4 g + 8 ks .. + 8, in the
+// order 0 4 1 5 2 6 3 7 the nibble masks produce: lane group g walks through its own
+// quarter of the latent, so a lane's codes (and its NKS / 4 quantizer groups' steps and
+// minima) are contiguous in the record and load as a few wide reads. W_d's operand follows
+// the same map (the prepared copy stores it so, form 1 loads it so); the contraction is
+// unchanged.
 
 // ---- form 1: W_d as stored (bf16), converted in the workgroup ---------------------------
 template <int NKS, int D, int BITS, typename OutT>
@@ -556,7 +581,8 @@ __global__ __launch_bounds__(dt::kThreads) void decode_tiles_kernel(
         for (int u = 0; u < 2; ++u) {
             const int lr = 32 * u + (tid >> 3);
             const int col = n0 + dt::kCols * c + 16 * chunk_tile<D>(h, lr >> 4) + (lr & 15);
-            r[u] = *reinterpret_cast<const uint4*>(wd + (size_t)col * d_c + k * kStageK + 8 * wk8);
+            // LDS position 8 wk8 of stage k is K-step 2 k + wk8 / 4, lane group wk8 % 4
+            r[u] = *reinterpret_cast<const uint4*>(wd + (size_t)col * d_c + 8 * (NKS * (wk8 & 3) + 2 * k + (wk8 >> 2)));
         }
     };
     auto store_w = [&](const uint4 (&r)[2], int slot) {
@@ -1298,13 +1324,17 @@ __global__ __launch_bounds__(w8::kThreads) void restore_attend_kernel(
     }
 }
 
-// rkv_prepare_decoder: W_d bf16 -> fp16, each 8 latent values in the fragment order
-// 0 4 1 5 2 6 3 7 (the conversion form 1 applies in LDS, so both forms multiply the same
-// operands in the same order).
-__global__ void prepare_decoder_kernel(const uint4* __restrict__ wd, uint4* __restrict__ w16, size_t n8) {
+// rkv_prepare_decoder: W_d bf16 -> fp16 in the restore's latent order: octet 4 ks + g of a
+// row (K-step ks, lane group g) holds the row's latent octet NKS g + ks (coordinates d_c / 4
+// g + 8 ks .. + 8), its 8 values in the fragment order 0 4 1 5 2 6 3 7 (the conversion form
+// 1 applies in LDS, so both forms multiply the same operands in the same order).
+__global__ void prepare_decoder_kernel(const uint4* __restrict__ wd, uint4* __restrict__ w16, size_t n8, int nks) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n8) {
-        const f16x8 h = w_to_f16(wd[i]);
+        const size_t per_row = 4 * (size_t)nks;  // octets per row (d_c / 8)
+        const size_t row = i / per_row;
+        const int o = (int)(i - row * per_row);
+        const f16x8 h = w_to_f16(wd[row * per_row + (size_t)nks * (o & 3) + (o >> 2)]);
         w16[i] = *reinterpret_cast<const uint4*>(&h);
     }
 }
@@ -1479,7 +1509,7 @@ hipError_t launch_prepare_decoder(const Shape& s, const void* wd, void* wd16, hi
     const unsigned threads = 256;
     const size_t blocks = (n8 + threads - 1) / threads;
     hipLaunchKernelGGL(prepare_decoder_kernel, dim3((unsigned)blocks), dim3(threads), 0, st,
-                       static_cast<const uint4*>(wd), static_cast<uint4*>(wd16), n8);
+                       static_cast<const uint4*>(wd), static_cast<uint4*>(wd16), n8, s.d_c / 32);
     return hipGetLastError();
 }
 
