@@ -893,12 +893,13 @@ __global__ __launch_bounds__(w8::kThreads) void decode_tiles_dl_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const bool first = c == 0 && h == 0;
-            // this pass's slices: issued at the start of the previous pass (by the set-up for
-            // the first, followed by the warm-up), followed by that pass's later W_d stages (1
-            // load each)
-            if (first) wait_vmcnt<kWarm>();
-            else wait_vmcnt<KST - 1>();
-            lds_barrier();
+            // this pass's slices: the first pass's came with the set-up (followed by the
+            // warm-up's loads); a later pass's were waited for in the previous pass's last
+            // stage, whose barrier made them visible
+            if (first) {
+                wait_vmcnt<kWarm>();
+                lds_barrier();
+            }
             if (mf.fused) pass_mean<true, 2>(acc, sRef + h * dt::kRefBuf, mf, ch, tg);
             else pass_mean<false, 2>(acc, sRef + h * dt::kRefBuf, mf, ch, tg);
 #pragma unroll
@@ -915,7 +916,10 @@ __global__ __launch_bounds__(w8::kThreads) void decode_tiles_dl_kernel(
                 // warm-up loads (stage x + 1 < NST came with the prologue), so there stage 0
                 // counts 4 + kWarm more and stages 1 .. NST - 2 count 8 + kWarm more. A count
                 // below the true one only waits longer.
-                if (first && k == 0) wait_vmcnt<NST - 2 + 4 + kWarm>();
+                // The last stage also waits for the next pass's slices (issued in the first
+                // stage, followed by the W_d loads of stages 1 .. KST - 2).
+                if (k == KST - 1) wait_vmcnt<(KST - 2 < NST - 2 ? KST - 2 : NST - 2)>();
+                else if (first && k == 0) wait_vmcnt<NST - 2 + 4 + kWarm>();
                 else if (first && k <= NST - 2) wait_vmcnt<NST - 2 + 8 + kWarm>();
                 else if (k >= 1 && k <= NST - 1) wait_vmcnt<NST - 2 + 4>();
                 else wait_vmcnt<NST - 2>();
@@ -1279,11 +1283,12 @@ __global__ __launch_bounds__(w8::kThreads) void restore_attend_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const bool first = c == 0 && h == 0;
-            // this pass's slices: issued at the start of the previous pass (by the set-up for
-            // the first), followed by that pass's later W_d stages (1 load each)
-            if (first) wait_vmcnt<0>();
-            else wait_vmcnt<KST - 1>();
-            lds_barrier();
+            // this pass's slices: the first pass's came with the set-up; a later pass's were
+            // waited for in the previous pass's last stage, whose barrier made them visible
+            if (first) {
+                wait_vmcnt<0>();
+                lds_barrier();
+            }
             if (mf.fused) pass_mean<true, 2>(acc, sRef + h * dt::kRefBuf, mf, ch, tg);
             else pass_mean<false, 2>(acc, sRef + h * dt::kRefBuf, mf, ch, tg);
 #pragma unroll
@@ -1294,7 +1299,8 @@ __global__ __launch_bounds__(w8::kThreads) void restore_attend_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
                 __builtin_amdgcn_sched_barrier(0);
                 // counts as in decode_tiles_dl_kernel without its warm-up
-                if (first && k == 0) wait_vmcnt<NST - 2 + 4>();
+                if (k == KST - 1) wait_vmcnt<(KST - 2 < NST - 2 ? KST - 2 : NST - 2)>();
+                else if (first && k == 0) wait_vmcnt<NST - 2 + 4>();
                 else if (first && k <= NST - 2) wait_vmcnt<NST - 2 + 8>();
                 else if (k >= 1 && k <= NST - 1) wait_vmcnt<NST - 2 + 4>();
                 else wait_vmcnt<NST - 2>();
