@@ -33,6 +33,8 @@
 
 #include <algorithm>
 
+#include <type_traits>
+
 #include "rkv_device.h"
 #include "rkv_gemm.h"
 #include "rkv_internal.h"
@@ -832,49 +834,63 @@ __global__ __launch_bounds__(s2::kThreads) void search_ring_kernel(
             const float* m_nrm = reinterpret_cast<const float*>(mb + 1024);
             const int lim = count - blk * s2::BM;  // slots at this offset and beyond are past the pool
             uint32_t bk[2][8];
+            // The block's candidates as keys, best 8 per token. MASKED: with the causal mask
+            // and the pool's end; without it when every candidate is visible to every token
+            // of this wavefront (the block is full and its last slot, whose position is the
+            // block's largest, lies before the wavefront's earliest token).
+            auto block_keys = [&](auto masked) {
+                constexpr bool kMasked = decltype(masked)::value;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                // group g: slot tile st = g / 2, rows i = 2 (g % 2) + {0, 1}
-                const int st = g >> 1;
-                int pe[8];
-                float ne[8];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int i = 2 * (g & 1) + h;
-                    const int off = 64 * wq + 32 * st + 8 * i + 4 * hl;
-                    const i32x4 p4 = lds_load<i32x4>(m_pos + off);
-                    const f32x4 n4 = lds_load<f32x4>(m_nrm + off);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        pe[4 * h + j] = (off + j < lim) ? p4[j] : INT_MAX;
-                        ne[4 * h + j] = n4[j];
-                    }
-                }
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    uint32_t gk[8];
+                for (int g = 0; g < 4; ++g) {
+                    // group g: slot tile st = g / 2, rows i = 2 (g % 2) + {0, 1}
+                    const int st = g >> 1;
+                    int pe[8];
+                    float ne[8];
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int i = 2 * (g & 1) + h;
+                        const int off = 64 * wq + 32 * st + 8 * i + 4 * hl;
+                        const f32x4 n4 = lds_load<f32x4>(m_nrm + off);
+                        if constexpr (kMasked) {
+                            const i32x4 p4 = lds_load<i32x4>(m_pos + off);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int c = 4 * h + j;
-                            uint32_t hb = __float_as_uint(fmaf(-2.f, acc[st][tt][4 * i + j], ne[c]));
-                            hb ^= (uint32_t)((int)hb >> 31) | 0x80000000u;
-                            gk[c] = pe[c] < tokpos_l[tt] ? ((hb & ~31u) | (uint32_t)(8 * g + c)) : 0xFFFFFFFFu;
+                            for (int j = 0; j < 4; ++j) pe[4 * h + j] = (off + j < lim) ? p4[j] : INT_MAX;
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) ne[4 * h + j] = n4[j];
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        uint32_t gk[8];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int i = 2 * (g & 1) + h;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const int c = 4 * h + j;
+                                uint32_t hb = __float_as_uint(fmaf(-2.f, acc[st][tt][4 * i + j], ne[c]));
+                                hb ^= (uint32_t)((int)hb >> 31) | 0x80000000u;
+                                const uint32_t key = (hb & ~31u) | (uint32_t)(8 * g + c);
+                                if constexpr (kMasked) gk[c] = pe[c] < tokpos_l[tt] ? key : 0xFFFFFFFFu;
+                                else gk[c] = key;
+                            }
+                        }
+                        sort8_32(gk);
+                        if (g == 0) {
+#pragma unroll
+                            for (int qq = 0; qq < 8; ++qq) bk[tt][qq] = gk[qq];
+                        } else {
+                            merge8_32(bk[tt], gk);
                         }
                     }
-                    sort8_32(gk);
-                    if (g == 0) {
-#pragma unroll
-                        for (int qq = 0; qq < 8; ++qq) bk[tt][qq] = gk[qq];
-                    } else {
-                        merge8_32(bk[tt], gk);
-                    }
+                    // keep each group's LDS reads next to their use
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                // keep each group's LDS reads next to their use
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            };
+            const bool vis =
+                __all(lim >= s2::BM && m_pos[s2::BM - 1] < min(tokpos_l[0], tokpos_l[1]));
+            if (vis) block_keys(std::false_type{});
+            else block_keys(std::true_type{});
             // lane-local index x -> slot offset 64 wq + 4 (lane / 32) + 32 st + 8 i + j
             const uint32_t sbase = (uint32_t)(blk * s2::BM + 64 * wq + 4 * hl);
 #pragma unroll
