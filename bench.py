@@ -593,6 +593,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mean-projection", action="store_true",
+                    help="skip the mean-projection step (counter runs: only the default step's launches)")
     ap.add_argument("--select-frac", type=float, default=0.3, help="read fraction for the extra selected-restore rate")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (HBM counter calibration)")
@@ -702,7 +704,8 @@ def main() -> int:
     torch.cuda.synchronize()
     sel_ms = sel_ev[0].elapsed_time(sel_ev[1]) / 20
 
-    mproj = time_mean_projection(rkv, wl, W, kv, refp, encp, idx_all, out, n_ref, stream, args, new_events)
+    mproj = None if args.no_mean_projection else time_mean_projection(rkv, wl, W, kv, refp, encp, idx_all, out,
+                                                                          n_ref, stream, args, new_events)
 
     n_enc = int(encp.shape[1])
     work = algorithmic_work(wl, n_enc)
