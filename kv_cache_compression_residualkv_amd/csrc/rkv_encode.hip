@@ -614,10 +614,13 @@ __global__ __launch_bounds__(kGemmThreads) void latent_quant_kernel(const T* __r
 // bf16 formats: W_c3 projection + quantizer on the direct-to-LDS ring: 256 tokens x 256
 // latent columns per workgroup of 8 wavefronts (wave w: tokens 128 (w / 4) .., columns
 // 64 (w % 4) ..), so each dH row and each W_c3 row is streamed half as often as with
-// 128-wide tiles.
+// 128-wide tiles. dH (read once, from HBM) runs on a three-stage ring, W_c3 (the same
+// for every workgroup, from L2) on two, which fills the 160 KB of LDS (measured 0.120 ->
+// 0.115 ms at 28672 tokens x d_c = 512; the same split slowed the SwiGLU kernel, whose
+// W_c1 | W_c2 stream does not stay in L2).
 namespace g2r {
 constexpr int kThreads = 512;
-constexpr int BM = 256, BN = 256, NST = 2;
+constexpr int BM = 256, BN = 256, NA = 3, NB = 2;
 struct Cfg {
     static constexpr int BM = g2r::BM, BN = g2r::BN, WM = 128, WN = 64;
     static constexpr int kQP = BN * 2 + 16;
@@ -625,7 +628,7 @@ struct Cfg {
     static constexpr int kThreads = g2r::kThreads;
     static constexpr int kNWN = 4;
 };
-constexpr size_t kRing = (size_t)NST * (BM + BN) * kStageK * 2;
+constexpr size_t kRing = ((size_t)NA * BM + (size_t)NB * BN) * kStageK * 2;
 constexpr size_t bytes = kRing > Cfg::kEpi ? kRing : Cfg::kEpi;
 static_assert(bytes <= 160 * 1024, "LDS budget");
 }  // namespace g2r
@@ -699,7 +702,8 @@ __global__ __launch_bounds__(g2r::kThreads) void latent_quant_ring_kernel(
             for (int j = 0; j < 4; ++j) c[i][j] = Mma<bf16_t>::step(c[i][j], f.a[i], f.b[j]);
     };
     const int ns = Kp / kStageK;
-    ring_mainloop_lrp<g2r::NST, G2Frag, 12, 32>(la, lb, ns, ns, smem, load, mma, acc, [](int, f32x4(&)[8][4], bool) {});
+    ring_mainloop_split<g2r::NA, g2r::NB, G2Frag, 12, 32>(la, lb, ns, smem, smem + g2r::NA * Op16<g2r::BM, 8>::kStageBytes,
+                                                         load, mma, acc);
     __syncthreads();
     quant_epilogue<C, f16_t>(acc, smem_u8, t0, c0, b, n, d_c, bits, pos, cap_tok, codes, code_bytes, scale, zmin);
 }

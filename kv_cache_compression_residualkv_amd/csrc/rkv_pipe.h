@@ -201,4 +201,66 @@ __device__ inline void ring_mainloop_lrp(const LA& a, const LB& b, int n_stages,
     }
 }
 
+// ring_mainloop_lrp with a ring per operand: A NA stages deep, B NA - 1. For a product
+// whose A rows come from HBM once while every workgroup re-reads the same B (served by
+// L2), the extra A stage keeps NA - 1 stages of A in flight against HBM latency within
+// the same LDS. Per stage s (slots s mod NA for A, s mod NB for B):
+//   read f1(s) | MFMA f0(s) | wait for stage s + 1, barrier |
+//   issue B(s + NB), then A(s + NA) | read f0(s + 1) | MFMA f1(s)
+// Loads are issued as A(0) B(0) .. A(NB-1) B(NB-1) A(NB), then B(s + NB) A(s + NA) in the
+// middle of stage s, so when stage s + 1 is waited for only A(s + NA - 1) may still be in
+// flight behind it.
+template <int NA, int NB, class F, int IL_R, int IL_M, class LA, class LB, class Ld, class Mm, class Acc>
+__device__ inline void ring_mainloop_split(const LA& a, const LB& b, int n_stages, char* lds_a, char* lds_b,
+                                           Ld&& load, Mm&& mma, Acc& acc) {
+    static_assert(NB >= 2 && NA == NB + 1, "A one stage deeper than B");
+    constexpr int kA = LA::kStageBytes, kB = LB::kStageBytes;
+    if (n_stages <= 0) return;
+#pragma unroll
+    for (int p = 0; p < NB; ++p) {
+        if (p < n_stages) {
+            a.issue(p, lds_a + p * kA);
+            b.issue(p, lds_b + p * kB);
+        }
+    }
+    if (NB < n_stages) a.issue(NB, lds_a + NB * kA);
+    // stage 0 landed: behind it at most NB - 1 full stages and A(NB)
+    if (n_stages > NB)
+        wait_vmcnt<(NB - 1) * (LA::kLoads + LB::kLoads) + LA::kLoads>();
+    else
+        wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    F f0, f1;
+    load(f0, lds_a, lds_b, 0);
+    int ia = 0, ib = 0;
+    for (int s = 0; s + 1 < n_stages; ++s) {
+        const char* sa = lds_a + ia * kA;
+        const char* sb = lds_b + ib * kB;
+        load(f1, sa, sb, 1);
+        mma(f0, acc);
+        if constexpr (IL_R > 0) interleave_reads<IL_R, IL_M>();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_lgkm0();
+        if (s + NA - 1 < n_stages)
+            wait_vmcnt<LA::kLoads>();
+        else
+            wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (s + NB < n_stages) b.issue(s + NB, lds_b + ib * kB);
+        if (s + NA < n_stages) a.issue(s + NA, lds_a + ia * kA);
+        ia = ia + 1 == NA ? 0 : ia + 1;
+        ib = ib + 1 == NB ? 0 : ib + 1;
+        load(f0, lds_a + ia * kA, lds_b + ib * kB, 0);
+        mma(f1, acc);
+        if constexpr (IL_R > 0) interleave_reads<IL_R, IL_M>();
+    }
+    {
+        load(f1, lds_a + ia * kA, lds_b + ib * kB, 1);
+        mma(f0, acc);
+        mma(f1, acc);
+    }
+}
+
 }  // namespace rkv
