@@ -229,47 +229,6 @@ __device__ inline f32x4 zero4() {
     return z;
 }
 
-// Reductions within 16-lane segments (lanes sharing lane/16, one DPP row) on the DPP
-// crossbar, with no LDS traffic: swap neighbours (quad_perm [1,0,3,2]), swap pairs
-// (quad_perm [2,3,0,1]), then lane i of each half row with lane 7 - i (row_half_mirror)
-// and lane i of the row with lane 15 - i (row_mirror). After the two quad steps every
-// lane of a quad holds the quad's result; each mirror pairs every lane with one of the
-// other half, so the result ends in every lane of the segment.
-namespace dpp {
-constexpr int kSwap1 = 0xB1, kSwap2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
-template <int CTRL>
-__device__ inline uint32_t mov(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ inline float movf(float v) {
-    return __uint_as_float(mov<CTRL>(__float_as_uint(v)));
-}
-}  // namespace dpp
-__device__ inline float seg16_min(float v) {
-    v = fminf(v, dpp::movf<dpp::kSwap1>(v));
-    v = fminf(v, dpp::movf<dpp::kSwap2>(v));
-    v = fminf(v, dpp::movf<dpp::kHalfMirror>(v));
-    return fminf(v, dpp::movf<dpp::kMirror>(v));
-}
-__device__ inline float seg16_max(float v) {
-    v = fmaxf(v, dpp::movf<dpp::kSwap1>(v));
-    v = fmaxf(v, dpp::movf<dpp::kSwap2>(v));
-    v = fmaxf(v, dpp::movf<dpp::kHalfMirror>(v));
-    return fmaxf(v, dpp::movf<dpp::kMirror>(v));
-}
-// bitwise OR over the 8 lanes of each half row (lanes sharing lane/8)
-__device__ inline uint32_t seg8_or(uint32_t v) {
-    v |= dpp::mov<dpp::kSwap1>(v);
-    v |= dpp::mov<dpp::kSwap2>(v);
-    return v | dpp::mov<dpp::kHalfMirror>(v);
-}
-// bitwise OR over the 16 lanes of each row
-__device__ inline uint32_t seg16_or(uint32_t v) {
-    const uint32_t h = seg8_or(v);
-    return h | dpp::mov<dpp::kMirror>(h);
-}
-
 // s / k correctly rounded for the reference-mean sums: s is a sum of at most 8 FP8
 // e4m3fn values (a multiple of 2^-9, |s| <= 8 * 448) and k = 1..8. With rk = RN(1/k),
 // q = s rk and one FMA correction of the residual, q + (s - q k) rk (Markstein's
