@@ -237,7 +237,9 @@ rkv_status rkv_encode(const rkv_config* cfg, const rkv_weights* w, rkv_cache* ca
 /* rkv_encode with optional per-kernel timing, for profiling harnesses. `events` is
  * NULL or points to RKV_ENCODE_PHASES + 1 hipEvent_t handles (created by the caller);
  * events[i] is recorded on `stream` just before kernel i and events[RKV_ENCODE_PHASES]
- * after the last one. Everything else is exactly rkv_encode. */
+ * after the last one. A NULL entry is skipped (a recorded timing event leaves the GPU
+ * idle for a few microseconds, so a harness may mark only the kernels it times).
+ * Everything else is exactly rkv_encode. */
 rkv_status rkv_encode_ex(const rkv_config* cfg, const rkv_weights* w, rkv_cache* cache, const void* kv,
                          int32_t kv_len, const int32_t* rows, const int32_t* pos, int32_t n, void* workspace,
                          size_t workspace_bytes, void* stream, void* const* events);

@@ -371,8 +371,9 @@ def rkv_encode(cfg: CodecConfig, weights: CodecWeights, cache: CodecCache, kv: t
                pos: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None, events=None) -> torch.Tensor:
     """Encode tokens into residual records. Returns the workspace used (allocated if None).
 
-    events: optional sequence of RKV_ENCODE_PHASES + 1 raw hipEvent_t handles (ints);
-    when given, rkv_encode_ex records them between the encode's kernels."""
+    events: optional sequence of RKV_ENCODE_PHASES + 1 raw hipEvent_t handles (ints, or
+    None to skip that mark); when given, rkv_encode_ex records them between the encode's
+    kernels."""
     kv, rows, pos = _rows_pos(kv, rows, pos, cache.batch)
     n = rows.shape[1]
     need = rkv_encode_workspace_bytes(cfg, cache.batch, n, cache.cap_ref)

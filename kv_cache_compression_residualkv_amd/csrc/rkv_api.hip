@@ -199,7 +199,7 @@ rkv_status rkv_encode_ex(const rkv_config* cfg, const rkv_weights* w, rkv_cache*
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RKV_ERR_ALIGNMENT;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     auto mark = [&](int i) -> hipError_t {
-        return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) : hipSuccess;
+        return events && events[i] ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) : hipSuccess;
     };
     hipError_t e = mark(0);
     if (e == hipSuccess) e = launch_search(s, c, p, kv, kv_len, rows, pos, n, workspace, hs);
