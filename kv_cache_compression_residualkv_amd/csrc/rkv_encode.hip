@@ -669,11 +669,31 @@ struct Cfg {
     static constexpr size_t kEpi = qe_bytes(WM, WN, g2r::kThreads / 64);
     static constexpr int kThreads = g2r::kThreads;
     static constexpr int kNWN = 4;
+    static constexpr int NA = g2r::NA, NB = g2r::NB;
 };
 constexpr size_t kRing = ((size_t)NA * BM + (size_t)NB * BN) * kStageK * 2;
 constexpr size_t bytes = kRing > Cfg::kEpi ? kRing : Cfg::kEpi;
 static_assert(bytes <= 160 * 1024, "LDS budget");
 }  // namespace g2r
+
+// Narrow tiles for a last run of at most 128 latent columns (d_c = 384 after one 256-wide
+// tile, or d_c <= 128): 512 tokens x 128 columns, the same 128 x 64 block per wavefront
+// (wave w: tokens 128 (w / 2) .., columns 64 (w % 2) ..) and the same MFMA sequence per
+// output element, both operands on two-stage rings (160 KB). A 256-wide tile there would
+// compute as many padded columns as real ones.
+namespace g2n {
+constexpr int BM = 512, BN = 128;
+struct Cfg {
+    static constexpr int BM = g2n::BM, BN = g2n::BN, WM = 128, WN = 64;
+    static constexpr size_t kEpi = qe_bytes(WM, WN, g2r::kThreads / 64);
+    static constexpr int kThreads = g2r::kThreads;
+    static constexpr int kNWN = 2;
+    static constexpr int NA = 2, NB = 2;
+};
+constexpr size_t kRing = (size_t)Cfg::NA * (BM + BN) * kStageK * 2;
+constexpr size_t bytes = kRing > Cfg::kEpi ? kRing : Cfg::kEpi;
+static_assert(bytes <= 160 * 1024, "LDS budget");
+}  // namespace g2n
 
 // W_c3 rows as the B operand: stage s reads K columns ((s mod (d_ff / 64)) * 64), so
 // the three planes of dH (K' = 3 d_ff) each meet the same W_c3.
@@ -696,30 +716,26 @@ struct G2Frag {
     bf16x8 b[4];
 };
 
-__global__ __launch_bounds__(g2r::kThreads) void latent_quant_ring_kernel(
-    const bf16_t* __restrict__ dh, int n, const bf16_t* __restrict__ w3, int d_ff, int d_c, int bits,
-    const int* __restrict__ pos, int cap_tok, uint8_t* __restrict__ codes, size_t code_bytes, f16_t* __restrict__ scale,
-    f16_t* __restrict__ zmin, int MT, int NT, int per) {
-    typedef g2r::Cfg C;
-    extern __shared__ __align__(16) unsigned char smem_u8[];
+// One tile of the ring quantizer: tokens t0 .. t0 + BM, latent columns c0 .. c0 + BN.
+template <class C>
+__device__ inline void quant_ring_tile(unsigned char* smem_u8, const bf16_t* __restrict__ dh, int n,
+                                       const bf16_t* __restrict__ w3, int d_ff, int d_c, int bits,
+                                       const int* __restrict__ pos, int cap_tok, uint8_t* __restrict__ codes,
+                                       size_t code_bytes, f16_t* __restrict__ scale, f16_t* __restrict__ zmin, int b,
+                                       int t0, int c0) {
+    static_assert(C::WM == 128 && C::WN == 64 && C::kThreads / 64 == 8, "one 128 x 64 block per wavefront");
     char* smem = reinterpret_cast<char*>(smem_u8);
-    const int tile = xcd_tile(blockIdx.x, per);
-    if (tile >= MT * NT) return;
-    const int mt = tile / NT, nt = tile - mt * NT;
-    const int b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::kNWN, wn = wave % C::kNWN;
-    const int t0 = mt * g2r::BM;
-    const int c0 = nt * g2r::BN;
     const int Kp = 3 * d_ff;
 
     // rows past n / d_c repeat the last valid row; their results are not stored
-    Op16<g2r::BM, 8> la;
+    Op16<C::BM, 8> la;
     la.init([&](int r) { return dh + ((size_t)b * n + min(t0 + r, n - 1)) * Kp; });
-    WrapOp16<g2r::BN, 8> lb;
+    WrapOp16<C::BN, 8> lb;
     lb.nkm = d_ff / kStageK;
 #pragma unroll
-    for (int u = 0; u < WrapOp16<g2r::BN, 8>::kLoads; ++u) {
+    for (int u = 0; u < WrapOp16<C::BN, 8>::kLoads; ++u) {
         const int blk = wave + 8 * u;
         const int r = 16 * (blk >> 1) + (lane >> 2);
         lb.src[u] = reinterpret_cast<const char*>(w3 + (size_t)min(c0 + r, d_c - 1) * d_ff) + 64 * (blk & 1) +
@@ -733,9 +749,9 @@ __global__ __launch_bounds__(g2r::kThreads) void latent_quant_ring_kernel(
         for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
     auto load = [&](G2Frag& f, const char* sa, const char* sb, int ks) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) f.b[j] = Op16<g2r::BN, 8>::template frag<bf16_t>(sb, 4 * wn + j, ks);
+        for (int j = 0; j < 4; ++j) f.b[j] = Op16<C::BN, 8>::template frag<bf16_t>(sb, 4 * wn + j, ks);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f.a[i] = Op16<g2r::BM, 8>::template frag<bf16_t>(sa, 8 * wm + i, ks);
+        for (int i = 0; i < 8; ++i) f.a[i] = Op16<C::BM, 8>::template frag<bf16_t>(sa, 8 * wm + i, ks);
     };
     auto mma = [&](const G2Frag& f, f32x4(&c)[8][4]) {
 #pragma unroll
@@ -744,10 +760,42 @@ __global__ __launch_bounds__(g2r::kThreads) void latent_quant_ring_kernel(
             for (int j = 0; j < 4; ++j) c[i][j] = Mma<bf16_t>::step(c[i][j], f.a[i], f.b[j]);
     };
     const int ns = Kp / kStageK;
-    ring_mainloop_split<g2r::NA, g2r::NB, G2Frag, 12, 32>(la, lb, ns, smem, smem + g2r::NA * Op16<g2r::BM, 8>::kStageBytes,
+    if constexpr (C::NA == C::NB + 1)
+        ring_mainloop_split<C::NA, C::NB, G2Frag, 12, 32>(la, lb, ns, smem, smem + C::NA * Op16<C::BM, 8>::kStageBytes,
                                                          load, mma, acc);
+    else
+        ring_mainloop_lrp<C::NA, G2Frag, 12, 32>(la, lb, ns, ns, smem, load, mma, acc,
+                                                 [](int, f32x4(&)[8][4], bool) {});
     __syncthreads();
     quant_epilogue<C, f16_t>(acc, smem_u8, t0, c0, b, n, d_c, bits, pos, cap_tok, codes, code_bytes, scale, zmin);
+}
+
+// The ring quantizer over all latent columns. Logical tiles come in groups of a 512-token
+// block: its 256-wide tiles (nw column tiles for each 256-token half, the last one padded
+// when the columns left after them exceed 128) and then, when at most 128 columns are left,
+// one narrow tile of the whole block over them. The XCD-grouped order puts a group on one
+// XCD at the same time, so the tiles of a token block stream its dH planes together
+// through that XCD's L2 (a separate launch of the narrow tiles re-read them from HBM).
+__global__ __launch_bounds__(g2r::kThreads) void latent_quant_ring_kernel(
+    const bf16_t* __restrict__ dh, int n, const bf16_t* __restrict__ w3, int d_ff, int d_c, int bits,
+    const int* __restrict__ pos, int cap_tok, uint8_t* __restrict__ codes, size_t code_bytes, f16_t* __restrict__ scale,
+    f16_t* __restrict__ zmin, int ngroups, int nw, int narrow, int per) {
+    extern __shared__ __align__(16) unsigned char smem_u8[];
+    const int per_group = 2 * nw + narrow;
+    const int tile = xcd_tile(blockIdx.x, per);
+    if (tile >= ngroups * per_group) return;
+    const int g = tile / per_group, k = tile - g * per_group;
+    const int b = blockIdx.y;
+    if (k < 2 * nw) {
+        const int half = k / nw, nt = k - half * nw;
+        const int t0 = g * g2n::BM + half * g2r::BM;
+        if (t0 >= n) return;
+        quant_ring_tile<g2r::Cfg>(smem_u8, dh, n, w3, d_ff, d_c, bits, pos, cap_tok, codes, code_bytes, scale, zmin, b,
+                                  t0, nt * g2r::BN);
+    } else {
+        quant_ring_tile<g2n::Cfg>(smem_u8, dh, n, w3, d_ff, d_c, bits, pos, cap_tok, codes, code_bytes, scale, zmin, b,
+                                  g * g2n::BM, nw * g2r::BN);
+    }
 }
 
 // ---- few tokens per sequence: one-wavefront tiles on deep rings --------------------------
@@ -1280,19 +1328,24 @@ static hipError_t latent_impl(const Shape& s, const CacheView& c, const EncodePl
 
 static hipError_t latent_ring_impl(const Shape& s, const CacheView& c, const EncodePlan& p, const int* pos, int n,
                                    const void* w3, void* ws, hipStream_t st) {
-    const size_t smem = g2r::bytes;
+    static_assert(g2n::BM == 2 * g2r::BM, "a 512-token group holds two 256-token tiles");
+    constexpr size_t smem = g2r::bytes > g2n::bytes ? g2r::bytes : g2n::bytes;
     auto kern = latent_quant_ring_kernel;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
+    // 256-wide column tiles over whole runs of 256 latent columns; a last run of at most
+    // 128 columns goes to the narrow tiles (192 stays on a padded 256-wide tile)
+    const int rem = s.d_c % g2r::BN;
+    const int narrow = (rem > 0 && rem <= g2n::BN) ? 1 : 0;
+    const int nw = narrow ? s.d_c / g2r::BN : (s.d_c + g2r::BN - 1) / g2r::BN;
+    const int ngroups = (n + g2n::BM - 1) / g2n::BM;
+    const int per = xcd_per(ngroups * (2 * nw + narrow));
     char* w = static_cast<char*>(ws);
-    const int MT = (n + g2r::BM - 1) / g2r::BM;
-    const int NT = (s.d_c + g2r::BN - 1) / g2r::BN;
-    const int per = xcd_per(MT * NT);
     hipLaunchKernelGGL(kern, dim3(8 * per, c.B), dim3(g2r::kThreads), smem, st,
                        reinterpret_cast<const bf16_t*>(w + p.off_dh), n, static_cast<const bf16_t*>(w3), s.d_ff, s.d_c,
                        s.bits, pos, c.cap_tok, c.codes, c.code_bytes, static_cast<f16_t*>(c.scale),
-                       static_cast<f16_t*>(c.zmin), MT, NT, per);
+                       static_cast<f16_t*>(c.zmin), ngroups, nw, narrow, per);
     return hipGetLastError();
 }
 
