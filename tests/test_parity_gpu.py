@@ -98,6 +98,9 @@ CASES = {
     "qwen-table1-dc384-int2": (4, dict(T=1600, d_ff=3072, d_c=384)),
     "qwen-table1-dc384-int4-batch2": (4, dict(T=700, d_ff=3072, d_c=384, bits=4, batch=2)),
     "qwen32b-table1-dff4096": (2, dict(T=800, d_ff=4096)),
+    # d_c = 128: the quantizer's narrow 512-token x 128-column tiles alone (no 256-wide
+    # tile), 4 latent K-steps in the restore
+    "llama-shape-dc128": (2, dict(T=1300, d_c=128)),
     # head_dim 64 in the bf16 formats (16 KV heads x 64: the 2048-wide joint vector, RoPE
     # pairs (j, j + 32), the restore's 64-column passes)
     "d64-bf16-int4": (2, dict(T=1100, n_kv_heads=16, head_dim=64)),
@@ -194,9 +197,11 @@ def test_streaming_equals_bulk_and_is_deterministic():
 
 def test_few_token_calls_equal_bulk_batched():
     """Calls with at most 4 tokens per sequence (pool scan, one-wavefront GEMMs) write the
-    same records as one bulk call (tiled search and GEMMs), batch of 3, INT4 and INT2, and
-    at Table I's Qwen2.5-7B codec shape (d_c = 384, d_ff = 3072)."""
-    for wid, T, bits, over in ((5, 300, 4, {}), (4, 400, 2, {}), (4, 260, 2, dict(d_ff=3072, d_c=384))):
+    same records as one bulk call (tiled search and GEMMs), batch of 3, INT4 and INT2, at
+    Table I's Qwen2.5-7B codec shape (d_c = 384, d_ff = 3072: 256-wide and narrow quantizer
+    tiles) and at d_c = 128 (narrow quantizer tiles alone)."""
+    for wid, T, bits, over in ((5, 300, 4, {}), (4, 400, 2, {}), (4, 260, 2, dict(d_ff=3072, d_c=384)),
+                               (5, 300, 4, dict(d_c=128))):
         wl = workload(wid, T=T, batch=3, bits=bits, **over)
         W = wl.make_weights()
         _banner(f"few-token calls vs bulk: wid={wid} T={T} B=3 bits={bits}")
