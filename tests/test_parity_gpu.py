@@ -101,6 +101,9 @@ CASES = {
     # d_c = 128: the quantizer's narrow 512-token x 128-column tiles alone (no 256-wide
     # tile), 4 latent K-steps in the restore
     "llama-shape-dc128": (2, dict(T=1300, d_c=128)),
+    # d_c = 64 in the bf16 formats: narrow quantizer tiles with half their columns past d_c,
+    # and the restore's general kernel (the token-tile restore takes multiples of 128)
+    "llama-shape-dc64": (2, dict(T=900, d_c=64)),
     # head_dim 64 in the bf16 formats (16 KV heads x 64: the 2048-wide joint vector, RoPE
     # pairs (j, j + 32), the restore's 64-column passes)
     "d64-bf16-int4": (2, dict(T=1100, n_kv_heads=16, head_dim=64)),
