@@ -480,7 +480,8 @@ __device__ inline float round_scalar<f16_t>(float v) { return (float)(f16_t)v; }
 // whole group in registers: min and max, one step division, the codes and their packing
 // in the record's byte order (dword d of a 4-bit group: columns 8d .. 8d + 7 at bits 4e;
 // of a 2-bit group: columns 16d .. 16d + 15 at bits 2e), written with one 16- or 8-byte
-// store. No workgroup barrier: a wavefront's LDS operations complete in order.
+// store (fp16 latents: four 16-byte stores). No workgroup barrier: a wavefront's LDS
+// operations complete in order.
 
 // Codes of a group: rint((v - zmin) / step) clamped to [0, levels], decided on the IEEE
 // fp32 quotient. x r (r = v_rcp_f32(step), 1 ulp) is within 2^-18 of that quotient wherever
